@@ -1,0 +1,173 @@
+/*
+ * mamba_ssm.h -- C-ABI of the MI355X (gfx950) Mamba-1 selective-scan hot path.
+ *
+ * Sources: docs.rs source pages of the mamba-rs crate:
+ *   [prefill.rs]   mamba-rs 0.6.4, src/mamba_ssm/gpu/prefill.rs   (prefill_body stages F4a-F4d)
+ *   [inference.rs] mamba-rs 0.5.1, src/mamba_ssm/gpu/inference.rs (GpuInferenceState; the f32
+ *                  step chain F4-F10; the mixed step chain's fused kernels)
+ * The pages give launch sites and argument lists; the update rule is the Mamba-1 selective
+ * SSM (zero-order hold on A, Euler on B):
+ *   delta = softplus(dt + dt_bias),  A = -exp(A_log)
+ *   h[n]  = exp(delta*A[n]) * h[n] + delta * B[n] * u
+ *   y     = (sum_n C[n]*h[n] + D*u) * silu(z)
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Every tensor pointer is a DEVICE pointer owned by the caller. The library allocates
+ *    nothing, never synchronizes, and never reads device memory on the host, so every call
+ *    can be captured into a HIP graph. `stream` is a hipStream_t (NULL = default stream);
+ *    all work is enqueued on it.
+ *  - I/O tensors (x, u, dt, B, C, z, y) share one element type, `io_dtype`: f32 or bf16.
+ *    Small parameters (conv_w, conv_b, dt_bias, A_log, D) and both recurrent states are
+ *    always f32, whatever io_dtype is ([inference.rs] mixed-precision engine: norms, biases,
+ *    a_log, D and conv weights stay f32; the recurrent state stays f32).
+ *  - Sizes are element counts; row strides are in elements of io_dtype.
+ *  - Recurrent state layout follows GpuInferenceState ([inference.rs]): per layer,
+ *    conv state [B][D][K] (d_conv slots, the last K raw inputs, oldest first) and SSM state
+ *    [B][D][N] (n fastest). A caller holding [layer][...] arenas passes base + layer offset.
+ *  - Errors: every argument is validated before anything is enqueued. A non-zero status
+ *    returns with nothing enqueued, and mamba_last_error() (thread-local) names the call
+ *    and the argument. Launch failures return MAMBA_EHIP with the HIP error text.
+ *    Device faults surface at the caller's next synchronization.
+ *  - Empty work: B == 0, D == 0 or (for the prefill calls) T == 0 is valid and leaves
+ *    every output untouched, except that a T == 0 scan with distinct in/out state pointers
+ *    copies ssm_state_in (or zeros) to ssm_state_out.
+ *  - Supported: 1 <= N <= 64, 1 <= K <= 8. N or K outside that returns MAMBA_EUNSUPPORTED
+ *    (never a silent early return).
+ */
+#ifndef MAMBA_SSM_H
+#define MAMBA_SSM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MAMBA_OK = 0,
+  MAMBA_EINVAL = 1,       /* bad pointer, size, stride, alignment or aliasing  */
+  MAMBA_EUNSUPPORTED = 2, /* N or K beyond what the kernels are built for     */
+  MAMBA_EWORKSPACE = 3,   /* workspace missing or smaller than required      */
+  MAMBA_EHIP = 4          /* a HIP runtime call or kernel launch failed       */
+} mamba_status;
+
+typedef enum { MAMBA_F32 = 0, MAMBA_BF16 = 1 } mamba_dtype;
+
+/* Thread-local description of the last failure on this thread ("" if none). */
+const char* mamba_last_error(void);
+
+/* Library version string. */
+const char* mamba_version(void);
+
+/*
+ * Prefill causal depthwise conv1d + SiLU over T tokens, carrying the conv state.
+ * [prefill.rs] prefill_body F4a: the tiled conv reads the x lane strided out of the
+ * in_proj output, applies the d_conv taps and bias, fuses SiLU, and reads then
+ * updates the persistent conv state. [inference.rs] GpuInferenceState: d_conv slots.
+ *
+ * Per channel (b, d), with the window X = [conv_state[b,d,0..K-1], x[b,0..T-1,d]]:
+ *   u[b,t,d]        = silu(conv_b[d] + sum_k conv_w[d,k] * X[t+1+k])
+ *   conv_state[b,d,:] <- X[T..T+K-1]   (the last K entries of the window)
+ * The last tap (k = K-1) multiplies the current token.
+ *
+ *   x            in   [B,T,*] io_dtype; element (b,t,d) at x[(b*T+t)*x_row_stride + d];
+ *                     x_row_stride >= D (2*D when x is the lane of an in_proj output).
+ *   conv_w       in   [D,K] f32.             conv_b  in  [D] f32, or NULL for zero bias.
+ *   conv_state   in/out [B,D,K] f32, updated in place; NULL = zero history, not written.
+ *   u            out  [B,T,D] io_dtype, contiguous; must not overlap any input.
+ */
+mamba_status mamba_conv1d_fwd(const void* x, int64_t x_row_stride, const float* conv_w,
+                              const float* conv_b, float* conv_state, void* u,
+                              mamba_dtype io_dtype, int B, int T, int D, int K, void* stream);
+
+/*
+ * Bytes of device workspace mamba_selective_scan_fwd needs for this shape (may be 0).
+ * The workspace carries chunk summaries between the kernels of one call; its contents
+ * on entry do not matter and are garbage on exit.
+ */
+size_t mamba_selective_scan_workspace_size(int B, int T, int D, int N);
+
+/*
+ * Prefill selective scan over T tokens: takes the carried SSM state and returns it.
+ * [prefill.rs] prefill_body F4c (delta = softplus of the dt_proj output plus bias) and
+ * F4d (the scan over all T, its y gated by silu(z) read from the in_proj output at a
+ * row stride, the final state written to the persistent SSM state, which prefill never
+ * zeroes); [inference.rs] GpuMambaInference::new (A = -exp(A_log) per layer).
+ *
+ * Per channel (b, d), h[n] starting from ssm_state_in[b,d,n]:
+ *   delta = softplus(dt[b,t,d] + dt_bias[d])   (delta_softplus != 0)
+ *         = dt[b,t,d] + dt_bias[d]             (delta_softplus == 0)
+ *   h[n]  = exp(delta * A[n]) * h[n] + delta * Bm[b,t,n] * u[b,t,d],  A[n] = -exp(A_log[d,n])
+ *   y[b,t,d] = (sum_n Cm[b,t,n]*h[n] + D_skip[d]*u[b,t,d]) * silu(z[b,t,d])
+ *   ssm_state_out[b,d,n] = h[n] after the last token
+ *
+ *   u, dt        in   [B,T,D] io_dtype, contiguous.
+ *   dt_bias      in   [D] f32, or NULL for zero.
+ *   A_log        in   [D,N] f32 (any values; no structure is assumed).
+ *   Bm, Cm       in   io_dtype; row (b,t) starts at (b*T+t)*bc_row_stride; n = 0..N-1 are
+ *                     the first N elements of the row (bc_row_stride >= N; e.g. B and C as
+ *                     column blocks of an x_proj output row).
+ *   D_skip       in   [D] f32, or NULL for zero.
+ *   z            in   io_dtype, element (b,t,d) at z[(b*T+t)*z_row_stride + d]
+ *                     (z_row_stride >= D), or NULL for no gate (y = the ungated value).
+ *   ssm_state_in in   [B,D,N] f32, or NULL for a zero initial state.
+ *   ssm_state_out out [B,D,N] f32, or NULL; may equal ssm_state_in (update in place) but
+ *                     must not partially overlap it.
+ *   y            out  [B,T,D] io_dtype, contiguous; must not overlap any input.
+ *   workspace    scratch of at least mamba_selective_scan_workspace_size(B,T,D,N) bytes,
+ *                256-byte aligned (NULL allowed when that size is 0).
+ */
+mamba_status mamba_selective_scan_fwd(const void* u, const void* dt, const float* dt_bias,
+                                      int delta_softplus, const float* A_log, const void* Bm,
+                                      const void* Cm, int64_t bc_row_stride, const float* D_skip,
+                                      const void* z, int64_t z_row_stride,
+                                      const float* ssm_state_in, float* ssm_state_out, void* y,
+                                      mamba_dtype io_dtype, int B, int T, int D, int N,
+                                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * One decode step of the conv for L independent layers in one launch.
+ * [inference.rs] step chain F4 (one-token conv on the d_conv-slot shift register, state
+ * mutated in place) + F4b (SiLU), fused as in the mixed chain's conv-step-with-SiLU
+ * kernel; GpuInferenceState for the layout.
+ *
+ * Per (l, b, d): shift conv_state[l,b,d,:] left by one, store x in slot K-1, then
+ *   u[l,b,d] = silu(conv_b[l,d] + sum_k conv_w[l,d,k] * conv_state[l,b,d,k]).
+ *
+ *   x            in   io_dtype; element (l,b,d) at x[(l*B+b)*x_row_stride + d], x_row_stride >= D.
+ *   conv_w       in   [L,D,K] f32.     conv_b  in  [L,D] f32, or NULL for zero.
+ *   conv_state   in/out [L,B,D,K] f32, updated in place.
+ *   u            out  [L,B,D] io_dtype, contiguous.
+ */
+mamba_status mamba_conv1d_step(const void* x, int64_t x_row_stride, const float* conv_w,
+                               const float* conv_b, float* conv_state, void* u,
+                               mamba_dtype io_dtype, int L, int B, int D, int K, void* stream);
+
+/*
+ * One decode step of the SSM for L independent layers in one launch, state in place.
+ * [inference.rs] step chain F7 (softplus of dt_proj output), F9 (one-token state update
+ * and readout with D, state mutated in place), F10 (silu(z) gate), and the mixed chain's
+ * fused kernel that reads B and C in place from the x_proj output and gates before the
+ * store. Same formula as mamba_selective_scan_fwd with T = 1.
+ *
+ *   u, dt        in   [L,B,D] io_dtype, contiguous.
+ *   dt_bias      in   [L,D] f32, or NULL.          A_log  in  [L,D,N] f32.
+ *   Bm, Cm       in   io_dtype, row (l,b) at (l*B+b)*bc_row_stride, n in the first N elements.
+ *   D_skip       in   [L,D] f32, or NULL.
+ *   z            in   io_dtype, element (l,b,d) at z[(l*B+b)*z_row_stride + d], or NULL.
+ *   ssm_state    in/out [L,B,D,N] f32, updated in place.
+ *   y            out  [L,B,D] io_dtype, contiguous.
+ */
+mamba_status mamba_ssm_step(const void* u, const void* dt, const float* dt_bias,
+                            int delta_softplus, const float* A_log, const void* Bm,
+                            const void* Cm, int64_t bc_row_stride, const float* D_skip,
+                            const void* z, int64_t z_row_stride, float* ssm_state, void* y,
+                            mamba_dtype io_dtype, int L, int B, int D, int N, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MAMBA_SSM_H */

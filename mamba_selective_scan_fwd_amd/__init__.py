@@ -1,0 +1,198 @@
+"""Python binding of the gfx950 Mamba-1 selective-scan C-ABI (include/mamba_ssm.h).
+
+The functions carry the C names and only marshal arguments: device pointers and the
+current HIP stream come from torch tensors, and every step of the computation runs in
+the HIP kernels of libmamba_ssm.so. There is no fallback: if the library is missing or
+a call fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "MambaError", "MAMBA_F32", "MAMBA_BF16", "library_path", "load_library", "symbols",
+    "mamba_version", "mamba_last_error", "mamba_conv1d_fwd", "mamba_selective_scan_fwd",
+    "mamba_selective_scan_workspace_size", "mamba_conv1d_step", "mamba_ssm_step",
+    "scan_workspace",
+]
+
+MAMBA_F32 = 0
+MAMBA_BF16 = 1
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_PKG, "libmamba_ssm.so")
+
+# exported symbol -> (argtypes, restype)
+_P, _I, _I64, _SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+symbols = {
+    "mamba_last_error": ([], ctypes.c_char_p),
+    "mamba_version": ([], ctypes.c_char_p),
+    "mamba_conv1d_fwd": ([_P, _I64, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P], _I),
+    "mamba_selective_scan_workspace_size": ([_I, _I, _I, _I], _SZ),
+    "mamba_selective_scan_fwd": ([_P, _P, _P, _I, _P, _P, _P, _I64, _P, _P, _I64, _P, _P, _P,
+                                  _I, _I, _I, _I, _I, _P, _SZ, _P], _I),
+    "mamba_conv1d_step": ([_P, _I64, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P], _I),
+    "mamba_ssm_step": ([_P, _P, _P, _I, _P, _P, _P, _I64, _P, _P, _I64, _P, _P, _I, _I, _I,
+                        _I, _I, _P], _I),
+}
+
+_STATUS = {1: "MAMBA_EINVAL", 2: "MAMBA_EUNSUPPORTED", 3: "MAMBA_EWORKSPACE", 4: "MAMBA_EHIP"}
+
+
+class MambaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libmamba_ssm.so from the package directory (raises if it is not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(library_path):
+            raise ImportError(f"{library_path} is not built; run __graft_entry__.build() or "
+                              "python -m mamba_selective_scan_fwd_amd._build")
+        lib = ctypes.CDLL(library_path)
+        for name, (argtypes, restype) in symbols.items():
+            f = getattr(lib, name)
+            f.argtypes = argtypes
+            f.restype = restype
+        _lib = lib
+    return _lib
+
+
+def mamba_version() -> str:
+    return load_library().mamba_version().decode()
+
+
+def mamba_last_error() -> str:
+    return load_library().mamba_last_error().decode()
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise MambaError(status, mamba_last_error())
+
+
+# ------------------------------------------------------------------ marshalling helpers
+
+def _ptr(t):
+    """Device pointer of a tensor, or NULL for None. Plain ints pass through (raw pointers)."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _io_dtype(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return MAMBA_F32
+    if t.dtype == torch.bfloat16:
+        return MAMBA_BF16
+    raise TypeError(f"unsupported I/O dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _row_stride(t, name: str) -> int:
+    """Row stride of a 3-D [outer, inner, width] view whose rows (outer, inner) are evenly
+    spaced: element (o, i, w) at (o * inner + i) * stride + w."""
+    if t.dim() != 3:
+        raise ValueError(f"{name} must be 3-D")
+    o, i, w = t.shape
+    if w > 1 and t.stride(2) != 1:
+        raise ValueError(f"{name}: the last dimension must be contiguous")
+    if i > 1:
+        rs = t.stride(1)
+        if o > 1 and t.stride(0) != i * rs:
+            raise ValueError(f"{name}: rows must be evenly spaced (stride(0) == shape[1] * stride(1))")
+        return rs
+    if o > 1:
+        return t.stride(0)
+    return max(w, 1)
+
+
+# --------------------------------------------------------------------------- the calls
+
+def mamba_conv1d_fwd(x, conv_w, conv_b, conv_state, u, stream=None) -> None:
+    """Prefill conv1d + SiLU. x: [B, T, >=D] view (last dim contiguous, rows may be wider,
+    e.g. the x lane of an in_proj output); conv_w [D, K] f32; conv_b [D] f32 or None;
+    conv_state [B, D, K] f32 (updated in place) or None; u [B, T, D] out."""
+    Bsz, T = x.shape[0], x.shape[1]
+    D, K = conv_w.shape
+    xs = _row_stride(x, "x")
+    _check(load_library().mamba_conv1d_fwd(
+        _ptr(x), xs, _ptr(conv_w), _ptr(conv_b), _ptr(conv_state), _ptr(u), _io_dtype(u),
+        Bsz, T, D, K, _stream(stream)))
+
+
+def mamba_selective_scan_workspace_size(B: int, T: int, D: int, N: int) -> int:
+    return int(load_library().mamba_selective_scan_workspace_size(B, T, D, N))
+
+
+def scan_workspace(B: int, T: int, D: int, N: int, device="cuda"):
+    """A device buffer large enough for mamba_selective_scan_fwd at this shape (or None)."""
+    import torch
+    n = mamba_selective_scan_workspace_size(B, T, D, N)
+    return torch.empty(n, dtype=torch.uint8, device=device) if n else None
+
+
+def mamba_selective_scan_fwd(u, dt, dt_bias, A_log, Bm, Cm, D_skip, z, ssm_state_in,
+                             ssm_state_out, y, delta_softplus=True, workspace=None,
+                             stream=None) -> None:
+    """Prefill selective scan. u, dt, y: [B, T, D] contiguous; Bm, Cm: [B, T, >=N] views
+    sharing one row stride; z: [B, T, >=D] view or None; A_log [D, N]; dt_bias, D_skip [D]
+    or None; states [B, D, N] f32 (in may be None; out may be None or equal to in).
+    workspace: a uint8 device tensor of mamba_selective_scan_workspace_size bytes."""
+    Bsz, T, D = u.shape
+    N = A_log.shape[1]
+    bcs = _row_stride(Bm, "Bm")
+    if _row_stride(Cm, "Cm") != bcs:
+        raise ValueError("Bm and Cm must share one row stride")
+    zs = _row_stride(z, "z") if z is not None else 0
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load_library().mamba_selective_scan_fwd(
+        _ptr(u), _ptr(dt), _ptr(dt_bias), int(bool(delta_softplus)), _ptr(A_log), _ptr(Bm),
+        _ptr(Cm), bcs, _ptr(D_skip), _ptr(z), zs, _ptr(ssm_state_in), _ptr(ssm_state_out),
+        _ptr(y), _io_dtype(u), Bsz, T, D, N, _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def mamba_conv1d_step(x, conv_w, conv_b, conv_state, u, stream=None) -> None:
+    """Decode conv step for L layers. x: [L, B, >=D] view; conv_w [L, D, K]; conv_b [L, D]
+    or None; conv_state [L, B, D, K] (in place); u [L, B, D]."""
+    L, Bsz = u.shape[0], u.shape[1]
+    _, D, K = conv_w.shape
+    xs = _row_stride(x, "x")
+    _check(load_library().mamba_conv1d_step(
+        _ptr(x), xs, _ptr(conv_w), _ptr(conv_b), _ptr(conv_state), _ptr(u), _io_dtype(u),
+        L, Bsz, D, K, _stream(stream)))
+
+
+def mamba_ssm_step(u, dt, dt_bias, A_log, Bm, Cm, D_skip, z, ssm_state, y,
+                   delta_softplus=True, stream=None) -> None:
+    """Decode SSM step for L layers. u, dt, y: [L, B, D]; Bm, Cm: [L, B, >=N] views sharing
+    one row stride; z: [L, B, >=D] view or None; A_log [L, D, N]; dt_bias, D_skip [L, D] or
+    None; ssm_state [L, B, D, N] (in place)."""
+    L, Bsz, D = u.shape
+    N = A_log.shape[2]
+    bcs = _row_stride(Bm, "Bm")
+    if _row_stride(Cm, "Cm") != bcs:
+        raise ValueError("Bm and Cm must share one row stride")
+    zs = _row_stride(z, "z") if z is not None else 0
+    _check(load_library().mamba_ssm_step(
+        _ptr(u), _ptr(dt), _ptr(dt_bias), int(bool(delta_softplus)), _ptr(A_log), _ptr(Bm),
+        _ptr(Cm), bcs, _ptr(D_skip), _ptr(z), zs, _ptr(ssm_state), _ptr(y), _io_dtype(u), L, Bsz,
+        D, N, _stream(stream)))

@@ -1,0 +1,291 @@
+// abi.cpp -- the extern "C" boundary: argument validation, error reporting, dispatch.
+//
+// Every call checks all of its arguments before anything is enqueued and reports the first
+// problem through a thread-local message, in the spirit of the pages' host code, which
+// validates buffer sizes before a prefill so that a bad request fails before any work
+// (prefill.rs page, mamba-rs 0.6.4, output-length check ahead of prefill_body) and turns
+// unsupported d_state into a loud error rather than a silent early return (inference.rs
+// page, mamba-rs 0.5.1, mixed chain, fused gather + step + gate guard).
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/mamba_ssm.h"
+#include "launch.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+constexpr int kMaxN = 64;
+constexpr int kMaxK = 8;
+constexpr int kMaxGridYZ = 65535;
+
+struct Fail {
+  mamba_status status;
+};
+
+[[noreturn]] void fail(mamba_status st, const char* fn, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = std::string(fn) + ": " + buf;
+  throw Fail{st};
+}
+
+size_t elem_size(mamba_dtype t) { return t == MAMBA_BF16 ? 2 : 4; }
+
+void check_dtype(const char* fn, mamba_dtype t) {
+  if (t != MAMBA_F32 && t != MAMBA_BF16) fail(MAMBA_EINVAL, fn, "io_dtype %d is not MAMBA_F32 or MAMBA_BF16", (int)t);
+}
+
+void check_ptr(const char* fn, const char* name, const void* p, size_t align, bool required) {
+  if (!p) {
+    if (required) fail(MAMBA_EINVAL, fn, "%s is NULL", name);
+    return;
+  }
+  if (reinterpret_cast<uintptr_t>(p) % align != 0)
+    fail(MAMBA_EINVAL, fn, "%s (%p) is not %zu-byte aligned", name, p, align);
+}
+
+// A tensor's byte range, for overlap checks. rows of `width` elements, `stride` apart.
+struct Range {
+  const char* name;
+  uintptr_t lo, hi;  // [lo, hi); empty when lo == hi
+};
+
+Range range(const char* name, const void* p, int64_t rows, int64_t stride, int64_t width,
+            size_t esize) {
+  if (!p || rows <= 0 || width <= 0) return {name, 0, 0};
+  const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+  return {name, lo, lo + (uintptr_t)(((rows - 1) * stride + width) * (int64_t)esize)};
+}
+
+void check_disjoint(const char* fn, const Range& out, std::initializer_list<Range> ins) {
+  if (out.lo == out.hi) return;
+  for (const Range& r : ins) {
+    if (r.lo == r.hi) continue;
+    if (out.lo < r.hi && r.lo < out.hi) fail(MAMBA_EINVAL, fn, "%s overlaps %s", out.name, r.name);
+  }
+}
+
+void check_hip(const char* fn, hipError_t e) {
+  if (e != hipSuccess) fail(MAMBA_EHIP, fn, "HIP error %d (%s)", (int)e, hipGetErrorString(e));
+}
+
+void check_dim(const char* fn, const char* name, int v) {
+  if (v < 0) fail(MAMBA_EINVAL, fn, "%s = %d is negative", name, v);
+}
+
+void check_state_dim(const char* fn, const char* name, int v, int max) {
+  if (v <= 0) fail(MAMBA_EINVAL, fn, "%s = %d must be at least 1", name, v);
+  if (v > max) fail(MAMBA_EUNSUPPORTED, fn, "%s = %d exceeds the supported maximum %d", name, v, max);
+}
+
+template <typename F>
+mamba_status guarded(F&& f) {
+  try {
+    f();
+    g_last_error.clear();
+    return MAMBA_OK;
+  } catch (const Fail& e) {
+    return e.status;
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mamba_last_error(void) { return g_last_error.c_str(); }
+
+const char* mamba_version(void) { return "mamba_selective_scan_fwd_amd 0.1.0 (gfx950)"; }
+
+mamba_status mamba_conv1d_fwd(const void* x, int64_t x_row_stride, const float* conv_w,
+                              const float* conv_b, float* conv_state, void* u,
+                              mamba_dtype io_dtype, int B, int T, int D, int K, void* stream) {
+  static const char* fn = "mamba_conv1d_fwd";
+  return guarded([&] {
+    check_dtype(fn, io_dtype);
+    check_dim(fn, "B", B);
+    check_dim(fn, "T", T);
+    check_dim(fn, "D", D);
+    check_state_dim(fn, "K", K, kMaxK);
+    if (B > kMaxGridYZ) fail(MAMBA_EUNSUPPORTED, fn, "B = %d exceeds %d", B, kMaxGridYZ);
+    if ((int64_t)B * T == 0 || D == 0) return;
+    const size_t es = elem_size(io_dtype);
+    if (x_row_stride < D) fail(MAMBA_EINVAL, fn, "x_row_stride = %lld is less than D = %d", (long long)x_row_stride, D);
+    check_ptr(fn, "x", x, es, true);
+    check_ptr(fn, "conv_w", conv_w, 4, true);
+    check_ptr(fn, "conv_b", conv_b, 4, false);
+    check_ptr(fn, "conv_state", conv_state, 4, false);
+    check_ptr(fn, "u", u, es, true);
+    const int64_t rows = (int64_t)B * T;
+    const Range rx = range("x", x, rows, x_row_stride, D, es);
+    const Range rw = range("conv_w", conv_w, D, K, K, 4);
+    const Range rb = range("conv_b", conv_b, 1, D, D, 4);
+    const Range rs = range("conv_state", conv_state, (int64_t)B * D, K, K, 4);
+    check_disjoint(fn, range("u", u, rows, D, D, es), {rx, rw, rb, rs});
+    check_disjoint(fn, rs, {rx, rw, rb});
+    mamba::ConvFwdArgs a{x, x_row_stride, conv_w, conv_b, conv_state, u, io_dtype == MAMBA_BF16,
+                         B, T, D, K};
+    check_hip(fn, mamba::launch_conv1d_fwd(a, static_cast<hipStream_t>(stream)));
+  });
+}
+
+size_t mamba_selective_scan_workspace_size(int B, int T, int D, int N) {
+  return mamba::plan_selective_scan(B, T, D, N).workspace_bytes;
+}
+
+mamba_status mamba_selective_scan_fwd(const void* u, const void* dt, const float* dt_bias,
+                                      int delta_softplus, const float* A_log, const void* Bm,
+                                      const void* Cm, int64_t bc_row_stride, const float* D_skip,
+                                      const void* z, int64_t z_row_stride,
+                                      const float* ssm_state_in, float* ssm_state_out, void* y,
+                                      mamba_dtype io_dtype, int B, int T, int D, int N,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
+  static const char* fn = "mamba_selective_scan_fwd";
+  return guarded([&] {
+    check_dtype(fn, io_dtype);
+    check_dim(fn, "B", B);
+    check_dim(fn, "T", T);
+    check_dim(fn, "D", D);
+    check_state_dim(fn, "N", N, kMaxN);
+    if (B > kMaxGridYZ) fail(MAMBA_EUNSUPPORTED, fn, "B = %d exceeds %d", B, kMaxGridYZ);
+    if (B == 0 || D == 0) return;
+    const size_t es = elem_size(io_dtype);
+    check_ptr(fn, "ssm_state_in", ssm_state_in, 4, false);
+    check_ptr(fn, "ssm_state_out", ssm_state_out, 4, false);
+    const int64_t nstate = (int64_t)B * D * N;
+    const Range rsi = range("ssm_state_in", ssm_state_in, 1, nstate, nstate, 4);
+    const Range rso = range("ssm_state_out", ssm_state_out, 1, nstate, nstate, 4);
+    if (ssm_state_in != ssm_state_out) check_disjoint(fn, rso, {rsi});
+    if (T == 0) {
+      check_hip(fn, mamba::launch_selective_scan_fwd(
+                        mamba::ScanFwdArgs{u, dt, dt_bias, delta_softplus != 0, A_log, Bm, Cm,
+                                           bc_row_stride, D_skip, z, z_row_stride, ssm_state_in,
+                                           ssm_state_out, y, io_dtype == MAMBA_BF16, B, T, D, N,
+                                           workspace},
+                        static_cast<hipStream_t>(stream)));
+      return;
+    }
+    if (bc_row_stride < N) fail(MAMBA_EINVAL, fn, "bc_row_stride = %lld is less than N = %d", (long long)bc_row_stride, N);
+    if (z && z_row_stride < D) fail(MAMBA_EINVAL, fn, "z_row_stride = %lld is less than D = %d", (long long)z_row_stride, D);
+    check_ptr(fn, "u", u, es, true);
+    check_ptr(fn, "dt", dt, es, true);
+    check_ptr(fn, "dt_bias", dt_bias, 4, false);
+    check_ptr(fn, "A_log", A_log, 4, true);
+    check_ptr(fn, "Bm", Bm, es, true);
+    check_ptr(fn, "Cm", Cm, es, true);
+    check_ptr(fn, "D_skip", D_skip, 4, false);
+    check_ptr(fn, "z", z, es, false);
+    check_ptr(fn, "y", y, es, true);
+    const size_t need = mamba::plan_selective_scan(B, T, D, N).workspace_bytes;
+    if (need > 0) {
+      if (!workspace) fail(MAMBA_EWORKSPACE, fn, "workspace is NULL but %zu bytes are required", need);
+      if (workspace_bytes < need) fail(MAMBA_EWORKSPACE, fn, "workspace_bytes = %zu but %zu are required", workspace_bytes, need);
+      if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) fail(MAMBA_EINVAL, fn, "workspace is not 256-byte aligned");
+    }
+    const int64_t rows = (int64_t)B * T;
+    const Range ru = range("u", u, rows, D, D, es);
+    const Range rdt = range("dt", dt, rows, D, D, es);
+    const Range rdb = range("dt_bias", dt_bias, 1, D, D, 4);
+    const Range ra = range("A_log", A_log, D, N, N, 4);
+    const Range rB = range("Bm", Bm, rows, bc_row_stride, N, es);
+    const Range rC = range("Cm", Cm, rows, bc_row_stride, N, es);
+    const Range rD = range("D_skip", D_skip, 1, D, D, 4);
+    const Range rz = range("z", z, rows, z_row_stride, D, es);
+    const Range rws = range("workspace", need ? workspace : nullptr, 1, (int64_t)need, (int64_t)need, 1);
+    const Range ry = range("y", y, rows, D, D, es);
+    check_disjoint(fn, ry, {ru, rdt, rdb, ra, rB, rC, rD, rz, rsi, rso, rws});
+    check_disjoint(fn, rso, {ru, rdt, rdb, ra, rB, rC, rD, rz, rws});
+    check_disjoint(fn, rws, {ru, rdt, rdb, ra, rB, rC, rD, rz, rsi});
+    mamba::ScanFwdArgs a{u, dt, dt_bias, delta_softplus != 0, A_log, Bm, Cm, bc_row_stride,
+                         D_skip, z, z_row_stride, ssm_state_in, ssm_state_out, y,
+                         io_dtype == MAMBA_BF16, B, T, D, N, workspace};
+    check_hip(fn, mamba::launch_selective_scan_fwd(a, static_cast<hipStream_t>(stream)));
+  });
+}
+
+mamba_status mamba_conv1d_step(const void* x, int64_t x_row_stride, const float* conv_w,
+                               const float* conv_b, float* conv_state, void* u,
+                               mamba_dtype io_dtype, int L, int B, int D, int K, void* stream) {
+  static const char* fn = "mamba_conv1d_step";
+  return guarded([&] {
+    check_dtype(fn, io_dtype);
+    check_dim(fn, "L", L);
+    check_dim(fn, "B", B);
+    check_dim(fn, "D", D);
+    check_state_dim(fn, "K", K, kMaxK);
+    if ((int64_t)L * B > kMaxGridYZ) fail(MAMBA_EUNSUPPORTED, fn, "L*B = %lld exceeds %d", (long long)L * B, kMaxGridYZ);
+    if ((int64_t)L * B == 0 || D == 0) return;
+    const size_t es = elem_size(io_dtype);
+    if (x_row_stride < D) fail(MAMBA_EINVAL, fn, "x_row_stride = %lld is less than D = %d", (long long)x_row_stride, D);
+    check_ptr(fn, "x", x, es, true);
+    check_ptr(fn, "conv_w", conv_w, 4, true);
+    check_ptr(fn, "conv_b", conv_b, 4, false);
+    check_ptr(fn, "conv_state", conv_state, 4, true);
+    check_ptr(fn, "u", u, es, true);
+    const int64_t rows = (int64_t)L * B;
+    const Range rx = range("x", x, rows, x_row_stride, D, es);
+    const Range rw = range("conv_w", conv_w, (int64_t)L * D, K, K, 4);
+    const Range rb = range("conv_b", conv_b, L, D, D, 4);
+    const Range rs = range("conv_state", conv_state, rows * D, K, K, 4);
+    check_disjoint(fn, range("u", u, rows, D, D, es), {rx, rw, rb, rs});
+    check_disjoint(fn, rs, {rx, rw, rb});
+    mamba::ConvStepArgs a{x, x_row_stride, conv_w, conv_b, conv_state, u, io_dtype == MAMBA_BF16,
+                          L, B, D, K};
+    check_hip(fn, mamba::launch_conv1d_step(a, static_cast<hipStream_t>(stream)));
+  });
+}
+
+mamba_status mamba_ssm_step(const void* u, const void* dt, const float* dt_bias,
+                            int delta_softplus, const float* A_log, const void* Bm,
+                            const void* Cm, int64_t bc_row_stride, const float* D_skip,
+                            const void* z, int64_t z_row_stride, float* ssm_state, void* y,
+                            mamba_dtype io_dtype, int L, int B, int D, int N, void* stream) {
+  static const char* fn = "mamba_ssm_step";
+  return guarded([&] {
+    check_dtype(fn, io_dtype);
+    check_dim(fn, "L", L);
+    check_dim(fn, "B", B);
+    check_dim(fn, "D", D);
+    check_state_dim(fn, "N", N, kMaxN);
+    if ((int64_t)L * B == 0 || D == 0) return;
+    const size_t es = elem_size(io_dtype);
+    if (bc_row_stride < N) fail(MAMBA_EINVAL, fn, "bc_row_stride = %lld is less than N = %d", (long long)bc_row_stride, N);
+    if (z && z_row_stride < D) fail(MAMBA_EINVAL, fn, "z_row_stride = %lld is less than D = %d", (long long)z_row_stride, D);
+    check_ptr(fn, "u", u, es, true);
+    check_ptr(fn, "dt", dt, es, true);
+    check_ptr(fn, "dt_bias", dt_bias, 4, false);
+    check_ptr(fn, "A_log", A_log, 4, true);
+    check_ptr(fn, "Bm", Bm, es, true);
+    check_ptr(fn, "Cm", Cm, es, true);
+    check_ptr(fn, "D_skip", D_skip, 4, false);
+    check_ptr(fn, "z", z, es, false);
+    check_ptr(fn, "ssm_state", ssm_state, 4, true);
+    check_ptr(fn, "y", y, es, true);
+    const int64_t rows = (int64_t)L * B;
+    const Range ru = range("u", u, rows, D, D, es);
+    const Range rdt = range("dt", dt, rows, D, D, es);
+    const Range rdb = range("dt_bias", dt_bias, L, D, D, 4);
+    const Range ra = range("A_log", A_log, (int64_t)L * D, N, N, 4);
+    const Range rB = range("Bm", Bm, rows, bc_row_stride, N, es);
+    const Range rC = range("Cm", Cm, rows, bc_row_stride, N, es);
+    const Range rD = range("D_skip", D_skip, L, D, D, 4);
+    const Range rz = range("z", z, rows, z_row_stride, D, es);
+    const Range rs = range("ssm_state", ssm_state, rows * D, N, N, 4);
+    check_disjoint(fn, range("y", y, rows, D, D, es), {ru, rdt, rdb, ra, rB, rC, rD, rz, rs});
+    check_disjoint(fn, rs, {ru, rdt, rdb, ra, rB, rC, rD, rz});
+    mamba::SsmStepArgs a{u, dt, dt_bias, delta_softplus != 0, A_log, Bm, Cm, bc_row_stride,
+                         D_skip, z, z_row_stride, ssm_state, y, io_dtype == MAMBA_BF16, L, B, D,
+                         N};
+    check_hip(fn, mamba::launch_ssm_step(a, static_cast<hipStream_t>(stream)));
+  });
+}
+
+}  // extern "C"

@@ -1,0 +1,52 @@
+// common.hpp -- element types and f32 math shared by the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mamba {
+
+// I/O element types. bf16 is the compiler's native __bf16: loads widen with a shift,
+// stores go through gfx950's v_cvt_pk_bf16_f32 (round to nearest even).
+using bf16 = __bf16;
+
+template <typename T>
+__device__ __forceinline__ float to_f32(T v) { return static_cast<float>(v); }
+
+template <typename T>
+__device__ __forceinline__ T from_f32(float v) { return static_cast<T>(v); }
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// exp(x) as 2^(x*log2 e) on the hardware exp2 (v_exp_f32).
+__device__ __forceinline__ float fast_exp(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
+
+// silu(z) = z * sigmoid(z) = z / (1 + exp(-z)). For z << 0, exp(-z) overflows to +inf and
+// the reciprocal gives 0, so silu -> -0 as it should.
+__device__ __forceinline__ float silu(float z) {
+  return z * __builtin_amdgcn_rcpf(1.0f + fast_exp(-z));
+}
+
+// log1p(e) for e in [0, 1], accurate to a few ulp: with w = 1 + e rounded, the factor
+// e / (w - 1) corrects the rounding of w (w - 1 is exact here), so the relative error is
+// that of the hardware log2 and reciprocal, not the absolute error of w. This is the
+// textbook compensated log1p (Goldberg, "What every computer scientist should know
+// about floating-point arithmetic", Theorem 4).
+__device__ __forceinline__ float log1p_small(float e) {
+  float w = 1.0f + e;
+  float dw = w - 1.0f;
+  float l = __builtin_amdgcn_logf(w) * kLn2;  // natural log of w
+  return dw == 0.0f ? e : l * (e * __builtin_amdgcn_rcpf(dw));
+}
+
+// softplus(v) = log(1 + exp(v)) = max(v, 0) + log1p(exp(-|v|)), with no overflow.
+// At the dt-bias values of Mamba layers (v around -7..-2) a plain log(1 + exp(v)) in f32
+// loses most of its digits; the compensated log1p keeps the relative error near 1e-7.
+__device__ __forceinline__ float softplus(float v) {
+  return fmaxf(v, 0.0f) + log1p_small(fast_exp(-fabsf(v)));
+}
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+}  // namespace mamba

@@ -1,0 +1,138 @@
+"""The C-ABI library on the CPU: it loads, exports every symbol include/mamba_ssm.h declares,
+and rejects bad arguments before touching the GPU (validation runs before any HIP call).
+No compute call is made here."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mamba_selective_scan_fwd_amd as m
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mamba_ssm.h")
+
+F32, BF16 = m.MAMBA_F32, m.MAMBA_BF16
+EINVAL, EUNSUP, EWS = 1, 2, 3
+FAKE = 0x7F0000000000  # a well-aligned address; never dereferenced (calls fail validation first)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mamba_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = m.load_library()
+    names = declared_functions()
+    assert {"mamba_conv1d_fwd", "mamba_selective_scan_fwd", "mamba_conv1d_step",
+            "mamba_ssm_step", "mamba_last_error"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in mamba_ssm.h but not exported"
+    assert set(names) == set(m.symbols), "binding symbol table and header disagree"
+
+
+def test_version_and_empty_error():
+    assert "gfx950" in m.mamba_version()
+
+
+def scan_call(**kw):
+    a = dict(u=FAKE, dt=FAKE, dt_bias=None, sp=1, A_log=FAKE, Bm=FAKE, Cm=FAKE, bcs=16, D_skip=None,
+             z=None, zs=0, si=None, so=None, y=FAKE + (1 << 30), io=F32, B=1, T=32, D=64, N=16,
+             ws=FAKE + (1 << 35), wsb=1 << 20, stream=None)
+    a.update(kw)
+    st = m.load_library().mamba_selective_scan_fwd(
+        a["u"], a["dt"], a["dt_bias"], a["sp"], a["A_log"], a["Bm"], a["Cm"], a["bcs"], a["D_skip"],
+        a["z"], a["zs"], a["si"], a["so"], a["y"], a["io"], a["B"], a["T"], a["D"], a["N"], a["ws"],
+        a["wsb"], a["stream"])
+    return st, m.mamba_last_error()
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(u=None), EINVAL, "u is NULL"),
+    (dict(N=0), EINVAL, "N = 0"),
+    (dict(N=65), EUNSUP, "N = 65"),
+    (dict(T=-1), EINVAL, "T = -1"),
+    (dict(io=7), EINVAL, "io_dtype"),
+    (dict(bcs=8), EINVAL, "bc_row_stride"),
+    (dict(z=FAKE + (1 << 31), zs=10), EINVAL, "z_row_stride"),
+    (dict(u=FAKE + 2), EINVAL, "aligned"),
+    (dict(so=FAKE + 64), EINVAL, "ssm_state_out overlaps u"),
+    (dict(y=FAKE), EINVAL, "y overlaps u"),
+    (dict(B=1, T=2048, D=1536, ws=None, wsb=0), EWS, "workspace"),
+])
+def test_scan_validation(kw, status, needle):
+    st, msg = scan_call(**kw)
+    assert st == status, msg
+    assert needle in msg and msg.startswith("mamba_selective_scan_fwd")
+
+
+def test_scan_workspace_too_small_and_misaligned():
+    need = m.mamba_selective_scan_workspace_size(1, 2048, 1536, 16)
+    assert need > 0
+    st, msg = scan_call(B=1, T=2048, D=1536, ws=FAKE + (1 << 34), wsb=need - 1)
+    assert st == EWS and "workspace_bytes" in msg
+    st, msg = scan_call(B=1, T=2048, D=1536, ws=FAKE + (1 << 34) + 4, wsb=need)
+    assert st == EINVAL and "256-byte" in msg
+
+
+def test_scan_empty_batch_is_noop():
+    st, msg = scan_call(u=None, dt=None, A_log=None, Bm=None, Cm=None, y=None, B=0, ws=None)
+    assert st == 0, msg
+    st, msg = scan_call(u=None, dt=None, A_log=None, Bm=None, Cm=None, y=None, D=0)
+    assert st == 0, msg
+
+
+def test_scan_state_partial_overlap_rejected():
+    st, msg = scan_call(si=FAKE + (1 << 33), so=FAKE + (1 << 33) + 64)
+    assert st == EINVAL and "ssm_state_out overlaps ssm_state_in" in msg
+
+
+def test_workspace_size_formula():
+    # one chunk (no carry) needs no workspace; the large shapes need one
+    assert m.mamba_selective_scan_workspace_size(1, 32, 64, 16) >= 0
+    assert m.mamba_selective_scan_workspace_size(8, 4096, 5120, 16) % 256 == 0
+    assert m.mamba_selective_scan_workspace_size(0, 32, 64, 16) == 0
+
+
+def test_conv_validation():
+    lib = m.load_library()
+    st = lib.mamba_conv1d_fwd(FAKE, 32, FAKE + (1 << 30), None, None, FAKE + (1 << 31), F32, 1, 8, 64, 4, None)
+    assert st == EINVAL and "x_row_stride" in m.mamba_last_error()
+    st = lib.mamba_conv1d_fwd(FAKE, 64, FAKE + (1 << 30), None, None, FAKE + (1 << 31), F32, 1, 8, 64, 9, None)
+    assert st == EUNSUP and "K = 9" in m.mamba_last_error()
+    st = lib.mamba_conv1d_fwd(FAKE, 64, FAKE + (1 << 30), None, None, FAKE, F32, 1, 8, 64, 4, None)
+    assert st == EINVAL and "u overlaps x" in m.mamba_last_error()
+    st = lib.mamba_conv1d_fwd(None, 64, None, None, None, None, F32, 1, 0, 64, 4, None)
+    assert st == 0  # T == 0: nothing to do
+
+
+def test_step_validation():
+    lib = m.load_library()
+    st = lib.mamba_conv1d_step(FAKE, 64, FAKE + (1 << 30), None, None, FAKE + (1 << 31), F32, 2, 3, 64, 4, None)
+    assert st == EINVAL and "conv_state is NULL" in m.mamba_last_error()
+    st = lib.mamba_conv1d_step(FAKE, 64, FAKE + (1 << 30), None, FAKE + (1 << 32), FAKE + (1 << 31), F32, 300, 300, 64, 4, None)
+    assert st == EUNSUP and "L*B" in m.mamba_last_error()
+    st = lib.mamba_ssm_step(FAKE, FAKE + (1 << 28), None, 1, FAKE + (1 << 29), FAKE + (1 << 30), FAKE + (1 << 31),
+                            16, None, None, 0, None, FAKE + (1 << 32), F32, 2, 3, 64, 16, None)
+    assert st == EINVAL and "ssm_state is NULL" in m.mamba_last_error()
+    st = lib.mamba_ssm_step(FAKE, FAKE + (1 << 28), None, 1, FAKE + (1 << 29), FAKE + (1 << 30), FAKE + (1 << 31),
+                            16, None, None, 0, FAKE + (1 << 33), FAKE + (1 << 32), F32, 2, 3, 64, 0, None)
+    assert st == EINVAL and "N = 0" in m.mamba_last_error()
+
+
+def test_errors_are_thread_local():
+    import threading
+    st, msg = scan_call(u=None)
+    assert st == EINVAL
+    seen = {}
+
+    def other():
+        seen["msg"] = m.mamba_last_error()
+
+    th = threading.Thread(target=other)
+    th.start()
+    th.join()
+    assert seen["msg"] == ""
+    assert "u is NULL" in m.mamba_last_error()

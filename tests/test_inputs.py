@@ -70,3 +70,8 @@ def test_config_table(name):
         assert (s.B, s.T, s.D, s.io) == (8, 4096, 5120, "bf16")
     if name == "c2":
         assert (s.L, s.B, s.D, s.steps) == (24, 64, 1536, 1000)
+
+
+def test_store_large_path_equals_bf16_round():
+    a = np.random.default_rng(3).normal(size=W._TORCH_ROUND_MIN + 17).astype(np.float32)
+    np.testing.assert_array_equal(W.store(a, "bf16").view(np.uint32), W.bf16_round(a).view(np.uint32))

@@ -110,10 +110,23 @@ def bf16_from_bits(b: np.ndarray) -> np.ndarray:
     return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
 
 
+_TORCH_ROUND_MIN = 1 << 20
+
+
 def store(a: np.ndarray, io: str) -> np.ndarray:
-    """The value a tensor holds once stored in the I/O dtype (f32 array either way)."""
+    """The value a tensor holds once stored in the I/O dtype (f32 array either way).
+    Large arrays are rounded with torch's CPU bf16 conversion, which is the same
+    round-to-nearest-even (checked against bf16_round in the tests), only faster."""
     a = np.asarray(a, dtype=np.float32)
-    return bf16_round(a) if io == "bf16" else a
+    if io != "bf16":
+        return a
+    if a.size >= _TORCH_ROUND_MIN:
+        try:
+            import torch
+        except ImportError:
+            return bf16_round(a)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(torch.bfloat16).to(torch.float32).numpy()
+    return bf16_round(a)
 
 
 # ------------------------------------------------------- parameter init recipe
