@@ -1,0 +1,354 @@
+#!/usr/bin/env python3
+"""Throughput of the Mamba-1 selective-scan hot path on one MI355X.
+
+A step is one pass of the prefill hot path over one batch of synthetic input already
+resident in HBM: mamba_conv1d_fwd (causal depthwise conv + SiLU) then
+mamba_selective_scan_fwd (softplus, discretisation, recurrence, readout, D skip, gate),
+both through the C-ABI, carrying the conv and SSM states from step to step.
+
+Default workload: the 130m-shaped prefill layer (B=1, T=2048, d_inner=1536, d_state=16,
+d_conv=4, f32 I/O). --config c3 runs the 2.8b-shaped layer (B=8, T=4096, d_inner=5120,
+bf16 I/O); --config c2 the batched decode step (24 layers, B=64, one token per step).
+
+Prints one JSON line. `value` is tokens/s/layer (batch tokens per step / step time);
+`roofline` covers the dominant kernel call, timed with HIP events on the stream it runs
+on; `cpu_baseline` is the f64 CPU oracle timed on the host on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+METRIC = "selective-scan prefill tokens/s/layer (d_inner=1536/5120) + HBM GB/s % peak"
+
+
+def parse_args(argv=None):
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--config", default="c1", choices=["c1", "c3", "c2"])
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=10.0,
+                   help="approximate CPU time budget for the oracle baseline")
+    return p.parse_args(argv)
+
+
+# ------------------------------------------------------------------ algorithmic bytes
+
+def conv_bytes(s, B, T, D, K):
+    """x in, u out (s bytes each), conv state read + written, taps and bias read."""
+    return 2 * s * B * T * D + 8 * B * D * K + 4 * D * (K + 1)
+
+
+def scan_bytes(s, B, T, D, N):
+    """u, dt, z in and y out (s bytes each); B and C rows in; SSM state read + written;
+    A_log, D and dt_bias read."""
+    return 4 * s * B * T * D + 2 * s * B * T * N + 8 * B * D * N + 4 * D * N + 8 * D
+
+
+def conv_step_bytes(s, L, B, D, K):
+    return L * (2 * s * B * D + 8 * B * D * K + 4 * D * (K + 1))
+
+
+def ssm_step_bytes(s, L, B, D, N):
+    return L * (4 * s * B * D + 2 * s * B * N + 8 * B * D * N + 4 * D * N + 8 * D)
+
+
+# ------------------------------------------------------------------ traffic from counters
+
+def measured_traffic(kernel_file: str, workload: str):
+    """HBM bytes per call from the committed rocprofv3 counter summary, if it was taken on
+    the current kernel source (its sha256 is recorded in the summary); else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.txt")
+    src = os.path.join(ROOT, "mamba_selective_scan_fwd_amd", "csrc", kernel_file)
+    if not os.path.exists(path) or not os.path.exists(src):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if fields.get("kernel_source_sha256") != digest:
+        return None
+    try:
+        return float(fields["hbm_bytes_per_call"])
+    except (KeyError, ValueError):
+        return None
+
+
+# ------------------------------------------------------------------ workloads
+
+def _events(torch):
+    return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+
+def bench_prefill(args, shape):
+    import numpy as np
+    import torch
+
+    import mamba_selective_scan_fwd_amd as m
+    import workloads as W
+
+    io = shape.io
+    iod = torch.bfloat16 if io == "bf16" else torch.float32
+    s = 2 if io == "bf16" else 4
+    B, T, D, N, K = shape.B, shape.T, shape.D, shape.N, shape.K
+    print(f"[bench] generating {shape.name} inputs B={B} T={T} D={D} N={N} io={io}",
+          file=sys.stderr, flush=True)
+    inp = W.prefill_inputs(shape)
+    dev = torch.device("cuda:0")
+
+    def up(a, as_io):
+        t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
+        return (t.to(iod) if as_io else t).to(dev)
+
+    x, z, dt = up(inp["x"], True), up(inp["z"], True), up(inp["dt"], True)
+    Bm, Cm = up(inp["Bm"], True), up(inp["Cm"], True)
+    p = {k: up(inp[k], False) for k in ("conv_w", "conv_b", "dt_bias", "A_log", "D_skip")}
+    conv_state = up(inp["conv_state"], False)
+    ssm_state = up(inp["ssm_state"], False)
+    u = torch.empty(B, T, D, dtype=iod, device=dev)
+    y = torch.empty(B, T, D, dtype=iod, device=dev)
+    ws = m.scan_workspace(B, T, D, N)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        m.mamba_conv1d_fwd(x, p["conv_w"], p["conv_b"], conv_state, u, stream=stream)
+        if ev:
+            ev[1].record(stream)
+        m.mamba_selective_scan_fwd(u, dt, p["dt_bias"], p["A_log"], Bm, Cm, p["D_skip"], z,
+                                   ssm_state, ssm_state, y, workspace=ws, stream=stream)
+        if ev:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done ({args.warmup} steps); timing {args.steps} steps",
+          file=sys.stderr, flush=True)
+
+    # per-call events over the timed region
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
+    t_start, t_end = _events(torch)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(evs[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    conv_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    scan_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    assert torch.isfinite(y.float()).all(), "non-finite output"
+
+    ms_step = total_ms / args.steps
+    tokens = B * T
+    cb = conv_bytes(s, B, T, D, K)
+    sb = scan_bytes(s, B, T, D, N)
+    conv_avg = sum(conv_ms) / len(conv_ms)
+    scan_avg = sum(scan_ms) / len(scan_ms)
+    calls = {
+        "mamba_conv1d_fwd": dict(avg_ms=conv_avg, min_ms=min(conv_ms), bytes=cb,
+                                 kernel_file="conv1d.hip"),
+        "mamba_selective_scan_fwd": dict(avg_ms=scan_avg, min_ms=min(scan_ms), bytes=sb,
+                                         kernel_file="scan.hip"),
+    }
+    dom_name = max(calls, key=lambda k: calls[k]["avg_ms"])
+    dom = calls[dom_name]
+    achieved = dom["bytes"] / (dom["avg_ms"] * 1e-3) / 1e9
+    traffic = measured_traffic(dom["kernel_file"], shape.name)
+    result = dict(
+        metric=METRIC,
+        value=tokens / (ms_step * 1e-3),
+        unit="tokens/s/layer",
+        ms_per_step=ms_step,
+        dtype="bf16" if io == "bf16" else "f32",
+        config=dict(workload=f"{shape.name}: single Mamba-1 layer prefill (conv1d_fwd + selective_scan_fwd), "
+                             f"B={B} T={T} d_inner={D} d_state={N} d_conv={K} io={io}",
+                    B=B, T=T, d_inner=D, d_state=N, d_conv=K, io_dtype=io,
+                    layer_bytes=cb + sb),
+        roofline=dict(bound="hbm", achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s",
+                      frac=achieved / HBM_PEAK_GBS, traffic=traffic, call=dom_name,
+                      algorithmic_bytes=dom["bytes"], avg_ms=dom["avg_ms"]),
+        calls={k: dict(avg_us=v["avg_ms"] * 1e3, min_us=v["min_ms"] * 1e3,
+                       gbs=v["bytes"] / (v["avg_ms"] * 1e-3) / 1e9) for k, v in calls.items()},
+        layer_gbs=(cb + sb) / (ms_step * 1e-3) / 1e9,
+    )
+    result["layer_hbm_frac"] = result["layer_gbs"] / HBM_PEAK_GBS
+    return result, inp
+
+
+def cpu_baseline_prefill(shape, inp, budget_s):
+    """The f64 oracle (conv + scan) on a bounded sample of the same workload, on the host's
+    cores. The sample is the full layer when it fits the budget, else the first D' channels
+    of every batch (all T), scaled to the whole layer by D / D'."""
+    import numpy as np
+
+    from oracle import oracle
+
+    B, T, D = shape.B, shape.T, shape.D
+    f64 = lambda a: np.ascontiguousarray(a, dtype=np.float64)
+
+    def run(dsub):
+        sl = slice(0, dsub)
+        a = dict(x=f64(inp["x"][:, :, sl]), z=f64(inp["z"][:, :, sl]), dt=f64(inp["dt"][:, :, sl]),
+                 Bm=f64(inp["Bm"]), Cm=f64(inp["Cm"]), conv_w=f64(inp["conv_w"][sl]),
+                 conv_b=f64(inp["conv_b"][sl]), conv_state=f64(inp["conv_state"][:, sl]),
+                 A_log=f64(inp["A_log"][sl]), D_skip=f64(inp["D_skip"][sl]),
+                 dt_bias=f64(inp["dt_bias"][sl]), ssm_state=f64(inp["ssm_state"][:, sl]))
+        t0 = time.perf_counter()
+        u, _ = oracle.conv1d_fwd(a["x"], a["conv_w"], a["conv_b"], a["conv_state"])
+        oracle.selective_scan_fwd(u, a["dt"], a["A_log"], a["Bm"], a["Cm"], a["D_skip"], a["z"],
+                                  a["dt_bias"], True, a["ssm_state"])
+        return time.perf_counter() - t0
+
+    probe_d = min(D, 64)
+    t_probe = run(probe_d)
+    est_full = t_probe * D / probe_d
+    if est_full <= budget_s / 2:
+        reps = max(1, int(budget_s / max(est_full, 1e-3) / 2))
+        elapsed = sum(run(D) for _ in range(reps))
+        value = B * T * reps / elapsed
+        sample = f"full layer (B={B}, T={T}, d_inner={D}) x {reps} runs"
+    else:
+        dsub = max(1, min(D, int(probe_d * budget_s / max(t_probe, 1e-6))))
+        elapsed = run(dsub)
+        value = B * T / (elapsed * D / dsub)
+        sample = (f"first {dsub} of {D} channels of every batch, all T={T}; "
+                  f"time scaled by {D}/{dsub}")
+    return dict(value=value, unit="tokens/s/layer", cores=oracle.threads(), kind="oracle",
+                sample=sample, seconds=elapsed)
+
+
+def bench_decode(args, shape):
+    import numpy as np
+    import torch
+
+    import mamba_selective_scan_fwd_amd as m
+    import workloads as W
+
+    L, B, D, N, K = shape.L, shape.B, shape.D, shape.N, shape.K
+    dev = torch.device("cuda:0")
+    P = W.decode_params(shape)
+    p = {k: torch.from_numpy(v).to(dev) for k, v in P.items()}
+    ring = 8  # distinct per-step inputs, resident in HBM, used round-robin
+    print(f"[bench] generating {ring} decode steps of inputs L={L} B={B} D={D}", file=sys.stderr, flush=True)
+    steps_in = []
+    for r in range(ring):
+        i = W.decode_step_inputs(shape, r)
+        steps_in.append({k: torch.from_numpy(v).to(dev) for k, v in i.items()})
+    cs = torch.zeros(L, B, D, K, device=dev)
+    hs = torch.zeros(L, B, D, N, device=dev)
+    u = torch.empty(L, B, D, device=dev)
+    y = torch.empty(L, B, D, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        si = steps_in[i % ring]
+        if ev:
+            ev[0].record(stream)
+        m.mamba_conv1d_step(si["x"], p["conv_w"], p["conv_b"], cs, u, stream=stream)
+        if ev:
+            ev[1].record(stream)
+        m.mamba_ssm_step(u, si["dt"], p["dt_bias"], p["A_log"], si["Bm"], si["Cm"], p["D_skip"],
+                         si["z"], hs, y, stream=stream)
+        if ev:
+            ev[2].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
+    t_start, t_end = _events(torch)
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(i, evs[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    conv_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    ssm_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    ms_step = total_ms / args.steps
+    cb = conv_step_bytes(4, L, B, D, K)
+    sb = ssm_step_bytes(4, L, B, D, N)
+    calls = {
+        "mamba_conv1d_step": dict(avg_ms=sum(conv_ms) / len(conv_ms), min_ms=min(conv_ms), bytes=cb,
+                                  kernel_file="conv1d.hip"),
+        "mamba_ssm_step": dict(avg_ms=sum(ssm_ms) / len(ssm_ms), min_ms=min(ssm_ms), bytes=sb,
+                               kernel_file="step.hip"),
+    }
+    dom_name = max(calls, key=lambda k: calls[k]["avg_ms"])
+    dom = calls[dom_name]
+    achieved = dom["bytes"] / (dom["avg_ms"] * 1e-3) / 1e9
+    result = dict(
+        metric=METRIC,
+        value=L * B / (ms_step * 1e-3),
+        unit="tokens/s/layer",
+        ms_per_step=ms_step,
+        dtype="f32",
+        config=dict(workload=f"{shape.name}: batched T=1 decode step, {L} independent layers in one "
+                             f"launch per call, B={B} d_inner={D} d_state={N} d_conv={K} f32",
+                    L=L, B=B, d_inner=D, d_state=N, d_conv=K, io_dtype="f32", step_bytes=cb + sb),
+        roofline=dict(bound="hbm", achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s",
+                      frac=achieved / HBM_PEAK_GBS,
+                      traffic=measured_traffic(dom["kernel_file"], shape.name), call=dom_name,
+                      algorithmic_bytes=dom["bytes"], avg_ms=dom["avg_ms"]),
+        calls={k: dict(avg_us=v["avg_ms"] * 1e3, min_us=v["min_ms"] * 1e3,
+                       gbs=v["bytes"] / (v["avg_ms"] * 1e-3) / 1e9) for k, v in calls.items()},
+        layer_gbs=(cb + sb) / (ms_step * 1e-3) / 1e9,
+    )
+    result["layer_hbm_frac"] = result["layer_gbs"] / HBM_PEAK_GBS
+    return result, None
+
+
+def main(argv=None):
+    args = parse_args(argv)
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: this build runs the hot path on one GPU only; --gpus {args.gpus} "
+              f"(WORLD_SIZE={world}) is not supported. The work shards across GPUs by batch or "
+              "d_inner with no communication; run one process per GPU on its own share.",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    shape = W.CONFIGS[args.config]
+    if args.config == "c2":
+        result, inp = bench_decode(args, shape)
+    else:
+        result, inp = bench_prefill(args, shape)
+    cpu = None
+    if not args.no_cpu_baseline and inp is not None:
+        print("[bench] timing the CPU oracle baseline", file=sys.stderr, flush=True)
+        cpu = cpu_baseline_prefill(shape, inp, args.cpu_seconds)
+    line = dict(
+        metric=result["metric"], value=result["value"], unit=result["unit"], n_gpus=1,
+        steps=args.steps, warmup=args.warmup, ms_per_step=result["ms_per_step"],
+        higher_is_better=True, scaling="weak", vs_baseline=None, dtype=result["dtype"],
+        data="synthetic", config=result["config"], roofline=result["roofline"],
+        cpu_baseline=cpu, calls=result["calls"], layer_gbs=result["layer_gbs"],
+        layer_hbm_frac=result["layer_hbm_frac"])
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

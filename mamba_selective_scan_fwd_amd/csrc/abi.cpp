@@ -22,6 +22,8 @@ thread_local std::string g_last_error;
 constexpr int kMaxN = 64;
 constexpr int kMaxK = 8;
 constexpr int kMaxGridYZ = 65535;
+// Row strides (in elements) the kernels address with 32-bit buffer offsets over 8-row blocks.
+constexpr int64_t kMaxRowStride = int64_t(1) << 24;
 
 struct Fail {
   mamba_status status;
@@ -119,6 +121,7 @@ mamba_status mamba_conv1d_fwd(const void* x, int64_t x_row_stride, const float* 
     if ((int64_t)B * T == 0 || D == 0) return;
     const size_t es = elem_size(io_dtype);
     if (x_row_stride < D) fail(MAMBA_EINVAL, fn, "x_row_stride = %lld is less than D = %d", (long long)x_row_stride, D);
+    if (x_row_stride > kMaxRowStride) fail(MAMBA_EUNSUPPORTED, fn, "x_row_stride = %lld exceeds %lld", (long long)x_row_stride, (long long)kMaxRowStride);
     check_ptr(fn, "x", x, es, true);
     check_ptr(fn, "conv_w", conv_w, 4, true);
     check_ptr(fn, "conv_b", conv_b, 4, false);
@@ -175,6 +178,8 @@ mamba_status mamba_selective_scan_fwd(const void* u, const void* dt, const float
     }
     if (bc_row_stride < N) fail(MAMBA_EINVAL, fn, "bc_row_stride = %lld is less than N = %d", (long long)bc_row_stride, N);
     if (z && z_row_stride < D) fail(MAMBA_EINVAL, fn, "z_row_stride = %lld is less than D = %d", (long long)z_row_stride, D);
+    if (D > kMaxRowStride || (z && z_row_stride > kMaxRowStride))
+      fail(MAMBA_EUNSUPPORTED, fn, "D or z_row_stride exceeds %lld elements", (long long)kMaxRowStride);
     check_ptr(fn, "u", u, es, true);
     check_ptr(fn, "dt", dt, es, true);
     check_ptr(fn, "dt_bias", dt_bias, 4, false);

@@ -6,61 +6,134 @@
 // the mixed chain's conv-step-with-SiLU kernel -- one token against the d_conv-slot shift
 // register held in GpuInferenceState.
 //
-// Layout: lanes run along d, so every load and store of a [.., T, D] row is coalesced
-// (64 consecutive channels per wave). Each thread walks a tile of tokens keeping the last
-// K-1 inputs in registers.
+// Layout: lanes run along d, so every load and store of a [.., T, D] row is coalesced. In the
+// prefill a thread owns 4 consecutive channels (16-byte f32 / 8-byte bf16 accesses) when the
+// shape allows, and walks a tile of tokens keeping the last K-1 inputs in registers, with the
+// next 8 rows already in flight.
+#include <algorithm>
+
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace mamba {
 
-// One thread per (b, d, token tile). Tile 0 of each channel is the only reader of the old
-// conv state (for t < K-1) and the only writer of the new one, so an in-place state update
-// never races with another tile.
-template <typename IO, int K>
+// V consecutive channels of one row, widened to f32 (V = 4: one 16-byte (f32) or 8-byte
+// (bf16) access; V = 1: one element).
+template <typename IO, int V>
+struct Vec {
+  static __device__ __forceinline__ void load(float (&v)[V], const IO* p) {
+    if constexpr (V == 1) {
+      v[0] = to_f32(p[0]);
+    } else if constexpr (sizeof(IO) == 4) {
+      const float4 f = *reinterpret_cast<const float4*>(p);
+      v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
+    } else {
+      const uint2 r = *reinterpret_cast<const uint2*>(p);
+      v[0] = __uint_as_float(r.x << 16);
+      v[1] = __uint_as_float(r.x & 0xffff0000u);
+      v[2] = __uint_as_float(r.y << 16);
+      v[3] = __uint_as_float(r.y & 0xffff0000u);
+    }
+  }
+  static __device__ __forceinline__ void store(IO* p, const float (&v)[V]) {
+    if constexpr (V == 1) {
+      p[0] = from_f32<IO>(v[0]);
+    } else if constexpr (sizeof(IO) == 4) {
+      *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+    } else {
+      IO h[4] = {from_f32<IO>(v[0]), from_f32<IO>(v[1]), from_f32<IO>(v[2]), from_f32<IO>(v[3])};
+      *reinterpret_cast<uint2*>(p) = *reinterpret_cast<const uint2*>(h);
+    }
+  }
+};
+
+// Tokens staged ahead: the rows of the next block are loaded while the current block is
+// computed, so each thread has one block of loads in flight.
+constexpr int kConvTB = 8;
+
+// One thread per (b, V channels, token tile). Tile 0 of each channel group is the only reader
+// of the old conv state (tiles after it start at t0 >= K-1) and the only writer of the new
+// one, so an in-place state update never races with another tile.
+template <typename IO, int K, int V>
 __global__ void __launch_bounds__(256) conv1d_fwd_kernel(
     const IO* __restrict__ x, int64_t x_row_stride, const float* __restrict__ conv_w,
     const float* __restrict__ conv_b, float* __restrict__ conv_state, IO* __restrict__ u, int B,
     int T, int D, int tile_t) {
-  const int d = blockIdx.x * blockDim.x + threadIdx.x;
+  const int d0 = (blockIdx.x * blockDim.x + threadIdx.x) * V;
   const int b = blockIdx.y;
   const int t0 = blockIdx.z * tile_t;
-  if (d >= D || t0 >= T) return;
+  if (d0 >= D || t0 >= T) return;
   const int t1 = min(T, t0 + tile_t);
 
-  float w[K];
+  float w[V][K], bias[V];
 #pragma unroll
-  for (int k = 0; k < K; ++k) w[k] = conv_w[(int64_t)d * K + k];
-  const float bias = conv_b ? conv_b[d] : 0.0f;
+  for (int v = 0; v < V; ++v) {
+#pragma unroll
+    for (int k = 0; k < K; ++k) w[v][k] = conv_w[(int64_t)(d0 + v) * K + k];
+    bias[v] = conv_b ? conv_b[d0 + v] : 0.0f;
+  }
 
-  // Window X = [state(K), x(T)]; token t needs X[t+1 .. t+K]. win[j] holds X[t+1+j] for
-  // j < K-1 before token t is read.
-  float old_state[K];
-  float win[K];
-  const IO* xb = x + (int64_t)b * T * x_row_stride + d;
-  float* st = conv_state ? conv_state + ((int64_t)b * D + d) * K : nullptr;
+  // Window X = [state(K), x(T)]; token t needs X[t+1 .. t+K]. win[v][j] holds X[t+1+j] of
+  // channel d0+v for j < K-1 before token t is read.
+  float old_state[V][K];
+  float win[V][K];
+  const IO* xb = x + (int64_t)b * T * x_row_stride + d0;
+  float* st = conv_state ? conv_state + ((int64_t)b * D + d0) * K : nullptr;
   if (t0 == 0) {
 #pragma unroll
-    for (int k = 0; k < K; ++k) old_state[k] = st ? st[k] : 0.0f;
+    for (int v = 0; v < V; ++v) {
 #pragma unroll
-    for (int j = 0; j + 1 < K; ++j) win[j] = old_state[j + 1];
+      for (int k = 0; k < K; ++k) old_state[v][k] = st ? st[v * K + k] : 0.0f;
+#pragma unroll
+      for (int j = 0; j + 1 < K; ++j) win[v][j] = old_state[v][j + 1];
+    }
   } else {
 #pragma unroll
     for (int j = 0; j + 1 < K; ++j) {
       const int tt = t0 - (K - 1) + j;  // X index t0+1+j  <->  token t0-(K-1)+j
-      win[j] = tt >= 0 ? to_f32(xb[(int64_t)tt * x_row_stride]) : (st ? st[K + tt] : 0.0f);
+      float r[V];
+      if (tt >= 0) {
+        Vec<IO, V>::load(r, xb + (int64_t)tt * x_row_stride);
+      } else {
+#pragma unroll
+        for (int v = 0; v < V; ++v) r[v] = st ? st[v * K + K + tt] : 0.0f;
+      }
+#pragma unroll
+      for (int v = 0; v < V; ++v) win[v][j] = r[v];
     }
   }
 
-  IO* ub = u + (int64_t)b * T * D + d;
-  for (int t = t0; t < t1; ++t) {
-    win[K - 1] = to_f32(xb[(int64_t)t * x_row_stride]);
-    float c = bias;
+  IO* ub = u + (int64_t)b * T * D + d0;
+  float cur[kConvTB][V], nxt[kConvTB][V];
 #pragma unroll
-    for (int k = 0; k < K; ++k) c = fmaf(w[k], win[k], c);
-    ub[(int64_t)t * D] = from_f32<IO>(silu(c));
+  for (int j = 0; j < kConvTB; ++j) Vec<IO, V>::load(cur[j], xb + (int64_t)min(t0 + j, t1 - 1) * x_row_stride);
+  for (int tb = t0; tb < t1; tb += kConvTB) {
+    if (tb + kConvTB < t1) {
 #pragma unroll
-    for (int j = 0; j + 1 < K; ++j) win[j] = win[j + 1];
+      for (int j = 0; j < kConvTB; ++j)
+        Vec<IO, V>::load(nxt[j], xb + (int64_t)min(tb + kConvTB + j, t1 - 1) * x_row_stride);
+    }
+#pragma unroll
+    for (int j = 0; j < kConvTB; ++j) {
+      const int t = tb + j;
+      if (t >= t1) break;
+      float out[V];
+#pragma unroll
+      for (int v = 0; v < V; ++v) {
+        win[v][K - 1] = cur[j][v];
+        float c = bias[v];
+#pragma unroll
+        for (int k = 0; k < K; ++k) c = fmaf(w[v][k], win[v][k], c);
+        out[v] = silu(c);
+#pragma unroll
+        for (int i = 0; i + 1 < K; ++i) win[v][i] = win[v][i + 1];
+      }
+      Vec<IO, V>::store(ub + (int64_t)t * D, out);
+    }
+#pragma unroll
+    for (int j = 0; j < kConvTB; ++j)
+#pragma unroll
+      for (int v = 0; v < V; ++v) cur[j][v] = nxt[j][v];
   }
 
   if (t0 == 0 && st) {
@@ -69,7 +142,15 @@ __global__ void __launch_bounds__(256) conv1d_fwd_kernel(
 #pragma unroll
     for (int k = 0; k < K; ++k) {
       const int i = T + k;
-      st[k] = i >= K ? to_f32(xb[(int64_t)(i - K) * x_row_stride]) : old_state[i];
+      float r[V];
+      if (i >= K) {
+        Vec<IO, V>::load(r, xb + (int64_t)(i - K) * x_row_stride);
+      } else {
+#pragma unroll
+        for (int v = 0; v < V; ++v) r[v] = old_state[v][i];
+      }
+#pragma unroll
+      for (int v = 0; v < V; ++v) st[v * K + k] = r[v];
     }
   }
 }
@@ -116,22 +197,37 @@ __global__ void __launch_bounds__(256) conv1d_step_kernel(
 
 // ------------------------------------------------------------------------------ launchers
 
-template <typename IO, int K>
-static hipError_t launch_conv_fwd_k(const ConvFwdArgs& a, hipStream_t s) {
-  const int threads = 64;
-  // Enough token tiles to put several waves on every SIMD; at least 16 tokens per tile so
-  // the K-1 halo reads stay a small fraction.
-  const int64_t waves_per_tile = (int64_t)a.B * ((a.D + threads - 1) / threads);
-  int tiles = (int)((4096 + waves_per_tile - 1) / waves_per_tile);
-  tiles = max(1, min(tiles, (a.T + 15) / 16));
-  // Tiles after the first must start at t0 >= K-1 so that only tile 0 reads the old state.
-  const int tile_t = max((a.T + tiles - 1) / tiles, K);
-  tiles = (a.T + tile_t - 1) / tile_t;
-  dim3 grid((a.D + threads - 1) / threads, a.B, tiles);
-  conv1d_fwd_kernel<IO, K><<<grid, threads, 0, s>>>(
+template <typename IO, int K, int V>
+static hipError_t launch_conv_fwd_kv(const ConvFwdArgs& a, hipStream_t s, int tile_t, int tiles) {
+  const int threads = 256;
+  const int lanes = (a.D + V - 1) / V;
+  dim3 grid((lanes + threads - 1) / threads, a.B, tiles);
+  conv1d_fwd_kernel<IO, K, V><<<grid, threads, 0, s>>>(
       static_cast<const IO*>(a.x), a.x_row_stride, a.conv_w, a.conv_b, a.conv_state,
       static_cast<IO*>(a.u), a.B, a.T, a.D, tile_t);
   return hipGetLastError();
+}
+
+// Token tiles: enough (b, channel group, tile) threads for ~16 waves per CU, tiles of at
+// least 16 tokens (the K-1 halo stays a small fraction) and at least K tokens (tiles after
+// the first never touch the old state). Four channels per thread when that still fills the
+// chip and rows are 16-byte aligned; one otherwise.
+template <typename IO, int K>
+static hipError_t launch_conv_fwd_k(const ConvFwdArgs& a, hipStream_t s) {
+  const int64_t target_threads = 256 * 16 * 64;
+  const size_t es = sizeof(IO);
+  const bool vec_ok = a.D % 4 == 0 && a.x_row_stride % 4 == 0 &&
+                      ((reinterpret_cast<uintptr_t>(a.x) | reinterpret_cast<uintptr_t>(a.u)) % (4 * es)) == 0 &&
+                      (reinterpret_cast<uintptr_t>(a.conv_w) % 16) == 0;
+  const int max_tiles = std::max(1, (a.T + 15) / 16);
+  const bool vec = vec_ok && (int64_t)a.B * (a.D / 4) * max_tiles >= target_threads;
+  const int64_t per_tile = (int64_t)a.B * (vec ? a.D / 4 : a.D);
+  int tiles = (int)std::min<int64_t>(max_tiles, (target_threads + per_tile - 1) / per_tile);
+  tiles = std::min(std::max(tiles, 1), 65535);  // grid z limit
+  const int tile_t = std::max((a.T + tiles - 1) / tiles, K);
+  tiles = (a.T + tile_t - 1) / tile_t;
+  return vec ? launch_conv_fwd_kv<IO, K, 4>(a, s, tile_t, tiles)
+             : launch_conv_fwd_kv<IO, K, 1>(a, s, tile_t, tiles);
 }
 
 template <typename IO>

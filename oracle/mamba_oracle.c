@@ -24,6 +24,9 @@
 #include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 /* softplus(v) = log(1 + exp(v)), in the overflow-free form.
  * [inference.rs] step chain F7 (dt_proj then softplus); [prefill.rs] prefill_body F4c. */
@@ -35,6 +38,15 @@ static double silu(double v) { return v / (1.0 + exp(-v)); }
 
 double oracle_softplus(double v) { return softplus(v); }
 double oracle_silu(double v) { return silu(v); }
+
+/* Threads the channel loops run on (for reporting the CPU baseline's core count). */
+int oracle_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
 
 /*
  * Prefill causal depthwise conv1d + SiLU over T tokens, carrying the conv state.

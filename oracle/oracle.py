@@ -65,6 +65,8 @@ def lib() -> ctypes.CDLL:
         L.oracle_softplus.restype = ctypes.c_double
         L.oracle_silu.argtypes = [ctypes.c_double]
         L.oracle_silu.restype = ctypes.c_double
+        L.oracle_threads.argtypes = []
+        L.oracle_threads.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -77,6 +79,11 @@ def _f64(a):
 
 def _p(a):
     return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def threads() -> int:
+    """OpenMP threads the oracle's channel loops use."""
+    return int(lib().oracle_threads())
 
 
 def softplus(v: float) -> float:
