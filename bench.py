@@ -41,6 +41,9 @@ def parse_args(argv=None):
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="approximate CPU time budget for the oracle baseline")
+    p.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
+                   help="only run a plain device copy of BYTES bytes a few times (the reference "
+                        "kernel for scaling rocprofv3 FETCH_SIZE/WRITE_SIZE) and exit")
     return p.parse_args(argv)
 
 
@@ -331,6 +334,15 @@ def main(argv=None):
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.calibrate_copy:
+        n = args.calibrate_copy // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps(dict(calibrate_copy_bytes=n * 4, launches=3)), flush=True)
+        return
     shape = W.CONFIGS[args.config]
     if args.config == "c2":
         result, inp = bench_decode(args, shape)

@@ -310,3 +310,65 @@ def test_decode_bf16_io():
     torch.cuda.synchronize()
     for l in range(2):
         assert rel_err(host(hs[l]), h_ref[l]) <= 2e-2
+
+
+def test_c2_full_size_1000_steps_sampled():
+    """The 24-layer, B=64, d_inner=1536 decode workload for 1000 steps in the launch
+    configuration bench.py times (both calls cover all 24 layers). Inputs are drawn per step
+    on the device; for 40 sampled (layer, batch, channel) triples the inputs are copied out and
+    the oracle replays all 1000 steps; y is checked at steps 0, 1, 9, 99, 499, 999 and both
+    states at the end."""
+    _say("case c2 full size: 24 layers, B64, D1536, 1000 steps")
+    shape = W.C2
+    L, Bsz, D, N, K = shape.L, shape.B, shape.D, shape.N, shape.K
+    P = W.decode_params(shape)
+    p = {k: dev(v) for k, v in P.items()}
+    cs = torch.zeros(L, Bsz, D, K, device="cuda")
+    hs = torch.zeros(L, Bsz, D, N, device="cuda")
+    u = torch.empty(L, Bsz, D, device="cuda")
+    y = torch.empty(L, Bsz, D, device="cuda")
+    g = np.random.default_rng(21)
+    picks = [(0, 0, 0), (L - 1, Bsz - 1, D - 1)] + [
+        (int(g.integers(L)), int(g.integers(Bsz)), int(g.integers(D))) for _ in range(38)]
+    li = torch.tensor([q[0] for q in picks], device="cuda")
+    bi = torch.tensor([q[1] for q in picks], device="cuda")
+    di = torch.tensor([q[2] for q in picks], device="cuda")
+    check_steps = {0, 1, 9, 99, 499, 999}
+    rec = {k: [] for k in ("x", "z", "dt", "Bm", "Cm")}
+    ys = {}
+    for t in range(shape.steps):
+        i = W.decode_step_inputs_torch(shape, t)
+        m.mamba_conv1d_step(i["x"], p["conv_w"], p["conv_b"], cs, u)
+        m.mamba_ssm_step(u, i["dt"], p["dt_bias"], p["A_log"], i["Bm"], i["Cm"], p["D_skip"], i["z"], hs, y)
+        for k in ("x", "z", "dt"):
+            rec[k].append(i[k][li, bi, di])
+        rec["Bm"].append(i["Bm"][li, bi])
+        rec["Cm"].append(i["Cm"][li, bi])
+        if t in check_steps:
+            ys[t] = y[li, bi, di].clone()
+        if t % 250 == 0:
+            _say(f"  c2 step {t}")
+    torch.cuda.synchronize()
+    r = {k: torch.stack(v).cpu().numpy() for k, v in rec.items()}  # [steps, picks, ...]
+    cs_g = cs[li, bi, di].cpu().numpy()
+    hs_g = hs[li, bi, di].cpu().numpy()
+    ys = {t: v.cpu().numpy() for t, v in ys.items()}
+    yref = {t: np.zeros(len(picks)) for t in ys}
+    for q, (l, b, d) in enumerate(picks):
+        sel = slice(d, d + 1)
+        c_ref = np.zeros((1, 1, K))
+        h_ref = np.zeros((1, 1, N))
+        for t in range(shape.steps):
+            u_ref, c_ref = oracle.conv1d_step(r["x"][t, q].reshape(1, 1), P["conv_w"][l, sel],
+                                              P["conv_b"][l, sel], c_ref)
+            y_ref, h_ref = oracle.ssm_step(u_ref, r["dt"][t, q].reshape(1, 1), P["A_log"][l, sel],
+                                           r["Bm"][t, q].reshape(1, N), r["Cm"][t, q].reshape(1, N),
+                                           P["D_skip"][l, sel], r["z"][t, q].reshape(1, 1),
+                                           P["dt_bias"][l, sel], h_ref)
+            if t in ys:
+                yref[t][q] = y_ref[0, 0]
+        assert rel_err(cs_g[q], c_ref[0, 0]) <= 1e-6, (l, b, d)
+        assert rel_err(hs_g[q], h_ref[0, 0]) <= 1e-4, (l, b, d)
+    errs = {t: rel_err(ys[t], yref[t]) for t in sorted(ys)}
+    _say("c2 sampled y errors by step", {t: f"{e:.2e}" for t, e in errs.items()})
+    assert max(errs.values()) <= 1e-4

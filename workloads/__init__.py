@@ -223,3 +223,35 @@ def decode_step_inputs(shape: DecodeShape, step: int, seed: int = 0, cfg: int = 
         out["Bm"].append(normal(rng(seed, cfg, BM, l, step), (shape.B, shape.N)))
         out["Cm"].append(normal(rng(seed, cfg, CM, l, step), (shape.B, shape.N)))
     return {k: store(np.stack(v), shape.io) for k, v in out.items()}
+
+
+# --------------------------------------------------- device-side decode inputs
+
+def torch_generator(seed: int, cfg: int, tensor: int, layer: int = 0, step: int = 0, device="cuda"):
+    """A torch generator on `device` keyed like rng(): for inputs too large to draw on the host
+    (1000 decode steps x 24 layers). Deterministic for a given torch build and device type."""
+    import torch
+
+    key = int(np.random.SeedSequence([seed, cfg, tensor, layer, step]).generate_state(1, np.uint64)[0])
+    g = torch.Generator(device=device)
+    g.manual_seed(key & ((1 << 63) - 1))
+    return g
+
+
+def decode_step_inputs_torch(shape: DecodeShape, step: int, seed: int = 0, cfg: int = 2,
+                             device="cuda") -> dict:
+    """Per-step decode inputs drawn on the device: x, z, dt [L,B,D]; Bm, Cm [L,B,N] (f32,
+    same distributions as decode_step_inputs, different streams)."""
+    import torch
+
+    L, B, D, N = shape.L, shape.B, shape.D, shape.N
+    out = {}
+    for name, tid, shp, std in (("x", X, (L, B, D), 1.0), ("z", Z, (L, B, D), 1.0),
+                                ("dt", DT, (L, B, D), 0.1), ("Bm", BM, (L, B, N), 1.0),
+                                ("Cm", CM, (L, B, N), 1.0)):
+        g = torch_generator(seed, cfg, tid, 0, step, device)
+        t = torch.randn(shp, generator=g, device=device, dtype=torch.float32)
+        out[name] = t * std if std != 1.0 else t
+    if shape.io == "bf16":
+        out = {k: v.to(torch.bfloat16) for k, v in out.items()}
+    return out
