@@ -8,7 +8,9 @@ both through the C-ABI, carrying the conv and SSM states from step to step.
 
 Default workload: the 130m-shaped prefill layer (B=1, T=2048, d_inner=1536, d_state=16,
 d_conv=4, f32 I/O). --config c3 runs the 2.8b-shaped layer (B=8, T=4096, d_inner=5120,
-bf16 I/O); --config c2 the batched decode step (24 layers, B=64, one token per step).
+bf16 I/O); --config c2 the batched decode step (24 layers, B=64, one token per step);
+--config c4 the full 24-layer 130m-shaped backbone prefill (B=4, T=2048, bf16 weights, MFMA
+GEMMs), one mamba_backbone_prefill call per step.
 
 Prints one JSON line. `value` is tokens/s/layer (batch tokens per step / step time);
 `roofline` covers the dominant kernel call, timed with HIP events on the stream it runs
@@ -29,6 +31,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 METRIC = "selective-scan prefill tokens/s/layer (d_inner=1536/5120) + HBM GB/s % peak"
 
 
@@ -37,7 +40,7 @@ def parse_args(argv=None):
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--config", default="c1", choices=["c1", "c3", "c2"])
+    p.add_argument("--config", default="c1", choices=["c1", "c3", "c2", "c4"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="approximate CPU time budget for the oracle baseline")
@@ -318,6 +321,180 @@ def bench_decode(args, shape):
     return result, None
 
 
+def gemm_flops(M, N, K):
+    return 2.0 * M * N * K
+
+
+def bench_backbone(args, shape):
+    """One step = one mamba_backbone_prefill call (embedding, 24 layers, norm_f, tied head).
+    A second timed region runs layer 0's chain through the piece entry points (the same
+    kernels the backbone call launches) with an event around every call, for the per-kernel
+    breakdown and the roofline of the dominant one."""
+    import numpy as np
+    import torch
+
+    import mamba_selective_scan_fwd_amd as m
+    import workloads as W
+
+    L, B, T, Dm, D, N, K, R = (shape.n_layers, shape.B, shape.T, shape.d_model, shape.D, shape.N,
+                               shape.K, shape.dt_rank)
+    xw = R + 2 * N
+    dev = torch.device("cuda:0")
+    print(f"[bench] generating {shape.name} weights and tokens (L={L} B={B} T={T})", file=sys.stderr,
+          flush=True)
+    w = W.backbone_weights(shape)
+    tok_np = W.backbone_tokens(shape)
+    bf = ("embed", "in_proj", "x_proj", "dt_proj", "out_proj")
+    t = {k: torch.from_numpy(np.ascontiguousarray(v)).to(torch.bfloat16 if k in bf else torch.float32).to(dev)
+         for k, v in w.items()}
+    wst = m.backbone_weights_struct(t)
+    dims = m.BackboneDims(L, Dm, D, N, K, R, shape.vocab, shape.vocab_padded, shape.eps)
+    tokens = torch.from_numpy(tok_np).to(dev)
+    cs = torch.zeros(L, B, D, K, device=dev)
+    hs = torch.zeros(L, B, D, N, device=dev)
+    logits = torch.empty(B, shape.vocab, device=dev)
+    ws = torch.empty(m.mamba_backbone_workspace_size(dims, B, T), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        m.mamba_backbone_prefill(dims, wst, tokens, cs, hs, logits, ws, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done ({args.warmup} steps); timing {args.steps} steps", file=sys.stderr,
+          flush=True)
+    t_start, t_end = _events(torch)
+    t_start.record(stream)
+    for _ in range(args.steps):
+        step()
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t_start.elapsed_time(t_end) / args.steps
+    assert torch.isfinite(logits).all(), "non-finite logits"
+
+    # per-kernel breakdown: layer 0 through the piece entry points
+    bt = B * T
+    h = torch.empty(bt, Dm, device=dev)
+    xn = torch.empty(bt, Dm, dtype=torch.bfloat16, device=dev)
+    proj = torch.empty(bt, 2 * D, device=dev)
+    u = torch.empty(B, T, D, device=dev)
+    xdbl = torch.empty(bt, xw, device=dev)
+    dtb = torch.empty(B, T, D, device=dev)
+    y = torch.empty(B, T, D, device=dev)
+    last = torch.empty(B, Dm, dtype=torch.bfloat16, device=dev)
+    lg2 = torch.empty(B, shape.vocab, device=dev)
+    sws = m.scan_workspace(B, T, D, N)
+    cs0 = torch.zeros(B, D, K, device=dev)
+    hs0 = torch.zeros(B, D, N, device=dev)
+    proj3 = proj.view(B, T, 2 * D)
+    xdbl3 = xdbl.view(B, T, xw)
+    pieces = [
+        ("embed_gather", lambda: m.mamba_embed_gather(tokens, t["embed"], h, shape.vocab, stream=stream),
+         None, 2 * bt * Dm + 4 * bt * Dm + 4 * bt),
+        ("rmsnorm", lambda: m.mamba_rmsnorm(h, t["norm_w"][0], shape.eps, xn, stream=stream),
+         None, 4 * bt * Dm + 2 * bt * Dm + 4 * Dm),
+        ("gemm in_proj", lambda: m.mamba_gemm_bf16(xn, t["in_proj"][0], proj, stream=stream),
+         gemm_flops(bt, 2 * D, Dm), 2 * bt * Dm + 2 * 2 * D * Dm + 4 * bt * 2 * D),
+        ("conv1d_fwd", lambda: m.mamba_conv1d_fwd(proj3[..., :D], t["conv_w"][0], t["conv_b"][0], cs0, u,
+                                                  stream=stream),
+         None, conv_bytes(4, B, T, D, K)),
+        ("gemm x_proj", lambda: m.mamba_gemm_bf16(u.view(bt, D), t["x_proj"][0], xdbl, stream=stream),
+         gemm_flops(bt, xw, D), 4 * bt * D + 2 * xw * D + 4 * bt * xw),
+        ("gemm dt_proj", lambda: m.mamba_gemm_bf16(xdbl, t["dt_proj"][0], dtb.view(bt, D), K=R, lda=xw,
+                                                   stream=stream),
+         gemm_flops(bt, D, R), 4 * bt * R + 2 * D * R + 4 * bt * D),
+        ("selective_scan_fwd", lambda: m.mamba_selective_scan_fwd(
+            u, dtb, t["dt_bias"][0], t["A_log"][0], xdbl3[..., R:R + N], xdbl3[..., R + N:],
+            t["D_skip"][0], proj3[..., D:], hs0, hs0, y, workspace=sws, stream=stream),
+         None, scan_bytes(4, B, T, D, N)),
+        ("gemm out_proj", lambda: m.mamba_gemm_bf16(y.view(bt, D), t["out_proj"][0], h, accumulate=True,
+                                                    stream=stream),
+         gemm_flops(bt, Dm, D), 4 * bt * D + 2 * Dm * D + 8 * bt * Dm),
+        ("gemm head", lambda: m.mamba_gemm_bf16(last, t["embed"], lg2, N=shape.vocab, stream=stream),
+         gemm_flops(B, shape.vocab, Dm), 2 * shape.vocab * Dm + 2 * B * Dm + 4 * B * shape.vocab),
+    ]
+    reps = max(5, min(args.steps, 50))
+    for _, fn, _, _ in pieces:
+        fn()
+    torch.cuda.synchronize()
+    evs = [[_events(torch) for _ in pieces] for _ in range(reps)]
+    for r in range(reps):
+        for (_, fn, _, _), (e0, e1) in zip(pieces, evs[r]):
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+    torch.cuda.synchronize()
+    calls = {}
+    for i, (name, _, flops, nbytes) in enumerate(pieces):
+        ms = [evs[r][i][0].elapsed_time(evs[r][i][1]) for r in range(reps)]
+        avg = sum(ms) / len(ms)
+        c = dict(avg_us=avg * 1e3, min_us=min(ms) * 1e3, gbs=nbytes / (avg * 1e-3) / 1e9)
+        if flops:
+            c["tflops"] = flops / (avg * 1e-3) / 1e12
+        calls[name] = c
+    per_layer = ("rmsnorm", "gemm in_proj", "conv1d_fwd", "gemm x_proj", "gemm dt_proj",
+                 "selective_scan_fwd", "gemm out_proj")
+    dom_name = max(per_layer, key=lambda k: calls[k]["avg_us"])
+    dom = calls[dom_name]
+    flops, nbytes = next((f, b) for n, _, f, b in pieces if n == dom_name)
+    if flops:
+        achieved = flops / (dom["avg_us"] * 1e-6) / 1e12
+        roof = dict(bound="mfma", achieved=achieved, peak=MFMA_BF16_PEAK_TFLOPS, unit="TFLOP/s",
+                    frac=achieved / MFMA_BF16_PEAK_TFLOPS, traffic=None, call=dom_name,
+                    algorithmic_flops=flops, avg_ms=dom["avg_us"] * 1e-3)
+    else:
+        achieved = nbytes / (dom["avg_us"] * 1e-6) / 1e9
+        kfile = "scan.hip" if "scan" in dom_name else "conv1d.hip"
+        roof = dict(bound="hbm", achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=achieved / HBM_PEAK_GBS, traffic=measured_traffic(kfile, shape.name),
+                    call=dom_name, algorithmic_bytes=nbytes, avg_ms=dom["avg_us"] * 1e-3)
+    layer_us = sum(calls[k]["avg_us"] for k in per_layer)
+    result = dict(
+        metric=METRIC,
+        value=B * T * L / (ms_step * 1e-3),
+        unit="tokens/s/layer",
+        ms_per_step=ms_step,
+        dtype="bf16",
+        config=dict(workload=f"{shape.name}: full {L}-layer Mamba-1 backbone prefill (embedding, RMSNorm, "
+                             f"in_proj/x_proj/dt_proj/out_proj bf16 MFMA GEMMs, conv1d, scan, residual, "
+                             f"norm_f, tied {shape.vocab}-vocab head), B={B} T={T} d_model={Dm} "
+                             f"d_inner={D} d_state={N} dt_rank={R}",
+                    B=B, T=T, n_layers=L, d_model=Dm, d_inner=D, d_state=N, d_conv=K, dt_rank=R,
+                    vocab=shape.vocab),
+        roofline=roof,
+        calls=calls,
+        backbone_tokens_per_s=B * T / (ms_step * 1e-3),
+        layer_chain_us=layer_us,
+        layer_gbs=None,
+        layer_hbm_frac=None,
+    )
+    return result, dict(weights=w, tokens=tok_np)
+
+
+def cpu_baseline_backbone(shape, data, budget_s):
+    """The f64 backbone oracle on sequence 0 of the batch over its first T' tokens, all layers
+    (T' from a probe so the run takes about budget_s)."""
+    from oracle import backbone as ob
+    from oracle import oracle
+
+    w, tok = data["weights"], data["tokens"]
+    L = shape.n_layers
+
+    def run(tp):
+        t0 = time.perf_counter()
+        ob.prefill(w, tok[:1, :tp], L, shape.D, shape.N, shape.dt_rank, shape.vocab, shape.eps)
+        return time.perf_counter() - t0
+
+    probe = min(shape.T, 64)
+    t_probe = run(probe)
+    tp = max(probe, min(shape.T, int(probe * budget_s / max(t_probe, 1e-6))))
+    elapsed = run(tp) if tp != probe else t_probe
+    return dict(value=tp * L / elapsed, unit="tokens/s/layer", cores=oracle.threads(), kind="oracle",
+                sample=f"sequence 0 of {shape.B}, first {tp} of {shape.T} tokens, all {L} layers and the head",
+                seconds=elapsed)
+
+
 def main(argv=None):
     args = parse_args(argv)
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -346,12 +523,17 @@ def main(argv=None):
     shape = W.CONFIGS[args.config]
     if args.config == "c2":
         result, inp = bench_decode(args, shape)
+    elif args.config == "c4":
+        result, inp = bench_backbone(args, shape)
     else:
         result, inp = bench_prefill(args, shape)
     cpu = None
     if not args.no_cpu_baseline and inp is not None:
         print("[bench] timing the CPU oracle baseline", file=sys.stderr, flush=True)
-        cpu = cpu_baseline_prefill(shape, inp, args.cpu_seconds)
+        if args.config == "c4":
+            cpu = cpu_baseline_backbone(shape, inp, args.cpu_seconds)
+        else:
+            cpu = cpu_baseline_prefill(shape, inp, args.cpu_seconds)
     line = dict(
         metric=result["metric"], value=result["value"], unit=result["unit"], n_gpus=1,
         steps=args.steps, warmup=args.warmup, ms_per_step=result["ms_per_step"],
@@ -359,6 +541,9 @@ def main(argv=None):
         data="synthetic", config=result["config"], roofline=result["roofline"],
         cpu_baseline=cpu, calls=result["calls"], layer_gbs=result["layer_gbs"],
         layer_hbm_frac=result["layer_hbm_frac"])
+    for extra in ("backbone_tokens_per_s", "layer_chain_us"):
+        if extra in result:
+            line[extra] = result[extra]
     print(json.dumps(line), flush=True)
 
 

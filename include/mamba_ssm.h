@@ -166,6 +166,98 @@ mamba_status mamba_ssm_step(const void* u, const void* dt, const float* dt_bias,
                             const void* z, int64_t z_row_stride, float* ssm_state, void* y,
                             mamba_dtype io_dtype, int L, int B, int D, int N, void* stream);
 
+/* ======================================================================================
+ * Full-backbone prefill (24-layer Mamba-1 stack) and the layer pieces around the SSM core.
+ * [prefill.rs] prefill_body: per layer RMSNorm (F1), in_proj (F2), conv + x_proj (F4a-F4b),
+ * dt_proj (F4c), scan (F4d), out_proj (F5), residual add (F6); then norm_f and the
+ * last-timestep gather. gpu_lm.rs page (mamba-rs 0.7.1): embedding lookup and the tied LM
+ * head, one GEMM against the embedding table with the vocabulary padded to a multiple of 64.
+ * Precision: weights bf16; GEMM operands bf16 (activations rounded as they enter the GEMM),
+ * f32 accumulation; residual stream, norms, conv, scan and states f32.
+ * ====================================================================================== */
+
+/*
+ * out[r, :] = E[tokens[r], :] as f32. tokens: [rows] int32 (ids outside [0, vocab) are
+ * clamped into range); E: [>= vocab, d_model] bf16, row-major; out: [rows, d_model] f32.
+ */
+mamba_status mamba_embed_gather(const int32_t* tokens, const void* E, float* out, int64_t rows,
+                                int vocab, int d_model, void* stream);
+
+/*
+ * RMSNorm: out[r, :] = x[r, :] / sqrt(mean(x[r, :]^2) + eps) * w  ([prefill.rs] F1 and norm_f).
+ * x: rows at x + r * x_row_stride (f32), d_model contiguous; w: [d_model] f32 or NULL (= 1);
+ * out: [rows, d_model] contiguous, f32 (out_dtype MAMBA_F32) or bf16 (MAMBA_BF16, the form
+ * a following GEMM takes). The last-token gather is x = h + (T-1)*d_model with
+ * x_row_stride = T*d_model.
+ */
+mamba_status mamba_rmsnorm(const float* x, int64_t x_row_stride, const float* w, float eps,
+                           void* out, mamba_dtype out_dtype, int64_t rows, int d_model,
+                           void* stream);
+
+/*
+ * C[M, N] = A[M, K] * W[N, K]^T   (accumulate == 0)
+ * C[M, N] += A[M, K] * W[N, K]^T  (accumulate != 0; the residual add fused into out_proj)
+ * A: f32 or bf16 (a_dtype), rows lda apart, rounded to bf16 on the way in; W: bf16, the
+ * nn.Linear layout (one row of K per output column), rows ldw apart; C: f32, rows ldc apart.
+ * bf16 MFMA (v_mfma_f32_16x16x32_bf16) with f32 accumulation; M <= 8 (with M * K * 4 bytes
+ * <= 64 KB) takes a streaming kernel instead (the LM head). accumulate != 0: C += A * W^T.
+ */
+mamba_status mamba_gemm_bf16(const void* A, mamba_dtype a_dtype, int64_t lda, const void* W,
+                             int64_t ldw, float* C, int64_t ldc, int M, int N, int K,
+                             int accumulate, void* stream);
+
+typedef struct mamba_backbone_dims {
+  int n_layers;      /* 24 for the 130m shape */
+  int d_model;       /* 768 */
+  int d_inner;       /* 1536 */
+  int d_state;       /* 16 (<= 64) */
+  int d_conv;        /* 4 (<= 8) */
+  int dt_rank;       /* 48 */
+  int vocab;         /* 50280: logits columns */
+  int vocab_padded;  /* 50304: rows of the embedding table (multiple of 64) */
+  float eps;         /* RMSNorm epsilon, 1e-5 */
+} mamba_backbone_dims;
+
+/* Device pointers to layer-stacked weights (index l is layer l, contiguous):
+ * embed [vocab_padded, d_model] bf16 (also the tied head; padded rows are never selected),
+ * norm_f [d_model] f32, norm_w [L, d_model] f32, in_proj [L, 2*d_inner, d_model] bf16
+ * (rows 0..d_inner-1 make the x lane, d_inner..2*d_inner-1 the z lane), conv_w
+ * [L, d_inner, d_conv] f32, conv_b [L, d_inner] f32, x_proj [L, dt_rank + 2*d_state, d_inner]
+ * bf16 (output columns: dt lane, then B, then C), dt_proj [L, d_inner, dt_rank] bf16,
+ * dt_bias [L, d_inner] f32, A_log [L, d_inner, d_state] f32, D_skip [L, d_inner] f32,
+ * out_proj [L, d_model, d_inner] bf16. */
+typedef struct mamba_backbone_weights {
+  const void* embed;
+  const float* norm_f;
+  const float* norm_w;
+  const void* in_proj;
+  const float* conv_w;
+  const float* conv_b;
+  const void* x_proj;
+  const void* dt_proj;
+  const float* dt_bias;
+  const float* A_log;
+  const float* D_skip;
+  const void* out_proj;
+} mamba_backbone_weights;
+
+/* Bytes of workspace mamba_backbone_prefill needs for B sequences of T tokens. */
+size_t mamba_backbone_workspace_size(const mamba_backbone_dims* dims, int B, int T);
+
+/*
+ * Prefill B prompts of T tokens through the whole backbone and return the logits of the last
+ * token of each ([prefill.rs] gpu_forward_inference_prefill; gpu_lm.rs compute_logits).
+ * tokens: [B, T] int32; conv_state [L][B][d_inner][d_conv] and ssm_state
+ * [L][B][d_inner][d_state] f32 in/out (prefill continues from them, as the pages' prefill
+ * never zeroes the state); logits: [B, vocab] f32. The layer loop runs on the host and
+ * enqueues every kernel on `stream`; nothing is synchronized or allocated.
+ */
+mamba_status mamba_backbone_prefill(const mamba_backbone_dims* dims,
+                                    const mamba_backbone_weights* weights,
+                                    const int32_t* tokens, int B, int T, float* conv_state,
+                                    float* ssm_state, float* logits, void* workspace,
+                                    size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -14,7 +14,8 @@ __all__ = [
     "MambaError", "MAMBA_F32", "MAMBA_BF16", "library_path", "load_library", "symbols",
     "mamba_version", "mamba_last_error", "mamba_conv1d_fwd", "mamba_selective_scan_fwd",
     "mamba_selective_scan_workspace_size", "mamba_conv1d_step", "mamba_ssm_step",
-    "scan_workspace",
+    "scan_workspace", "mamba_embed_gather", "mamba_rmsnorm", "mamba_gemm_bf16",
+    "BackboneDims", "BackboneWeights", "mamba_backbone_workspace_size", "mamba_backbone_prefill",
 ]
 
 MAMBA_F32 = 0
@@ -35,7 +36,26 @@ symbols = {
     "mamba_conv1d_step": ([_P, _I64, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P], _I),
     "mamba_ssm_step": ([_P, _P, _P, _I, _P, _P, _P, _I64, _P, _P, _I64, _P, _P, _I, _I, _I,
                         _I, _I, _P], _I),
+    "mamba_embed_gather": ([_P, _P, _P, _I64, _I, _I, _P], _I),
+    "mamba_rmsnorm": ([_P, _I64, _P, ctypes.c_float, _P, _I, _I64, _I, _P], _I),
+    "mamba_gemm_bf16": ([_P, _I, _I64, _P, _I64, _P, _I64, _I, _I, _I, _I, _P], _I),
+    "mamba_backbone_workspace_size": ([_P, _I, _I], _SZ),
+    "mamba_backbone_prefill": ([_P, _P, _P, _I, _I, _P, _P, _P, _P, _SZ, _P], _I),
 }
+
+
+class BackboneDims(ctypes.Structure):
+    """mamba_backbone_dims."""
+    _fields_ = [("n_layers", ctypes.c_int), ("d_model", ctypes.c_int), ("d_inner", ctypes.c_int),
+                ("d_state", ctypes.c_int), ("d_conv", ctypes.c_int), ("dt_rank", ctypes.c_int),
+                ("vocab", ctypes.c_int), ("vocab_padded", ctypes.c_int), ("eps", ctypes.c_float)]
+
+
+class BackboneWeights(ctypes.Structure):
+    """mamba_backbone_weights: device pointers of the layer-stacked weights."""
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "embed", "norm_f", "norm_w", "in_proj", "conv_w", "conv_b", "x_proj", "dt_proj",
+        "dt_bias", "A_log", "D_skip", "out_proj")]
 
 _STATUS = {1: "MAMBA_EINVAL", 2: "MAMBA_EUNSUPPORTED", 3: "MAMBA_EWORKSPACE", 4: "MAMBA_EHIP"}
 
@@ -196,3 +216,67 @@ def mamba_ssm_step(u, dt, dt_bias, A_log, Bm, Cm, D_skip, z, ssm_state, y,
         _ptr(u), _ptr(dt), _ptr(dt_bias), int(bool(delta_softplus)), _ptr(A_log), _ptr(Bm),
         _ptr(Cm), bcs, _ptr(D_skip), _ptr(z), zs, _ptr(ssm_state), _ptr(y), _io_dtype(u), L, Bsz,
         D, N, _stream(stream)))
+
+
+# ------------------------------------------------------------------ backbone pieces
+
+def mamba_embed_gather(tokens, E, out, vocab, stream=None) -> None:
+    """out[r, :] = E[tokens[r], :]. tokens int32 [rows]; E bf16 [>= vocab, d_model]; out f32."""
+    rows = tokens.numel()
+    _check(load_library().mamba_embed_gather(_ptr(tokens), _ptr(E), _ptr(out), rows, vocab,
+                                             E.shape[1], _stream(stream)))
+
+
+def mamba_rmsnorm(x, w, eps, out, rows=None, x_row_stride=None, stream=None) -> None:
+    """RMSNorm of `rows` rows of x (row stride x_row_stride, default contiguous) into out
+    (f32 or bf16, [rows, d_model] contiguous)."""
+    d_model = out.shape[-1]
+    rows = out.numel() // d_model if rows is None else rows
+    xs = d_model if x_row_stride is None else x_row_stride
+    _check(load_library().mamba_rmsnorm(_ptr(x), xs, _ptr(w), float(eps), _ptr(out), _io_dtype(out),
+                                        rows, d_model, _stream(stream)))
+
+
+def mamba_gemm_bf16(A, W, C, accumulate=False, M=None, N=None, K=None, lda=None, ldw=None,
+                    ldc=None, stream=None) -> None:
+    """C[M, N] (+)= A[M, K] @ W[N, K]^T with bf16 operands and f32 accumulation."""
+    M = A.shape[0] if M is None else M
+    K = W.shape[1] if K is None else K
+    N = W.shape[0] if N is None else N
+    lda = A.stride(0) if lda is None else lda
+    ldw = W.stride(0) if ldw is None else ldw
+    ldc = C.stride(0) if ldc is None else ldc
+    _check(load_library().mamba_gemm_bf16(_ptr(A), _io_dtype(A), lda, _ptr(W), ldw, _ptr(C), ldc, M,
+                                          N, K, int(bool(accumulate)), _stream(stream)))
+
+
+def mamba_backbone_workspace_size(dims: BackboneDims, B: int, T: int) -> int:
+    return int(load_library().mamba_backbone_workspace_size(ctypes.byref(dims), B, T))
+
+
+def mamba_backbone_prefill(dims: BackboneDims, weights: BackboneWeights, tokens, conv_state,
+                           ssm_state, logits, workspace, stream=None) -> None:
+    """Prefill B prompts of T tokens through the whole backbone; logits of each last token."""
+    Bsz, T = tokens.shape
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(load_library().mamba_backbone_prefill(
+        ctypes.byref(dims), ctypes.byref(weights), _ptr(tokens), Bsz, T, _ptr(conv_state),
+        _ptr(ssm_state), _ptr(logits), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+_BACKBONE_BF16 = ("embed", "in_proj", "x_proj", "dt_proj", "out_proj")
+
+
+def backbone_weights_struct(t: dict) -> BackboneWeights:
+    """Build the mamba_backbone_weights struct from a dict of contiguous device tensors (bf16
+    for the embedding and the projections, f32 for the rest). The caller keeps the tensors
+    alive while the struct is in use."""
+    import torch
+    w = BackboneWeights()
+    for name, _ in BackboneWeights._fields_:
+        x = t[name]
+        want = torch.bfloat16 if name in _BACKBONE_BF16 else torch.float32
+        if x.dtype != want or not x.is_contiguous() or not x.is_cuda:
+            raise ValueError(f"backbone weight {name}: need a contiguous device {want} tensor")
+        setattr(w, name, x.data_ptr())
+    return w

@@ -8,6 +8,7 @@
 // page, mamba-rs 0.5.1, mixed chain, fused gather + step + gate guard).
 #include <hip/hip_runtime.h>
 
+#include <climits>
 #include <cstdarg>
 #include <cstdio>
 #include <string>
@@ -290,6 +291,136 @@ mamba_status mamba_ssm_step(const void* u, const void* dt, const float* dt_bias,
                          D_skip, z, z_row_stride, ssm_state, y, io_dtype == MAMBA_BF16, L, B, D,
                          N};
     check_hip(fn, mamba::launch_ssm_step(a, static_cast<hipStream_t>(stream)));
+  });
+}
+
+mamba_status mamba_embed_gather(const int32_t* tokens, const void* E, float* out, int64_t rows,
+                                int vocab, int d_model, void* stream) {
+  static const char* fn = "mamba_embed_gather";
+  return guarded([&] {
+    if (rows < 0) fail(MAMBA_EINVAL, fn, "rows = %lld is negative", (long long)rows);
+    if (vocab <= 0 || d_model <= 0) fail(MAMBA_EINVAL, fn, "vocab = %d and d_model = %d must be positive", vocab, d_model);
+    if (rows == 0) return;
+    if (rows > INT32_MAX) fail(MAMBA_EUNSUPPORTED, fn, "rows = %lld exceeds 2^31-1", (long long)rows);
+    check_ptr(fn, "tokens", tokens, 4, true);
+    check_ptr(fn, "E", E, 2, true);
+    check_ptr(fn, "out", out, 4, true);
+    check_disjoint(fn, range("out", out, rows, d_model, d_model, 4),
+                   {range("tokens", tokens, 1, rows, rows, 4), range("E", E, vocab, d_model, d_model, 2)});
+    check_hip(fn, mamba::launch_embed_gather(tokens, E, out, rows, vocab, d_model, static_cast<hipStream_t>(stream)));
+  });
+}
+
+mamba_status mamba_rmsnorm(const float* x, int64_t x_row_stride, const float* w, float eps,
+                           void* out, mamba_dtype out_dtype, int64_t rows, int d_model,
+                           void* stream) {
+  static const char* fn = "mamba_rmsnorm";
+  return guarded([&] {
+    check_dtype(fn, out_dtype);
+    if (rows < 0 || d_model < 0) fail(MAMBA_EINVAL, fn, "rows and d_model must be non-negative");
+    if (rows == 0 || d_model == 0) return;
+    if (rows > INT32_MAX) fail(MAMBA_EUNSUPPORTED, fn, "rows = %lld exceeds 2^31-1", (long long)rows);
+    if (x_row_stride < d_model) fail(MAMBA_EINVAL, fn, "x_row_stride = %lld is less than d_model = %d", (long long)x_row_stride, d_model);
+    if (!(eps >= 0.0f)) fail(MAMBA_EINVAL, fn, "eps must be a non-negative number");
+    const size_t es = elem_size(out_dtype);
+    check_ptr(fn, "x", x, 4, true);
+    check_ptr(fn, "w", w, 4, false);
+    check_ptr(fn, "out", out, es, true);
+    check_disjoint(fn, range("out", out, rows, d_model, d_model, es),
+                   {range("x", x, rows, x_row_stride, d_model, 4), range("w", w, 1, d_model, d_model, 4)});
+    check_hip(fn, mamba::launch_rmsnorm(x, x_row_stride, w, eps, out, out_dtype == MAMBA_BF16, rows,
+                                        d_model, static_cast<hipStream_t>(stream)));
+  });
+}
+
+mamba_status mamba_gemm_bf16(const void* A, mamba_dtype a_dtype, int64_t lda, const void* W,
+                             int64_t ldw, float* C, int64_t ldc, int M, int N, int K,
+                             int accumulate, void* stream) {
+  static const char* fn = "mamba_gemm_bf16";
+  return guarded([&] {
+    check_dtype(fn, a_dtype);
+    check_dim(fn, "M", M);
+    check_dim(fn, "N", N);
+    check_dim(fn, "K", K);
+    if (M == 0 || N == 0) return;
+    if (lda < K || ldw < K || ldc < N) fail(MAMBA_EINVAL, fn, "leading dimensions must be at least K (A, W) and N (C)");
+    if (M > 65535 * 64) fail(MAMBA_EUNSUPPORTED, fn, "M = %d exceeds %d", M, 65535 * 64);
+    const size_t es = elem_size(a_dtype);
+    check_ptr(fn, "A", A, es, true);
+    check_ptr(fn, "W", W, 2, true);
+    check_ptr(fn, "C", C, 4, true);
+    check_disjoint(fn, range("C", C, M, ldc, N, 4),
+                   {range("A", A, M, lda, K, es), range("W", W, N, ldw, K, 2)});
+    check_hip(fn, mamba::launch_gemm_bf16(A, a_dtype == MAMBA_BF16, lda, W, ldw, C, ldc, M, N, K,
+                                          accumulate != 0, static_cast<hipStream_t>(stream)));
+  });
+}
+
+static void check_backbone_dims(const char* fn, const mamba_backbone_dims* d) {
+  if (!d) fail(MAMBA_EINVAL, fn, "dims is NULL");
+  if (d->n_layers < 0) fail(MAMBA_EINVAL, fn, "n_layers = %d is negative", d->n_layers);
+  if (d->d_model <= 0 || d->d_inner <= 0 || d->dt_rank <= 0 || d->vocab <= 0)
+    fail(MAMBA_EINVAL, fn, "d_model, d_inner, dt_rank and vocab must be positive");
+  check_state_dim(fn, "d_state", d->d_state, kMaxN);
+  check_state_dim(fn, "d_conv", d->d_conv, kMaxK);
+  if (d->vocab_padded < d->vocab) fail(MAMBA_EINVAL, fn, "vocab_padded = %d is less than vocab = %d", d->vocab_padded, d->vocab);
+  if (!(d->eps >= 0.0f)) fail(MAMBA_EINVAL, fn, "eps must be a non-negative number");
+  if (2LL * d->d_inner > kMaxRowStride) fail(MAMBA_EUNSUPPORTED, fn, "d_inner = %d too large", d->d_inner);
+}
+
+size_t mamba_backbone_workspace_size(const mamba_backbone_dims* dims, int B, int T) {
+  if (!dims || B <= 0 || T <= 0) return 0;
+  return mamba::backbone_workspace_bytes(*dims, B, T);
+}
+
+mamba_status mamba_backbone_prefill(const mamba_backbone_dims* dims,
+                                    const mamba_backbone_weights* w, const int32_t* tokens,
+                                    int B, int T, float* conv_state, float* ssm_state,
+                                    float* logits, void* workspace, size_t workspace_bytes,
+                                    void* stream) {
+  static const char* fn = "mamba_backbone_prefill";
+  return guarded([&] {
+    check_backbone_dims(fn, dims);
+    if (!w) fail(MAMBA_EINVAL, fn, "weights is NULL");
+    check_dim(fn, "B", B);
+    check_dim(fn, "T", T);
+    if (B == 0 || T == 0) return;
+    if (B > kMaxGridYZ) fail(MAMBA_EUNSUPPORTED, fn, "B = %d exceeds %d", B, kMaxGridYZ);
+    if ((int64_t)B * T > INT32_MAX / 2) fail(MAMBA_EUNSUPPORTED, fn, "B * T too large");
+    const mamba_backbone_dims& d = *dims;
+    check_ptr(fn, "embed", w->embed, 2, true);
+    check_ptr(fn, "norm_f", w->norm_f, 4, true);
+    check_ptr(fn, "norm_w", w->norm_w, 4, d.n_layers > 0);
+    check_ptr(fn, "in_proj", w->in_proj, 2, d.n_layers > 0);
+    check_ptr(fn, "conv_w", w->conv_w, 4, d.n_layers > 0);
+    check_ptr(fn, "conv_b", w->conv_b, 4, d.n_layers > 0);
+    check_ptr(fn, "x_proj", w->x_proj, 2, d.n_layers > 0);
+    check_ptr(fn, "dt_proj", w->dt_proj, 2, d.n_layers > 0);
+    check_ptr(fn, "dt_bias", w->dt_bias, 4, d.n_layers > 0);
+    check_ptr(fn, "A_log", w->A_log, 4, d.n_layers > 0);
+    check_ptr(fn, "D_skip", w->D_skip, 4, d.n_layers > 0);
+    check_ptr(fn, "out_proj", w->out_proj, 2, d.n_layers > 0);
+    check_ptr(fn, "tokens", tokens, 4, true);
+    check_ptr(fn, "conv_state", conv_state, 4, d.n_layers > 0);
+    check_ptr(fn, "ssm_state", ssm_state, 4, d.n_layers > 0);
+    check_ptr(fn, "logits", logits, 4, true);
+    const size_t need = mamba::backbone_workspace_bytes(d, B, T);
+    if (!workspace) fail(MAMBA_EWORKSPACE, fn, "workspace is NULL but %zu bytes are required", need);
+    if (workspace_bytes < need) fail(MAMBA_EWORKSPACE, fn, "workspace_bytes = %zu but %zu are required", workspace_bytes, need);
+    if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) fail(MAMBA_EINVAL, fn, "workspace is not 256-byte aligned");
+    const int64_t L = d.n_layers;
+    const Range rws = range("workspace", workspace, 1, (int64_t)need, (int64_t)need, 1);
+    const Range rlog = range("logits", logits, B, d.vocab, d.vocab, 4);
+    const Range rcs = range("conv_state", conv_state, L * B * d.d_inner, d.d_conv, d.d_conv, 4);
+    const Range rss = range("ssm_state", ssm_state, L * B * d.d_inner, d.d_state, d.d_state, 4);
+    const Range rtok = range("tokens", tokens, 1, (int64_t)B * T, (int64_t)B * T, 4);
+    const Range remb = range("embed", w->embed, d.vocab_padded, d.d_model, d.d_model, 2);
+    check_disjoint(fn, rws, {rlog, rcs, rss, rtok, remb});
+    check_disjoint(fn, rlog, {rcs, rss, rtok, remb});
+    check_disjoint(fn, rcs, {rss, rtok, remb});
+    check_disjoint(fn, rss, {rtok, remb});
+    check_hip(fn, mamba::run_backbone_prefill(d, *w, tokens, B, T, conv_state, ssm_state, logits,
+                                              workspace, static_cast<hipStream_t>(stream)));
   });
 }
 

@@ -1,0 +1,108 @@
+// backbone_run.cpp -- the native layer loop of the full-backbone prefill.
+//
+// prefill.rs page (mamba-rs 0.6.4): gpu_forward_inference_prefill and prefill_body -- embed,
+// then per layer F1 RMSNorm, F2 in_proj, F4a conv over the x lane of the in_proj output (row
+// stride 2*d_inner), F4b x_proj, F4c dt_proj (its bias goes into the scan as dt_bias), F4d the
+// scan with B and C read in place from the x_proj output and the gate from the z lane, F5
+// out_proj and F6 the residual add (fused here into out_proj as an accumulating GEMM); then
+// norm_f on the last timestep of each sequence and the tied LM head (gpu_lm.rs page, mamba-rs
+// 0.7.1). The loop runs on the host and only enqueues kernels: no synchronization, no
+// allocation, so it can be captured into a HIP graph like every other call.
+#include <hip/hip_runtime.h>
+
+#include "../../include/mamba_ssm.h"
+#include "launch.hpp"
+
+namespace mamba {
+
+static size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct BackboneLayout {
+  size_t h, xn, proj, u, xdbl, dt, y, last, scan, total;
+};
+
+BackboneLayout backbone_layout(const mamba_backbone_dims& d, int B, int T) {
+  const size_t bt = (size_t)B * T;
+  const size_t xw = (size_t)d.dt_rank + 2 * (size_t)d.d_state;
+  BackboneLayout l{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += a256(bytes);
+    return at;
+  };
+  l.h = take(bt * d.d_model * 4);
+  l.xn = take(bt * d.d_model * 2);
+  l.proj = take(bt * 2 * (size_t)d.d_inner * 4);
+  l.u = take(bt * d.d_inner * 4);
+  l.xdbl = take(bt * xw * 4);
+  l.dt = take(bt * d.d_inner * 4);
+  l.y = take(bt * d.d_inner * 4);
+  l.last = take((size_t)B * d.d_model * 2);
+  l.scan = take(plan_selective_scan(B, T, d.d_inner, d.d_state).workspace_bytes);
+  l.total = off;
+  return l;
+}
+
+size_t backbone_workspace_bytes(const mamba_backbone_dims& d, int B, int T) {
+  return backbone_layout(d, B, T).total;
+}
+
+hipError_t run_backbone_prefill(const mamba_backbone_dims& d, const mamba_backbone_weights& w,
+                                const int32_t* tokens, int B, int T, float* conv_state,
+                                float* ssm_state, float* logits, void* workspace, hipStream_t s) {
+  const BackboneLayout lay = backbone_layout(d, B, T);
+  char* ws = static_cast<char*>(workspace);
+  float* h = reinterpret_cast<float*>(ws + lay.h);
+  void* xn = ws + lay.xn;
+  float* proj = reinterpret_cast<float*>(ws + lay.proj);
+  float* u = reinterpret_cast<float*>(ws + lay.u);
+  float* xdbl = reinterpret_cast<float*>(ws + lay.xdbl);
+  float* dt = reinterpret_cast<float*>(ws + lay.dt);
+  float* y = reinterpret_cast<float*>(ws + lay.y);
+  void* last = ws + lay.last;
+  void* scan_ws = ws + lay.scan;
+
+  const int64_t bt = (int64_t)B * T;
+  const int Dm = d.d_model, D = d.d_inner, N = d.d_state, K = d.d_conv, R = d.dt_rank;
+  const int xw = R + 2 * N;
+  const auto* in_proj = static_cast<const bf16_storage*>(w.in_proj);
+  const auto* x_proj = static_cast<const bf16_storage*>(w.x_proj);
+  const auto* dt_proj = static_cast<const bf16_storage*>(w.dt_proj);
+  const auto* out_proj = static_cast<const bf16_storage*>(w.out_proj);
+
+  hipError_t e = launch_embed_gather(tokens, w.embed, h, bt, d.vocab, Dm, s);
+  if (e != hipSuccess) return e;
+  for (int l = 0; l < d.n_layers; ++l) {
+    // F1: normed activations, already bf16 for the in_proj GEMM
+    if ((e = launch_rmsnorm(h, Dm, w.norm_w + (int64_t)l * Dm, d.eps, xn, true, bt, Dm, s)) != hipSuccess) return e;
+    // F2: proj = xn @ in_proj^T   [bt, 2D]: x lane | z lane
+    if ((e = launch_gemm_bf16(xn, true, Dm, in_proj + (int64_t)l * 2 * D * Dm, Dm, proj, 2 * D, (int)bt,
+                              2 * D, Dm, false, s)) != hipSuccess) return e;
+    // F4a: conv + SiLU over the x lane, carrying this layer's conv state
+    ConvFwdArgs ca{proj, 2 * D, w.conv_w + (int64_t)l * D * K, w.conv_b + (int64_t)l * D,
+                   conv_state + (int64_t)l * B * D * K, u, false, B, T, D, K};
+    if ((e = launch_conv1d_fwd(ca, s)) != hipSuccess) return e;
+    // F4b: xdbl = u @ x_proj^T   [bt, R + 2N]: dt lane | B | C
+    if ((e = launch_gemm_bf16(u, false, D, x_proj + (int64_t)l * xw * D, D, xdbl, xw, (int)bt, xw, D,
+                              false, s)) != hipSuccess) return e;
+    // F4c: dt = xdbl[:, :R] @ dt_proj^T   [bt, D]  (bias applied in the scan)
+    if ((e = launch_gemm_bf16(xdbl, false, xw, dt_proj + (int64_t)l * D * R, R, dt, D, (int)bt, D, R,
+                              false, s)) != hipSuccess) return e;
+    // F4d: the scan, B/C read in place from xdbl, the gate from the z lane of proj
+    ScanFwdArgs sa{u, dt, w.dt_bias + (int64_t)l * D, true, w.A_log + (int64_t)l * D * N,
+                   xdbl + R, xdbl + R + N, xw, w.D_skip + (int64_t)l * D, proj + D, 2 * D,
+                   ssm_state + (int64_t)l * B * D * N, ssm_state + (int64_t)l * B * D * N, y,
+                   false, B, T, D, N, scan_ws};
+    if ((e = launch_selective_scan_fwd(sa, s)) != hipSuccess) return e;
+    // F5 + F6: h += y @ out_proj^T
+    if ((e = launch_gemm_bf16(y, false, D, out_proj + (int64_t)l * Dm * D, D, h, Dm, (int)bt, Dm, D,
+                              true, s)) != hipSuccess) return e;
+  }
+  // norm_f on the last timestep of each sequence, then the tied head against the embedding
+  if ((e = launch_rmsnorm(h + (int64_t)(T - 1) * Dm, (int64_t)T * Dm, w.norm_f, d.eps, last, true, B,
+                          Dm, s)) != hipSuccess) return e;
+  return launch_gemm_bf16(last, true, Dm, w.embed, Dm, logits, d.vocab, B, d.vocab, Dm, false, s);
+}
+
+}  // namespace mamba

@@ -7,7 +7,15 @@
 #include <stddef.h>
 #include <stdint.h>
 
+struct mamba_backbone_dims;
+struct mamba_backbone_weights;
+
 namespace mamba {
+
+// Opaque 2-byte storage unit for bf16 arrays in host code (pointer arithmetic only).
+struct bf16_storage {
+  unsigned short bits;
+};
 
 struct ConvFwdArgs {
   const void* x;
@@ -79,7 +87,23 @@ struct ScanPlan {
 
 ScanPlan plan_selective_scan(int B, int T, int D, int N);
 
+hipError_t launch_embed_gather(const int32_t* tokens, const void* E, float* out, int64_t rows,
+                               int vocab, int Dm, hipStream_t s);
+hipError_t launch_rmsnorm(const float* x, int64_t x_row_stride, const float* w, float eps,
+                          void* out, bool out_bf16, int64_t rows, int Dm, hipStream_t s);
+hipError_t launch_gemm_bf16(const void* A, bool a_bf16, int64_t lda, const void* W, int64_t ldw,
+                            float* C, int64_t ldc, int M, int N, int K, bool accumulate,
+                            hipStream_t s);
+// Largest M the few-row GEMM takes, and its LDS budget for the staged rows (M * K floats).
+constexpr int kSkinnyGemmMaxM = 8;
+constexpr int64_t kSkinnyGemmMaxLds = 64 * 1024;
+
 hipError_t launch_conv1d_fwd(const ConvFwdArgs& a, hipStream_t s);
+
+size_t backbone_workspace_bytes(const mamba_backbone_dims& d, int B, int T);
+hipError_t run_backbone_prefill(const mamba_backbone_dims& d, const mamba_backbone_weights& w,
+                                const int32_t* tokens, int B, int T, float* conv_state,
+                                float* ssm_state, float* logits, void* workspace, hipStream_t s);
 hipError_t launch_conv1d_step(const ConvStepArgs& a, hipStream_t s);
 hipError_t launch_selective_scan_fwd(const ScanFwdArgs& a, hipStream_t s);
 hipError_t launch_ssm_step(const SsmStepArgs& a, hipStream_t s);

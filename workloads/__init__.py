@@ -255,3 +255,31 @@ def decode_step_inputs_torch(shape: DecodeShape, step: int, seed: int = 0, cfg: 
     if shape.io == "bf16":
         out = {k: v.to(torch.bfloat16) for k, v in out.items()}
     return out
+
+
+# ------------------------------------------------------------ backbone (c4) weights
+
+def backbone_weights(shape: BackboneShape, seed: int = 0, cfg: int = 4) -> dict:
+    """Random-init weights of the Mamba-1 backbone (host, numpy f32; bf16 weights hold
+    bf16-exact values). Embedding and projections ~ N(0, 0.02^2) stored bf16 (nn.Linear layout
+    [out, in]; the embedding is [vocab_padded, d_model] with zero padding rows); SSM parameters
+    as in the single-layer workloads; norm weights 1."""
+    L, Dm, D, N, K, R = shape.n_layers, shape.d_model, shape.D, shape.N, shape.K, shape.dt_rank
+    def w(tid, layer, shp):
+        return store(normal(rng(seed, cfg, tid, layer), shp, std=0.02), "bf16")
+    embed = np.zeros((shape.vocab_padded, Dm), np.float32)
+    embed[:shape.vocab] = w(EMBED, 0, (shape.vocab, Dm))
+    out = dict(embed=embed, norm_f=np.ones(Dm, np.float32), norm_w=np.ones((L, Dm), np.float32),
+               in_proj=np.stack([w(W_IN, l, (2 * D, Dm)) for l in range(L)]),
+               x_proj=np.stack([w(W_X, l, (R + 2 * N, D)) for l in range(L)]),
+               dt_proj=np.stack([w(W_DT, l, (D, R)) for l in range(L)]),
+               out_proj=np.stack([w(W_OUT, l, (Dm, D)) for l in range(L)]))
+    ps = [layer_params(D, N, K, seed, cfg, l) for l in range(L)]
+    for k in ("conv_w", "conv_b", "dt_bias", "A_log", "D_skip"):
+        out[k] = np.stack([p[k] for p in ps])
+    return out
+
+
+def backbone_tokens(shape: BackboneShape, seed: int = 0, cfg: int = 4) -> np.ndarray:
+    """Token ids uniform in [0, vocab), [B, T] int32."""
+    return rng(seed, cfg, TOKENS).integers(0, shape.vocab, size=(shape.B, shape.T)).astype(np.int32)
