@@ -4,326 +4,292 @@
 // output + bias)) and F4d (scan over all T, y gated by silu(z) read at a row stride, final
 // state into the persistent SSM state); inference.rs page (mamba-rs 0.5.1),
 // GpuMambaInference::new (A = -exp(A_log)). Softplus, A = -exp(A_log), the D skip and the
-// gate are all fused here, so u, dt, z are read once and y is written once.
+// gate are all fused here: u, dt, z, B and C are read once and y is written once.
 //
-// Layout. Lanes run along d (64 consecutive channels per wave): u/dt/z/y rows are read and
-// written coalesced, and the B/C rows of token t are the same for every lane of the wave,
-// so they are loaded once as scalars and used as SGPR operands. Each lane keeps its N
-// states in registers and walks the tokens of its chunk in order.
+// Workgroup = 64 consecutive channels x all NP (padded) states, as kWaves waves. Wave q
+// owns states [q*S, (q+1)*S) of every channel (lanes run along d, S = NP / kWaves states
+// in registers per lane), so a channel's recurrence is split over the waves by state, not
+// by time: there is no rescan and the whole T of a chunk is walked once.
 //
-// T parallelism. T is cut into `chunks` pieces so that B * ceil(D/64) * chunks waves fill
-// the chip. A chunk's effect on the state is the affine map h -> P*h + H per (b, d, n), with
-// P = exp(A * sum(delta)) and H the state reached from h = 0. Three kernels:
-//   1. summary: (P, H) of every chunk but the last;
-//   2. prefix:  start state of every chunk, folding the maps in token order from the
-//               carried input state (one thread per (b, d, n));
-//   3. output:  every chunk rescans its tokens from its start state, writing y; the last
-//               chunk writes the final state.
-// With one chunk only kernel 3 runs, straight from the carried state.
+// The per-token work that does not depend on the state is shared through LDS, in blocks of
+// kWaves tokens: in each block wave q computes delta (softplus) and delta*u for token q of
+// the block and silu(z) for the same token, and stages part of the block's B/C rows; every
+// wave then reads delta, delta*u and its states' B/C values for the block's tokens from LDS
+// and advances its S states, leaving its partial C.h per token in LDS; after the barrier
+// wave q adds the kWaves partials of token q, the D skip and the gate, and stores y. The
+// block buffers are double-buffered, so one barrier per block orders everything.
+//
+// T parallelism: when B * ceil(D/64) workgroups cannot fill the chip, T is cut into chunks.
+// A chunk acts on the state as h -> P*h + H per (b, d, n), P = exp(A * sum(delta)) and H the
+// state it reaches from h = 0. A summary pass computes (sum(delta), H) of every chunk but
+// the last; the output pass starts each chunk from the carried state folded through the
+// maps of the chunks before it (few chunks, so each workgroup folds them itself).
 #include <algorithm>
+#include <type_traits>
 
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace mamba {
 
-constexpr int kScanWave = 64;
-// Tokens staged in registers ahead of use: u/dt/z of the next block are loaded while the
-// current block is computed, so memory latency hides behind one block of work.
-constexpr int kTB = 8;
-// Third dword of a raw buffer resource on gfx9-family parts (32-bit data, no swizzle).
-constexpr int kBufferFlags = 0x00020000;
+constexpr int kLanes = 64;
+constexpr int kWaves = 8;          // waves per workgroup; also tokens per block
+constexpr int kThreads = kLanes * kWaves;
 
-using rsrc_t = __amdgpu_buffer_rsrc_t;
-
-// The packed B/C rows are read-only for the whole call; reading them through the constant
-// address space lets the compiler use scalar loads for these wave-uniform rows regardless of
-// what the kernel stores elsewhere.
-using cfloat = __attribute__((address_space(4))) const float;
-__device__ __forceinline__ cfloat* as_constant(const float* p) {
-  return (cfloat*)(p);
-}
-
-__device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, kBufferFlags);
-}
-
-template <typename IO>
-__device__ __forceinline__ float bload(rsrc_t r, uint32_t voff, uint32_t soff) {
-  if constexpr (sizeof(IO) == 4) {
-    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0));
-  } else {
-    return __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, (int)voff, (int)soff, 0) << 16);
-  }
-}
-
-// A * log2(e) with A = -exp(A_log); states padded past N get 0 (decay 1; their B and C
-// entries are packed as 0, so they stay 0 and add nothing).
-template <int NP>
-__device__ __forceinline__ void load_a2(float (&a2)[NP], const float* __restrict__ A_log, int d,
-                                        int N) {
-#pragma unroll
-  for (int n = 0; n < NP; ++n)
-    a2[n] = n < N ? -__builtin_amdgcn_exp2f(A_log[(int64_t)d * N + n] * kLog2e) * kLog2e : 0.0f;
-}
-
-__device__ __forceinline__ float make_delta(float dtv, float bias, bool sp) {
-  const float v = dtv + bias;
-  return sp ? softplus(v) : v;
-}
-
-// One block of kTB tokens of a [rows, row_stride] tensor for this lane's channel. The
-// resource is rebased at the block so 32-bit offsets never overflow; tokens past t_end
-// re-read the last valid row (never out of bounds; those values are not used).
-template <typename IO>
-struct BlockReader {
-  const IO* base;       // element (row0 + t0, d0) -- the chunk's first row, wave's channel 0
-  int64_t row_stride;   // elements
-  uint32_t voff;        // this lane's byte offset in a row
-
-  __device__ __forceinline__ void load(float (&dst)[kTB], int tb_rel, int n_valid) const {
-    const IO* p = base + (int64_t)tb_rel * row_stride;
-    const uint32_t rs_bytes = (uint32_t)(row_stride * sizeof(IO));
-    const rsrc_t r = make_rsrc(p, (uint32_t)(kTB * rs_bytes));
-#pragma unroll
-    for (int j = 0; j < kTB; ++j) dst[j] = bload<IO>(r, voff, (uint32_t)min(j, n_valid - 1) * rs_bytes);
-  }
+struct ScanParams {
+  const void* u;
+  const void* dt;
+  const void* Bm;
+  const void* Cm;
+  const void* z;
+  void* y;
+  const float* dt_bias;
+  const float* A_log;
+  const float* D_skip;
+  const float* state_in;   // [B][D][N] or NULL
+  float* state_out;        // [B][D][N] or NULL
+  float* sum_ws;           // [B][chunks][D]      sum of delta per chunk (chunks > 1)
+  float* h_ws;             // [B][chunks][N][D]   chunk end state from h = 0 (chunks > 1)
+  float* start_ws;         // [B][N][D]           copy of the carried state (chunks > 1)
+  int64_t bc_row_stride;
+  int64_t z_row_stride;
+  int B, T, D, N;
+  int chunk_t, chunks;
+  int softplus;
 };
 
-// Pack B and C into f32 rows [B[0..NP), C[0..NP)] per token, zero padded past N, so the
-// scan kernels read one contiguous row per token with scalar loads and no conversion.
-template <typename IO, int NP>
-__global__ void __launch_bounds__(256) pack_bc_kernel(const IO* __restrict__ Bm,
-                                                      const IO* __restrict__ Cm,
-                                                      int64_t bc_row_stride,
-                                                      float* __restrict__ out, int64_t rows,
-                                                      int N) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= rows * 2 * NP) return;
-  const int64_t r = i / (2 * NP);
-  const int k = (int)(i % (2 * NP));
-  const int n = k < NP ? k : k - NP;
-  const IO* src = k < NP ? Bm : Cm;
-  out[i] = n < N ? to_f32(src[r * bc_row_stride + n]) : 0.0f;
+// A * log2(e) for A = -exp(A_log) of state n (0 for padded states: decay 1, and their B and
+// C are staged as 0, so they stay 0 and add nothing).
+__device__ __forceinline__ float a_log2(const float* __restrict__ A_log, int d, int n, int N) {
+  return n < N ? -__builtin_amdgcn_exp2f(A_log[(int64_t)d * N + n] * kLog2e) * kLog2e : 0.0f;
 }
 
-// Chunk c of channel (b, d): the affine map h -> P*h + H it applies to the state, with
-// P = exp(A * sum(delta)) and H the state it produces from h = 0. Chunks are disjoint runs of
-// chunk_t tokens. Output layout [b][d][c][n] (n fastest), chunks 0 .. chunks-2.
-template <typename IO, int NP>
-__global__ void __launch_bounds__(kScanWave) scan_chunk_summary_kernel(
-    const IO* __restrict__ u, const IO* __restrict__ dt, const float* __restrict__ dt_bias,
-    int delta_softplus, const float* __restrict__ A_log, const float* __restrict__ bc,
-    float* __restrict__ P_out, float* __restrict__ H_out, int B, int T, int D, int N,
-    int chunk_t, int chunks) {
-  const int d0 = blockIdx.x * kScanWave;
-  const int d = d0 + threadIdx.x;
+// OUT = false: summary pass over chunks 0 .. chunks-2 (no y). OUT = true: the output pass.
+template <typename IO, int NP, bool OUT, bool GATE>
+__global__ void __launch_bounds__(kThreads) scan_kernel(const ScanParams p) {
+  constexpr int S = NP / kWaves;  // states per lane
+  constexpr int BCW = 2 * NP;     // staged B/C row: per wave group [B(S) | C(S)]
+  static_assert(S >= 2 && S * kWaves == NP, "state split");
+
+  __shared__ float2 s_dd[2][kWaves][kLanes];                     // (delta, delta*u)
+  __shared__ __attribute__((aligned(16))) float s_bc[2][kWaves][BCW];
+  __shared__ float s_yp[OUT ? 2 : 1][OUT ? kWaves : 1][kWaves][kLanes];  // partial C.h
+
+  const int lane = threadIdx.x & (kLanes - 1);
+  // wave index, made explicitly wave-uniform so row arithmetic stays scalar
+  const int q = __builtin_amdgcn_readfirstlane(threadIdx.x / kLanes);
+  const int d = blockIdx.x * kLanes + lane;
+  const bool dval = d < p.D;
+  const int dc = dval ? d : p.D - 1;  // clamped channel for loads of masked lanes
   const int b = blockIdx.y;
   const int c = blockIdx.z;
-  if (d >= D) return;
-  const int t0 = c * chunk_t;
-  const int t1 = min(T, t0 + chunk_t);
-  const int64_t row0 = (int64_t)b * T;
+  const int N = p.N, D = p.D;
+  const int t0 = c * p.chunk_t;
+  const int len = min(p.T, t0 + p.chunk_t) - t0;
+  const int nblk = (len + kWaves - 1) / kWaves;
+  const int64_t row0 = (int64_t)b * p.T + t0;  // first row of the chunk
 
-  float a2[NP];
-  load_a2<NP>(a2, A_log, d, N);
-  const float bias = dt_bias ? dt_bias[d] : 0.0f;
-  const bool sp = delta_softplus != 0;
+  const IO* __restrict__ u = static_cast<const IO*>(p.u);
+  const IO* __restrict__ dt = static_cast<const IO*>(p.dt);
+  const IO* __restrict__ Bm = static_cast<const IO*>(p.Bm);
+  const IO* __restrict__ Cm = static_cast<const IO*>(p.Cm);
+  const IO* __restrict__ z = static_cast<const IO*>(p.z);
 
-  float H[NP];
+  float a2[S];
 #pragma unroll
-  for (int n = 0; n < NP; ++n) H[n] = 0.0f;
+  for (int s = 0; s < S; ++s) a2[s] = a_log2(p.A_log, dc, q * S + s, N);
+  const float bias = p.dt_bias ? p.dt_bias[dc] : 0.0f;
+  const float dskip = p.D_skip ? p.D_skip[dc] : 0.0f;
+  const bool sp = p.softplus != 0;
+
+  // ---- start state
+  float h[S];
+  if constexpr (OUT) {
+    if (p.chunks == 1) {
+#pragma unroll
+      for (int s = 0; s < S; ++s) {
+        const int n = q * S + s;
+        h[s] = (p.state_in && n < N) ? p.state_in[((int64_t)b * D + dc) * N + n] : 0.0f;
+      }
+    } else {
+      // carried state, then the maps of chunks 0 .. c-1 in token order
+#pragma unroll
+      for (int s = 0; s < S; ++s) {
+        const int n = q * S + s;
+        h[s] = n < N ? p.start_ws[((int64_t)b * N + n) * D + dc] : 0.0f;
+      }
+      for (int cc = 0; cc < c; ++cc) {
+        const int64_t bc_ = (int64_t)b * p.chunks + cc;
+        const float sd = p.sum_ws[bc_ * D + dc];
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+          const int n = q * S + s;
+          if (n < N) h[s] = fmaf(__builtin_amdgcn_exp2f(a2[s] * sd), h[s], p.h_ws[(bc_ * N + n) * D + dc]);
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int s = 0; s < S; ++s) h[s] = 0.0f;
+    if (c == 0 && dval) {  // keep the carried state for the output pass (it may be updated in place)
+#pragma unroll
+      for (int s = 0; s < S; ++s) {
+        const int n = q * S + s;
+        if (n < N)
+          p.start_ws[((int64_t)b * N + n) * D + d] =
+              p.state_in ? p.state_in[((int64_t)b * D + d) * N + n] : 0.0f;
+      }
+    }
+  }
+
+  // ---- per-token loads of this wave's token in block k, and its B/C staging values
+  // Thread i < kWaves * BCW stages entry i of the block: token i / BCW, slot i % BCW.
+  constexpr int BC_PER_T = (kWaves * BCW + kThreads - 1) / kThreads;
+  // Loads are never predicated: a token past the chunk re-reads the chunk's last row and a
+  // padded state re-reads state N-1 (in bounds; such values are replaced by 0 when staged or
+  // never read), so no load result has to be merged with an older value.
+  const IO* __restrict__ dt_l = dt + dc;
+  const IO* __restrict__ u_l = u + dc;
+  const IO* __restrict__ z_l = z + dc;
+  auto load_tok = [&](int k, float& rdt, float& ru, float& rz) {
+    const int64_t row = row0 + min(k * kWaves + q, len - 1);  // wave-uniform
+    rdt = to_f32(dt_l[row * D]);
+    ru = to_f32(u_l[row * D]);
+    if constexpr (OUT && GATE) rz = to_f32(z_l[row * p.z_row_stride]);
+  };
+  auto bc_slot = [&](int r, int& j, int& n, bool& isC) {
+    const int i = threadIdx.x + r * kThreads;
+    j = i / BCW;
+    const int slot = i % BCW;
+    const int w = slot % (2 * S);
+    isC = w >= S;
+    n = slot / (2 * S) * S + (isC ? w - S : w);
+  };
+  auto load_bc = [&](int k, float (&v)[BC_PER_T]) {
+#pragma unroll
+    for (int r = 0; r < BC_PER_T; ++r) {
+      if (threadIdx.x + r * kThreads < kWaves * BCW) {  // whole waves
+        int j, n;
+        bool isC;
+        bc_slot(r, j, n, isC);
+        const IO* src = isC ? Cm : Bm;
+        v[r] = to_f32(src[(row0 + min(k * kWaves + j, len - 1)) * p.bc_row_stride + min(n, N - 1)]);
+      }
+    }
+  };
+  auto store_bc = [&](int k, int buf, const float (&v)[BC_PER_T]) {
+#pragma unroll
+    for (int r = 0; r < BC_PER_T; ++r) {
+      const int i = threadIdx.x + r * kThreads;
+      if (i < kWaves * BCW) {
+        int j, n;
+        bool isC;
+        bc_slot(r, j, n, isC);
+        const bool ok = k * kWaves + j < len && n < N && (OUT || !isC);
+        s_bc[buf][j][i % BCW] = ok ? v[r] : 0.0f;
+      }
+    }
+  };
+
+  // Register sets by block parity: the values of block m live in set m & 1, so the loop,
+  // unrolled by two, never copies a register that a load is still filling.
+  float pf_dt[2] = {0.0f, 0.0f}, pf_u[2] = {0.0f, 0.0f}, pf_z[2] = {0.0f, 0.0f};
+  float pf_bc[2][BC_PER_T];
+  float u_blk[2] = {0.0f, 0.0f}, g_blk[2] = {1.0f, 1.0f};  // u, silu(z) of this wave's token
+
+  // stage A: delta, delta*u of this wave's token of block m into LDS; B/C rows of block m
+  auto stage_a = [&](int m, auto P) {
+    constexpr int st = decltype(P)::value;
+    const float delta = sp ? softplus(pf_dt[st] + bias) : pf_dt[st] + bias;
+    s_dd[st][q][lane] = make_float2(delta, delta * pf_u[st]);
+    u_blk[st] = pf_u[st];
+    if constexpr (OUT && GATE) g_blk[st] = silu(pf_z[st]);
+    store_bc(m, st, pf_bc[st]);
+  };
+
   float sum_delta = 0.0f;
-
-  const int64_t first = (row0 + t0) * D + d0;
-  const uint32_t voff = (uint32_t)(threadIdx.x * sizeof(IO));
-  const BlockReader<IO> ru{u + first, D, voff};
-  const BlockReader<IO> rdt{dt + first, D, voff};
-  cfloat* bcp = as_constant(bc) + (row0 + t0) * (2 * NP);
-
-  float cu[kTB], cdt[kTB], nu[kTB], ndt[kTB];
-  ru.load(cu, 0, min(kTB, t1 - t0));
-  rdt.load(cdt, 0, min(kTB, t1 - t0));
-  float bv[NP];
-#pragma unroll
-  for (int n = 0; n < NP; ++n) bv[n] = bcp[n];
-  for (int tb = t0; tb < t1; tb += kTB) {
-    if (tb + kTB < t1) {
-      ru.load(nu, tb + kTB - t0, min(kTB, t1 - tb - kTB));
-      rdt.load(ndt, tb + kTB - t0, min(kTB, t1 - tb - kTB));
-    }
-#pragma unroll
-    for (int j = 0; j < kTB; ++j) {
-      const int t = tb + j;
-      if (t >= t1) break;
-      cfloat* bcn = t + 1 < t1 ? bcp + 2 * NP : bcp;
-      float bn[NP];
-#pragma unroll
-      for (int n = 0; n < NP; ++n) bn[n] = bcn[n];
-      const float delta = make_delta(cdt[j], bias, sp);
-      const float du = delta * cu[j];
-#pragma unroll
-      for (int n = 0; n < NP; ++n) {
-        const float a = __builtin_amdgcn_exp2f(delta * a2[n]);
-        H[n] = fmaf(a, H[n], du * bv[n]);
-      }
-      sum_delta += delta;
-#pragma unroll
-      for (int n = 0; n < NP; ++n) bv[n] = bn[n];
-      bcp = bcn;
-    }
-#pragma unroll
-    for (int j = 0; j < kTB; ++j) {
-      cu[j] = nu[j];
-      cdt[j] = ndt[j];
-    }
-  }
-
-  const int64_t off = (((int64_t)b * D + d) * chunks + c) * N;
-#pragma unroll
-  for (int n = 0; n < NP; ++n) {
-    if (n < N) {
-      P_out[off + n] = __builtin_amdgcn_exp2f(sum_delta * a2[n]);
-      H_out[off + n] = H[n];
-    }
-  }
-}
-
-// Start state of every chunk: h_in[c] = map_{c-1}( ... map_0(state_in)). One thread per
-// (b, d, n), layout [b][d][c][n]: the threads of a channel read contiguous bytes per chunk.
-// Loads are issued kPrefixBatch chunks ahead of the dependent fma chain.
-constexpr int kPrefixBatch = 8;
-
-__global__ void __launch_bounds__(256) scan_chunk_prefix_kernel(
-    const float* __restrict__ P, const float* __restrict__ H, const float* state_in,
-    float* __restrict__ H_in, int64_t bdn, int N, int chunks) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // (b*D + d)*N + n
-  if (i >= bdn) return;
-  const int64_t ch = i / N;
-  const int n = (int)(i % N);
-  const int64_t base = ch * chunks * N + n;
-  float h = state_in ? state_in[i] : 0.0f;
-  H_in[base] = h;
-  for (int c0 = 0; c0 + 1 < chunks; c0 += kPrefixBatch) {
-    float p[kPrefixBatch], q[kPrefixBatch];
-#pragma unroll
-    for (int j = 0; j < kPrefixBatch; ++j) {
-      const int c = min(c0 + j, chunks - 2);
-      p[j] = P[base + (int64_t)c * N];
-      q[j] = H[base + (int64_t)c * N];
-    }
-#pragma unroll
-    for (int j = 0; j < kPrefixBatch; ++j) {
-      if (c0 + j + 1 < chunks) {
-        h = fmaf(p[j], h, q[j]);
-        H_in[base + (int64_t)(c0 + j + 1) * N] = h;
+  // one block: stage A of block k+1, loads of block k+2, stage B of block k, barrier, finish
+  auto block = [&](int k, auto P) {
+    constexpr int st = decltype(P)::value;  // == k & 1
+    constexpr int nx = st ^ 1;
+    if (k + 1 < nblk) {
+      stage_a(k + 1, std::integral_constant<int, nx>{});
+      if (k + 2 < nblk) {
+        load_tok(k + 2, pf_dt[st], pf_u[st], pf_z[st]);
+        load_bc(k + 2, pf_bc[st]);
       }
     }
-  }
-}
 
-// Rescan each chunk from its start state, writing y for every token; the last chunk writes
-// the final state. h_start: [b][d][c][n] start states (chunks > 1) or the carried state
-// [b][d][n] (one chunk), or NULL for zeros.
-template <typename IO, int NP, bool GATE>
-__global__ void __launch_bounds__(kScanWave) scan_chunk_output_kernel(
-    const IO* __restrict__ u, const IO* __restrict__ dt, const float* __restrict__ dt_bias,
-    int delta_softplus, const float* __restrict__ A_log, const float* __restrict__ bc,
-    const float* __restrict__ D_skip, const IO* __restrict__ z, int64_t z_row_stride,
-    const float* h_start, float* state_out, IO* __restrict__ y, int B, int T, int D, int N,
-    int chunk_t, int chunks) {
-  const int d0 = blockIdx.x * kScanWave;
-  const int d = d0 + threadIdx.x;
-  const int b = blockIdx.y;
-  const int c = blockIdx.z;
-  if (d >= D) return;
-  const int t0 = c * chunk_t;
-  const int t1 = min(T, t0 + chunk_t);
-  const int64_t row0 = (int64_t)b * T;
-
-  float a2[NP];
-  load_a2<NP>(a2, A_log, d, N);
-  const float bias = dt_bias ? dt_bias[d] : 0.0f;
-  const float dskip = D_skip ? D_skip[d] : 0.0f;
-  const bool sp = delta_softplus != 0;
-
-  float h[NP];
-  const float* hs = h_start ? h_start + (((int64_t)b * D + d) * chunks + c) * N : nullptr;
+    // stage B: every wave advances its S states over the block's tokens
+    const int nj = min(kWaves, len - k * kWaves);
+    const float* bcg = &s_bc[st][0][q * 2 * S];
 #pragma unroll
-  for (int n = 0; n < NP; ++n) h[n] = (hs && n < N) ? hs[n] : 0.0f;
-
-  const int64_t first = (row0 + t0) * D + d0;
-  const uint32_t voff = (uint32_t)(threadIdx.x * sizeof(IO));
-  const BlockReader<IO> ru{u + first, D, voff};
-  const BlockReader<IO> rdt{dt + first, D, voff};
-  const BlockReader<IO> rz{GATE ? z + (row0 + t0) * z_row_stride + d0 : nullptr, z_row_stride, voff};
-  cfloat* bcp = as_constant(bc) + (row0 + t0) * (2 * NP);
-  // y goes through the restrict pointer (not a buffer store), so the compiler knows it does
-  // not alias the packed B/C rows and keeps those as scalar loads.
-  IO* yp = y + (row0 + t0) * D + d;
-
-  float cu[kTB], cdt[kTB], cz[kTB], nu[kTB], ndt[kTB], nz[kTB];
-  ru.load(cu, 0, min(kTB, t1 - t0));
-  rdt.load(cdt, 0, min(kTB, t1 - t0));
-  if constexpr (GATE) rz.load(cz, 0, min(kTB, t1 - t0));
-  float bv[NP], cv[NP];
+    for (int j = 0; j < kWaves; ++j) {
+      if (j >= nj) break;
+      const float2 dd = s_dd[st][j][lane];
+      const float* bcr = bcg + j * BCW;
+      float bv[S], cv[S];
 #pragma unroll
-  for (int n = 0; n < NP; ++n) {
-    bv[n] = bcp[n];
-    cv[n] = bcp[NP + n];
-  }
-  for (int tb = t0; tb < t1; tb += kTB) {
-    if (tb + kTB < t1) {
-      const int nv = min(kTB, t1 - tb - kTB);
-      ru.load(nu, tb + kTB - t0, nv);
-      rdt.load(ndt, tb + kTB - t0, nv);
-      if constexpr (GATE) rz.load(nz, tb + kTB - t0, nv);
-    }
-#pragma unroll
-    for (int j = 0; j < kTB; ++j) {
-      const int t = tb + j;
-      if (t >= t1) break;
-      cfloat* bcn = t + 1 < t1 ? bcp + 2 * NP : bcp;
-      float bn[NP], cn[NP];
-#pragma unroll
-      for (int n = 0; n < NP; ++n) {
-        bn[n] = bcn[n];
-        cn[n] = bcn[NP + n];
+      for (int s2 = 0; s2 < S; ++s2) {
+        bv[s2] = bcr[s2];
+        if constexpr (OUT) cv[s2] = bcr[S + s2];
       }
-      const float uv = cu[j];
-      const float delta = make_delta(cdt[j], bias, sp);
-      const float du = delta * uv;
       float acc = 0.0f;
 #pragma unroll
-      for (int n = 0; n < NP; ++n) {
-        const float a = __builtin_amdgcn_exp2f(delta * a2[n]);
-        h[n] = fmaf(a, h[n], du * bv[n]);
-        acc = fmaf(cv[n], h[n], acc);
+      for (int s2 = 0; s2 < S; ++s2) {
+        const float a = __builtin_amdgcn_exp2f(dd.x * a2[s2]);
+        h[s2] = fmaf(a, h[s2], dd.y * bv[s2]);
+        if constexpr (OUT) acc = fmaf(cv[s2], h[s2], acc);
       }
-      acc = fmaf(dskip, uv, acc);
-      if constexpr (GATE) acc *= silu(cz[j]);
-      *yp = from_f32<IO>(acc);
-      yp += D;
+      if constexpr (OUT) s_yp[st][j][q][lane] = acc;
+      else sum_delta += dd.x;
+    }
+    __syncthreads();
+
+    // finishing step: token q of the block
+    if constexpr (OUT) {
+      if (q < nj) {
+        float yv = 0.0f;
 #pragma unroll
-      for (int n = 0; n < NP; ++n) {
-        bv[n] = bn[n];
-        cv[n] = cn[n];
+        for (int w = 0; w < kWaves; ++w) yv += s_yp[st][q][w][lane];
+        yv = fmaf(dskip, u_blk[st], yv);
+        if constexpr (GATE) yv *= g_blk[st];
+        if (dval) static_cast<IO*>(p.y)[(row0 + k * kWaves + q) * D + d] = from_f32<IO>(yv);
       }
-      bcp = bcn;
     }
-#pragma unroll
-    for (int j = 0; j < kTB; ++j) {
-      cu[j] = nu[j];
-      cdt[j] = ndt[j];
-      if constexpr (GATE) cz[j] = nz[j];
-    }
+  };
+
+  // prologue: block 0 staged, block 1 in flight
+  load_tok(0, pf_dt[0], pf_u[0], pf_z[0]);
+  load_bc(0, pf_bc[0]);
+  stage_a(0, std::integral_constant<int, 0>{});
+  if (nblk > 1) {
+    load_tok(1, pf_dt[1], pf_u[1], pf_z[1]);
+    load_bc(1, pf_bc[1]);
+  }
+  __syncthreads();
+  for (int k = 0; k < nblk; k += 2) {
+    block(k, std::integral_constant<int, 0>{});
+    if (k + 1 < nblk) block(k + 1, std::integral_constant<int, 1>{});
   }
 
-  if (c == chunks - 1 && state_out) {
-    float* so = state_out + ((int64_t)b * D + d) * N;
+  if (!dval) return;
+  if constexpr (OUT) {
+    if (c == p.chunks - 1 && p.state_out) {
 #pragma unroll
-    for (int n = 0; n < NP; ++n)
-      if (n < N) so[n] = h[n];
+      for (int s = 0; s < S; ++s) {
+        const int n = q * S + s;
+        if (n < N) p.state_out[((int64_t)b * D + d) * N + n] = h[s];
+      }
+    }
+  } else {
+    const int64_t bc_ = (int64_t)b * p.chunks + c;
+    if (q == 0) p.sum_ws[bc_ * D + d] = sum_delta;
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      const int n = q * S + s;
+      if (n < N) p.h_ws[(bc_ * N + n) * D + d] = h[s];
+    }
   }
 }
 
@@ -339,10 +305,10 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Launch-plan constants (overridable at build time for tuning sweeps).
 #ifndef MAMBA_SCAN_TARGET_WAVES
-#define MAMBA_SCAN_TARGET_WAVES 8192  // ~8 waves per SIMD (256 CUs x 4 SIMDs) to hide latency
+#define MAMBA_SCAN_TARGET_WAVES 4096  // ~4 waves per SIMD (256 CUs x 4 SIMDs)
 #endif
 #ifndef MAMBA_SCAN_MIN_CHUNK
-#define MAMBA_SCAN_MIN_CHUNK 48  // tokens per chunk, at least (per-chunk setup stays small)
+#define MAMBA_SCAN_MIN_CHUNK 64  // tokens per chunk, at least
 #endif
 
 static int padded_n(int N) { return N <= 16 ? 16 : (N <= 32 ? 32 : 64); }
@@ -350,60 +316,63 @@ static int padded_n(int N) { return N <= 16 ? 16 : (N <= 32 ? 32 : 64); }
 ScanPlan plan_selective_scan(int B, int T, int D, int N) {
   ScanPlan p{1, T, 0};
   if (B <= 0 || T <= 0 || D <= 0 || N <= 0) return p;
-  const int64_t waves_per_chunk = (int64_t)B * ((D + kScanWave - 1) / kScanWave);
-  const int64_t target_waves = MAMBA_SCAN_TARGET_WAVES;
-  int64_t chunks = (target_waves + waves_per_chunk - 1) / waves_per_chunk;
+  const int64_t waves_per_chunk = (int64_t)B * ((D + kLanes - 1) / kLanes) * kWaves;
+  int64_t chunks = (MAMBA_SCAN_TARGET_WAVES + waves_per_chunk - 1) / waves_per_chunk;
   chunks = std::max<int64_t>(1, std::min<int64_t>(chunks, T / MAMBA_SCAN_MIN_CHUNK));
-  const int chunk_t = (int)((T + chunks - 1) / chunks);
+  // whole blocks of kWaves tokens per chunk
+  int chunk_t = (int)((T + chunks - 1) / chunks);
+  chunk_t = (chunk_t + kWaves - 1) / kWaves * kWaves;
   p.chunks = (T + chunk_t - 1) / chunk_t;
   p.chunk_t = chunk_t;
-  // [packed B|C rows: B*T*2*NP f32] then, with several chunks, P, H and start states.
-  p.workspace_bytes = align256(sizeof(float) * (size_t)B * T * 2 * padded_n(N));
-  if (p.chunks > 1) p.workspace_bytes += 3 * align256(sizeof(float) * (size_t)p.chunks * B * D * N);
+  if (p.chunks > 1) {
+    const size_t bcd = (size_t)B * p.chunks * D;
+    p.workspace_bytes = align256(sizeof(float) * bcd) + align256(sizeof(float) * bcd * N) +
+                        align256(sizeof(float) * (size_t)B * N * D);
+  }
   return p;
 }
 
 template <typename IO, int NP>
-static hipError_t launch_scan_np(const ScanFwdArgs& a, const ScanPlan& p, hipStream_t s) {
-  const dim3 blk(kScanWave);
-  const int gx = (a.D + kScanWave - 1) / kScanWave;
-  const IO* u = static_cast<const IO*>(a.u);
-  const IO* dt = static_cast<const IO*>(a.dt);
-  const IO* z = static_cast<const IO*>(a.z);
-  IO* y = static_cast<IO*>(a.y);
-  char* ws = static_cast<char*>(a.workspace);
-  const int64_t rows = (int64_t)a.B * a.T;
-  float* bc = reinterpret_cast<float*>(ws);
-  ws += align256(sizeof(float) * (size_t)rows * 2 * NP);
-  pack_bc_kernel<IO, NP><<<dim3((unsigned)((rows * 2 * NP + 255) / 256)), 256, 0, s>>>(
-      static_cast<const IO*>(a.Bm), static_cast<const IO*>(a.Cm), a.bc_row_stride, bc, rows, a.N);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const float* h_start = a.state_in;
-  if (p.chunks > 1) {
-    const int64_t bdn = (int64_t)a.B * a.D * a.N;
-    const size_t per = align256(sizeof(float) * (size_t)p.chunks * bdn);
-    float* P = reinterpret_cast<float*>(ws);
-    float* H = reinterpret_cast<float*>(ws + per);
-    float* Hin = reinterpret_cast<float*>(ws + 2 * per);
-    scan_chunk_summary_kernel<IO, NP><<<dim3(gx, a.B, p.chunks - 1), blk, 0, s>>>(
-        u, dt, a.dt_bias, a.delta_softplus, a.A_log, bc, P, H, a.B, a.T, a.D, a.N, p.chunk_t,
-        p.chunks);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    scan_chunk_prefix_kernel<<<dim3((unsigned)((bdn + 255) / 256)), 256, 0, s>>>(
-        P, H, a.state_in, Hin, bdn, a.N, p.chunks);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    h_start = Hin;
+static hipError_t launch_scan_np(const ScanFwdArgs& a, const ScanPlan& pl, hipStream_t s) {
+  ScanParams p{};
+  p.u = a.u;
+  p.dt = a.dt;
+  p.Bm = a.Bm;
+  p.Cm = a.Cm;
+  p.z = a.z;
+  p.y = a.y;
+  p.dt_bias = a.dt_bias;
+  p.A_log = a.A_log;
+  p.D_skip = a.D_skip;
+  p.state_in = a.state_in;
+  p.state_out = a.state_out;
+  p.bc_row_stride = a.bc_row_stride;
+  p.z_row_stride = a.z_row_stride;
+  p.B = a.B;
+  p.T = a.T;
+  p.D = a.D;
+  p.N = a.N;
+  p.chunk_t = pl.chunk_t;
+  p.chunks = pl.chunks;
+  p.softplus = a.delta_softplus ? 1 : 0;
+  const unsigned gx = (unsigned)((a.D + kLanes - 1) / kLanes);
+  if (pl.chunks > 1) {
+    char* ws = static_cast<char*>(a.workspace);
+    const size_t bcd = (size_t)a.B * pl.chunks * a.D;
+    p.sum_ws = reinterpret_cast<float*>(ws);
+    ws += align256(sizeof(float) * bcd);
+    p.h_ws = reinterpret_cast<float*>(ws);
+    ws += align256(sizeof(float) * bcd * a.N);
+    p.start_ws = reinterpret_cast<float*>(ws);
+    scan_kernel<IO, NP, false, false><<<dim3(gx, a.B, pl.chunks - 1), kThreads, 0, s>>>(p);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
-  if (z) {
-    scan_chunk_output_kernel<IO, NP, true><<<dim3(gx, a.B, p.chunks), blk, 0, s>>>(
-        u, dt, a.dt_bias, a.delta_softplus, a.A_log, bc, a.D_skip, z, a.z_row_stride, h_start,
-        a.state_out, y, a.B, a.T, a.D, a.N, p.chunk_t, p.chunks);
-  } else {
-    scan_chunk_output_kernel<IO, NP, false><<<dim3(gx, a.B, p.chunks), blk, 0, s>>>(
-        u, dt, a.dt_bias, a.delta_softplus, a.A_log, bc, a.D_skip, nullptr, 0, h_start,
-        a.state_out, y, a.B, a.T, a.D, a.N, p.chunk_t, p.chunks);
-  }
+  const dim3 grid(gx, a.B, pl.chunks);
+  if (a.z)
+    scan_kernel<IO, NP, true, true><<<grid, kThreads, 0, s>>>(p);
+  else
+    scan_kernel<IO, NP, true, false><<<grid, kThreads, 0, s>>>(p);
   return hipGetLastError();
 }
 
