@@ -33,8 +33,13 @@
 namespace mamba {
 
 constexpr int kLanes = 64;
-constexpr int kWaves = 8;          // waves per workgroup; also tokens per block
-constexpr int kThreads = kLanes * kWaves;
+constexpr int kTB = 8;  // tokens per block (one LDS exchange and one barrier per block)
+
+#ifndef MAMBA_SCAN_CH
+#define MAMBA_SCAN_CH 64  // channels per workgroup (32 or 64)
+#endif
+constexpr int kCh = MAMBA_SCAN_CH;
+constexpr int kWaves = kTB * kCh / kLanes;  // one per-token item per thread and block
 
 struct ScanParams {
   const void* u;
@@ -64,43 +69,74 @@ __device__ __forceinline__ float a_log2(const float* __restrict__ A_log, int d, 
   return n < N ? -__builtin_amdgcn_exp2f(A_log[(int64_t)d * N + n] * kLog2e) * kLog2e : 0.0f;
 }
 
-// OUT = false: summary pass over chunks 0 .. chunks-2 (no y). OUT = true: the output pass.
-template <typename IO, int NP, bool OUT, bool GATE>
-__global__ void __launch_bounds__(kThreads) scan_kernel(const ScanParams p) {
-  constexpr int S = NP / kWaves;  // states per lane
-  constexpr int BCW = 2 * NP;     // staged B/C row: per wave group [B(S) | C(S)]
-  static_assert(S >= 2 && S * kWaves == NP, "state split");
+// Load one element at byte offset `lane_off` of a row whose address is wave-uniform: the row
+// address stays in scalar registers and the load takes the per-lane offset, so no vector
+// address arithmetic is spent per token.
+template <typename IO>
+__device__ __forceinline__ float load_at(const IO* row, uint32_t lane_off) {
+  return to_f32(*reinterpret_cast<const IO*>(reinterpret_cast<const char*>(row) + lane_off));
+}
 
-  __shared__ float2 s_dd[2][kWaves][kLanes];                     // (delta, delta*u)
-  __shared__ __attribute__((aligned(16))) float s_bc[2][kWaves][BCW];
-  __shared__ float s_yp[OUT ? 2 : 1][OUT ? kWaves : 1][kWaves][kLanes];  // partial C.h
+// OUT = false: summary pass over chunks 0 .. chunks-2 (no y). OUT = true: the output pass.
+//
+// Workgroup: CH channels x NP states as W waves. Lane l of wave q holds channel l % CH and
+// state group g = q * H + l / CH (H = 64 / CH groups per wave), i.e. states [g*S, g*S+S) with
+// S = NP / (W * H). The per-token work of a block (kTB tokens x CH channels) is one item per
+// thread: item i = q * 64 + l is token i / CH, channel i % CH.
+template <typename IO, int NP, int CH, int W, bool OUT, bool GATE>
+__global__ void __launch_bounds__(kLanes * W) __attribute__((amdgpu_waves_per_eu(5)))
+scan_kernel(const ScanParams p) {
+  constexpr int H = kLanes / CH;     // state groups per wave
+  constexpr int G = W * H;           // state groups per workgroup
+  constexpr int S = NP / G;          // states per lane
+  constexpr int NT = kLanes * W;
+  constexpr int BCW = 2 * NP;        // staged B/C row: per group [B(S) | C(S)]
+  static_assert(S >= 1 && S * G == NP, "state split");
+  static_assert(kTB * CH == NT, "one per-token item per thread and block");
+
+  __shared__ float2 s_dd[2][kTB][CH];  // (delta, delta*u)
+  __shared__ __attribute__((aligned(16))) float s_bc[2][kTB][BCW];
+  __shared__ float s_yp[OUT ? 2 : 1][OUT ? kTB : 1][G][CH];  // partial C.h per group
 
   const int lane = threadIdx.x & (kLanes - 1);
-  // wave index, made explicitly wave-uniform so row arithmetic stays scalar
+  // wave index, explicitly wave-uniform so that row arithmetic stays scalar
   const int q = __builtin_amdgcn_readfirstlane(threadIdx.x / kLanes);
-  const int d = blockIdx.x * kLanes + lane;
-  const bool dval = d < p.D;
-  const int dc = dval ? d : p.D - 1;  // clamped channel for loads of masked lanes
+  const int ch = lane % CH;          // this lane's channel in the scan
+  const int g = q * H + lane / CH;   // this lane's state group
+  const int d0 = blockIdx.x * CH;
   const int b = blockIdx.y;
   const int c = blockIdx.z;
   const int N = p.N, D = p.D;
   const int t0 = c * p.chunk_t;
   const int len = min(p.T, t0 + p.chunk_t) - t0;
-  const int nblk = (len + kWaves - 1) / kWaves;
+  const int nblk = (len + kTB - 1) / kTB;
   const int64_t row0 = (int64_t)b * p.T + t0;  // first row of the chunk
+  const int64_t bcs = p.bc_row_stride;
+  const int d = d0 + ch;
+  const int dc = min(d, D - 1);  // clamped channel for loads of masked lanes
+
+  // per-token item of this thread: token ij of the block (ij = it_wave + it_lane), channel ic
+  const int it_wave = q * kLanes / CH;  // wave-uniform part of the token index
+  const int it_lane = lane / CH;
+  const int ic = lane % CH;
+  const int di = d0 + ic;
+  const int dic = min(di, D - 1);
 
   const IO* __restrict__ u = static_cast<const IO*>(p.u);
   const IO* __restrict__ dt = static_cast<const IO*>(p.dt);
-  const IO* __restrict__ Bm = static_cast<const IO*>(p.Bm);
-  const IO* __restrict__ Cm = static_cast<const IO*>(p.Cm);
   const IO* __restrict__ z = static_cast<const IO*>(p.z);
+  // byte offsets of this thread's item in a block's first row (the row address is scalar)
+  const uint32_t off_x = ((uint32_t)it_lane * (uint32_t)D + (uint32_t)dic) * (uint32_t)sizeof(IO);
+  const uint32_t off_z =
+      ((uint32_t)it_lane * (uint32_t)p.z_row_stride + (uint32_t)dic) * (uint32_t)sizeof(IO);
 
   float a2[S];
 #pragma unroll
-  for (int s = 0; s < S; ++s) a2[s] = a_log2(p.A_log, dc, q * S + s, N);
-  const float bias = p.dt_bias ? p.dt_bias[dc] : 0.0f;
-  const float dskip = p.D_skip ? p.D_skip[dc] : 0.0f;
+  for (int s = 0; s < S; ++s) a2[s] = a_log2(p.A_log, dc, g * S + s, N);
+  const float bias = p.dt_bias ? p.dt_bias[dic] : 0.0f;
+  const float dskip = p.D_skip ? p.D_skip[dic] : 0.0f;
   const bool sp = p.softplus != 0;
+  const bool dval = d < D;
 
   // ---- start state
   float h[S];
@@ -108,23 +144,34 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(const ScanParams p) {
     if (p.chunks == 1) {
 #pragma unroll
       for (int s = 0; s < S; ++s) {
-        const int n = q * S + s;
+        const int n = g * S + s;
         h[s] = (p.state_in && n < N) ? p.state_in[((int64_t)b * D + dc) * N + n] : 0.0f;
       }
     } else {
       // carried state, then the maps of chunks 0 .. c-1 in token order
 #pragma unroll
       for (int s = 0; s < S; ++s) {
-        const int n = q * S + s;
+        const int n = g * S + s;
         h[s] = n < N ? p.start_ws[((int64_t)b * N + n) * D + dc] : 0.0f;
       }
-      for (int cc = 0; cc < c; ++cc) {
-        const int64_t bc_ = (int64_t)b * p.chunks + cc;
-        const float sd = p.sum_ws[bc_ * D + dc];
+      // predecessors in groups of kFold: all of a group's loads are issued before its fmas
+      constexpr int kFold = S <= 2 ? 8 : (S <= 4 ? 4 : 1);
+      for (int c0 = 0; c0 < c; c0 += kFold) {
+        float sd[kFold], hv[kFold][S];
 #pragma unroll
-        for (int s = 0; s < S; ++s) {
-          const int n = q * S + s;
-          if (n < N) h[s] = fmaf(__builtin_amdgcn_exp2f(a2[s] * sd), h[s], p.h_ws[(bc_ * N + n) * D + dc]);
+        for (int f = 0; f < kFold; ++f) {
+          const int64_t bc_ = (int64_t)b * p.chunks + min(c0 + f, c - 1);
+          sd[f] = p.sum_ws[bc_ * D + dc];
+#pragma unroll
+          for (int s = 0; s < S; ++s) hv[f][s] = p.h_ws[(bc_ * N + min(g * S + s, N - 1)) * D + dc];
+        }
+#pragma unroll
+        for (int f = 0; f < kFold; ++f) {
+          if (c0 + f < c) {
+#pragma unroll
+            for (int s = 0; s < S; ++s)
+              if (g * S + s < N) h[s] = fmaf(__builtin_amdgcn_exp2f(a2[s] * sd[f]), h[s], hv[f][s]);
+          }
         }
       }
     }
@@ -134,7 +181,7 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(const ScanParams p) {
     if (c == 0 && dval) {  // keep the carried state for the output pass (it may be updated in place)
 #pragma unroll
       for (int s = 0; s < S; ++s) {
-        const int n = q * S + s;
+        const int n = g * S + s;
         if (n < N)
           p.start_ws[((int64_t)b * N + n) * D + d] =
               p.state_in ? p.state_in[((int64_t)b * D + d) * N + n] : 0.0f;
@@ -142,131 +189,152 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(const ScanParams p) {
     }
   }
 
-  // ---- per-token loads of this wave's token in block k, and its B/C staging values
-  // Thread i < kWaves * BCW stages entry i of the block: token i / BCW, slot i % BCW.
-  constexpr int BC_PER_T = (kWaves * BCW + kThreads - 1) / kThreads;
-  // Loads are never predicated: a token past the chunk re-reads the chunk's last row and a
-  // padded state re-reads state N-1 (in bounds; such values are replaced by 0 when staged or
-  // never read), so no load result has to be merged with an older value.
-  const IO* __restrict__ dt_l = dt + dc;
-  const IO* __restrict__ u_l = u + dc;
-  const IO* __restrict__ z_l = z + dc;
-  auto load_tok = [&](int k, float& rdt, float& ru, float& rz) {
-    const int64_t row = row0 + min(k * kWaves + q, len - 1);  // wave-uniform
-    rdt = to_f32(dt_l[row * D]);
-    ru = to_f32(u_l[row * D]);
-    if constexpr (OUT && GATE) rz = to_f32(z_l[row * p.z_row_stride]);
-  };
-  auto bc_slot = [&](int r, int& j, int& n, bool& isC) {
-    const int i = threadIdx.x + r * kThreads;
-    j = i / BCW;
-    const int slot = i % BCW;
-    const int w = slot % (2 * S);
-    isC = w >= S;
-    n = slot / (2 * S) * S + (isC ? w - S : w);
-  };
-  auto load_bc = [&](int k, float (&v)[BC_PER_T]) {
+  // ---- B/C staging: thread i < kTB * BCW stages entry i of a block (token i / BCW, slot
+  // i % BCW; the slots of group g are [B(gS..gS+S) | C(gS..gS+S)]).
+  constexpr int BC_PER_T = (kTB * BCW + NT - 1) / NT;
+  const IO* bc_src[BC_PER_T];  // this thread's B or C entry, token bc_j of the chunk's block 0
+  int bc_j[BC_PER_T];
+  bool bc_use[BC_PER_T];
 #pragma unroll
-    for (int r = 0; r < BC_PER_T; ++r) {
-      if (threadIdx.x + r * kThreads < kWaves * BCW) {  // whole waves
-        int j, n;
-        bool isC;
-        bc_slot(r, j, n, isC);
-        const IO* src = isC ? Cm : Bm;
-        v[r] = to_f32(src[(row0 + min(k * kWaves + j, len - 1)) * p.bc_row_stride + min(n, N - 1)]);
-      }
-    }
-  };
-  auto store_bc = [&](int k, int buf, const float (&v)[BC_PER_T]) {
-#pragma unroll
-    for (int r = 0; r < BC_PER_T; ++r) {
-      const int i = threadIdx.x + r * kThreads;
-      if (i < kWaves * BCW) {
-        int j, n;
-        bool isC;
-        bc_slot(r, j, n, isC);
-        const bool ok = k * kWaves + j < len && n < N && (OUT || !isC);
-        s_bc[buf][j][i % BCW] = ok ? v[r] : 0.0f;
-      }
-    }
-  };
+  for (int r = 0; r < BC_PER_T; ++r) {
+    const int i = threadIdx.x + r * NT;
+    const int slot = i % BCW, w = slot % (2 * S);
+    const bool isC = w >= S;
+    const int n = slot / (2 * S) * S + (isC ? w - S : w);
+    bc_j[r] = i / BCW;
+    bc_use[r] = i < kTB * BCW && n < N && (OUT || !isC);
+    bc_src[r] = static_cast<const IO*>(isC ? p.Cm : p.Bm) + (row0 + bc_j[r]) * bcs + min(n, N - 1);
+  }
 
-  // Register sets by block parity: the values of block m live in set m & 1, so the loop,
-  // unrolled by two, never copies a register that a load is still filling.
-  float pf_dt[2] = {0.0f, 0.0f}, pf_u[2] = {0.0f, 0.0f}, pf_z[2] = {0.0f, 0.0f};
-  float pf_bc[2][BC_PER_T];
-  float u_blk[2] = {0.0f, 0.0f}, g_blk[2] = {1.0f, 1.0f};  // u, silu(z) of this wave's token
-
-  // stage A: delta, delta*u of this wave's token of block m into LDS; B/C rows of block m
-  auto stage_a = [&](int m, auto P) {
+  // Loads are never predicated on the token: a token past the chunk re-reads the chunk's last
+  // row (in bounds; such values are never used), so no load result is merged with an older
+  // value and nothing waits on a load before its use.
+  float pf_dt[2], pf_u[2], pf_z[2], pf_bc[2][BC_PER_T];
+  float u_blk[2], g_blk[2];  // u and silu(z) of this thread's item, for the finish
+  auto load_block = [&](int k, auto P) {
     constexpr int st = decltype(P)::value;
-    const float delta = sp ? softplus(pf_dt[st] + bias) : pf_dt[st] + bias;
-    s_dd[st][q][lane] = make_float2(delta, delta * pf_u[st]);
+    if (k * kTB + kTB <= len) {
+      // full block: scalar row address + the thread's fixed byte offset
+      const int64_t row = row0 + k * kTB + it_wave;
+      pf_dt[st] = load_at(dt + row * D, off_x);
+      pf_u[st] = load_at(u + row * D, off_x);
+      if constexpr (OUT && GATE) pf_z[st] = load_at(z + row * p.z_row_stride, off_z);
+      const int64_t step = (int64_t)k * kTB * bcs;
+#pragma unroll
+      for (int r = 0; r < BC_PER_T; ++r)
+        if (threadIdx.x + r * NT < kTB * BCW) pf_bc[st][r] = to_f32(bc_src[r][step]);  // whole waves
+    } else {
+      const int64_t row = row0 + min(k * kTB + it_wave + it_lane, len - 1);
+      pf_dt[st] = to_f32(dt[row * D + dic]);
+      pf_u[st] = to_f32(u[row * D + dic]);
+      if constexpr (OUT && GATE) pf_z[st] = to_f32(z[row * p.z_row_stride + dic]);
+#pragma unroll
+      for (int r = 0; r < BC_PER_T; ++r)
+        if (threadIdx.x + r * NT < kTB * BCW)
+          pf_bc[st][r] = to_f32(bc_src[r][(int64_t)(min(k * kTB + bc_j[r], len - 1) - bc_j[r]) * bcs]);
+    }
+  };
+
+  // stage A: delta and delta*u of this thread's item of block k into LDS, B/C of block k
+  auto stage_a = [&](int k, auto P) {
+    constexpr int st = decltype(P)::value;
+    const float v = pf_dt[st] + bias;
+    const float delta = sp ? softplus(v) : v;
+    s_dd[st][it_wave + it_lane][ic] = make_float2(delta, delta * pf_u[st]);
     u_blk[st] = pf_u[st];
     if constexpr (OUT && GATE) g_blk[st] = silu(pf_z[st]);
-    store_bc(m, st, pf_bc[st]);
+#pragma unroll
+    for (int r = 0; r < BC_PER_T; ++r) {
+      const int i = threadIdx.x + r * NT;
+      if (i < kTB * BCW)
+        s_bc[st][bc_j[r]][i % BCW] = (bc_use[r] && k * kTB + bc_j[r] < len) ? pf_bc[st][r] : 0.0f;
+    }
   };
 
   float sum_delta = 0.0f;
+  // stage B: the LDS operands of one token (delta, delta*u, and this group's B and C)
+  struct TokOps {
+    float2 dd;
+    float bv[S], cv[S];
+  };
+  auto read_token = [&](int st, int j, TokOps& o) {
+    o.dd = s_dd[st][j][ch];
+    const float* bcr = &s_bc[st][j][g * 2 * S];
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      o.bv[s] = bcr[s];
+      if constexpr (OUT) o.cv[s] = bcr[S + s];
+    }
+  };
+  // advance the S states by one token; the partial C.h goes to LDS
+  auto scan_token = [&](int st, int j, const TokOps& o) {
+    float acc = 0.0f;
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      const float a = __builtin_amdgcn_exp2f(o.dd.x * a2[s]);
+      h[s] = fmaf(a, h[s], o.dd.y * o.bv[s]);
+      if constexpr (OUT) acc = s == 0 ? o.cv[0] * h[0] : fmaf(o.cv[s], h[s], acc);
+    }
+    if constexpr (OUT) s_yp[st][j][g][ch] = acc;
+    else sum_delta += o.dd.x;
+  };
+  // Token j+1's LDS reads are issued before token j's arithmetic (one token of look-ahead:
+  // the read latency hides behind a token of work); the scheduling barriers stop the compiler
+  // from hoisting further, which would cost more registers than it saves.
+  auto scan_block = [&](int st, int nj) {
+    TokOps cur, nxt;
+    read_token(st, 0, cur);
+    if (nj == kTB) {
+#pragma unroll
+      for (int j = 0; j < kTB; ++j) {
+        if (j + 1 < kTB) read_token(st, j + 1, nxt);
+        scan_token(st, j, cur);
+        cur = nxt;
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+      for (int j = 0; j < nj; ++j) {
+        if (j + 1 < nj) read_token(st, j + 1, nxt);
+        scan_token(st, j, cur);
+        cur = nxt;
+      }
+    }
+  };
+
   // one block: stage A of block k+1, loads of block k+2, stage B of block k, barrier, finish
   auto block = [&](int k, auto P) {
     constexpr int st = decltype(P)::value;  // == k & 1
-    constexpr int nx = st ^ 1;
     if (k + 1 < nblk) {
-      stage_a(k + 1, std::integral_constant<int, nx>{});
-      if (k + 2 < nblk) {
-        load_tok(k + 2, pf_dt[st], pf_u[st], pf_z[st]);
-        load_bc(k + 2, pf_bc[st]);
-      }
+      stage_a(k + 1, std::integral_constant<int, st ^ 1>{});
+      if (k + 2 < nblk) load_block(k + 2, P);
     }
-
-    // stage B: every wave advances its S states over the block's tokens
-    const int nj = min(kWaves, len - k * kWaves);
-    const float* bcg = &s_bc[st][0][q * 2 * S];
-#pragma unroll
-    for (int j = 0; j < kWaves; ++j) {
-      if (j >= nj) break;
-      const float2 dd = s_dd[st][j][lane];
-      const float* bcr = bcg + j * BCW;
-      float bv[S], cv[S];
-#pragma unroll
-      for (int s2 = 0; s2 < S; ++s2) {
-        bv[s2] = bcr[s2];
-        if constexpr (OUT) cv[s2] = bcr[S + s2];
-      }
-      float acc = 0.0f;
-#pragma unroll
-      for (int s2 = 0; s2 < S; ++s2) {
-        const float a = __builtin_amdgcn_exp2f(dd.x * a2[s2]);
-        h[s2] = fmaf(a, h[s2], dd.y * bv[s2]);
-        if constexpr (OUT) acc = fmaf(cv[s2], h[s2], acc);
-      }
-      if constexpr (OUT) s_yp[st][j][q][lane] = acc;
-      else sum_delta += dd.x;
-    }
+    const int nj = min(kTB, len - k * kTB);
+    scan_block(st, nj);
     __syncthreads();
 
-    // finishing step: token q of the block
+    // finish: this thread's item of the block
     if constexpr (OUT) {
-      if (q < nj) {
-        float yv = 0.0f;
+      const int j = it_wave + it_lane;
+      if (j < nj) {
+        float part[G];
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) yv += s_yp[st][q][w][lane];
+        for (int w = 0; w < G; ++w) part[w] = s_yp[st][j][w][ic];
+#pragma unroll
+        for (int span = 1; span < G; span *= 2)  // pairwise tree: short dependency chain
+#pragma unroll
+          for (int w = 0; w + span < G; w += 2 * span) part[w] += part[w + span];
+        float yv = part[0];
         yv = fmaf(dskip, u_blk[st], yv);
         if constexpr (GATE) yv *= g_blk[st];
-        if (dval) static_cast<IO*>(p.y)[(row0 + k * kWaves + q) * D + d] = from_f32<IO>(yv);
+        if (di < D) static_cast<IO*>(p.y)[(row0 + k * kTB + j) * D + di] = from_f32<IO>(yv);
       }
     }
   };
 
   // prologue: block 0 staged, block 1 in flight
-  load_tok(0, pf_dt[0], pf_u[0], pf_z[0]);
-  load_bc(0, pf_bc[0]);
+  load_block(0, std::integral_constant<int, 0>{});
   stage_a(0, std::integral_constant<int, 0>{});
-  if (nblk > 1) {
-    load_tok(1, pf_dt[1], pf_u[1], pf_z[1]);
-    load_bc(1, pf_bc[1]);
-  }
+  if (nblk > 1) load_block(1, std::integral_constant<int, 1>{});
   __syncthreads();
   for (int k = 0; k < nblk; k += 2) {
     block(k, std::integral_constant<int, 0>{});
@@ -278,16 +346,16 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(const ScanParams p) {
     if (c == p.chunks - 1 && p.state_out) {
 #pragma unroll
       for (int s = 0; s < S; ++s) {
-        const int n = q * S + s;
+        const int n = g * S + s;
         if (n < N) p.state_out[((int64_t)b * D + d) * N + n] = h[s];
       }
     }
   } else {
     const int64_t bc_ = (int64_t)b * p.chunks + c;
-    if (q == 0) p.sum_ws[bc_ * D + d] = sum_delta;
+    if (g == 0) p.sum_ws[bc_ * D + d] = sum_delta;
 #pragma unroll
     for (int s = 0; s < S; ++s) {
-      const int n = q * S + s;
+      const int n = g * S + s;
       if (n < N) p.h_ws[(bc_ * N + n) * D + d] = h[s];
     }
   }
@@ -316,12 +384,12 @@ static int padded_n(int N) { return N <= 16 ? 16 : (N <= 32 ? 32 : 64); }
 ScanPlan plan_selective_scan(int B, int T, int D, int N) {
   ScanPlan p{1, T, 0};
   if (B <= 0 || T <= 0 || D <= 0 || N <= 0) return p;
-  const int64_t waves_per_chunk = (int64_t)B * ((D + kLanes - 1) / kLanes) * kWaves;
+  const int64_t waves_per_chunk = (int64_t)B * ((D + kCh - 1) / kCh) * kWaves;
   int64_t chunks = (MAMBA_SCAN_TARGET_WAVES + waves_per_chunk - 1) / waves_per_chunk;
   chunks = std::max<int64_t>(1, std::min<int64_t>(chunks, T / MAMBA_SCAN_MIN_CHUNK));
-  // whole blocks of kWaves tokens per chunk
+  // whole blocks of kTB tokens per chunk
   int chunk_t = (int)((T + chunks - 1) / chunks);
-  chunk_t = (chunk_t + kWaves - 1) / kWaves * kWaves;
+  chunk_t = (chunk_t + kTB - 1) / kTB * kTB;
   p.chunks = (T + chunk_t - 1) / chunk_t;
   p.chunk_t = chunk_t;
   if (p.chunks > 1) {
@@ -334,6 +402,9 @@ ScanPlan plan_selective_scan(int B, int T, int D, int N) {
 
 template <typename IO, int NP>
 static hipError_t launch_scan_np(const ScanFwdArgs& a, const ScanPlan& pl, hipStream_t s) {
+  // 64 states per channel: 64-channel workgroups keep the states per lane at 8
+  constexpr int CH = NP == 64 ? 64 : kCh;
+  constexpr int W = kTB * CH / kLanes;
   ScanParams p{};
   p.u = a.u;
   p.dt = a.dt;
@@ -355,7 +426,7 @@ static hipError_t launch_scan_np(const ScanFwdArgs& a, const ScanPlan& pl, hipSt
   p.chunk_t = pl.chunk_t;
   p.chunks = pl.chunks;
   p.softplus = a.delta_softplus ? 1 : 0;
-  const unsigned gx = (unsigned)((a.D + kLanes - 1) / kLanes);
+  const unsigned gx = (unsigned)((a.D + CH - 1) / CH);
   if (pl.chunks > 1) {
     char* ws = static_cast<char*>(a.workspace);
     const size_t bcd = (size_t)a.B * pl.chunks * a.D;
@@ -364,15 +435,15 @@ static hipError_t launch_scan_np(const ScanFwdArgs& a, const ScanPlan& pl, hipSt
     p.h_ws = reinterpret_cast<float*>(ws);
     ws += align256(sizeof(float) * bcd * a.N);
     p.start_ws = reinterpret_cast<float*>(ws);
-    scan_kernel<IO, NP, false, false><<<dim3(gx, a.B, pl.chunks - 1), kThreads, 0, s>>>(p);
+    scan_kernel<IO, NP, CH, W, false, false><<<dim3(gx, a.B, pl.chunks - 1), kLanes * W, 0, s>>>(p);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   const dim3 grid(gx, a.B, pl.chunks);
   if (a.z)
-    scan_kernel<IO, NP, true, true><<<grid, kThreads, 0, s>>>(p);
+    scan_kernel<IO, NP, CH, W, true, true><<<grid, kLanes * W, 0, s>>>(p);
   else
-    scan_kernel<IO, NP, true, false><<<grid, kThreads, 0, s>>>(p);
+    scan_kernel<IO, NP, CH, W, true, false><<<grid, kLanes * W, 0, s>>>(p);
   return hipGetLastError();
 }
 
