@@ -17,9 +17,6 @@
 
 namespace mamba {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
 // ------------------------------------------------------------------------- embedding
 
 // out[r, :] = E[tokens[r], :] (bf16 -> f32). One block per row. Ids outside [0, vocab) are
@@ -61,64 +58,132 @@ __global__ void __launch_bounds__(256) rmsnorm_kernel(const float* __restrict__ 
 // ------------------------------------------------------------------------- GEMM (MFMA)
 //
 // C[M, N] (+)= A[M, K] * W[N, K]^T with A f32 or bf16 (rounded to bf16 when staged), W bf16
-// (nn.Linear layout: one row of K per output column), C f32. Block tile BM x BN x 32, four
-// waves in a 2 x 2 grid, each wave (BM/2) x (BN/2) as 16 x 16 tiles of
-// v_mfma_f32_16x16x32_bf16. Operand fragments: lane l holds row (l % 16) and k = 8*(l/16)+0..7
-// of A (of W for B); the result holds rows 4*(l/16)+0..3 of column l % 16.
-// LDS rows are 40 bf16 (32 + 8 pad): the 16-byte fragment reads of each group of 8 lanes fall
-// on disjoint banks. Double-buffered: the next k-slab is fetched to registers while the
-// current one is multiplied.
+// (nn.Linear layout: one row of K per output column), C f32.
+//
+// Block tile BM x BN x BK, WGM x WGN waves, each wave a (BM/WGM) x (BN/WGN) tile made of
+// 16 x 16 tiles of v_mfma_f32_16x16x32_bf16. Operand fragments: lane l holds row (l % 16)
+// and k = 8*(l/16)+0..7 of A (of W for B); the result holds rows 4*(l/16)+0..3 of column
+// l % 16. Global loads move 8 consecutive k (16 bytes of bf16, 32 of f32) per thread and
+// chunk, adjacent threads adjacent chunks of a row; staged tiles sit in LDS as bf16 rows of
+// BK + 8 elements (the pad spreads the 16-byte fragment reads over the banks). LDS is double
+// buffered: the next k-slab is loaded into registers while the current one is multiplied,
+// and one barrier per slab orders the buffers. VEC = false is the element-wise path for
+// unaligned or ragged operands.
 
-constexpr int kBK = 32;
-constexpr int kLdsK = kBK + 8;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-template <typename AT, int BM, int BN>
-__global__ void __launch_bounds__(256) gemm_bf16_kernel(const AT* __restrict__ A, int64_t lda,
-                                                        const bf16* __restrict__ W, int64_t ldw,
-                                                        float* __restrict__ C, int64_t ldc,
-                                                        int M, int N, int K, int accumulate) {
-  constexpr int WM = BM / 2, WN = BN / 2;
-  constexpr int TM = WM / 16, TN = WN / 16;
-  constexpr int A_PER_T = BM * kBK / 256;  // elements of A each thread stages per slab
-  constexpr int W_PER_T = BN * kBK / 256;
-  static_assert(A_PER_T == 16 || A_PER_T == 8 || A_PER_T == 4, "A staging width");
-  static_assert(W_PER_T == 16 || W_PER_T == 8 || W_PER_T == 4, "W staging width");
-  __shared__ __attribute__((aligned(16))) bf16 As[2][BM * kLdsK];
-  __shared__ __attribute__((aligned(16))) bf16 Ws[2][BN * kLdsK];
+template <typename AT>
+struct Chunk;  // 8 consecutive elements of a row, as loaded
+template <>
+struct Chunk<bf16> {
+  uint4 v;
+};
+template <>
+struct Chunk<float> {
+  float4 lo, hi;
+};
+
+template <typename AT>
+__device__ __forceinline__ void load_chunk(Chunk<AT>& c, const AT* p);
+template <>
+__device__ __forceinline__ void load_chunk<bf16>(Chunk<bf16>& c, const bf16* p) {
+  c.v = *reinterpret_cast<const uint4*>(p);
+}
+template <>
+__device__ __forceinline__ void load_chunk<float>(Chunk<float>& c, const float* p) {
+  c.lo = *reinterpret_cast<const float4*>(p);
+  c.hi = *reinterpret_cast<const float4*>(p + 4);
+}
+template <typename AT>
+__device__ __forceinline__ void zero_chunk(Chunk<AT>& c);
+template <>
+__device__ __forceinline__ void zero_chunk<bf16>(Chunk<bf16>& c) {
+  c.v = make_uint4(0, 0, 0, 0);
+}
+template <>
+__device__ __forceinline__ void zero_chunk<float>(Chunk<float>& c) {
+  c.lo = c.hi = make_float4(0.f, 0.f, 0.f, 0.f);
+}
+// 8 elements as bf16 (RNE for f32)
+__device__ __forceinline__ bf16x8 to_bf16x8(const Chunk<bf16>& c) {
+  return __builtin_bit_cast(bf16x8, c.v);
+}
+__device__ __forceinline__ bf16x8 to_bf16x8(const Chunk<float>& c) {
+  bf16x8 r;
+  r[0] = (bf16)c.lo.x; r[1] = (bf16)c.lo.y; r[2] = (bf16)c.lo.z; r[3] = (bf16)c.lo.w;
+  r[4] = (bf16)c.hi.x; r[5] = (bf16)c.hi.y; r[6] = (bf16)c.hi.z; r[7] = (bf16)c.hi.w;
+  return r;
+}
+// element-wise chunk load with bounds (ragged K, unaligned rows)
+template <typename AT>
+__device__ __forceinline__ bf16x8 load_chunk_scalar(const AT* row, int k0, int K) {
+  bf16x8 r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = k0 + i < K ? (bf16)to_f32(row[k0 + i]) : (bf16)0.0f;
+  return r;
+}
+
+template <typename AT, int BM, int BN, int BK, int WGM, int WGN, bool VEC>
+__global__ void __launch_bounds__(64 * WGM * WGN) gemm_mfma_kernel(
+    const AT* __restrict__ A, int64_t lda, const bf16* __restrict__ W, int64_t ldw,
+    float* __restrict__ C, int64_t ldc, int M, int N, int K, int accumulate) {
+  constexpr int NT = 64 * WGM * WGN;
+  constexpr int WTM = BM / WGM, WTN = BN / WGN;  // wave tile
+  constexpr int TM = WTM / 16, TN = WTN / 16;
+  constexpr int LDK = BK + 8;
+  constexpr int CPR = BK / 8;  // chunks per row
+  constexpr int A_CH = BM * CPR / NT, W_CH = BN * CPR / NT;
+  static_assert(TM * 16 == WTM && TN * 16 == WTN && BK % 32 == 0, "tile shape");
+  static_assert(A_CH * NT == BM * CPR && W_CH * NT == BN * CPR, "staging split");
+  __shared__ __attribute__((aligned(16))) bf16 As[2][BM * LDK];
+  __shared__ __attribute__((aligned(16))) bf16 Ws[2][BN * LDK];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WGN, wn = wave % WGN;
   const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
 
-  // staging coordinates: thread -> (row, k offset) of the slab
-  constexpr int A_TPR = kBK / A_PER_T;  // threads per row
-  constexpr int W_TPR = kBK / W_PER_T;
-  const int a_row = tid / A_TPR, a_k = (tid % A_TPR) * A_PER_T;
-  const int w_row = tid / W_TPR, w_k = (tid % W_TPR) * W_PER_T;
-
-  float ra[A_PER_T], rw[W_PER_T];
+  bf16x8 ra[A_CH], rw[W_CH];
   auto fetch = [&](int k0) {
-    const int gm = m0 + a_row;
 #pragma unroll
-    for (int i = 0; i < A_PER_T; ++i) {
-      const int gk = k0 + a_k + i;
-      ra[i] = (gm < M && gk < K) ? to_f32(A[(int64_t)gm * lda + gk]) : 0.0f;
+    for (int i = 0; i < A_CH; ++i) {
+      const int c = tid + i * NT, r = c / CPR, kc = (c % CPR) * 8;
+      const int gm = m0 + r, gk = k0 + kc;
+      if constexpr (VEC) {
+        Chunk<AT> ch;
+        if (gm < M && gk < K) load_chunk<AT>(ch, A + (int64_t)gm * lda + gk);
+        else zero_chunk<AT>(ch);
+        ra[i] = to_bf16x8(ch);
+      } else {
+        ra[i] = gm < M ? load_chunk_scalar(A + (int64_t)gm * lda, gk, K) : bf16x8{};
+      }
     }
-    const int gn = n0 + w_row;
 #pragma unroll
-    for (int i = 0; i < W_PER_T; ++i) {
-      const int gk = k0 + w_k + i;
-      rw[i] = (gn < N && gk < K) ? to_f32(W[(int64_t)gn * ldw + gk]) : 0.0f;
+    for (int i = 0; i < W_CH; ++i) {
+      const int c = tid + i * NT, r = c / CPR, kc = (c % CPR) * 8;
+      const int gn = n0 + r, gk = k0 + kc;
+      if constexpr (VEC) {
+        Chunk<bf16> ch;
+        if (gn < N && gk < K) load_chunk<bf16>(ch, W + (int64_t)gn * ldw + gk);
+        else zero_chunk<bf16>(ch);
+        rw[i] = to_bf16x8(ch);
+      } else {
+        rw[i] = gn < N ? load_chunk_scalar(W + (int64_t)gn * ldw, gk, K) : bf16x8{};
+      }
     }
   };
   auto stash = [&](int buf) {
-    bf16* a = &As[buf][a_row * kLdsK + a_k];
 #pragma unroll
-    for (int i = 0; i < A_PER_T; ++i) a[i] = from_f32<bf16>(ra[i]);
-    bf16* w = &Ws[buf][w_row * kLdsK + w_k];
+    for (int i = 0; i < A_CH; ++i) {
+      const int c = tid + i * NT;
+      *reinterpret_cast<bf16x8*>(&As[buf][(c / CPR) * LDK + (c % CPR) * 8]) = ra[i];
+    }
 #pragma unroll
-    for (int i = 0; i < W_PER_T; ++i) w[i] = from_f32<bf16>(rw[i]);
+    for (int i = 0; i < W_CH; ++i) {
+      const int c = tid + i * NT;
+      *reinterpret_cast<bf16x8*>(&Ws[buf][(c / CPR) * LDK + (c % CPR) * 8]) = rw[i];
+    }
   };
 
   f32x4 acc[TM][TN];
@@ -127,30 +192,31 @@ __global__ void __launch_bounds__(256) gemm_bf16_kernel(const AT* __restrict__ A
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-  const int nk = (K + kBK - 1) / kBK;
+  const int nk = (K + BK - 1) / BK;
   fetch(0);
   stash(0);
   __syncthreads();
   const int frow = lane & 15, fk = (lane >> 4) * 8;
   for (int kt = 0; kt < nk; ++kt) {
     const int buf = kt & 1;
-    if (kt + 1 < nk) fetch((kt + 1) * kBK);
-    bf16x8 af[TM], bfr[TN];
+    if (kt + 1 < nk) fetch((kt + 1) * BK);
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
-      af[i] = *reinterpret_cast<const bf16x8*>(&As[buf][(wm * WM + i * 16 + frow) * kLdsK + fk]);
+    for (int kk = 0; kk < BK; kk += 32) {
+      bf16x8 af[TM], bfr[TN];
 #pragma unroll
-    for (int j = 0; j < TN; ++j)
-      bfr[j] = *reinterpret_cast<const bf16x8*>(&Ws[buf][(wn * WN + j * 16 + frow) * kLdsK + fk]);
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
+      for (int i = 0; i < TM; ++i)
+        af[i] = *reinterpret_cast<const bf16x8*>(&As[buf][(wm * WTM + i * 16 + frow) * LDK + kk + fk]);
 #pragma unroll
       for (int j = 0; j < TN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-    if (kt + 1 < nk) {
-      stash(buf ^ 1);
-      __syncthreads();
+        bfr[j] = *reinterpret_cast<const bf16x8*>(&Ws[buf][(wn * WTN + j * 16 + frow) * LDK + kk + fk]);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
     }
+    if (kt + 1 < nk) stash(buf ^ 1);
+    __syncthreads();
   }
 
   // epilogue: lane holds rows 4*(lane/16)+0..3 of column lane%16 of each 16x16 tile
@@ -159,11 +225,11 @@ __global__ void __launch_bounds__(256) gemm_bf16_kernel(const AT* __restrict__ A
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
-      const int gn = n0 + wn * WN + j * 16 + ccol;
+      const int gn = n0 + wn * WTN + j * 16 + ccol;
       if (gn >= N) continue;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int gm = m0 + wm * WM + i * 16 + crow + r;
+        const int gm = m0 + wm * WTM + i * 16 + crow + r;
         if (gm >= M) continue;
         float* cp = C + (int64_t)gm * ldc + gn;
         *cp = accumulate ? *cp + acc[i][j][r] : acc[i][j][r];
@@ -237,11 +303,16 @@ hipError_t launch_rmsnorm(const float* x, int64_t x_row_stride, const float* w, 
   return hipGetLastError();
 }
 
-template <typename AT, int BM, int BN>
+template <typename AT, int BM, int BN, int BK, int WGM, int WGN>
 static hipError_t gemm_tile(const AT* A, int64_t lda, const bf16* W, int64_t ldw, float* C,
-                            int64_t ldc, int M, int N, int K, bool acc, hipStream_t s) {
-  dim3 grid((unsigned)((N + BN - 1) / BN), (unsigned)((M + BM - 1) / BM));
-  gemm_bf16_kernel<AT, BM, BN><<<grid, 256, 0, s>>>(A, lda, W, ldw, C, ldc, M, N, K, acc ? 1 : 0);
+                            int64_t ldc, int M, int N, int K, bool acc, bool vec, hipStream_t s) {
+  const dim3 grid((unsigned)((N + BN - 1) / BN), (unsigned)((M + BM - 1) / BM));
+  if (vec)
+    gemm_mfma_kernel<AT, BM, BN, BK, WGM, WGN, true><<<grid, 64 * WGM * WGN, 0, s>>>(
+        A, lda, W, ldw, C, ldc, M, N, K, acc ? 1 : 0);
+  else
+    gemm_mfma_kernel<AT, BM, BN, BK, WGM, WGN, false><<<grid, 64 * WGM * WGN, 0, s>>>(
+        A, lda, W, ldw, C, ldc, M, N, K, acc ? 1 : 0);
   return hipGetLastError();
 }
 
@@ -254,10 +325,13 @@ static hipError_t gemm_at(const AT* A, int64_t lda, const bf16* W, int64_t ldw, 
                                                                      acc ? 1 : 0);
     return hipGetLastError();
   }
-  // Wide outputs take 128 x 128 tiles; narrow ones (x_proj's 80 columns) 64 x 32 so that the
-  // grid still covers the chip.
-  if (N >= 256) return gemm_tile<AT, 128, 128>(A, lda, W, ldw, C, ldc, M, N, K, acc, s);
-  return gemm_tile<AT, 64, 32>(A, lda, W, ldw, C, ldc, M, N, K, acc, s);
+  // 16-byte chunk loads need every row start and the K extent on 8-element boundaries
+  const bool vec = K % 8 == 0 && lda % 8 == 0 && ldw % 8 == 0 &&
+                   reinterpret_cast<uintptr_t>(A) % 16 == 0 && reinterpret_cast<uintptr_t>(W) % 16 == 0;
+  // Wide outputs: 128 x 128 tiles, 2 x 2 waves. Narrow ones (x_proj's 80 columns): 32 x 80
+  // tiles, one column tile, so that the grid still covers the chip.
+  if (N >= 128) return gemm_tile<AT, 128, 128, 64, 2, 2>(A, lda, W, ldw, C, ldc, M, N, K, acc, vec, s);
+  return gemm_tile<AT, 32, 80, 64, 2, 1>(A, lda, W, ldw, C, ldc, M, N, K, acc, vec, s);
 }
 
 hipError_t launch_gemm_bf16(const void* A, bool a_bf16, int64_t lda, const void* W, int64_t ldw,
