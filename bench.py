@@ -71,6 +71,12 @@ def ssm_step_bytes(s, L, B, D, N):
     return L * (4 * s * B * D + 2 * s * B * N + 8 * B * D * N + 4 * D * N + 8 * D)
 
 
+def decode_step_bytes(s, L, B, D, N, K):
+    """The fused step: x, dt, z in and y out; B and C rows; both states read and written;
+    conv taps and bias, A_log, D and dt_bias read (u stays on chip)."""
+    return L * (4 * s * B * D + 2 * s * B * N + 8 * B * D * (N + K) + 4 * D * (K + 1) + 4 * D * N + 8 * D)
+
+
 # ------------------------------------------------------------------ traffic from counters
 
 def measured_traffic(kernel_file: str, workload: str):
@@ -192,7 +198,7 @@ def bench_prefill(args, shape):
                       algorithmic_bytes=dom["bytes"], avg_ms=dom["avg_ms"]),
         calls={k: dict(avg_us=v["avg_ms"] * 1e3, min_us=v["min_ms"] * 1e3,
                        gbs=v["bytes"] / (v["avg_ms"] * 1e-3) / 1e9) for k, v in calls.items()},
-        layer_gbs=(cb + sb) / (ms_step * 1e-3) / 1e9,
+        layer_gbs=sb / (ms_step * 1e-3) / 1e9,
     )
     result["layer_hbm_frac"] = result["layer_gbs"] / HBM_PEAK_GBS
     return result, inp
@@ -259,7 +265,6 @@ def bench_decode(args, shape):
         steps_in.append({k: torch.from_numpy(v).to(dev) for k, v in i.items()})
     cs = torch.zeros(L, B, D, K, device=dev)
     hs = torch.zeros(L, B, D, N, device=dev)
-    u = torch.empty(L, B, D, device=dev)
     y = torch.empty(L, B, D, device=dev)
     stream = torch.cuda.current_stream()
 
@@ -267,18 +272,15 @@ def bench_decode(args, shape):
         si = steps_in[i % ring]
         if ev:
             ev[0].record(stream)
-        m.mamba_conv1d_step(si["x"], p["conv_w"], p["conv_b"], cs, u, stream=stream)
+        m.mamba_decode_step(si["x"], p["conv_w"], p["conv_b"], cs, si["dt"], p["dt_bias"], p["A_log"],
+                            si["Bm"], si["Cm"], p["D_skip"], si["z"], hs, y, stream=stream)
         if ev:
             ev[1].record(stream)
-        m.mamba_ssm_step(u, si["dt"], p["dt_bias"], p["A_log"], si["Bm"], si["Cm"], p["D_skip"],
-                         si["z"], hs, y, stream=stream)
-        if ev:
-            ev[2].record(stream)
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
+    evs = [_events(torch) for _ in range(args.steps)]
     t_start, t_end = _events(torch)
     t_start.record(stream)
     for i in range(args.steps):
@@ -286,18 +288,14 @@ def bench_decode(args, shape):
     t_end.record(stream)
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
-    conv_ms = [e[0].elapsed_time(e[1]) for e in evs]
-    ssm_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    step_ms = [e[0].elapsed_time(e[1]) for e in evs]
     ms_step = total_ms / args.steps
-    cb = conv_step_bytes(4, L, B, D, K)
-    sb = ssm_step_bytes(4, L, B, D, N)
+    sb = decode_step_bytes(4, L, B, D, N, K)
     calls = {
-        "mamba_conv1d_step": dict(avg_ms=sum(conv_ms) / len(conv_ms), min_ms=min(conv_ms), bytes=cb,
-                                  kernel_file="conv1d.hip"),
-        "mamba_ssm_step": dict(avg_ms=sum(ssm_ms) / len(ssm_ms), min_ms=min(ssm_ms), bytes=sb,
-                               kernel_file="step.hip"),
+        "mamba_decode_step": dict(avg_ms=sum(step_ms) / len(step_ms), min_ms=min(step_ms), bytes=sb,
+                                  kernel_file="step.hip"),
     }
-    dom_name = max(calls, key=lambda k: calls[k]["avg_ms"])
+    dom_name = "mamba_decode_step"
     dom = calls[dom_name]
     achieved = dom["bytes"] / (dom["avg_ms"] * 1e-3) / 1e9
     result = dict(
@@ -306,16 +304,16 @@ def bench_decode(args, shape):
         unit="tokens/s/layer",
         ms_per_step=ms_step,
         dtype="f32",
-        config=dict(workload=f"{shape.name}: batched T=1 decode step, {L} independent layers in one "
-                             f"launch per call, B={B} d_inner={D} d_state={N} d_conv={K} f32",
-                    L=L, B=B, d_inner=D, d_state=N, d_conv=K, io_dtype="f32", step_bytes=cb + sb),
+        config=dict(workload=f"{shape.name}: batched T=1 decode step (fused conv + SSM step), {L} "
+                             f"independent layers in one launch, B={B} d_inner={D} d_state={N} d_conv={K} f32",
+                    L=L, B=B, d_inner=D, d_state=N, d_conv=K, io_dtype="f32", step_bytes=sb),
         roofline=dict(bound="hbm", achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s",
                       frac=achieved / HBM_PEAK_GBS,
                       traffic=measured_traffic(dom["kernel_file"], shape.name), call=dom_name,
                       algorithmic_bytes=dom["bytes"], avg_ms=dom["avg_ms"]),
         calls={k: dict(avg_us=v["avg_ms"] * 1e3, min_us=v["min_ms"] * 1e3,
                        gbs=v["bytes"] / (v["avg_ms"] * 1e-3) / 1e9) for k, v in calls.items()},
-        layer_gbs=(cb + sb) / (ms_step * 1e-3) / 1e9,
+        layer_gbs=sb / (ms_step * 1e-3) / 1e9,
     )
     result["layer_hbm_frac"] = result["layer_gbs"] / HBM_PEAK_GBS
     return result, None

@@ -140,6 +140,7 @@ mamba_status mamba_selective_scan_fwd(const void* u, const void* dt, const float
  *   conv_w       in   [L,D,K] f32.     conv_b  in  [L,D] f32, or NULL for zero.
  *   conv_state   in/out [L,B,D,K] f32, updated in place.
  *   u            out  [L,B,D] io_dtype, contiguous.
+ * L*B above 65535 is MAMBA_EUNSUPPORTED.
  */
 mamba_status mamba_conv1d_step(const void* x, int64_t x_row_stride, const float* conv_w,
                                const float* conv_b, float* conv_state, void* u,
@@ -159,12 +160,35 @@ mamba_status mamba_conv1d_step(const void* x, int64_t x_row_stride, const float*
  *   z            in   io_dtype, element (l,b,d) at z[(l*B+b)*z_row_stride + d], or NULL.
  *   ssm_state    in/out [L,B,D,N] f32, updated in place.
  *   y            out  [L,B,D] io_dtype, contiguous.
+ * L*B above 65535 is MAMBA_EUNSUPPORTED.
  */
 mamba_status mamba_ssm_step(const void* u, const void* dt, const float* dt_bias,
                             int delta_softplus, const float* A_log, const void* Bm,
                             const void* Cm, int64_t bc_row_stride, const float* D_skip,
                             const void* z, int64_t z_row_stride, float* ssm_state, void* y,
                             mamba_dtype io_dtype, int L, int B, int D, int N, void* stream);
+
+/*
+ * One decode step of the whole SSM core -- conv, SiLU, softplus, state update, readout, D
+ * skip and gate -- for L independent layers in one launch: mamba_conv1d_step followed by
+ * mamba_ssm_step, fused so that u does not go through memory. [inference.rs] step chain
+ * F4/F4b then F7-F10 (the pages fuse each half; this call fuses the two halves).
+ *
+ *   x, x_row_stride, conv_w, conv_b, conv_state   as mamba_conv1d_step (conv_state in place).
+ *   dt, dt_bias, delta_softplus, A_log, Bm, Cm, bc_row_stride, D_skip, z, z_row_stride,
+ *   ssm_state                                      as mamba_ssm_step (ssm_state in place).
+ *   u            out  [L,B,D] io_dtype, or NULL to skip writing it. In bf16 the SSM half
+ *                     uses u rounded to bf16, exactly as the two separate calls do.
+ *   y            out  [L,B,D] io_dtype, contiguous.
+ * Errors as the two separate calls; y, u and the states must not overlap any input.
+ */
+mamba_status mamba_decode_step(const void* x, int64_t x_row_stride, const float* conv_w,
+                               const float* conv_b, float* conv_state, const void* dt,
+                               const float* dt_bias, int delta_softplus, const float* A_log,
+                               const void* Bm, const void* Cm, int64_t bc_row_stride,
+                               const float* D_skip, const void* z, int64_t z_row_stride,
+                               float* ssm_state, void* u, void* y, mamba_dtype io_dtype, int L,
+                               int B, int D, int K, int N, void* stream);
 
 /* ======================================================================================
  * Full-backbone prefill (24-layer Mamba-1 stack) and the layer pieces around the SSM core.

@@ -36,6 +36,8 @@ symbols = {
     "mamba_conv1d_step": ([_P, _I64, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P], _I),
     "mamba_ssm_step": ([_P, _P, _P, _I, _P, _P, _P, _I64, _P, _P, _I64, _P, _P, _I, _I, _I,
                         _I, _I, _P], _I),
+    "mamba_decode_step": ([_P, _I64, _P, _P, _P, _P, _P, _I, _P, _P, _P, _I64, _P, _P, _I64, _P, _P,
+                           _P, _I, _I, _I, _I, _I, _I, _P], _I),
     "mamba_embed_gather": ([_P, _P, _P, _I64, _I, _I, _P], _I),
     "mamba_rmsnorm": ([_P, _I64, _P, ctypes.c_float, _P, _I, _I64, _I, _P], _I),
     "mamba_gemm_bf16": ([_P, _I, _I64, _P, _I64, _P, _I64, _I, _I, _I, _I, _P], _I),
@@ -216,6 +218,24 @@ def mamba_ssm_step(u, dt, dt_bias, A_log, Bm, Cm, D_skip, z, ssm_state, y,
         _ptr(u), _ptr(dt), _ptr(dt_bias), int(bool(delta_softplus)), _ptr(A_log), _ptr(Bm),
         _ptr(Cm), bcs, _ptr(D_skip), _ptr(z), zs, _ptr(ssm_state), _ptr(y), _io_dtype(u), L, Bsz,
         D, N, _stream(stream)))
+
+
+def mamba_decode_step(x, conv_w, conv_b, conv_state, dt, dt_bias, A_log, Bm, Cm, D_skip, z,
+                      ssm_state, y, u=None, delta_softplus=True, stream=None) -> None:
+    """Fused conv step + SSM step for L layers. x, dt, z: [L, B, D] (x and z may be row-strided
+    lanes); Bm, Cm: [L, B, >=N] rows; conv_state [L, B, D, K]; ssm_state [L, B, D, N]."""
+    L, Bsz, D = y.shape
+    K = conv_state.shape[-1]
+    N = ssm_state.shape[-1]
+    xs = _row_stride(x, "x")
+    bcs = _row_stride(Bm, "Bm")
+    if _row_stride(Cm, "Cm") != bcs:
+        raise ValueError("Bm and Cm must share a row stride")
+    zs = _row_stride(z, "z") if z is not None else 0
+    _check(load_library().mamba_decode_step(
+        _ptr(x), xs, _ptr(conv_w), _ptr(conv_b), _ptr(conv_state), _ptr(dt), _ptr(dt_bias),
+        int(bool(delta_softplus)), _ptr(A_log), _ptr(Bm), _ptr(Cm), bcs, _ptr(D_skip), _ptr(z), zs,
+        _ptr(ssm_state), _ptr(u), _ptr(y), _io_dtype(y), L, Bsz, D, K, N, _stream(stream)))
 
 
 # ------------------------------------------------------------------ backbone pieces

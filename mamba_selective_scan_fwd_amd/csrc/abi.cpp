@@ -261,6 +261,7 @@ mamba_status mamba_ssm_step(const void* u, const void* dt, const float* dt_bias,
     check_dim(fn, "B", B);
     check_dim(fn, "D", D);
     check_state_dim(fn, "N", N, kMaxN);
+    if ((int64_t)L * B > kMaxGridYZ) fail(MAMBA_EUNSUPPORTED, fn, "L*B = %lld exceeds %d", (long long)L * B, kMaxGridYZ);
     if ((int64_t)L * B == 0 || D == 0) return;
     const size_t es = elem_size(io_dtype);
     if (bc_row_stride < N) fail(MAMBA_EINVAL, fn, "bc_row_stride = %lld is less than N = %d", (long long)bc_row_stride, N);
@@ -291,6 +292,67 @@ mamba_status mamba_ssm_step(const void* u, const void* dt, const float* dt_bias,
                          D_skip, z, z_row_stride, ssm_state, y, io_dtype == MAMBA_BF16, L, B, D,
                          N};
     check_hip(fn, mamba::launch_ssm_step(a, static_cast<hipStream_t>(stream)));
+  });
+}
+
+mamba_status mamba_decode_step(const void* x, int64_t x_row_stride, const float* conv_w,
+                               const float* conv_b, float* conv_state, const void* dt,
+                               const float* dt_bias, int delta_softplus, const float* A_log,
+                               const void* Bm, const void* Cm, int64_t bc_row_stride,
+                               const float* D_skip, const void* z, int64_t z_row_stride,
+                               float* ssm_state, void* u, void* y, mamba_dtype io_dtype, int L,
+                               int B, int D, int K, int N, void* stream) {
+  static const char* fn = "mamba_decode_step";
+  return guarded([&] {
+    check_dtype(fn, io_dtype);
+    check_dim(fn, "L", L);
+    check_dim(fn, "B", B);
+    check_dim(fn, "D", D);
+    check_state_dim(fn, "K", K, kMaxK);
+    check_state_dim(fn, "N", N, kMaxN);
+    if ((int64_t)L * B > kMaxGridYZ) fail(MAMBA_EUNSUPPORTED, fn, "L*B = %lld exceeds %d", (long long)L * B, kMaxGridYZ);
+    if ((int64_t)L * B == 0 || D == 0) return;
+    const size_t es = elem_size(io_dtype);
+    if (x_row_stride < D) fail(MAMBA_EINVAL, fn, "x_row_stride = %lld is less than D = %d", (long long)x_row_stride, D);
+    if (bc_row_stride < N) fail(MAMBA_EINVAL, fn, "bc_row_stride = %lld is less than N = %d", (long long)bc_row_stride, N);
+    if (z && z_row_stride < D) fail(MAMBA_EINVAL, fn, "z_row_stride = %lld is less than D = %d", (long long)z_row_stride, D);
+    check_ptr(fn, "x", x, es, true);
+    check_ptr(fn, "conv_w", conv_w, 4, true);
+    check_ptr(fn, "conv_b", conv_b, 4, false);
+    check_ptr(fn, "conv_state", conv_state, 4, true);
+    check_ptr(fn, "dt", dt, es, true);
+    check_ptr(fn, "dt_bias", dt_bias, 4, false);
+    check_ptr(fn, "A_log", A_log, 4, true);
+    check_ptr(fn, "Bm", Bm, es, true);
+    check_ptr(fn, "Cm", Cm, es, true);
+    check_ptr(fn, "D_skip", D_skip, 4, false);
+    check_ptr(fn, "z", z, es, false);
+    check_ptr(fn, "ssm_state", ssm_state, 4, true);
+    check_ptr(fn, "u", u, es, false);
+    check_ptr(fn, "y", y, es, true);
+    const int64_t rows = (int64_t)L * B;
+    const Range rx = range("x", x, rows, x_row_stride, D, es);
+    const Range rw = range("conv_w", conv_w, (int64_t)L * D, K, K, 4);
+    const Range rb = range("conv_b", conv_b, L, D, D, 4);
+    const Range rcs = range("conv_state", conv_state, rows * D, K, K, 4);
+    const Range rdt = range("dt", dt, rows, D, D, es);
+    const Range rdb = range("dt_bias", dt_bias, L, D, D, 4);
+    const Range ra = range("A_log", A_log, (int64_t)L * D, N, N, 4);
+    const Range rB = range("Bm", Bm, rows, bc_row_stride, N, es);
+    const Range rC = range("Cm", Cm, rows, bc_row_stride, N, es);
+    const Range rD = range("D_skip", D_skip, L, D, D, 4);
+    const Range rz = range("z", z, rows, z_row_stride, D, es);
+    const Range rss = range("ssm_state", ssm_state, rows * D, N, N, 4);
+    const Range ru = range("u", u, rows, D, D, es);
+    const Range ry = range("y", y, rows, D, D, es);
+    check_disjoint(fn, ry, {rx, rw, rb, rcs, rdt, rdb, ra, rB, rC, rD, rz, rss, ru});
+    check_disjoint(fn, ru, {rx, rw, rb, rcs, rdt, rdb, ra, rB, rC, rD, rz, rss});
+    check_disjoint(fn, rss, {rx, rw, rb, rcs, rdt, rdb, ra, rB, rC, rD, rz});
+    check_disjoint(fn, rcs, {rx, rw, rb, rdt, rdb, ra, rB, rC, rD, rz});
+    mamba::DecodeStepArgs a{x, x_row_stride, conv_w, conv_b, conv_state, dt, dt_bias,
+                            delta_softplus != 0, A_log, Bm, Cm, bc_row_stride, D_skip, z,
+                            z_row_stride, ssm_state, u, y, io_dtype == MAMBA_BF16, L, B, D, K, N};
+    check_hip(fn, mamba::launch_decode_step(a, static_cast<hipStream_t>(stream)));
   });
 }
 

@@ -87,6 +87,33 @@ struct ScanPlan {
 
 ScanPlan plan_selective_scan(int B, int T, int D, int N);
 
+// Largest conv width the kernels take.
+constexpr int kMaxConvK = 8;
+
+struct DecodeStepArgs {
+  const void* x;
+  int64_t x_row_stride;
+  const float* conv_w;
+  const float* conv_b;
+  float* conv_state;
+  const void* dt;
+  const float* dt_bias;
+  bool delta_softplus;
+  const float* A_log;
+  const void* Bm;
+  const void* Cm;
+  int64_t bc_row_stride;
+  const float* D_skip;
+  const void* z;
+  int64_t z_row_stride;
+  float* ssm_state;
+  void* u;  // optional
+  void* y;
+  bool bf16;
+  int L, B, D, K, N;
+};
+hipError_t launch_decode_step(const DecodeStepArgs& a, hipStream_t s);
+
 hipError_t launch_embed_gather(const int32_t* tokens, const void* E, float* out, int64_t rows,
                                int vocab, int Dm, hipStream_t s);
 hipError_t launch_rmsnorm(const float* x, int64_t x_row_stride, const float* w, float eps,

@@ -15,34 +15,52 @@
 
 namespace mamba {
 
+// Four consecutive B (or C) values of row `row` starting at n0, as f32; VEC loads them as one
+// 16-byte (f32) or 8-byte (bf16) access.
+template <typename IO, bool VEC>
+__device__ __forceinline__ void load4(const IO* row, int n0, int N, float (&v)[4]) {
+  if constexpr (VEC) {
+    if constexpr (sizeof(IO) == 4) {
+      const float4 t = *reinterpret_cast<const float4*>(row + n0);
+      v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
+    } else {
+      const uint2 t = *reinterpret_cast<const uint2*>(row + n0);
+      v[0] = __uint_as_float(t.x << 16); v[1] = __uint_as_float(t.x & 0xffff0000u);
+      v[2] = __uint_as_float(t.y << 16); v[3] = __uint_as_float(t.y & 0xffff0000u);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = n0 + j < N ? to_f32(row[n0 + j]) : 0.0f;
+  }
+}
+
+// Grid: x over (channel, lane) pairs of one (layer, batch) row, y = l * B + b.
 template <typename IO, int NQ, bool VEC>
 __global__ void __launch_bounds__(256) ssm_step_kernel(
     const IO* __restrict__ u, const IO* __restrict__ dt, const float* __restrict__ dt_bias,
     int delta_softplus, const float* __restrict__ A_log, const IO* __restrict__ Bm,
     const IO* __restrict__ Cm, int64_t bc_row_stride, const float* __restrict__ D_skip,
     const IO* __restrict__ z, int64_t z_row_stride, float* __restrict__ state,
-    IO* __restrict__ y, int L, int B, int D, int N) {
-  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t ch = gid / NQ;  // ((l * B + b) * D + d)
-  const int q = (int)(gid % NQ);
-  const int64_t nch = (int64_t)L * B * D;
-  if (ch >= nch) return;  // whole NQ-lane groups drop out together
-  const int d = (int)(ch % D);
-  const int64_t lb = ch / D;
-  const int l = (int)(lb / B);
+    IO* __restrict__ y, int B, int D, int N) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  const int d = t / NQ;
+  const int q = t % NQ;
+  if (d >= D) return;  // whole NQ-lane groups drop out together
+  const int lb = blockIdx.y;  // l * B + b
+  const int l = lb / B;
+  const int64_t ch = (int64_t)lb * D + d;
+  const int64_t ld = (int64_t)l * D + d;
 
   const float uv = to_f32(u[ch]);
-  const float v = to_f32(dt[ch]) + (dt_bias ? dt_bias[(int64_t)l * D + d] : 0.0f);
+  const float v = to_f32(dt[ch]) + (dt_bias ? dt_bias[ld] : 0.0f);
   const float delta = delta_softplus ? softplus(v) : v;
   const float du = delta * uv;
 
   float* hs = state + ch * N;
-  const float* al = A_log + ((int64_t)l * D + d) * N;
-  const IO* brow = Bm + lb * bc_row_stride;
-  const IO* crow = Cm + lb * bc_row_stride;
+  const float* al = A_log + ld * N;
   const int n0 = 4 * q;
 
-  float h[4], alog[4];
+  float h[4], alog[4], bv[4], cv[4];
   if constexpr (VEC) {
     const float4 hv = *reinterpret_cast<const float4*>(hs + n0);
     const float4 av = *reinterpret_cast<const float4*>(al + n0);
@@ -55,15 +73,16 @@ __global__ void __launch_bounds__(256) ssm_step_kernel(
       alog[j] = n0 + j < N ? al[n0 + j] : 0.0f;
     }
   }
+  load4<IO, VEC>(Bm + (int64_t)lb * bc_row_stride, n0, N, bv);
+  load4<IO, VEC>(Cm + (int64_t)lb * bc_row_stride, n0, N, cv);
   float part = 0.0f;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int n = n0 + j;
-    if (VEC || n < N) {
-      const float a = __builtin_amdgcn_exp2f(delta * (-expf(alog[j]) * kLog2e));
-      h[j] = fmaf(a, h[j], du * to_f32(brow[n]));
-      part = fmaf(to_f32(crow[n]), h[j], part);
-    }
+    // A * log2(e), A = -exp(A_log); padded states (VEC false, n >= N) have B = C = 0
+    const float a2 = -__builtin_amdgcn_exp2f(alog[j] * kLog2e) * kLog2e;
+    const float a = __builtin_amdgcn_exp2f(delta * a2);
+    h[j] = fmaf(a, h[j], du * bv[j]);
+    part = fmaf(cv[j], h[j], part);
   }
   if constexpr (VEC) {
     *reinterpret_cast<float4*>(hs + n0) = make_float4(h[0], h[1], h[2], h[3]);
@@ -75,32 +94,163 @@ __global__ void __launch_bounds__(256) ssm_step_kernel(
 #pragma unroll
   for (int m = NQ / 2; m >= 1; m /= 2) part += __shfl_xor(part, m, NQ);
   if (q == 0) {
-    float yv = fmaf(D_skip ? D_skip[(int64_t)l * D + d] : 0.0f, uv, part);
-    if (z) yv *= silu(to_f32(z[lb * z_row_stride + d]));
+    float yv = fmaf(D_skip ? D_skip[ld] : 0.0f, uv, part);
+    if (z) yv *= silu(to_f32(z[(int64_t)lb * z_row_stride + d]));
     y[ch] = from_f32<IO>(yv);
   }
 }
 
 template <typename IO, int NQ>
 static hipError_t launch_step_nq(const SsmStepArgs& a, hipStream_t s) {
-  const int64_t threads = (int64_t)a.L * a.B * a.D * NQ;
-  const unsigned blocks = (unsigned)((threads + 255) / 256);
-  const bool vec = a.N % 4 == 0 && ((reinterpret_cast<uintptr_t>(a.state) |
-                                     reinterpret_cast<uintptr_t>(a.A_log)) & 15) == 0;
+  const dim3 grid((unsigned)(((int64_t)a.D * NQ + 255) / 256), (unsigned)(a.L * a.B));
+  const size_t es = sizeof(IO);
+  // 16-byte state / A_log rows and 4-element aligned B/C rows
+  const bool vec = a.N % 4 == 0 && a.bc_row_stride % 4 == 0 &&
+                   ((reinterpret_cast<uintptr_t>(a.state) | reinterpret_cast<uintptr_t>(a.A_log)) & 15) == 0 &&
+                   ((reinterpret_cast<uintptr_t>(a.Bm) | reinterpret_cast<uintptr_t>(a.Cm)) % (4 * es)) == 0;
   if (vec) {
-    ssm_step_kernel<IO, NQ, true><<<blocks, 256, 0, s>>>(
+    ssm_step_kernel<IO, NQ, true><<<grid, 256, 0, s>>>(
         static_cast<const IO*>(a.u), static_cast<const IO*>(a.dt), a.dt_bias, a.delta_softplus,
         a.A_log, static_cast<const IO*>(a.Bm), static_cast<const IO*>(a.Cm), a.bc_row_stride,
         a.D_skip, static_cast<const IO*>(a.z), a.z_row_stride, a.state, static_cast<IO*>(a.y),
-        a.L, a.B, a.D, a.N);
+        a.B, a.D, a.N);
   } else {
-    ssm_step_kernel<IO, NQ, false><<<blocks, 256, 0, s>>>(
+    ssm_step_kernel<IO, NQ, false><<<grid, 256, 0, s>>>(
         static_cast<const IO*>(a.u), static_cast<const IO*>(a.dt), a.dt_bias, a.delta_softplus,
         a.A_log, static_cast<const IO*>(a.Bm), static_cast<const IO*>(a.Cm), a.bc_row_stride,
         a.D_skip, static_cast<const IO*>(a.z), a.z_row_stride, a.state, static_cast<IO*>(a.y),
-        a.L, a.B, a.D, a.N);
+        a.B, a.D, a.N);
   }
   return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------- fused step
+//
+// One decode step of the whole SSM core, conv and SSM fused (the pages' step chain fuses
+// the conv with its SiLU and the SSM update with its gate; here the two are one kernel, so
+// u never goes through HBM). The NQ lanes of a channel each evaluate the K-tap conv (the
+// taps are one 16-byte read for K = 4, shared by the lanes through the cache); lane 0 writes
+// the shifted conv state and, when asked, u.
+template <typename IO, int NQ, bool VEC>
+__global__ void __launch_bounds__(256) decode_step_kernel(const DecodeStepArgs a) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  const int d = t / NQ;
+  const int q = t % NQ;
+  const int D = a.D, N = a.N, K = a.K;
+  if (d >= D) return;  // whole NQ-lane groups drop out together
+  const int lb = blockIdx.y;  // l * B + b
+  const int l = lb / a.B;
+  const int64_t ch = (int64_t)lb * D + d;
+  const int64_t ld = (int64_t)l * D + d;
+
+  // conv: shift register of the last K raw inputs, oldest first
+  float* cst = a.conv_state + ch * K;
+  const float* w = a.conv_w + ld * K;
+  float sreg[kMaxConvK];
+  const float xin = to_f32(static_cast<const IO*>(a.x)[(int64_t)lb * a.x_row_stride + d]);
+  float c = a.conv_b ? a.conv_b[ld] : 0.0f;
+  if (VEC && K == 4) {
+    const float4 sv = *reinterpret_cast<const float4*>(cst);
+    const float4 wv = *reinterpret_cast<const float4*>(w);
+    sreg[0] = sv.y; sreg[1] = sv.z; sreg[2] = sv.w; sreg[3] = xin;
+    c = fmaf(wv.x, sreg[0], c);
+    c = fmaf(wv.y, sreg[1], c);
+    c = fmaf(wv.z, sreg[2], c);
+    c = fmaf(wv.w, sreg[3], c);
+    if (q == 0) *reinterpret_cast<float4*>(cst) = make_float4(sreg[0], sreg[1], sreg[2], sreg[3]);
+  } else {
+#pragma unroll
+    for (int k = 0; k < kMaxConvK; ++k) {
+      if (k + 1 < K) sreg[k] = cst[k + 1];
+      else if (k + 1 == K) sreg[k] = xin;
+    }
+#pragma unroll
+    for (int k = 0; k < kMaxConvK; ++k)
+      if (k < K) c = fmaf(w[k], sreg[k], c);
+    if (q == 0) {
+#pragma unroll
+      for (int k = 0; k < kMaxConvK; ++k)
+        if (k < K) cst[k] = sreg[k];
+    }
+  }
+  const float uv = silu(c);
+  if (q == 0 && a.u) static_cast<IO*>(a.u)[ch] = from_f32<IO>(uv);
+  // an IO-typed u feeds the SSM, as with the two separate calls
+  const float us = to_f32(from_f32<IO>(uv));
+
+  const float v = to_f32(static_cast<const IO*>(a.dt)[ch]) + (a.dt_bias ? a.dt_bias[ld] : 0.0f);
+  const float delta = a.delta_softplus ? softplus(v) : v;
+  const float du = delta * us;
+
+  float* hs = a.ssm_state + ch * N;
+  const float* al = a.A_log + ld * N;
+  const int n0 = 4 * q;
+  float h[4], alog[4], bv[4], cv[4];
+  if constexpr (VEC) {
+    const float4 hv = *reinterpret_cast<const float4*>(hs + n0);
+    const float4 av = *reinterpret_cast<const float4*>(al + n0);
+    h[0] = hv.x; h[1] = hv.y; h[2] = hv.z; h[3] = hv.w;
+    alog[0] = av.x; alog[1] = av.y; alog[2] = av.z; alog[3] = av.w;
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      h[j] = n0 + j < N ? hs[n0 + j] : 0.0f;
+      alog[j] = n0 + j < N ? al[n0 + j] : 0.0f;
+    }
+  }
+  load4<IO, VEC>(static_cast<const IO*>(a.Bm) + (int64_t)lb * a.bc_row_stride, n0, N, bv);
+  load4<IO, VEC>(static_cast<const IO*>(a.Cm) + (int64_t)lb * a.bc_row_stride, n0, N, cv);
+  float part = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float a2 = -__builtin_amdgcn_exp2f(alog[j] * kLog2e) * kLog2e;
+    const float ad = __builtin_amdgcn_exp2f(delta * a2);
+    h[j] = fmaf(ad, h[j], du * bv[j]);
+    part = fmaf(cv[j], h[j], part);
+  }
+  if constexpr (VEC) {
+    *reinterpret_cast<float4*>(hs + n0) = make_float4(h[0], h[1], h[2], h[3]);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (n0 + j < N) hs[n0 + j] = h[j];
+  }
+#pragma unroll
+  for (int m = NQ / 2; m >= 1; m /= 2) part += __shfl_xor(part, m, NQ);
+  if (q == 0) {
+    float yv = fmaf(a.D_skip ? a.D_skip[ld] : 0.0f, us, part);
+    if (a.z) yv *= silu(to_f32(static_cast<const IO*>(a.z)[(int64_t)lb * a.z_row_stride + d]));
+    static_cast<IO*>(a.y)[ch] = from_f32<IO>(yv);
+  }
+}
+
+template <typename IO, int NQ>
+static hipError_t launch_decode_nq(const DecodeStepArgs& a, hipStream_t s) {
+  const dim3 grid((unsigned)(((int64_t)a.D * NQ + 255) / 256), (unsigned)(a.L * a.B));
+  const size_t es = sizeof(IO);
+  const bool vec = a.N % 4 == 0 && a.bc_row_stride % 4 == 0 &&
+                   ((reinterpret_cast<uintptr_t>(a.ssm_state) | reinterpret_cast<uintptr_t>(a.A_log) |
+                     reinterpret_cast<uintptr_t>(a.conv_state) | reinterpret_cast<uintptr_t>(a.conv_w)) & 15) == 0 &&
+                   ((reinterpret_cast<uintptr_t>(a.Bm) | reinterpret_cast<uintptr_t>(a.Cm)) % (4 * es)) == 0;
+  if (vec)
+    decode_step_kernel<IO, NQ, true><<<grid, 256, 0, s>>>(a);
+  else
+    decode_step_kernel<IO, NQ, false><<<grid, 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+template <typename IO>
+static hipError_t launch_decode_io(const DecodeStepArgs& a, hipStream_t s) {
+  const int nq = (a.N + 3) / 4;
+  if (nq <= 1) return launch_decode_nq<IO, 1>(a, s);
+  if (nq <= 2) return launch_decode_nq<IO, 2>(a, s);
+  if (nq <= 4) return launch_decode_nq<IO, 4>(a, s);
+  if (nq <= 8) return launch_decode_nq<IO, 8>(a, s);
+  return launch_decode_nq<IO, 16>(a, s);
+}
+
+hipError_t launch_decode_step(const DecodeStepArgs& a, hipStream_t s) {
+  return a.bf16 ? launch_decode_io<bf16>(a, s) : launch_decode_io<float>(a, s);
 }
 
 template <typename IO>

@@ -120,6 +120,22 @@ def test_step_validation():
     st = lib.mamba_ssm_step(FAKE, FAKE + (1 << 28), None, 1, FAKE + (1 << 29), FAKE + (1 << 30), FAKE + (1 << 31),
                             16, None, None, 0, FAKE + (1 << 33), FAKE + (1 << 32), F32, 2, 3, 64, 0, None)
     assert st == EINVAL and "N = 0" in m.mamba_last_error()
+    st = lib.mamba_ssm_step(FAKE, FAKE + (1 << 28), None, 1, FAKE + (1 << 29), FAKE + (1 << 30), FAKE + (1 << 31),
+                            16, None, None, 0, FAKE + (1 << 33), FAKE + (1 << 32), F32, 300, 300, 64, 16, None)
+    assert st == EUNSUP and "L*B" in m.mamba_last_error()
+
+
+def test_decode_step_validation():
+    lib = m.load_library()
+    args = lambda cs, L, B: (FAKE, 64, FAKE + (1 << 28), None, cs, FAKE + (1 << 29), None, 1, FAKE + (1 << 30),
+                             FAKE + (1 << 31), FAKE + (1 << 32), 16, None, None, 0, FAKE + (1 << 33), None,
+                             FAKE + (1 << 34), F32, L, B, 64, 4, 16, None)
+    st = lib.mamba_decode_step(*args(None, 2, 3))
+    assert st == EINVAL and "conv_state is NULL" in m.mamba_last_error()
+    st = lib.mamba_decode_step(*args(FAKE + (1 << 35), 300, 300))
+    assert st == EUNSUP and "L*B" in m.mamba_last_error()
+    st = lib.mamba_decode_step(*args(FAKE + (1 << 33), 2, 3))
+    assert st == EINVAL and "overlaps" in m.mamba_last_error()
 
 
 def test_errors_are_thread_local():

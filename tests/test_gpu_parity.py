@@ -225,8 +225,9 @@ def test_channel_isolation_of_nonfinite_input():
 
 # ------------------------------------------------------------------ decode steps
 
-def _decode_run(shape: W.DecodeShape, steps: int, seed=0, layers=None):
-    """Run `steps` decode steps of all layers on the GPU (host-generated inputs)."""
+def _decode_run(shape: W.DecodeShape, steps: int, seed=0, fused=False):
+    """Run `steps` decode steps of all layers on the GPU (host-generated inputs), through the
+    two calls or through the fused mamba_decode_step."""
     L, Bsz, D, N, K = shape.L, shape.B, shape.D, shape.N, shape.K
     P = W.decode_params(shape, seed=seed)
     p = {k: dev(v) for k, v in P.items()}
@@ -238,19 +239,24 @@ def _decode_run(shape: W.DecodeShape, steps: int, seed=0, layers=None):
         ins.append(i)
         u = torch.empty(L, Bsz, D, device="cuda")
         y = torch.empty(L, Bsz, D, device="cuda")
-        m.mamba_conv1d_step(dev(i["x"]), p["conv_w"], p["conv_b"], cs, u)
-        m.mamba_ssm_step(u, dev(i["dt"]), p["dt_bias"], p["A_log"], dev(i["Bm"]), dev(i["Cm"]),
-                         p["D_skip"], dev(i["z"]), hs, y)
+        if fused:
+            m.mamba_decode_step(dev(i["x"]), p["conv_w"], p["conv_b"], cs, dev(i["dt"]), p["dt_bias"],
+                                p["A_log"], dev(i["Bm"]), dev(i["Cm"]), p["D_skip"], dev(i["z"]), hs, y, u=u)
+        else:
+            m.mamba_conv1d_step(dev(i["x"]), p["conv_w"], p["conv_b"], cs, u)
+            m.mamba_ssm_step(u, dev(i["dt"]), p["dt_bias"], p["A_log"], dev(i["Bm"]), dev(i["Cm"]),
+                             p["D_skip"], dev(i["z"]), hs, y)
         ys.append(host(y))
         us.append(host(u))
     torch.cuda.synchronize()
     return P, ins, ys, us, host(cs), host(hs)
 
 
-def test_decode_steps_small_full_check():
-    _say("case decode L2 B3 D100 N16 30 steps")
+@pytest.mark.parametrize("fused", [False, True])
+def test_decode_steps_small_full_check(fused):
+    _say(f"case decode L2 B3 D100 N16 30 steps fused={fused}")
     shape = W.DecodeShape("d", L=2, B=3, D=100, N=16, K=4, steps=30)
-    P, ins, ys, us, cs, hs = _decode_run(shape, 30)
+    P, ins, ys, us, cs, hs = _decode_run(shape, 30, fused=fused)
     for l in range(2):
         c_ref = np.zeros((3, 100, 4))
         h_ref = np.zeros((3, 100, 16))
@@ -263,6 +269,45 @@ def test_decode_steps_small_full_check():
             assert rel_err(ys[t][l], y_ref) <= 1e-4, (l, t)
         assert rel_err(cs[l], c_ref) <= 1e-4
         assert rel_err(hs[l], h_ref) <= 1e-4
+
+
+@pytest.mark.parametrize("io,N,K,strided", [("f32", 16, 4, False), ("bf16", 16, 4, True),
+                                             ("f32", 5, 3, True), ("bf16", 64, 8, False)])
+def test_fused_decode_equals_two_calls(io, N, K, strided):
+    """mamba_decode_step computes exactly what mamba_conv1d_step then mamba_ssm_step compute
+    (same operations in the same order; bf16 u rounded as the two calls store it), including
+    the element-wise paths (N = 5, K = 3) and x / z read as lanes of wider rows."""
+    _say(f"case fused decode == two calls io={io} N={N} K={K} strided={strided}")
+    L, Bsz, D = 3, 5, 96
+    shape = W.DecodeShape("f", L=L, B=Bsz, D=D, N=N, K=K, steps=4, io=io)
+    P = W.decode_params(shape, seed=4)
+    p = {k: dev(v) for k, v in P.items()}
+    iod = torch.bfloat16 if io == "bf16" else torch.float32
+    g = torch.Generator(device="cuda").manual_seed(5)
+    st = {n: torch.randn(L, Bsz, D, sz, device="cuda", generator=g) * 0.5 for n, sz in (("c", K), ("h", N))}
+    c1, h1 = st["c"].clone(), st["h"].clone()
+    c2, h2 = st["c"].clone(), st["h"].clone()
+    for t in range(4):
+        i = W.decode_step_inputs(shape, t, seed=4)
+        if strided:  # x and z as the two halves of one [L, B, 2D] buffer
+            xz = torch.cat([dev(i["x"], io), dev(i["z"], io)], dim=2)
+            x, z = xz[..., :D], xz[..., D:]
+        else:
+            x, z = dev(i["x"], io), dev(i["z"], io)
+        dt, Bm, Cm = dev(i["dt"], io), dev(i["Bm"], io), dev(i["Cm"], io)
+        u1 = torch.empty(L, Bsz, D, dtype=iod, device="cuda")
+        y1 = torch.empty_like(u1)
+        m.mamba_conv1d_step(x, p["conv_w"], p["conv_b"], c1, u1)
+        m.mamba_ssm_step(u1, dt, p["dt_bias"], p["A_log"], Bm, Cm, p["D_skip"], z, h1, y1)
+        u2 = torch.empty_like(u1)
+        y2 = torch.empty_like(u1)
+        m.mamba_decode_step(x, p["conv_w"], p["conv_b"], c2, dt, p["dt_bias"], p["A_log"], Bm, Cm,
+                            p["D_skip"], z, h2, y2, u=u2 if t % 2 == 0 else None)
+        torch.cuda.synchronize()
+        if t % 2 == 0:
+            assert torch.equal(u1, u2), t
+        assert torch.equal(y1, y2), t
+    assert torch.equal(c1, c2) and torch.equal(h1, h2)
 
 
 def test_decode_step_equals_one_token_prefill():
@@ -314,7 +359,8 @@ def test_decode_bf16_io():
 
 def test_c2_full_size_1000_steps_sampled():
     """The 24-layer, B=64, d_inner=1536 decode workload for 1000 steps in the launch
-    configuration bench.py times (both calls cover all 24 layers). Inputs are drawn per step
+    configuration bench.py times (the fused step, one launch for all 24 layers; u is written
+    too and checked at the sampled channels against the oracle's). Inputs are drawn per step
     on the device; for 40 sampled (layer, batch, channel) triples the inputs are copied out and
     the oracle replays all 1000 steps; y is checked at steps 0, 1, 9, 99, 499, 999 and both
     states at the end."""
@@ -335,17 +381,18 @@ def test_c2_full_size_1000_steps_sampled():
     di = torch.tensor([q[2] for q in picks], device="cuda")
     check_steps = {0, 1, 9, 99, 499, 999}
     rec = {k: [] for k in ("x", "z", "dt", "Bm", "Cm")}
-    ys = {}
+    ys, us_ = {}, {}
     for t in range(shape.steps):
         i = W.decode_step_inputs_torch(shape, t)
-        m.mamba_conv1d_step(i["x"], p["conv_w"], p["conv_b"], cs, u)
-        m.mamba_ssm_step(u, i["dt"], p["dt_bias"], p["A_log"], i["Bm"], i["Cm"], p["D_skip"], i["z"], hs, y)
+        m.mamba_decode_step(i["x"], p["conv_w"], p["conv_b"], cs, i["dt"], p["dt_bias"], p["A_log"],
+                            i["Bm"], i["Cm"], p["D_skip"], i["z"], hs, y, u=u)
         for k in ("x", "z", "dt"):
             rec[k].append(i[k][li, bi, di])
         rec["Bm"].append(i["Bm"][li, bi])
         rec["Cm"].append(i["Cm"][li, bi])
         if t in check_steps:
             ys[t] = y[li, bi, di].clone()
+            us_[t] = u[li, bi, di].clone()
         if t % 250 == 0:
             _say(f"  c2 step {t}")
     torch.cuda.synchronize()
@@ -353,7 +400,9 @@ def test_c2_full_size_1000_steps_sampled():
     cs_g = cs[li, bi, di].cpu().numpy()
     hs_g = hs[li, bi, di].cpu().numpy()
     ys = {t: v.cpu().numpy() for t, v in ys.items()}
+    us_ = {t: v.cpu().numpy() for t, v in us_.items()}
     yref = {t: np.zeros(len(picks)) for t in ys}
+    uref = {t: np.zeros(len(picks)) for t in ys}
     for q, (l, b, d) in enumerate(picks):
         sel = slice(d, d + 1)
         c_ref = np.zeros((1, 1, K))
@@ -367,8 +416,11 @@ def test_c2_full_size_1000_steps_sampled():
                                            P["dt_bias"][l, sel], h_ref)
             if t in ys:
                 yref[t][q] = y_ref[0, 0]
+                uref[t][q] = u_ref[0, 0]
         assert rel_err(cs_g[q], c_ref[0, 0]) <= 1e-6, (l, b, d)
         assert rel_err(hs_g[q], h_ref[0, 0]) <= 1e-4, (l, b, d)
     errs = {t: rel_err(ys[t], yref[t]) for t in sorted(ys)}
+    uerrs = {t: rel_err(us_[t], uref[t]) for t in sorted(us_)}
     _say("c2 sampled y errors by step", {t: f"{e:.2e}" for t, e in errs.items()})
     assert max(errs.values()) <= 1e-4
+    assert max(uerrs.values()) <= 1e-4
