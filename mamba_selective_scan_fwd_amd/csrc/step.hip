@@ -131,112 +131,148 @@ static hipError_t launch_step_nq(const SsmStepArgs& a, hipStream_t s) {
 // u never goes through HBM). The NQ lanes of a channel each evaluate the K-tap conv (the
 // taps are one 16-byte read for K = 4, shared by the lanes through the cache); lane 0 writes
 // the shifted conv state and, when asked, u.
-template <typename IO, int NQ, bool VEC>
+template <typename IO, int NQ, bool VEC, int R>
 __global__ void __launch_bounds__(256) decode_step_kernel(const DecodeStepArgs a) {
   const int t = blockIdx.x * 256 + threadIdx.x;
   const int d = t / NQ;
   const int q = t % NQ;
   const int D = a.D, N = a.N, K = a.K;
   if (d >= D) return;  // whole NQ-lane groups drop out together
-  const int lb = blockIdx.y;  // l * B + b
-  const int l = lb / a.B;
-  const int64_t ch = (int64_t)lb * D + d;
+  // R consecutive (layer, batch) rows of one layer (the launcher ensures B % R == 0): the
+  // layer's parameters are read and A is computed once for all R rows, and R rows of state
+  // traffic are in flight per thread.
+  const int lb0 = blockIdx.y * R;
+  const int l = lb0 / a.B;
   const int64_t ld = (int64_t)l * D + d;
+  const int n0 = 4 * q;
 
-  // conv: shift register of the last K raw inputs, oldest first
-  float* cst = a.conv_state + ch * K;
   const float* w = a.conv_w + ld * K;
-  float sreg[kMaxConvK];
-  const float xin = to_f32(static_cast<const IO*>(a.x)[(int64_t)lb * a.x_row_stride + d]);
-  float c = a.conv_b ? a.conv_b[ld] : 0.0f;
+  float wk[kMaxConvK];
   if (VEC && K == 4) {
-    const float4 sv = *reinterpret_cast<const float4*>(cst);
     const float4 wv = *reinterpret_cast<const float4*>(w);
-    sreg[0] = sv.y; sreg[1] = sv.z; sreg[2] = sv.w; sreg[3] = xin;
-    c = fmaf(wv.x, sreg[0], c);
-    c = fmaf(wv.y, sreg[1], c);
-    c = fmaf(wv.z, sreg[2], c);
-    c = fmaf(wv.w, sreg[3], c);
-    if (q == 0) *reinterpret_cast<float4*>(cst) = make_float4(sreg[0], sreg[1], sreg[2], sreg[3]);
+    wk[0] = wv.x; wk[1] = wv.y; wk[2] = wv.z; wk[3] = wv.w;
   } else {
 #pragma unroll
-    for (int k = 0; k < kMaxConvK; ++k) {
-      if (k + 1 < K) sreg[k] = cst[k + 1];
-      else if (k + 1 == K) sreg[k] = xin;
-    }
+    for (int k = 0; k < kMaxConvK; ++k) wk[k] = k < K ? w[k] : 0.0f;
+  }
+  const float cb = a.conv_b ? a.conv_b[ld] : 0.0f;
+  const float bias = a.dt_bias ? a.dt_bias[ld] : 0.0f;
+  const float dskip = a.D_skip ? a.D_skip[ld] : 0.0f;
+  float a2[4];
+  {
+    const float* al = a.A_log + ld * N;
+    float alog[4];
+    if constexpr (VEC) {
+      const float4 av = *reinterpret_cast<const float4*>(al + n0);
+      alog[0] = av.x; alog[1] = av.y; alog[2] = av.z; alog[3] = av.w;
+    } else {
 #pragma unroll
-    for (int k = 0; k < kMaxConvK; ++k)
-      if (k < K) c = fmaf(w[k], sreg[k], c);
-    if (q == 0) {
+      for (int j = 0; j < 4; ++j) alog[j] = n0 + j < N ? al[n0 + j] : 0.0f;
+    }
+    // A * log2(e), A = -exp(A_log); padded states (VEC false, n >= N) have B = C = 0
+#pragma unroll
+    for (int j = 0; j < 4; ++j) a2[j] = -__builtin_amdgcn_exp2f(alog[j] * kLog2e) * kLog2e;
+  }
+
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int lb = lb0 + r;
+    const int64_t ch = (int64_t)lb * D + d;
+
+    // conv: shift register of the last K raw inputs, oldest first
+    float* cst = a.conv_state + ch * K;
+    float sreg[kMaxConvK];
+    const float xin = to_f32(static_cast<const IO*>(a.x)[(int64_t)lb * a.x_row_stride + d]);
+    float c = cb;
+    if (VEC && K == 4) {
+      const float4 sv = *reinterpret_cast<const float4*>(cst);
+      sreg[0] = sv.y; sreg[1] = sv.z; sreg[2] = sv.w; sreg[3] = xin;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) c = fmaf(wk[k], sreg[k], c);
+      if (q == 0) *reinterpret_cast<float4*>(cst) = make_float4(sreg[0], sreg[1], sreg[2], sreg[3]);
+    } else {
+#pragma unroll
+      for (int k = 0; k < kMaxConvK; ++k) {
+        if (k + 1 < K) sreg[k] = cst[k + 1];
+        else if (k + 1 == K) sreg[k] = xin;
+      }
 #pragma unroll
       for (int k = 0; k < kMaxConvK; ++k)
-        if (k < K) cst[k] = sreg[k];
+        if (k < K) c = fmaf(wk[k], sreg[k], c);
+      if (q == 0) {
+#pragma unroll
+        for (int k = 0; k < kMaxConvK; ++k)
+          if (k < K) cst[k] = sreg[k];
+      }
     }
-  }
-  const float uv = silu(c);
-  if (q == 0 && a.u) static_cast<IO*>(a.u)[ch] = from_f32<IO>(uv);
-  // an IO-typed u feeds the SSM, as with the two separate calls
-  const float us = to_f32(from_f32<IO>(uv));
+    const float uv = silu(c);
+    if (q == 0 && a.u) static_cast<IO*>(a.u)[ch] = from_f32<IO>(uv);
+    // an IO-typed u feeds the SSM, as with the two separate calls
+    const float us = to_f32(from_f32<IO>(uv));
 
-  const float v = to_f32(static_cast<const IO*>(a.dt)[ch]) + (a.dt_bias ? a.dt_bias[ld] : 0.0f);
-  const float delta = a.delta_softplus ? softplus(v) : v;
-  const float du = delta * us;
+    const float v = to_f32(static_cast<const IO*>(a.dt)[ch]) + bias;
+    const float delta = a.delta_softplus ? softplus(v) : v;
+    const float du = delta * us;
 
-  float* hs = a.ssm_state + ch * N;
-  const float* al = a.A_log + ld * N;
-  const int n0 = 4 * q;
-  float h[4], alog[4], bv[4], cv[4];
-  if constexpr (VEC) {
-    const float4 hv = *reinterpret_cast<const float4*>(hs + n0);
-    const float4 av = *reinterpret_cast<const float4*>(al + n0);
-    h[0] = hv.x; h[1] = hv.y; h[2] = hv.z; h[3] = hv.w;
-    alog[0] = av.x; alog[1] = av.y; alog[2] = av.z; alog[3] = av.w;
-  } else {
+    float* hs = a.ssm_state + ch * N;
+    float h[4], bv[4], cv[4];
+    if constexpr (VEC) {
+      const float4 hv = *reinterpret_cast<const float4*>(hs + n0);
+      h[0] = hv.x; h[1] = hv.y; h[2] = hv.z; h[3] = hv.w;
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) h[j] = n0 + j < N ? hs[n0 + j] : 0.0f;
+    }
+    load4<IO, VEC>(static_cast<const IO*>(a.Bm) + (int64_t)lb * a.bc_row_stride, n0, N, bv);
+    load4<IO, VEC>(static_cast<const IO*>(a.Cm) + (int64_t)lb * a.bc_row_stride, n0, N, cv);
+    float part = 0.0f;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      h[j] = n0 + j < N ? hs[n0 + j] : 0.0f;
-      alog[j] = n0 + j < N ? al[n0 + j] : 0.0f;
+      const float ad = __builtin_amdgcn_exp2f(delta * a2[j]);
+      h[j] = fmaf(ad, h[j], du * bv[j]);
+      part = fmaf(cv[j], h[j], part);
+    }
+    if constexpr (VEC) {
+      *reinterpret_cast<float4*>(hs + n0) = make_float4(h[0], h[1], h[2], h[3]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (n0 + j < N) hs[n0 + j] = h[j];
+    }
+#pragma unroll
+    for (int m = NQ / 2; m >= 1; m /= 2) part += __shfl_xor(part, m, NQ);
+    if (q == 0) {
+      float yv = fmaf(dskip, us, part);
+      if (a.z) yv *= silu(to_f32(static_cast<const IO*>(a.z)[(int64_t)lb * a.z_row_stride + d]));
+      static_cast<IO*>(a.y)[ch] = from_f32<IO>(yv);
     }
   }
-  load4<IO, VEC>(static_cast<const IO*>(a.Bm) + (int64_t)lb * a.bc_row_stride, n0, N, bv);
-  load4<IO, VEC>(static_cast<const IO*>(a.Cm) + (int64_t)lb * a.bc_row_stride, n0, N, cv);
-  float part = 0.0f;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const float a2 = -__builtin_amdgcn_exp2f(alog[j] * kLog2e) * kLog2e;
-    const float ad = __builtin_amdgcn_exp2f(delta * a2);
-    h[j] = fmaf(ad, h[j], du * bv[j]);
-    part = fmaf(cv[j], h[j], part);
-  }
-  if constexpr (VEC) {
-    *reinterpret_cast<float4*>(hs + n0) = make_float4(h[0], h[1], h[2], h[3]);
-  } else {
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (n0 + j < N) hs[n0 + j] = h[j];
-  }
-#pragma unroll
-  for (int m = NQ / 2; m >= 1; m /= 2) part += __shfl_xor(part, m, NQ);
-  if (q == 0) {
-    float yv = fmaf(a.D_skip ? a.D_skip[ld] : 0.0f, us, part);
-    if (a.z) yv *= silu(to_f32(static_cast<const IO*>(a.z)[(int64_t)lb * a.z_row_stride + d]));
-    static_cast<IO*>(a.y)[ch] = from_f32<IO>(yv);
-  }
+}
+
+#ifndef MAMBA_DECODE_ROWS
+#define MAMBA_DECODE_ROWS 2  // (layer, batch) rows per thread when B allows
+#endif
+
+template <typename IO, int NQ, int R>
+static hipError_t launch_decode_nqr(const DecodeStepArgs& a, bool vec, hipStream_t s) {
+  const dim3 grid((unsigned)(((int64_t)a.D * NQ + 255) / 256), (unsigned)(a.L * a.B / R));
+  if (vec)
+    decode_step_kernel<IO, NQ, true, R><<<grid, 256, 0, s>>>(a);
+  else
+    decode_step_kernel<IO, NQ, false, R><<<grid, 256, 0, s>>>(a);
+  return hipGetLastError();
 }
 
 template <typename IO, int NQ>
 static hipError_t launch_decode_nq(const DecodeStepArgs& a, hipStream_t s) {
-  const dim3 grid((unsigned)(((int64_t)a.D * NQ + 255) / 256), (unsigned)(a.L * a.B));
   const size_t es = sizeof(IO);
   const bool vec = a.N % 4 == 0 && a.bc_row_stride % 4 == 0 &&
                    ((reinterpret_cast<uintptr_t>(a.ssm_state) | reinterpret_cast<uintptr_t>(a.A_log) |
                      reinterpret_cast<uintptr_t>(a.conv_state) | reinterpret_cast<uintptr_t>(a.conv_w)) & 15) == 0 &&
                    ((reinterpret_cast<uintptr_t>(a.Bm) | reinterpret_cast<uintptr_t>(a.Cm)) % (4 * es)) == 0;
-  if (vec)
-    decode_step_kernel<IO, NQ, true><<<grid, 256, 0, s>>>(a);
-  else
-    decode_step_kernel<IO, NQ, false><<<grid, 256, 0, s>>>(a);
-  return hipGetLastError();
+  if (MAMBA_DECODE_ROWS > 1 && a.B % MAMBA_DECODE_ROWS == 0)
+    return launch_decode_nqr<IO, NQ, MAMBA_DECODE_ROWS>(a, vec, s);
+  return launch_decode_nqr<IO, NQ, 1>(a, vec, s);
 }
 
 template <typename IO>
