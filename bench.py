@@ -2,9 +2,9 @@
 """Throughput of the Mamba-1 selective-scan hot path on one MI355X.
 
 A step is one pass of the prefill hot path over one batch of synthetic input already
-resident in HBM: mamba_conv1d_fwd (causal depthwise conv + SiLU) then
-mamba_selective_scan_fwd (softplus, discretisation, recurrence, readout, D skip, gate),
-both through the C-ABI, carrying the conv and SSM states from step to step.
+resident in HBM: mamba_conv_scan_fwd, the fused causal depthwise conv + SiLU, softplus,
+discretisation, recurrence, readout, D skip and gate, through the C-ABI, carrying the conv
+and SSM states from step to step.
 
 Default workload: the 130m-shaped prefill layer (B=1, T=2048, d_inner=1536, d_state=16,
 d_conv=4, f32 I/O). --config c3 runs the 2.8b-shaped layer (B=8, T=4096, d_inner=5120,
@@ -41,6 +41,10 @@ def parse_args(argv=None):
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--config", default="c1", choices=["c1", "c3", "c2", "c4"])
+    p.add_argument("--path", default="auto", choices=["auto", "fused", "split"],
+                   help="prefill: one fused mamba_conv_scan_fwd call, or mamba_conv1d_fwd then "
+                        "mamba_selective_scan_fwd; auto = fused for f32 I/O, split for bf16 (where "
+                        "the scan is arithmetic-bound and the conv is cheaper as its own pass)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="approximate CPU time budget for the oracle baseline")
@@ -55,6 +59,13 @@ def parse_args(argv=None):
 def conv_bytes(s, B, T, D, K):
     """x in, u out (s bytes each), conv state read + written, taps and bias read."""
     return 2 * s * B * T * D + 8 * B * D * K + 4 * D * (K + 1)
+
+
+def conv_scan_bytes(s, B, T, D, N, K):
+    """The fused layer call: x, dt, z in and y out (s bytes each); B and C rows in; both
+    states read and written; conv taps and bias, A_log, D and dt_bias read (u stays on chip)."""
+    return (4 * s * B * T * D + 2 * s * B * T * N + 8 * B * D * (N + K) + 4 * D * (K + 1)
+            + 4 * D * N + 8 * D)
 
 
 def scan_bytes(s, B, T, D, N):
@@ -131,27 +142,35 @@ def bench_prefill(args, shape):
     p = {k: up(inp[k], False) for k in ("conv_w", "conv_b", "dt_bias", "A_log", "D_skip")}
     conv_state = up(inp["conv_state"], False)
     ssm_state = up(inp["ssm_state"], False)
-    u = torch.empty(B, T, D, dtype=iod, device=dev)
     y = torch.empty(B, T, D, dtype=iod, device=dev)
     ws = m.scan_workspace(B, T, D, N)
     stream = torch.cuda.current_stream()
 
+    fused = args.path == "fused" or (args.path == "auto" and io == "f32")
+    u = None if fused else torch.empty(B, T, D, dtype=iod, device=dev)
+
     def step(ev=None):
         if ev:
             ev[0].record(stream)
-        m.mamba_conv1d_fwd(x, p["conv_w"], p["conv_b"], conv_state, u, stream=stream)
-        if ev:
-            ev[1].record(stream)
-        m.mamba_selective_scan_fwd(u, dt, p["dt_bias"], p["A_log"], Bm, Cm, p["D_skip"], z,
-                                   ssm_state, ssm_state, y, workspace=ws, stream=stream)
+        if fused:
+            m.mamba_conv_scan_fwd(x, p["conv_w"], p["conv_b"], conv_state, dt, p["dt_bias"], p["A_log"],
+                                  Bm, Cm, p["D_skip"], z, ssm_state, ssm_state, y, workspace=ws, stream=stream)
+            if ev:
+                ev[1].record(stream)
+        else:
+            m.mamba_conv1d_fwd(x, p["conv_w"], p["conv_b"], conv_state, u, stream=stream)
+            if ev:
+                ev[1].record(stream)
+            m.mamba_selective_scan_fwd(u, dt, p["dt_bias"], p["A_log"], Bm, Cm, p["D_skip"], z,
+                                       ssm_state, ssm_state, y, workspace=ws, stream=stream)
         if ev:
             ev[2].record(stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    print(f"[bench] warmup done ({args.warmup} steps); timing {args.steps} steps",
-          file=sys.stderr, flush=True)
+    print(f"[bench] warmup done ({args.warmup} steps); timing {args.steps} steps ("
+          f"{'fused' if fused else 'split'} path)", file=sys.stderr, flush=True)
 
     # per-call events over the timed region
     evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
@@ -163,22 +182,26 @@ def bench_prefill(args, shape):
     t_end.record(stream)
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
-    conv_ms = [e[0].elapsed_time(e[1]) for e in evs]
-    scan_ms = [e[1].elapsed_time(e[2]) for e in evs]
     assert torch.isfinite(y.float()).all(), "non-finite output"
 
     ms_step = total_ms / args.steps
     tokens = B * T
-    cb = conv_bytes(s, B, T, D, K)
-    sb = scan_bytes(s, B, T, D, N)
-    conv_avg = sum(conv_ms) / len(conv_ms)
-    scan_avg = sum(scan_ms) / len(scan_ms)
-    calls = {
-        "mamba_conv1d_fwd": dict(avg_ms=conv_avg, min_ms=min(conv_ms), bytes=cb,
-                                 kernel_file="conv1d.hip"),
-        "mamba_selective_scan_fwd": dict(avg_ms=scan_avg, min_ms=min(scan_ms), bytes=sb,
-                                         kernel_file="scan.hip"),
-    }
+    if fused:
+        lb = conv_scan_bytes(s, B, T, D, N, K)
+        call_ms = [e[0].elapsed_time(e[2]) for e in evs]
+        calls = {"mamba_conv_scan_fwd": dict(avg_ms=sum(call_ms) / len(call_ms), min_ms=min(call_ms),
+                                             bytes=lb, kernel_file="scan.hip")}
+    else:
+        cb, sb = conv_bytes(s, B, T, D, K), scan_bytes(s, B, T, D, N)
+        lb = cb + sb
+        conv_ms = [e[0].elapsed_time(e[1]) for e in evs]
+        scan_ms = [e[1].elapsed_time(e[2]) for e in evs]
+        calls = {
+            "mamba_conv1d_fwd": dict(avg_ms=sum(conv_ms) / len(conv_ms), min_ms=min(conv_ms), bytes=cb,
+                                     kernel_file="conv1d.hip"),
+            "mamba_selective_scan_fwd": dict(avg_ms=sum(scan_ms) / len(scan_ms), min_ms=min(scan_ms),
+                                             bytes=sb, kernel_file="scan.hip"),
+        }
     dom_name = max(calls, key=lambda k: calls[k]["avg_ms"])
     dom = calls[dom_name]
     achieved = dom["bytes"] / (dom["avg_ms"] * 1e-3) / 1e9
@@ -189,16 +212,18 @@ def bench_prefill(args, shape):
         unit="tokens/s/layer",
         ms_per_step=ms_step,
         dtype="bf16" if io == "bf16" else "f32",
-        config=dict(workload=f"{shape.name}: single Mamba-1 layer prefill (conv1d_fwd + selective_scan_fwd), "
-                             f"B={B} T={T} d_inner={D} d_state={N} d_conv={K} io={io}",
-                    B=B, T=T, d_inner=D, d_state=N, d_conv=K, io_dtype=io,
-                    layer_bytes=cb + sb),
+        config=dict(workload=f"{shape.name}: single Mamba-1 layer prefill (causal conv1d + SiLU + selective "
+                             f"scan; " + ("one fused mamba_conv_scan_fwd call" if fused else
+                                          "mamba_conv1d_fwd then mamba_selective_scan_fwd") +
+                             f"), B={B} T={T} d_inner={D} d_state={N} d_conv={K} io={io}",
+                    B=B, T=T, d_inner=D, d_state=N, d_conv=K, io_dtype=io, layer_bytes=lb,
+                    path="fused" if fused else "split"),
         roofline=dict(bound="hbm", achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s",
                       frac=achieved / HBM_PEAK_GBS, traffic=traffic, call=dom_name,
                       algorithmic_bytes=dom["bytes"], avg_ms=dom["avg_ms"]),
         calls={k: dict(avg_us=v["avg_ms"] * 1e3, min_us=v["min_ms"] * 1e3,
                        gbs=v["bytes"] / (v["avg_ms"] * 1e-3) / 1e9) for k, v in calls.items()},
-        layer_gbs=sb / (ms_step * 1e-3) / 1e9,
+        layer_gbs=lb / (ms_step * 1e-3) / 1e9,
     )
     result["layer_hbm_frac"] = result["layer_gbs"] / HBM_PEAK_GBS
     return result, inp

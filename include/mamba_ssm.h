@@ -83,9 +83,10 @@ mamba_status mamba_conv1d_fwd(const void* x, int64_t x_row_stride, const float* 
                               mamba_dtype io_dtype, int B, int T, int D, int K, void* stream);
 
 /*
- * Bytes of device workspace mamba_selective_scan_fwd needs for this shape (may be 0).
- * The workspace carries chunk summaries between the kernels of one call; its contents
- * on entry do not matter and are garbage on exit.
+ * Bytes of device workspace mamba_selective_scan_fwd (and mamba_conv_scan_fwd) needs for
+ * this shape (may be 0). The workspace carries chunk summaries and copies of the incoming
+ * states between the kernels of one call; its contents on entry do not matter and are
+ * garbage on exit.
  */
 size_t mamba_selective_scan_workspace_size(int B, int T, int D, int N);
 
@@ -126,6 +127,31 @@ mamba_status mamba_selective_scan_fwd(const void* u, const void* dt, const float
                                       const float* ssm_state_in, float* ssm_state_out, void* y,
                                       mamba_dtype io_dtype, int B, int T, int D, int N,
                                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The whole prefill of one layer's SSM core in one call: mamba_conv1d_fwd followed by
+ * mamba_selective_scan_fwd, fused so that u need not go through memory. [prefill.rs]
+ * prefill_body F4a (conv + SiLU from the carried conv state) then F4c/F4d (softplus, scan,
+ * gate); the pages fuse the conv with its SiLU and the scan with its gate, this call fuses
+ * the two.
+ *
+ *   x, x_row_stride, conv_w, conv_b, conv_state, K     as mamba_conv1d_fwd (conv_state in
+ *                     place; NULL means zeros and no state is written).
+ *   dt ... ssm_state_in, ssm_state_out, y, N, workspace as mamba_selective_scan_fwd; the
+ *                     workspace size is mamba_selective_scan_workspace_size(B, T, D, N).
+ *   u            out  [B,T,D] io_dtype, or NULL to skip writing it. The scan uses u rounded
+ *                     to io_dtype, so the result equals the two separate calls exactly.
+ * Errors as the two separate calls; u, y, the states and the workspace must not overlap any
+ * input. T = 0 leaves the conv state as it is and passes the SSM state through.
+ */
+mamba_status mamba_conv_scan_fwd(const void* x, int64_t x_row_stride, const float* conv_w,
+                                 const float* conv_b, float* conv_state, const void* dt,
+                                 const float* dt_bias, int delta_softplus, const float* A_log,
+                                 const void* Bm, const void* Cm, int64_t bc_row_stride,
+                                 const float* D_skip, const void* z, int64_t z_row_stride,
+                                 const float* ssm_state_in, float* ssm_state_out, void* u, void* y,
+                                 mamba_dtype io_dtype, int B, int T, int D, int K, int N,
+                                 void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * One decode step of the conv for L independent layers in one launch.

@@ -57,6 +57,14 @@ struct ScanFwdArgs {
   bool bf16;
   int B, T, D, N;
   void* workspace;
+  // fused conv (x != NULL): u is computed from x in the kernel and optionally written
+  const void* x = nullptr;
+  int64_t x_row_stride = 0;
+  const float* conv_w = nullptr;
+  const float* conv_b = nullptr;
+  float* conv_state = nullptr;
+  void* u_out = nullptr;
+  int K = 0;
 };
 
 struct SsmStepArgs {

@@ -36,7 +36,7 @@ constexpr int kLanes = 64;
 constexpr int kTB = 8;  // tokens per block (one LDS exchange and one barrier per block)
 
 #ifndef MAMBA_SCAN_CH
-#define MAMBA_SCAN_CH 64  // channels per workgroup (32 or 64)
+#define MAMBA_SCAN_CH 32  // channels per workgroup (32 or 64)
 #endif
 constexpr int kCh = MAMBA_SCAN_CH;
 constexpr int kWaves = kTB * kCh / kLanes;  // one per-token item per thread and block
@@ -56,9 +56,17 @@ struct ScanParams {
   float* sum_ws;           // [B][chunks][D]      sum of delta per chunk (chunks > 1)
   float* h_ws;             // [B][chunks][N][D]   chunk end state from h = 0 (chunks > 1)
   float* start_ws;         // [B][N][D]           copy of the carried state (chunks > 1)
+  // fused conv (u computed from x in the kernel)
+  const void* x;           // x[b,t,d] at (b*T+t)*x_row_stride + d
+  const float* conv_w;     // [D][K]
+  const float* conv_b;     // [D] or NULL
+  float* conv_state;       // [B][D][K] in/out, or NULL (zeros, not written)
+  float* conv_ws;          // [B][D][K] copy of the incoming conv state (chunks > 1)
+  void* u_out;             // [B][T][D] or NULL
+  int64_t x_row_stride;
   int64_t bc_row_stride;
   int64_t z_row_stride;
-  int B, T, D, N;
+  int B, T, D, N, K;
   int chunk_t, chunks;
   int softplus;
 };
@@ -83,7 +91,11 @@ __device__ __forceinline__ float load_at(const IO* row, uint32_t lane_off) {
 // state group g = q * H + l / CH (H = 64 / CH groups per wave), i.e. states [g*S, g*S+S) with
 // S = NP / (W * H). The per-token work of a block (kTB tokens x CH channels) is one item per
 // thread: item i = q * 64 + l is token i / CH, channel i % CH.
-template <typename IO, int NP, int CH, int W, bool OUT, bool GATE>
+// KC = 0: u is an input. KC > 0: the causal depthwise conv + SiLU is fused in -- each
+// per-token item reads its K raw inputs (x rows t-K+1 .. t, the carried conv state before
+// the sequence start) and computes u itself (rounded to the I/O type, as a stored u would
+// be); KC = 4 is the compile-time 4-tap case, KC = kMaxConvK any K <= 8 at run time.
+template <typename IO, int NP, int CH, int W, bool OUT, bool GATE, int KC>
 __global__ void __launch_bounds__(kLanes * W) __attribute__((amdgpu_waves_per_eu(5)))
 scan_kernel(const ScanParams p) {
   constexpr int H = kLanes / CH;     // state groups per wave
@@ -138,6 +150,25 @@ scan_kernel(const ScanParams p) {
   const bool sp = p.softplus != 0;
   const bool dval = d < D;
 
+  // fused conv: taps and bias of this thread's item channel, and where the incoming conv
+  // state is read (the output pass of a chunked call reads the copy the summary pass made,
+  // since the last chunk overwrites the state in place)
+  constexpr int KM = KC > 0 ? KC : 1;
+  const int K = KC == kMaxConvK ? p.K : KM;
+  float wk[KM];
+  float cbias = 0.0f;
+  const float* cs_old = nullptr;
+  const IO* __restrict__ xin = static_cast<const IO*>(p.x);
+  uint32_t off_xx = 0;
+  if constexpr (KC > 0) {
+#pragma unroll
+    for (int kk = 0; kk < KM; ++kk) wk[kk] = kk < K ? p.conv_w[(int64_t)dic * K + kk] : 0.0f;
+    cbias = p.conv_b ? p.conv_b[dic] : 0.0f;
+    // (a NULL conv state means zeros: the copy is then never made nor read)
+    cs_old = !p.conv_state ? nullptr : (OUT && p.chunks > 1) ? p.conv_ws : p.conv_state;
+    off_xx = ((uint32_t)it_lane * (uint32_t)p.x_row_stride + (uint32_t)dic) * (uint32_t)sizeof(IO);
+  }
+
   // ---- start state
   float h[S];
   if constexpr (OUT) {
@@ -186,6 +217,12 @@ scan_kernel(const ScanParams p) {
           p.start_ws[((int64_t)b * N + n) * D + d] =
               p.state_in ? p.state_in[((int64_t)b * D + d) * N + n] : 0.0f;
       }
+      if constexpr (KC > 0) {
+        if (g == 0 && p.conv_state) {
+          for (int kk = 0; kk < K; ++kk)
+            p.conv_ws[((int64_t)b * D + d) * K + kk] = p.conv_state[((int64_t)b * D + d) * K + kk];
+        }
+      }
     }
   }
 
@@ -210,14 +247,39 @@ scan_kernel(const ScanParams p) {
   // row (in bounds; such values are never used), so no load result is merged with an older
   // value and nothing waits on a load before its use.
   float pf_dt[2], pf_u[2], pf_z[2], pf_bc[2][BC_PER_T];
+  float pf_x[2][KM];  // fused conv: the item's K raw inputs, oldest first
   float u_blk[2], g_blk[2];  // u and silu(z) of this thread's item, for the finish
+  // fused conv, general case (the sequence start or a partial block): token tg of the
+  // sequence needs X[tg+1 .. tg+K] of X = [conv state (K), x (T)]
+  auto load_conv_inputs = [&](int k, int st) {
+    if constexpr (KC > 0) {
+      const int tg = t0 + min(k * kTB + it_wave + it_lane, len - 1);
+#pragma unroll
+      for (int kk = 0; kk < KM; ++kk) {
+        if (kk < K) {
+          const int rel = tg + 1 + kk - K;  // x token, or a state slot when negative
+          pf_x[st][kk] = rel >= 0 ? to_f32(xin[((int64_t)b * p.T + rel) * p.x_row_stride + dic])
+                         : (cs_old ? cs_old[((int64_t)b * D + dic) * K + K + rel] : 0.0f);
+        }
+      }
+    }
+  };
   auto load_block = [&](int k, auto P) {
     constexpr int st = decltype(P)::value;
     if (k * kTB + kTB <= len) {
       // full block: scalar row address + the thread's fixed byte offset
       const int64_t row = row0 + k * kTB + it_wave;
       pf_dt[st] = load_at(dt + row * D, off_x);
-      pf_u[st] = load_at(u + row * D, off_x);
+      if constexpr (KC == 0) {
+        pf_u[st] = load_at(u + row * D, off_x);
+      } else if (t0 + k * kTB >= K - 1) {
+        // every tap of every item in the block is an x row: scalar rows, fixed lane offset
+#pragma unroll
+        for (int kk = 0; kk < KM; ++kk)
+          if (kk < K) pf_x[st][kk] = load_at(xin + (row + 1 + kk - K) * p.x_row_stride, off_xx);
+      } else {
+        load_conv_inputs(k, st);
+      }
       if constexpr (OUT && GATE) pf_z[st] = load_at(z + row * p.z_row_stride, off_z);
       const int64_t step = (int64_t)k * kTB * bcs;
 #pragma unroll
@@ -226,7 +288,8 @@ scan_kernel(const ScanParams p) {
     } else {
       const int64_t row = row0 + min(k * kTB + it_wave + it_lane, len - 1);
       pf_dt[st] = to_f32(dt[row * D + dic]);
-      pf_u[st] = to_f32(u[row * D + dic]);
+      if constexpr (KC == 0) pf_u[st] = to_f32(u[row * D + dic]);
+      else load_conv_inputs(k, st);
       if constexpr (OUT && GATE) pf_z[st] = to_f32(z[row * p.z_row_stride + dic]);
 #pragma unroll
       for (int r = 0; r < BC_PER_T; ++r)
@@ -238,6 +301,20 @@ scan_kernel(const ScanParams p) {
   // stage A: delta and delta*u of this thread's item of block k into LDS, B/C of block k
   auto stage_a = [&](int k, auto P) {
     constexpr int st = decltype(P)::value;
+    if constexpr (KC > 0) {
+      // conv + SiLU in the order of the stand-alone conv kernel, rounded to the I/O type
+      float cv = cbias;
+#pragma unroll
+      for (int kk = 0; kk < KM; ++kk)
+        if (kk < K) cv = fmaf(wk[kk], pf_x[st][kk], cv);
+      const IO uo = from_f32<IO>(silu(cv));
+      pf_u[st] = to_f32(uo);
+      if constexpr (OUT) {
+        const int j = it_wave + it_lane;
+        if (p.u_out && di < D && k * kTB + j < len)
+          static_cast<IO*>(p.u_out)[(row0 + k * kTB + j) * D + di] = uo;
+      }
+    }
     const float v = pf_dt[st] + bias;
     const float delta = sp ? softplus(v) : v;
     s_dd[st][it_wave + it_lane][ic] = make_float2(delta, delta * pf_u[st]);
@@ -350,6 +427,17 @@ scan_kernel(const ScanParams p) {
         if (n < N) p.state_out[((int64_t)b * D + d) * N + n] = h[s];
       }
     }
+    if constexpr (KC > 0) {
+      // new conv state X[T .. T+K-1]: x tokens T-K .. T-1, or (T < K) the old state shifted
+      if (c == p.chunks - 1 && p.conv_state && g == 0) {
+        for (int kk = 0; kk < K; ++kk) {
+          const int i = p.T + kk;
+          p.conv_state[((int64_t)b * D + d) * K + kk] =
+              i >= K ? to_f32(xin[((int64_t)b * p.T + i - K) * p.x_row_stride + d])
+                     : (cs_old ? cs_old[((int64_t)b * D + d) * K + i] : 0.0f);
+        }
+      }
+    }
   } else {
     const int64_t bc_ = (int64_t)b * p.chunks + c;
     if (g == 0) p.sum_ws[bc_ * D + d] = sum_delta;
@@ -393,15 +481,18 @@ ScanPlan plan_selective_scan(int B, int T, int D, int N) {
   p.chunks = (T + chunk_t - 1) / chunk_t;
   p.chunk_t = chunk_t;
   if (p.chunks > 1) {
+    // chunk sums, chunk end states, the carried SSM state, and (fused conv) the carried
+    // conv state
     const size_t bcd = (size_t)B * p.chunks * D;
     p.workspace_bytes = align256(sizeof(float) * bcd) + align256(sizeof(float) * bcd * N) +
-                        align256(sizeof(float) * (size_t)B * N * D);
+                        align256(sizeof(float) * (size_t)B * N * D) +
+                        align256(sizeof(float) * (size_t)B * D * kMaxConvK);
   }
   return p;
 }
 
-template <typename IO, int NP>
-static hipError_t launch_scan_np(const ScanFwdArgs& a, const ScanPlan& pl, hipStream_t s) {
+template <typename IO, int NP, int KC>
+static hipError_t launch_scan_npk(const ScanFwdArgs& a, const ScanPlan& pl, hipStream_t s) {
   // 64 states per channel: 64-channel workgroups keep the states per lane at 8
   constexpr int CH = NP == 64 ? 64 : kCh;
   constexpr int W = kTB * CH / kLanes;
@@ -417,12 +508,19 @@ static hipError_t launch_scan_np(const ScanFwdArgs& a, const ScanPlan& pl, hipSt
   p.D_skip = a.D_skip;
   p.state_in = a.state_in;
   p.state_out = a.state_out;
+  p.x = a.x;
+  p.conv_w = a.conv_w;
+  p.conv_b = a.conv_b;
+  p.conv_state = a.conv_state;
+  p.u_out = a.u_out;
+  p.x_row_stride = a.x_row_stride;
   p.bc_row_stride = a.bc_row_stride;
   p.z_row_stride = a.z_row_stride;
   p.B = a.B;
   p.T = a.T;
   p.D = a.D;
   p.N = a.N;
+  p.K = a.K;
   p.chunk_t = pl.chunk_t;
   p.chunks = pl.chunks;
   p.softplus = a.delta_softplus ? 1 : 0;
@@ -435,16 +533,25 @@ static hipError_t launch_scan_np(const ScanFwdArgs& a, const ScanPlan& pl, hipSt
     p.h_ws = reinterpret_cast<float*>(ws);
     ws += align256(sizeof(float) * bcd * a.N);
     p.start_ws = reinterpret_cast<float*>(ws);
-    scan_kernel<IO, NP, CH, W, false, false><<<dim3(gx, a.B, pl.chunks - 1), kLanes * W, 0, s>>>(p);
+    ws += align256(sizeof(float) * (size_t)a.B * a.N * a.D);
+    p.conv_ws = reinterpret_cast<float*>(ws);
+    scan_kernel<IO, NP, CH, W, false, false, KC><<<dim3(gx, a.B, pl.chunks - 1), kLanes * W, 0, s>>>(p);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   const dim3 grid(gx, a.B, pl.chunks);
   if (a.z)
-    scan_kernel<IO, NP, CH, W, true, true><<<grid, kLanes * W, 0, s>>>(p);
+    scan_kernel<IO, NP, CH, W, true, true, KC><<<grid, kLanes * W, 0, s>>>(p);
   else
-    scan_kernel<IO, NP, CH, W, true, false><<<grid, kLanes * W, 0, s>>>(p);
+    scan_kernel<IO, NP, CH, W, true, false, KC><<<grid, kLanes * W, 0, s>>>(p);
   return hipGetLastError();
+}
+
+template <typename IO, int NP>
+static hipError_t launch_scan_np(const ScanFwdArgs& a, const ScanPlan& pl, hipStream_t s) {
+  if (!a.x) return launch_scan_npk<IO, NP, 0>(a, pl, s);
+  if (a.K == 4) return launch_scan_npk<IO, NP, 4>(a, pl, s);
+  return launch_scan_npk<IO, NP, kMaxConvK>(a, pl, s);
 }
 
 template <typename IO>

@@ -44,9 +44,10 @@ def host(t) -> np.ndarray:
     return t.detach().float().cpu().numpy()
 
 
-def gpu_layer(inp: dict, io: str, chunks=None, in_place_state=True, stream=None):
-    """conv1d_fwd then selective_scan_fwd on the GPU. chunks: list of T-piece lengths to run
-    the prefill in several calls carrying both states (None: one call).
+def gpu_layer(inp: dict, io: str, chunks=None, in_place_state=True, stream=None, fused=False):
+    """conv1d_fwd then selective_scan_fwd on the GPU (fused: one mamba_conv_scan_fwd call,
+    u written too). chunks: list of T-piece lengths to run the prefill in several calls
+    carrying both states (None: one call).
     Returns dict of torch tensors: u, y, conv_state, ssm_state."""
     B, T, D = inp["x"].shape
     N = inp["A_log"].shape[1]
@@ -71,11 +72,16 @@ def gpu_layer(inp: dict, io: str, chunks=None, in_place_state=True, stream=None)
             Bs, Cs = Bm[:, sl].contiguous(), Cm[:, sl].contiguous()
         us = torch.empty(B, n, D, dtype=iod, device="cuda")
         ys = torch.empty(B, n, D, dtype=iod, device="cuda")
-        m.mamba_conv1d_fwd(xs, p["conv_w"], p["conv_b"], conv_state, us, stream=stream)
         ws = m.scan_workspace(B, n, D, N)
         out_state = ssm_state if in_place_state else torch.empty_like(ssm_state)
-        m.mamba_selective_scan_fwd(us, dts, p["dt_bias"], p["A_log"], Bs, Cs, p["D_skip"], zs,
-                                   ssm_state, out_state, ys, workspace=ws, stream=stream)
+        if fused:
+            m.mamba_conv_scan_fwd(xs, p["conv_w"], p["conv_b"], conv_state, dts, p["dt_bias"],
+                                  p["A_log"], Bs, Cs, p["D_skip"], zs, ssm_state, out_state, ys,
+                                  u=us, workspace=ws, stream=stream)
+        else:
+            m.mamba_conv1d_fwd(xs, p["conv_w"], p["conv_b"], conv_state, us, stream=stream)
+            m.mamba_selective_scan_fwd(us, dts, p["dt_bias"], p["A_log"], Bs, Cs, p["D_skip"], zs,
+                                       ssm_state, out_state, ys, workspace=ws, stream=stream)
         ssm_state = out_state
         u[:, sl] = us
         y[:, sl] = ys

@@ -44,10 +44,11 @@ def test_c0_full():
     _check(gpu_layer(inp, "f32"), oracle_layer(inp), "f32", "c0")
 
 
-def test_c1_full_size_all_channels():
-    _say("case c1 f32 B1 T2048 D1536 N16")
+@pytest.mark.parametrize("fused", [False, True])
+def test_c1_full_size_all_channels(fused):
+    _say(f"case c1 f32 B1 T2048 D1536 N16 fused={fused}")
     inp = W.prefill_inputs(W.C1)
-    _check(gpu_layer(inp, "f32"), oracle_layer(inp), "f32", "c1")
+    _check(gpu_layer(inp, "f32", fused=fused), oracle_layer(inp), "f32", "c1")
 
 
 @pytest.fixture(scope="module")
@@ -56,17 +57,19 @@ def c3_inputs():
     return W.prefill_inputs(W.C3)
 
 
-def test_c3_full_size_one_shot_sampled(c3_inputs):
-    _say("case c3 one-shot T4096, 48 sampled channels")
+@pytest.mark.parametrize("fused", [False, True])
+def test_c3_full_size_one_shot_sampled(c3_inputs, fused):
+    _say(f"case c3 one-shot T4096, 48 sampled channels fused={fused}")
     chans = pick_channels(8, 5120, 48, seed=3)
-    g = gpu_layer(c3_inputs, "bf16")
+    g = gpu_layer(c3_inputs, "bf16", fused=fused)
     _check(gather_channels(g, chans), oracle_layer(c3_inputs, chans), "bf16", "c3 one-shot")
 
 
-def test_c3_chunked_4x1024_matches_oracle_and_one_shot(c3_inputs):
-    _say("case c3 4 x 1024 chunks with carried state")
+@pytest.mark.parametrize("fused", [False, True])
+def test_c3_chunked_4x1024_matches_oracle_and_one_shot(c3_inputs, fused):
+    _say(f"case c3 4 x 1024 chunks with carried state fused={fused}")
     chans = pick_channels(8, 5120, 48, seed=4)
-    g4 = gpu_layer(c3_inputs, "bf16", chunks=[1024] * 4)
+    g4 = gpu_layer(c3_inputs, "bf16", chunks=[1024] * 4, fused=fused)
     _check(gather_channels(g4, chans), oracle_layer(c3_inputs, chans), "bf16", "c3 4x1024")
     g1 = gpu_layer(c3_inputs, "bf16")
     diff = {k: rel_err(host(g4[k]), host(g1[k])) for k in ("y", "ssm_state", "conv_state")}
@@ -91,28 +94,80 @@ RAGGED = [
 ]
 
 
+@pytest.mark.parametrize("fused", [False, True])
 @pytest.mark.parametrize("B,T,D,N,K,io", RAGGED)
-def test_ragged_shapes_random_params(B, T, D, N, K, io):
-    _say(f"case ragged B{B} T{T} D{D} N{N} K{K} {io}")
+def test_ragged_shapes_random_params(B, T, D, N, K, io, fused):
+    _say(f"case ragged B{B} T{T} D{D} N{N} K{K} {io} fused={fused}")
     s = W.PrefillShape("r", B=B, T=T, D=D, N=N, K=K, io=io)
     inp = W.prefill_inputs(s, seed=5, random_alog=True, random_extras=True, random_state=True)
-    _check(gpu_layer(inp, io), oracle_layer(inp), io, f"ragged {B},{T},{D},{N},{K},{io}")
+    _check(gpu_layer(inp, io, fused=fused), oracle_layer(inp), io, f"ragged {B},{T},{D},{N},{K},{io}")
 
 
+@pytest.mark.parametrize("fused", [False, True])
 @pytest.mark.parametrize("T", [1, 2, 3, 5, 16, 33])
-def test_short_sequences_and_state_shift(T):
+def test_short_sequences_and_state_shift(T, fused):
     """T below K-1 exercises the conv state shift; T=1 is the prefill of one token."""
-    _say(f"case short T{T}")
+    _say(f"case short T{T} fused={fused}")
     s = W.PrefillShape("s", B=2, T=T, D=80, N=16, K=4)
     inp = W.prefill_inputs(s, seed=6, random_state=True, random_extras=True)
-    _check(gpu_layer(inp, "f32"), oracle_layer(inp), "f32", f"short T{T}")
+    _check(gpu_layer(inp, "f32", fused=fused), oracle_layer(inp), "f32", f"short T{T}")
 
 
-def test_split_prefill_pieces_equal_oracle():
-    _say("case split prefill [1,2,5,100,292]")
+@pytest.mark.parametrize("fused", [False, True])
+def test_split_prefill_pieces_equal_oracle(fused):
+    _say(f"case split prefill [1,2,5,100,292] fused={fused}")
     s = W.PrefillShape("p", B=2, T=400, D=96, N=16, K=4)
     inp = W.prefill_inputs(s, seed=7, random_state=True)
-    _check(gpu_layer(inp, "f32", chunks=[1, 2, 5, 100, 292]), oracle_layer(inp), "f32", "split")
+    _check(gpu_layer(inp, "f32", chunks=[1, 2, 5, 100, 292], fused=fused), oracle_layer(inp), "f32", "split")
+
+
+FUSED_EQ = [
+    # (B, T, D, N, K, io, strided_x): one chunk, several chunks (T split over workgroups),
+    # the run-time-K path (K = 3, N = 5), a sequence shorter than the conv window, bf16
+    (2, 300, 128, 16, 4, "f32", False),
+    (1, 2048, 128, 16, 4, "f32", True),
+    (2, 777, 96, 5, 3, "f32", True),
+    (3, 2, 64, 16, 4, "f32", False),
+    (2, 1500, 192, 16, 4, "bf16", True),
+    (1, 1024, 64, 64, 8, "bf16", False),
+]
+
+
+@pytest.mark.parametrize("B,T,D,N,K,io,strided", FUSED_EQ)
+def test_fused_prefill_equals_two_calls(B, T, D, N, K, io, strided):
+    """mamba_conv_scan_fwd computes exactly what mamba_conv1d_fwd then
+    mamba_selective_scan_fwd compute: the conv in the same order, u rounded to the I/O type
+    as stored, the same scan. Bit-for-bit on y, u and both states; also with u not written
+    and the conv state NULL."""
+    _say(f"case fused prefill == two calls B{B} T{T} D{D} N{N} K{K} {io} strided={strided}")
+    s = W.PrefillShape("fe", B=B, T=T, D=D, N=N, K=K, io=io)
+    inp = W.prefill_inputs(s, seed=9, random_alog=True, random_extras=True, random_state=True)
+    iod = torch.bfloat16 if io == "bf16" else torch.float32
+    if strided:  # x and z as the two halves of one [B, T, 2D] buffer (the in_proj layout)
+        xz = torch.cat([dev(inp["x"], io), dev(inp["z"], io)], dim=2)
+        x, z = xz[..., :D], xz[..., D:]
+    else:
+        x, z = dev(inp["x"], io), dev(inp["z"], io)
+    dt, Bm, Cm = dev(inp["dt"], io), dev(inp["Bm"], io), dev(inp["Cm"], io)
+    p = {k: dev(inp[k]) for k in ("conv_w", "conv_b", "dt_bias", "A_log", "D_skip")}
+    ws = m.scan_workspace(B, T, D, N)
+    for conv_null in (False, True):
+        cs1 = None if conv_null else dev(inp["conv_state"])
+        cs2 = None if conv_null else dev(inp["conv_state"])
+        hs1, hs2 = dev(inp["ssm_state"]), dev(inp["ssm_state"])
+        u1 = torch.empty(B, T, D, dtype=iod, device="cuda")
+        y1 = torch.empty_like(u1)
+        m.mamba_conv1d_fwd(x, p["conv_w"], p["conv_b"], cs1, u1)
+        m.mamba_selective_scan_fwd(u1, dt, p["dt_bias"], p["A_log"], Bm, Cm, p["D_skip"], z, hs1, hs1, y1,
+                                   workspace=ws)
+        u2 = torch.empty_like(u1)
+        y2 = torch.empty_like(u1)
+        m.mamba_conv_scan_fwd(x, p["conv_w"], p["conv_b"], cs2, dt, p["dt_bias"], p["A_log"], Bm, Cm,
+                              p["D_skip"], z, hs2, hs2, y2, u=None if conv_null else u2, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(y1, y2) and torch.equal(hs1, hs2), conv_null
+        if not conv_null:
+            assert torch.equal(u1, u2) and torch.equal(cs1, cs2)
 
 
 def test_out_of_place_state_and_null_state_in():
