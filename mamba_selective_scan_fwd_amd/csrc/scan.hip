@@ -115,7 +115,16 @@ scan_kernel(const ScanParams p) {
   const int q = __builtin_amdgcn_readfirstlane(threadIdx.x / kLanes);
   const int ch = lane % CH;          // this lane's channel in the scan
   const int g = q * H + lane / CH;   // this lane's state group
-  const int d0 = blockIdx.x * CH;
+  // Channel group of this workgroup. Workgroups go to the 8 XCDs (each with its own L2) in
+  // round-robin order of their linear id. When a group's rows are narrower than a 128-byte
+  // line (bf16, 32 channels), groups 2p and 2p+1 -- the two halves of the same lines -- are
+  // given workgroup ids 8 apart, so both land on one XCD and the line is fetched once.
+  int cgrp = blockIdx.x;
+  if constexpr (CH * sizeof(IO) < 128) {
+    const int x16 = blockIdx.x & ~15;
+    if (x16 + 16 <= (int)gridDim.x) cgrp = x16 + 2 * (blockIdx.x & 7) + ((blockIdx.x >> 3) & 1);
+  }
+  const int d0 = cgrp * CH;
   const int b = blockIdx.y;
   const int c = blockIdx.z;
   const int N = p.N, D = p.D;
