@@ -308,6 +308,48 @@ mamba_status mamba_backbone_prefill(const mamba_backbone_dims* dims,
                                     float* ssm_state, float* logits, void* workspace,
                                     size_t workspace_bytes, void* stream);
 
+/*
+ * One decode step of the whole backbone: one new token per sequence through all layers and
+ * the tied head. [inference.rs] the backbone step chain F1-F12 (RMSNorm, in_proj, conv step
+ * on the x lane, x_proj, dt_proj, softplus + state update + readout + D skip, silu(z) gate,
+ * out_proj, residual) and [gpu_lm.rs] norm_f + the tied head; the conv and SSM states are
+ * the ones mamba_backbone_prefill leaves, so a prefill followed by decode steps continues
+ * each sequence.
+ *
+ *   tokens       in   [B] int32, the next token of each sequence.
+ *   conv_state, ssm_state  in/out, layouts as mamba_backbone_prefill, updated in place.
+ *   logits       out  [B, vocab] f32.
+ *   workspace    at least mamba_backbone_decode_workspace_size(dims, B) bytes, 256-byte aligned.
+ * Nothing is allocated or synchronized: the call can be captured into a HIP graph.
+ */
+size_t mamba_backbone_decode_workspace_size(const mamba_backbone_dims* dims, int B);
+mamba_status mamba_backbone_decode_step(const mamba_backbone_dims* dims,
+                                        const mamba_backbone_weights* weights,
+                                        const int32_t* tokens, int B, float* conv_state,
+                                        float* ssm_state, float* logits, void* workspace,
+                                        size_t workspace_bytes, void* stream);
+
+/*
+ * The decode step captured once into a HIP graph and replayed (the inference.rs page
+ * captures its decode chain the same way, so a step costs one graph launch instead of one
+ * launch per kernel). The graph records the pointers given here: before each launch the
+ * caller writes the next tokens into the same `tokens` buffer; the states, logits and
+ * workspace are the same buffers every time.
+ *   mamba_backbone_decode_graph_create  validates as mamba_backbone_decode_step, captures on
+ *       a private stream and instantiates; *graph receives the handle (NULL on failure).
+ *       Host-side graph objects are created here; no device memory is allocated.
+ *   mamba_graph_launch   enqueues one replay on `stream`.
+ *   mamba_graph_destroy  frees the handle (NULL is a no-op).
+ */
+typedef struct mamba_graph mamba_graph;
+mamba_status mamba_backbone_decode_graph_create(const mamba_backbone_dims* dims,
+                                                const mamba_backbone_weights* weights,
+                                                const int32_t* tokens, int B, float* conv_state,
+                                                float* ssm_state, float* logits, void* workspace,
+                                                size_t workspace_bytes, mamba_graph** graph);
+mamba_status mamba_graph_launch(mamba_graph* graph, void* stream);
+void mamba_graph_destroy(mamba_graph* graph);
+
 #ifdef __cplusplus
 }
 #endif

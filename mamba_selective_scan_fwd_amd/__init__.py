@@ -45,6 +45,12 @@ symbols = {
     "mamba_gemm_bf16": ([_P, _I, _I64, _P, _I64, _P, _I64, _I, _I, _I, _I, _P], _I),
     "mamba_backbone_workspace_size": ([_P, _I, _I], _SZ),
     "mamba_backbone_prefill": ([_P, _P, _P, _I, _I, _P, _P, _P, _P, _SZ, _P], _I),
+    "mamba_backbone_decode_workspace_size": ([_P, _I], _SZ),
+    "mamba_backbone_decode_step": ([_P, _P, _P, _I, _P, _P, _P, _P, _SZ, _P], _I),
+    "mamba_backbone_decode_graph_create": ([_P, _P, _P, _I, _P, _P, _P, _P, _SZ,
+                                            ctypes.POINTER(ctypes.c_void_p)], _I),
+    "mamba_graph_launch": ([_P, _P], _I),
+    "mamba_graph_destroy": ([_P], None),
 }
 
 
@@ -324,3 +330,46 @@ def backbone_weights_struct(t: dict) -> BackboneWeights:
             raise ValueError(f"backbone weight {name}: need a contiguous device {want} tensor")
         setattr(w, name, x.data_ptr())
     return w
+
+
+def mamba_backbone_decode_workspace_size(dims: BackboneDims, B: int) -> int:
+    return int(load_library().mamba_backbone_decode_workspace_size(ctypes.byref(dims), B))
+
+
+def mamba_backbone_decode_step(dims: BackboneDims, weights: BackboneWeights, tokens, conv_state,
+                               ssm_state, logits, workspace, stream=None) -> None:
+    """One decode step of the whole backbone: tokens [B] int32 -> logits [B, vocab]; states in
+    place."""
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(load_library().mamba_backbone_decode_step(
+        ctypes.byref(dims), ctypes.byref(weights), _ptr(tokens), tokens.numel(), _ptr(conv_state),
+        _ptr(ssm_state), _ptr(logits), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+class DecodeGraph:
+    """The backbone decode step captured into a HIP graph (mamba_backbone_decode_graph_create).
+    The buffers given here are baked in: write the next tokens into `tokens`, then launch()."""
+
+    def __init__(self, dims: BackboneDims, weights: BackboneWeights, tokens, conv_state, ssm_state,
+                 logits, workspace):
+        self._keep = (dims, weights, tokens, conv_state, ssm_state, logits, workspace)
+        handle = ctypes.c_void_p()
+        ws_bytes = workspace.numel() * workspace.element_size()
+        _check(load_library().mamba_backbone_decode_graph_create(
+            ctypes.byref(dims), ctypes.byref(weights), _ptr(tokens), tokens.numel(), _ptr(conv_state),
+            _ptr(ssm_state), _ptr(logits), _ptr(workspace), ws_bytes, ctypes.byref(handle)))
+        self._h = handle
+
+    def launch(self, stream=None) -> None:
+        _check(load_library().mamba_graph_launch(self._h, _stream(stream)))
+
+    def close(self) -> None:
+        if self._h:
+            load_library().mamba_graph_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -528,6 +528,46 @@ size_t mamba_backbone_workspace_size(const mamba_backbone_dims* dims, int B, int
   return mamba::backbone_workspace_bytes(*dims, B, T);
 }
 
+// Shared checks of the backbone calls: weights, tokens [ntok], states, logits [B, vocab] and
+// a workspace of at least `need` bytes, all mutually disjoint where written.
+static void check_backbone_call(const char* fn, const mamba_backbone_dims& d,
+                                const mamba_backbone_weights* w, const int32_t* tokens,
+                                int64_t ntok, int B, const float* conv_state,
+                                const float* ssm_state, const float* logits, const void* workspace,
+                                size_t workspace_bytes, size_t need) {
+  if (!w) fail(MAMBA_EINVAL, fn, "weights is NULL");
+  check_ptr(fn, "embed", w->embed, 2, true);
+  check_ptr(fn, "norm_f", w->norm_f, 4, true);
+  check_ptr(fn, "norm_w", w->norm_w, 4, d.n_layers > 0);
+  check_ptr(fn, "in_proj", w->in_proj, 2, d.n_layers > 0);
+  check_ptr(fn, "conv_w", w->conv_w, 4, d.n_layers > 0);
+  check_ptr(fn, "conv_b", w->conv_b, 4, d.n_layers > 0);
+  check_ptr(fn, "x_proj", w->x_proj, 2, d.n_layers > 0);
+  check_ptr(fn, "dt_proj", w->dt_proj, 2, d.n_layers > 0);
+  check_ptr(fn, "dt_bias", w->dt_bias, 4, d.n_layers > 0);
+  check_ptr(fn, "A_log", w->A_log, 4, d.n_layers > 0);
+  check_ptr(fn, "D_skip", w->D_skip, 4, d.n_layers > 0);
+  check_ptr(fn, "out_proj", w->out_proj, 2, d.n_layers > 0);
+  check_ptr(fn, "tokens", tokens, 4, true);
+  check_ptr(fn, "conv_state", conv_state, 4, d.n_layers > 0);
+  check_ptr(fn, "ssm_state", ssm_state, 4, d.n_layers > 0);
+  check_ptr(fn, "logits", logits, 4, true);
+  if (!workspace) fail(MAMBA_EWORKSPACE, fn, "workspace is NULL but %zu bytes are required", need);
+  if (workspace_bytes < need) fail(MAMBA_EWORKSPACE, fn, "workspace_bytes = %zu but %zu are required", workspace_bytes, need);
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) fail(MAMBA_EINVAL, fn, "workspace is not 256-byte aligned");
+  const int64_t L = d.n_layers;
+  const Range rws = range("workspace", workspace, 1, (int64_t)need, (int64_t)need, 1);
+  const Range rlog = range("logits", logits, B, d.vocab, d.vocab, 4);
+  const Range rcs = range("conv_state", conv_state, L * B * d.d_inner, d.d_conv, d.d_conv, 4);
+  const Range rss = range("ssm_state", ssm_state, L * B * d.d_inner, d.d_state, d.d_state, 4);
+  const Range rtok = range("tokens", tokens, 1, ntok, ntok, 4);
+  const Range remb = range("embed", w->embed, d.vocab_padded, d.d_model, d.d_model, 2);
+  check_disjoint(fn, rws, {rlog, rcs, rss, rtok, remb});
+  check_disjoint(fn, rlog, {rcs, rss, rtok, remb});
+  check_disjoint(fn, rcs, {rss, rtok, remb});
+  check_disjoint(fn, rss, {rtok, remb});
+}
+
 mamba_status mamba_backbone_prefill(const mamba_backbone_dims* dims,
                                     const mamba_backbone_weights* w, const int32_t* tokens,
                                     int B, int T, float* conv_state, float* ssm_state,
@@ -536,47 +576,96 @@ mamba_status mamba_backbone_prefill(const mamba_backbone_dims* dims,
   static const char* fn = "mamba_backbone_prefill";
   return guarded([&] {
     check_backbone_dims(fn, dims);
-    if (!w) fail(MAMBA_EINVAL, fn, "weights is NULL");
     check_dim(fn, "B", B);
     check_dim(fn, "T", T);
     if (B == 0 || T == 0) return;
     if (B > kMaxGridYZ) fail(MAMBA_EUNSUPPORTED, fn, "B = %d exceeds %d", B, kMaxGridYZ);
     if ((int64_t)B * T > INT32_MAX / 2) fail(MAMBA_EUNSUPPORTED, fn, "B * T too large");
     const mamba_backbone_dims& d = *dims;
-    check_ptr(fn, "embed", w->embed, 2, true);
-    check_ptr(fn, "norm_f", w->norm_f, 4, true);
-    check_ptr(fn, "norm_w", w->norm_w, 4, d.n_layers > 0);
-    check_ptr(fn, "in_proj", w->in_proj, 2, d.n_layers > 0);
-    check_ptr(fn, "conv_w", w->conv_w, 4, d.n_layers > 0);
-    check_ptr(fn, "conv_b", w->conv_b, 4, d.n_layers > 0);
-    check_ptr(fn, "x_proj", w->x_proj, 2, d.n_layers > 0);
-    check_ptr(fn, "dt_proj", w->dt_proj, 2, d.n_layers > 0);
-    check_ptr(fn, "dt_bias", w->dt_bias, 4, d.n_layers > 0);
-    check_ptr(fn, "A_log", w->A_log, 4, d.n_layers > 0);
-    check_ptr(fn, "D_skip", w->D_skip, 4, d.n_layers > 0);
-    check_ptr(fn, "out_proj", w->out_proj, 2, d.n_layers > 0);
-    check_ptr(fn, "tokens", tokens, 4, true);
-    check_ptr(fn, "conv_state", conv_state, 4, d.n_layers > 0);
-    check_ptr(fn, "ssm_state", ssm_state, 4, d.n_layers > 0);
-    check_ptr(fn, "logits", logits, 4, true);
-    const size_t need = mamba::backbone_workspace_bytes(d, B, T);
-    if (!workspace) fail(MAMBA_EWORKSPACE, fn, "workspace is NULL but %zu bytes are required", need);
-    if (workspace_bytes < need) fail(MAMBA_EWORKSPACE, fn, "workspace_bytes = %zu but %zu are required", workspace_bytes, need);
-    if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) fail(MAMBA_EINVAL, fn, "workspace is not 256-byte aligned");
-    const int64_t L = d.n_layers;
-    const Range rws = range("workspace", workspace, 1, (int64_t)need, (int64_t)need, 1);
-    const Range rlog = range("logits", logits, B, d.vocab, d.vocab, 4);
-    const Range rcs = range("conv_state", conv_state, L * B * d.d_inner, d.d_conv, d.d_conv, 4);
-    const Range rss = range("ssm_state", ssm_state, L * B * d.d_inner, d.d_state, d.d_state, 4);
-    const Range rtok = range("tokens", tokens, 1, (int64_t)B * T, (int64_t)B * T, 4);
-    const Range remb = range("embed", w->embed, d.vocab_padded, d.d_model, d.d_model, 2);
-    check_disjoint(fn, rws, {rlog, rcs, rss, rtok, remb});
-    check_disjoint(fn, rlog, {rcs, rss, rtok, remb});
-    check_disjoint(fn, rcs, {rss, rtok, remb});
-    check_disjoint(fn, rss, {rtok, remb});
+    check_backbone_call(fn, d, w, tokens, (int64_t)B * T, B, conv_state, ssm_state, logits, workspace,
+                        workspace_bytes, mamba::backbone_workspace_bytes(d, B, T));
     check_hip(fn, mamba::run_backbone_prefill(d, *w, tokens, B, T, conv_state, ssm_state, logits,
                                               workspace, static_cast<hipStream_t>(stream)));
   });
+}
+
+size_t mamba_backbone_decode_workspace_size(const mamba_backbone_dims* dims, int B) {
+  if (!dims || B <= 0) return 0;
+  return mamba::backbone_decode_workspace_bytes(*dims, B);
+}
+
+static void check_decode_call(const char* fn, const mamba_backbone_dims* dims,
+                              const mamba_backbone_weights* w, const int32_t* tokens, int B,
+                              const float* conv_state, const float* ssm_state, const float* logits,
+                              const void* workspace, size_t workspace_bytes) {
+  check_backbone_dims(fn, dims);
+  check_dim(fn, "B", B);
+  if (B == 0) fail(MAMBA_EINVAL, fn, "B = 0");
+  if ((int64_t)B > kMaxGridYZ) fail(MAMBA_EUNSUPPORTED, fn, "B = %d exceeds %d", B, kMaxGridYZ);
+  check_backbone_call(fn, *dims, w, tokens, B, B, conv_state, ssm_state, logits, workspace,
+                      workspace_bytes, mamba::backbone_decode_workspace_bytes(*dims, B));
+}
+
+mamba_status mamba_backbone_decode_step(const mamba_backbone_dims* dims,
+                                        const mamba_backbone_weights* w, const int32_t* tokens,
+                                        int B, float* conv_state, float* ssm_state, float* logits,
+                                        void* workspace, size_t workspace_bytes, void* stream) {
+  static const char* fn = "mamba_backbone_decode_step";
+  return guarded([&] {
+    check_decode_call(fn, dims, w, tokens, B, conv_state, ssm_state, logits, workspace, workspace_bytes);
+    check_hip(fn, mamba::run_backbone_decode(*dims, *w, tokens, B, conv_state, ssm_state, logits,
+                                             workspace, static_cast<hipStream_t>(stream)));
+  });
+}
+
+// A captured decode step: the instantiated graph of every kernel launch of one
+// mamba_backbone_decode_step with fixed pointers.
+struct mamba_graph {
+  hipGraphExec_t exec = nullptr;
+};
+
+mamba_status mamba_backbone_decode_graph_create(const mamba_backbone_dims* dims,
+                                                const mamba_backbone_weights* w,
+                                                const int32_t* tokens, int B, float* conv_state,
+                                                float* ssm_state, float* logits, void* workspace,
+                                                size_t workspace_bytes, mamba_graph** out) {
+  static const char* fn = "mamba_backbone_decode_graph_create";
+  return guarded([&] {
+    if (!out) fail(MAMBA_EINVAL, fn, "out is NULL");
+    *out = nullptr;
+    check_decode_call(fn, dims, w, tokens, B, conv_state, ssm_state, logits, workspace, workspace_bytes);
+    // capture on a private stream (default priority), so the caller's streams are untouched
+    hipStream_t cs = nullptr;
+    check_hip(fn, hipStreamCreateWithFlags(&cs, hipStreamNonBlocking));
+    hipGraph_t graph = nullptr;
+    hipError_t e = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal);
+    if (e == hipSuccess) {
+      const hipError_t run = mamba::run_backbone_decode(*dims, *w, tokens, B, conv_state, ssm_state,
+                                                        logits, workspace, cs);
+      e = hipStreamEndCapture(cs, &graph);
+      if (run != hipSuccess) e = run;
+    }
+    hipGraphExec_t exec = nullptr;
+    if (e == hipSuccess) e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+    if (graph) (void)hipGraphDestroy(graph);
+    (void)hipStreamDestroy(cs);
+    check_hip(fn, e);
+    *out = new mamba_graph{exec};
+  });
+}
+
+mamba_status mamba_graph_launch(mamba_graph* g, void* stream) {
+  static const char* fn = "mamba_graph_launch";
+  return guarded([&] {
+    if (!g || !g->exec) fail(MAMBA_EINVAL, fn, "graph is NULL");
+    check_hip(fn, hipGraphLaunch(g->exec, static_cast<hipStream_t>(stream)));
+  });
+}
+
+void mamba_graph_destroy(mamba_graph* g) {
+  if (!g) return;
+  if (g->exec) (void)hipGraphExecDestroy(g->exec);
+  delete g;
 }
 
 }  // extern "C"

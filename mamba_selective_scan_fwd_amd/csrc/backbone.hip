@@ -329,9 +329,11 @@ static hipError_t gemm_at(const AT* A, int64_t lda, const bf16* W, int64_t ldw, 
   const bool vec = K % 8 == 0 && lda % 8 == 0 && ldw % 8 == 0 &&
                    reinterpret_cast<uintptr_t>(A) % 16 == 0 && reinterpret_cast<uintptr_t>(W) % 16 == 0;
   // Wide outputs: 128 x 128 tiles, 2 x 2 waves. Narrow ones (x_proj's 80 columns): 32 x 80
-  // tiles, one column tile, so that the grid still covers the chip.
-  if (N >= 128) return gemm_tile<AT, 128, 128, 64, 2, 2>(A, lda, W, ldw, C, ldc, M, N, K, acc, vec, s);
-  return gemm_tile<AT, 32, 80, 64, 2, 1>(A, lda, W, ldw, C, ldc, M, N, K, acc, vec, s);
+  // tiles, one column tile, so that the grid still covers the chip. Few rows (a decode step's
+  // batch): 64 x 32 tiles, so that streaming the weights is spread over more workgroups.
+  if (N < 128) return gemm_tile<AT, 32, 80, 64, 2, 1>(A, lda, W, ldw, C, ldc, M, N, K, acc, vec, s);
+  if (M <= 64) return gemm_tile<AT, 64, 32, 64, 2, 1>(A, lda, W, ldw, C, ldc, M, N, K, acc, vec, s);
+  return gemm_tile<AT, 128, 128, 64, 2, 2>(A, lda, W, ldw, C, ldc, M, N, K, acc, vec, s);
 }
 
 hipError_t launch_gemm_bf16(const void* A, bool a_bf16, int64_t lda, const void* W, int64_t ldw,

@@ -105,4 +105,87 @@ hipError_t run_backbone_prefill(const mamba_backbone_dims& d, const mamba_backbo
   return launch_gemm_bf16(last, true, Dm, w.embed, Dm, logits, d.vocab, B, d.vocab, Dm, false, s);
 }
 
+// ----------------------------------------------------------------------------- decode step
+//
+// inference.rs page (mamba-rs 0.5.1), the step chain F1-F12 of the backbone engine: embed one
+// token per sequence, then per layer RMSNorm (F1), in_proj (F2), the conv step on the x lane
+// (F4, F4b), x_proj (F5), dt_proj (F6), softplus + state update + readout + D skip (F7-F9),
+// the silu(z) gate (F10), out_proj (F11) and the residual (F12); then norm_f and the tied head
+// (gpu_lm.rs page). Same weights and state layout as the prefill, so a prefill followed by
+// decode steps continues one sequence.
+
+struct DecodeLayout {
+  size_t h, xn, proj, u, xdbl, dt, y, last, total;
+};
+
+static DecodeLayout decode_layout(const mamba_backbone_dims& d, int B) {
+  const size_t xw = (size_t)d.dt_rank + 2 * (size_t)d.d_state;
+  DecodeLayout l{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += a256(bytes);
+    return at;
+  };
+  l.h = take((size_t)B * d.d_model * 4);
+  l.xn = take((size_t)B * d.d_model * 2);
+  l.proj = take((size_t)B * 2 * d.d_inner * 4);
+  l.u = take((size_t)B * d.d_inner * 4);
+  l.xdbl = take((size_t)B * xw * 4);
+  l.dt = take((size_t)B * d.d_inner * 4);
+  l.y = take((size_t)B * d.d_inner * 4);
+  l.last = take((size_t)B * d.d_model * 2);
+  l.total = off;
+  return l;
+}
+
+size_t backbone_decode_workspace_bytes(const mamba_backbone_dims& d, int B) {
+  return decode_layout(d, B).total;
+}
+
+hipError_t run_backbone_decode(const mamba_backbone_dims& d, const mamba_backbone_weights& w,
+                               const int32_t* tokens, int B, float* conv_state, float* ssm_state,
+                               float* logits, void* workspace, hipStream_t s) {
+  const DecodeLayout lay = decode_layout(d, B);
+  char* ws = static_cast<char*>(workspace);
+  float* h = reinterpret_cast<float*>(ws + lay.h);
+  void* xn = ws + lay.xn;
+  float* proj = reinterpret_cast<float*>(ws + lay.proj);
+  float* u = reinterpret_cast<float*>(ws + lay.u);
+  float* xdbl = reinterpret_cast<float*>(ws + lay.xdbl);
+  float* dt = reinterpret_cast<float*>(ws + lay.dt);
+  float* y = reinterpret_cast<float*>(ws + lay.y);
+  void* last = ws + lay.last;
+
+  const int Dm = d.d_model, D = d.d_inner, N = d.d_state, K = d.d_conv, R = d.dt_rank;
+  const int xw = R + 2 * N;
+  const auto* in_proj = static_cast<const bf16_storage*>(w.in_proj);
+  const auto* x_proj = static_cast<const bf16_storage*>(w.x_proj);
+  const auto* dt_proj = static_cast<const bf16_storage*>(w.dt_proj);
+  const auto* out_proj = static_cast<const bf16_storage*>(w.out_proj);
+
+  hipError_t e = launch_embed_gather(tokens, w.embed, h, B, d.vocab, Dm, s);
+  if (e != hipSuccess) return e;
+  for (int l = 0; l < d.n_layers; ++l) {
+    if ((e = launch_rmsnorm(h, Dm, w.norm_w + (int64_t)l * Dm, d.eps, xn, true, B, Dm, s)) != hipSuccess) return e;
+    if ((e = launch_gemm_bf16(xn, true, Dm, in_proj + (int64_t)l * 2 * D * Dm, Dm, proj, 2 * D, B, 2 * D, Dm,
+                              false, s)) != hipSuccess) return e;
+    ConvStepArgs ca{proj, 2 * D, w.conv_w + (int64_t)l * D * K, w.conv_b + (int64_t)l * D,
+                    conv_state + (int64_t)l * B * D * K, u, false, 1, B, D, K};
+    if ((e = launch_conv1d_step(ca, s)) != hipSuccess) return e;
+    if ((e = launch_gemm_bf16(u, false, D, x_proj + (int64_t)l * xw * D, D, xdbl, xw, B, xw, D, false, s)) !=
+        hipSuccess) return e;
+    if ((e = launch_gemm_bf16(xdbl, false, xw, dt_proj + (int64_t)l * D * R, R, dt, D, B, D, R, false, s)) !=
+        hipSuccess) return e;
+    SsmStepArgs sa{u, dt, w.dt_bias + (int64_t)l * D, true, w.A_log + (int64_t)l * D * N, xdbl + R,
+                   xdbl + R + N, xw, w.D_skip + (int64_t)l * D, proj + D, 2 * D,
+                   ssm_state + (int64_t)l * B * D * N, y, false, 1, B, D, N};
+    if ((e = launch_ssm_step(sa, s)) != hipSuccess) return e;
+    if ((e = launch_gemm_bf16(y, false, D, out_proj + (int64_t)l * Dm * D, D, h, Dm, B, Dm, D, true, s)) !=
+        hipSuccess) return e;
+  }
+  if ((e = launch_rmsnorm(h, Dm, w.norm_f, d.eps, last, true, B, Dm, s)) != hipSuccess) return e;
+  return launch_gemm_bf16(last, true, Dm, w.embed, Dm, logits, d.vocab, B, d.vocab, Dm, false, s);
+}
+
 }  // namespace mamba

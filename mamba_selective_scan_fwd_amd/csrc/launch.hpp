@@ -139,6 +139,10 @@ size_t backbone_workspace_bytes(const mamba_backbone_dims& d, int B, int T);
 hipError_t run_backbone_prefill(const mamba_backbone_dims& d, const mamba_backbone_weights& w,
                                 const int32_t* tokens, int B, int T, float* conv_state,
                                 float* ssm_state, float* logits, void* workspace, hipStream_t s);
+size_t backbone_decode_workspace_bytes(const mamba_backbone_dims& d, int B);
+hipError_t run_backbone_decode(const mamba_backbone_dims& d, const mamba_backbone_weights& w,
+                               const int32_t* tokens, int B, float* conv_state, float* ssm_state,
+                               float* logits, void* workspace, hipStream_t s);
 hipError_t launch_conv1d_step(const ConvStepArgs& a, hipStream_t s);
 hipError_t launch_selective_scan_fwd(const ScanFwdArgs& a, hipStream_t s);
 hipError_t launch_ssm_step(const SsmStepArgs& a, hipStream_t s);

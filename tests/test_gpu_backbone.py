@@ -42,6 +42,10 @@ GEMM_CASES = [
     (8, 1000, 33, "f32", False),       # few-row path, ragged K
     (3, 768, 1536, "f32", True),       # few-row path accumulating (a 1-token prefill of 3 prompts)
     (8, 200, 3000, "f32", False),      # few rows but M * K beyond the staging LDS: MFMA tiles
+    (64, 3072, 768, "bf16", False),    # a decode step's in_proj (B = 64): 64 x 32 tiles
+    (64, 768, 1536, "f32", True),      # a decode step's out_proj + residual
+    (40, 1536, 48, "f32", False),      # dt_proj at B = 40
+    (64, 50280, 768, "bf16", False),   # the head at B = 64
 ]
 
 
@@ -239,3 +243,145 @@ def test_backbone_full_size_24_layers():
              f"max-rel {s_max:.2e} normwise {s_nw:.2e}")
         assert np.isfinite(e_max) and e_max <= max(TOL_BF16, 3 * s_max), name
         assert e_nw <= max(TOL_BF16, 3 * s_nw), name
+
+
+# ------------------------------------------------------------------ decode steps of the backbone
+
+def _prefill_then_decode(s, t, st, tokens, n_prefill, graph=False):
+    """GPU: prefill the first n_prefill tokens, then one decode step per remaining token
+    (eager or replayed from the captured graph). Returns the logits after every step and the
+    final states."""
+    B, T = tokens.shape
+    L = s.n_layers
+    dims = _dims(s)
+    cs = torch.zeros(L, B, s.D, s.K, device="cuda")
+    hs = torch.zeros(L, B, s.D, s.N, device="cuda")
+    logits = torch.empty(B, s.vocab, device="cuda")
+    tok = torch.from_numpy(np.ascontiguousarray(tokens)).cuda()
+    ws = torch.empty(m.mamba_backbone_workspace_size(dims, B, n_prefill), dtype=torch.uint8, device="cuda")
+    m.mamba_backbone_prefill(dims, st, tok[:, :n_prefill].contiguous(), cs, hs, logits, ws)
+    out = [host(logits)]
+    wsd = torch.empty(m.mamba_backbone_decode_workspace_size(dims, B), dtype=torch.uint8, device="cuda")
+    step_tok = torch.empty(B, dtype=torch.int32, device="cuda")
+    g = m.DecodeGraph(dims, st, step_tok, cs, hs, logits, wsd) if graph else None
+    for i in range(n_prefill, T):
+        step_tok.copy_(tok[:, i])
+        if graph:
+            g.launch()
+        else:
+            m.mamba_backbone_decode_step(dims, st, step_tok, cs, hs, logits, wsd)
+        out.append(host(logits))
+    torch.cuda.synchronize()
+    if g is not None:
+        g.close()
+    return out, host(cs), host(hs)
+
+
+def _oracle_prefill_then_decode(s, w, tokens, n_prefill, accum="f64"):
+    lg, cs, hs, _ = ob.prefill(w, tokens[:, :n_prefill], s.n_layers, s.D, s.N, s.dt_rank, s.vocab, s.eps,
+                               accum=accum)
+    out = [lg]
+    for i in range(n_prefill, tokens.shape[1]):
+        lg, cs, hs, _ = ob.prefill(w, tokens[:, i:i + 1], s.n_layers, s.D, s.N, s.dt_rank, s.vocab, s.eps,
+                                   conv_state=cs, ssm_state=hs, accum=accum)
+        out.append(lg)
+    return out, cs, hs
+
+
+@pytest.mark.parametrize("graph", [False, True])
+def test_backbone_decode_small_vs_oracle(graph):
+    """Prefill 20 tokens, then 6 decode steps of the 3-layer stack, eager or from the graph;
+    logits after every step and the final states against the oracle (one-token prefills
+    carrying the states)."""
+    _say(f"case backbone decode small L3 B3, 20 + 6 tokens, graph={graph}")
+    s = SMALL
+    w = W.backbone_weights(s, seed=14)
+    tok = W.backbone_tokens(W.BackboneShape("small26", n_layers=3, B=3, T=26, d_model=64, D=128, N=16,
+                                            K=4, dt_rank=8, vocab=200, vocab_padded=256), seed=14)
+    t, st = _upload(w)
+    got, cs, hs = _prefill_then_decode(s, t, st, tok, 20, graph=graph)
+    ref, rcs, rhs = _oracle_prefill_then_decode(s, w, tok, 20)
+    for i, (g_, r_) in enumerate(zip(got, ref)):
+        e = rel_err(g_, r_)
+        assert e <= TOL_BF16, (i, e)
+    _check_backbone("small decode", (got[-1], cs, hs), (ref[-1], rcs, rhs))
+
+
+def test_backbone_decode_step_equals_one_token_prefill():
+    """A decode step and a one-token prefill from the same states run the same GEMMs and the
+    same conv arithmetic; only the scan's readout sum order differs (to rounding)."""
+    _say("case backbone decode step == one-token prefill")
+    s = SMALL
+    w = W.backbone_weights(s, seed=15)
+    tok = W.backbone_tokens(s, seed=15)
+    t, st = _upload(w)
+    dims = _dims(s)
+    B, L = s.B, s.n_layers
+    cs = torch.randn(L, B, s.D, s.K, device="cuda") * 0.5
+    hs = torch.randn(L, B, s.D, s.N, device="cuda") * 0.5
+    cs2, hs2 = cs.clone(), hs.clone()
+    one = torch.from_numpy(np.ascontiguousarray(tok[:, :1])).cuda()
+    lg1 = torch.empty(B, s.vocab, device="cuda")
+    lg2 = torch.empty_like(lg1)
+    ws = torch.empty(m.mamba_backbone_workspace_size(dims, B, 1), dtype=torch.uint8, device="cuda")
+    m.mamba_backbone_prefill(dims, st, one, cs, hs, lg1, ws)
+    wsd = torch.empty(m.mamba_backbone_decode_workspace_size(dims, B), dtype=torch.uint8, device="cuda")
+    m.mamba_backbone_decode_step(dims, st, one[:, 0].contiguous(), cs2, hs2, lg2, wsd)
+    torch.cuda.synchronize()
+    assert torch.equal(cs, cs2)
+    assert rel_err(host(lg2), host(lg1)) <= 1e-4
+    assert rel_err(host(hs2), host(hs)) <= 1e-5
+
+
+def test_backbone_decode_graph_replays_equal_eager():
+    """Replays of the captured decode step, interleaved with eager steps on copies of the
+    states and synchronizations, give exactly the eager results every time."""
+    _say("case decode graph replays == eager steps")
+    s = SMALL
+    w = W.backbone_weights(s, seed=16)
+    tok = W.backbone_tokens(s, seed=16)
+    t, st = _upload(w)
+    dims = _dims(s)
+    B, L = s.B, s.n_layers
+    g0 = torch.Generator(device="cuda").manual_seed(3)
+    cs_g = torch.randn(L, B, s.D, s.K, device="cuda", generator=g0)
+    hs_g = torch.randn(L, B, s.D, s.N, device="cuda", generator=g0)
+    cs_e, hs_e = cs_g.clone(), hs_g.clone()
+    lg_g = torch.empty(B, s.vocab, device="cuda")
+    lg_e = torch.empty_like(lg_g)
+    ws_g = torch.empty(m.mamba_backbone_decode_workspace_size(dims, B), dtype=torch.uint8, device="cuda")
+    ws_e = torch.empty_like(ws_g)
+    tk_g = torch.empty(B, dtype=torch.int32, device="cuda")
+    tk_e = torch.empty_like(tk_g)
+    graph = m.DecodeGraph(dims, st, tk_g, cs_g, hs_g, lg_g, ws_g)
+    for i in range(6):
+        col = torch.from_numpy(np.ascontiguousarray(tok[:, i])).cuda()
+        tk_g.copy_(col)
+        tk_e.copy_(col)
+        graph.launch()
+        m.mamba_backbone_decode_step(dims, st, tk_e, cs_e, hs_e, lg_e, ws_e)
+        torch.cuda.synchronize()
+        assert torch.equal(lg_g, lg_e), i
+        assert torch.equal(cs_g, cs_e) and torch.equal(hs_g, hs_e), i
+    graph.close()
+
+
+def test_backbone_decode_full_size():
+    """The 130m shapes (24 layers, vocab 50280), B = 4: prefill 24 tokens, then 4 decode steps
+    from the captured graph, against the oracle. The bar is three times the spread between
+    the oracle's f64 and f32 GEMM summations (as for the 24-layer prefill), and at least the
+    bf16 bar."""
+    s0 = W.C4
+    s = W.BackboneShape("c4-decode", n_layers=24, B=4, T=28)
+    _say("case backbone decode full shapes L24 B4, 24 + 4 tokens, graph")
+    w = W.backbone_weights(s0)
+    tok = W.backbone_tokens(s0)[:, :28]
+    t, st = _upload(w)
+    got, cs, hs = _prefill_then_decode(s, t, st, tok, 24, graph=True)
+    ref, rcs, rhs = _oracle_prefill_then_decode(s, w, tok, 24)
+    alt, acs, ahs = _oracle_prefill_then_decode(s, w, tok, 24, accum="f32")
+    for name, g_, r_, a_ in (("logits", got[-1], ref[-1], alt[-1]), ("conv_state", cs, rcs, acs),
+                             ("ssm_state", hs, rhs, ahs)):
+        e, spread = rel_err(g_, r_), rel_err(a_, r_)
+        _say(f"  {name}: gpu max-rel {e:.2e} | oracle f32-vs-f64 {spread:.2e}")
+        assert np.isfinite(e) and e <= max(TOL_BF16, 3 * spread), name
