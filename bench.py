@@ -10,7 +10,8 @@ Default workload: the 130m-shaped prefill layer (B=1, T=2048, d_inner=1536, d_st
 d_conv=4, f32 I/O). --config c3 runs the 2.8b-shaped layer (B=8, T=4096, d_inner=5120,
 bf16 I/O); --config c2 the batched decode step (24 layers, B=64, one token per step);
 --config c4 the full 24-layer 130m-shaped backbone prefill (B=4, T=2048, bf16 weights, MFMA
-GEMMs), one mamba_backbone_prefill call per step.
+GEMMs), one mamba_backbone_prefill call per step; --config c4d one decode step of that
+backbone for 64 sequences (after a 64-token prefill), replayed from its captured HIP graph.
 
 Prints one JSON line. `value` is tokens/s/layer (batch tokens per step / step time);
 `roofline` covers the dominant kernel call, timed with HIP events on the stream it runs
@@ -40,7 +41,7 @@ def parse_args(argv=None):
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--config", default="c1", choices=["c1", "c3", "c2", "c4"])
+    p.add_argument("--config", default="c1", choices=["c1", "c3", "c2", "c4", "c4d"])
     p.add_argument("--path", default="auto", choices=["auto", "fused", "split"],
                    help="prefill: one fused mamba_conv_scan_fwd call, or mamba_conv1d_fwd then "
                         "mamba_selective_scan_fwd; auto = fused for f32 I/O, split for bf16 (where "
@@ -495,6 +496,89 @@ def bench_backbone(args, shape):
     return result, dict(weights=w, tokens=tok_np)
 
 
+def bench_backbone_decode(args, shape):
+    """One step = one replay of the captured backbone decode step (one token for each of B
+    sequences through all layers and the head). Eager (one launch per kernel) is timed too."""
+    import numpy as np
+    import torch
+
+    import mamba_selective_scan_fwd_amd as m
+    import workloads as W
+
+    B, P = 64, 64  # sequences, prefill length before the timed decode steps
+    L, Dm, D, N, K, R = shape.n_layers, shape.d_model, shape.D, shape.N, shape.K, shape.dt_rank
+    dev = torch.device("cuda:0")
+    print(f"[bench] generating backbone weights (L={L}) and {B} x {P} prompt tokens", file=sys.stderr, flush=True)
+    w = W.backbone_weights(shape)
+    bs = W.BackboneShape("c4d", n_layers=L, B=B, T=P + args.steps + args.warmup + 8)
+    tok = torch.from_numpy(W.backbone_tokens(bs)).to(dev)
+    bf = ("embed", "in_proj", "x_proj", "dt_proj", "out_proj")
+    t = {k: torch.from_numpy(np.ascontiguousarray(v)).to(torch.bfloat16 if k in bf else torch.float32).to(dev)
+         for k, v in w.items()}
+    wst = m.backbone_weights_struct(t)
+    dims = m.BackboneDims(L, Dm, D, N, K, R, shape.vocab, shape.vocab_padded, shape.eps)
+    cs = torch.zeros(L, B, D, K, device=dev)
+    hs = torch.zeros(L, B, D, N, device=dev)
+    logits = torch.empty(B, shape.vocab, device=dev)
+    ws = torch.empty(m.mamba_backbone_workspace_size(dims, B, P), dtype=torch.uint8, device=dev)
+    m.mamba_backbone_prefill(dims, wst, tok[:, :P].contiguous(), cs, hs, logits, ws)
+    wsd = torch.empty(m.mamba_backbone_decode_workspace_size(dims, B), dtype=torch.uint8, device=dev)
+    step_tok = torch.empty(B, dtype=torch.int32, device=dev)
+    graph = m.DecodeGraph(dims, wst, step_tok, cs, hs, logits, wsd)
+    stream = torch.cuda.current_stream()
+    pos = [P]
+
+    def next_tokens():
+        step_tok.copy_(tok[:, pos[0]])
+        pos[0] += 1
+
+    for _ in range(args.warmup):
+        next_tokens()
+        graph.launch(stream)
+    torch.cuda.synchronize()
+    t0, t1 = _events(torch)
+    t0.record(stream)
+    for _ in range(args.steps):
+        next_tokens()
+        graph.launch(stream)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_graph = t0.elapsed_time(t1) / args.steps
+    # eager, for context (same number of steps, states keep advancing)
+    e0, e1 = _events(torch)
+    e0.record(stream)
+    for _ in range(min(args.steps, 8)):
+        m.mamba_backbone_decode_step(dims, wst, step_tok, cs, hs, logits, wsd, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_eager = e0.elapsed_time(e1) / min(args.steps, 8)
+    assert torch.isfinite(logits).all(), "non-finite logits"
+    graph.close()
+    # the step is weight-streaming bound: every layer's projections and the head are read once
+    wbytes = 2 * (L * (2 * D * Dm + (R + 2 * N) * D + D * R + Dm * D) + shape.vocab * Dm)
+    sbytes = 8 * L * B * D * (N + K)
+    nbytes = wbytes + sbytes
+    achieved = nbytes / (ms_graph * 1e-3) / 1e9
+    result = dict(
+        metric=METRIC,
+        value=B * L / (ms_graph * 1e-3),
+        unit="tokens/s/layer",
+        ms_per_step=ms_graph,
+        dtype="bf16",
+        config=dict(workload=f"c4d: one decode step of the {L}-layer 130m-shaped backbone for B={B} sequences "
+                             f"(after a {P}-token prefill), replayed from its captured HIP graph",
+                    B=B, n_layers=L, d_model=Dm, d_inner=D, d_state=N, vocab=shape.vocab),
+        roofline=dict(bound="hbm", achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s",
+                      frac=achieved / HBM_PEAK_GBS, traffic=None, call="decode step (graph)",
+                      algorithmic_bytes=nbytes, avg_ms=ms_graph),
+        calls={"graph replay": dict(avg_us=ms_graph * 1e3), "eager step": dict(avg_us=ms_eager * 1e3)},
+        backbone_tokens_per_s=B / (ms_graph * 1e-3),
+        layer_gbs=None,
+        layer_hbm_frac=None,
+    )
+    return result, None
+
+
 def cpu_baseline_backbone(shape, data, budget_s):
     """The f64 backbone oracle on sequence 0 of the batch over its first T' tokens, all layers
     (T' from a probe so the run takes about budget_s)."""
@@ -543,11 +627,13 @@ def main(argv=None):
         torch.cuda.synchronize()
         print(json.dumps(dict(calibrate_copy_bytes=n * 4, launches=3)), flush=True)
         return
-    shape = W.CONFIGS[args.config]
+    shape = W.CONFIGS.get(args.config, W.C4)
     if args.config == "c2":
         result, inp = bench_decode(args, shape)
     elif args.config == "c4":
         result, inp = bench_backbone(args, shape)
+    elif args.config == "c4d":
+        result, inp = bench_backbone_decode(args, W.C4)
     else:
         result, inp = bench_prefill(args, shape)
     cpu = None
