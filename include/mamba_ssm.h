@@ -309,6 +309,36 @@ mamba_status mamba_backbone_prefill(const mamba_backbone_dims* dims,
                                     size_t workspace_bytes, void* stream);
 
 /*
+ * Prefill variants of mamba_backbone_prefill (the pages' prefill output and batching
+ * options): [prefill.rs] the prefill that returns the norm_f output of every position
+ * instead of only the last one, the prefill from raw input rows instead of token ids, and a
+ * ragged batch in which each sequence has its own length (the pages fall back to step-by-step
+ * decoding for it; here one batched call).
+ *
+ *   tokens   in   [B, T] int32, or NULL when embeds is given (exactly one of the two).
+ *   embeds   in   [B, T, d_model] f32 raw input rows (the residual stream starts there).
+ *   lengths  in   [B] int32 device array or NULL (= T for all). Sequences are right-padded to
+ *                 T; each one's states are taken after its own last token (a length is
+ *                 clamped to [0, T]; 0 leaves that sequence's states unchanged). Outputs at
+ *                 padded positions are unspecified.
+ *   logits   out  [B, vocab] f32: the head on each sequence's last valid token, or NULL.
+ *   hidden   out  [B, T, d_model] f32: norm_f of the residual stream at every position, or NULL.
+ * At least one of logits and hidden. Workspace: mamba_backbone_workspace_size(dims, B, T).
+ */
+typedef struct mamba_prefill_io {
+  const int32_t* tokens;
+  const float* embeds;
+  const int32_t* lengths;
+  float* logits;
+  float* hidden;
+} mamba_prefill_io;
+mamba_status mamba_backbone_prefill_ex(const mamba_backbone_dims* dims,
+                                       const mamba_backbone_weights* weights,
+                                       const mamba_prefill_io* io, int B, int T,
+                                       float* conv_state, float* ssm_state, void* workspace,
+                                       size_t workspace_bytes, void* stream);
+
+/*
  * One decode step of the whole backbone: one new token per sequence through all layers and
  * the tied head. [inference.rs] the backbone step chain F1-F12 (RMSNorm, in_proj, conv step
  * on the x lane, x_proj, dt_proj, softplus + state update + readout + D skip, silu(z) gate,

@@ -45,6 +45,7 @@ symbols = {
     "mamba_gemm_bf16": ([_P, _I, _I64, _P, _I64, _P, _I64, _I, _I, _I, _I, _P], _I),
     "mamba_backbone_workspace_size": ([_P, _I, _I], _SZ),
     "mamba_backbone_prefill": ([_P, _P, _P, _I, _I, _P, _P, _P, _P, _SZ, _P], _I),
+    "mamba_backbone_prefill_ex": ([_P, _P, _P, _I, _I, _P, _P, _P, _SZ, _P], _I),
     "mamba_backbone_decode_workspace_size": ([_P, _I], _SZ),
     "mamba_backbone_decode_step": ([_P, _P, _P, _I, _P, _P, _P, _P, _SZ, _P], _I),
     "mamba_backbone_decode_graph_create": ([_P, _P, _P, _I, _P, _P, _P, _P, _SZ,
@@ -66,6 +67,11 @@ class BackboneWeights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "embed", "norm_f", "norm_w", "in_proj", "conv_w", "conv_b", "x_proj", "dt_proj",
         "dt_bias", "A_log", "D_skip", "out_proj")]
+
+class PrefillIO(ctypes.Structure):
+    """mamba_prefill_io."""
+    _fields_ = [(n, ctypes.c_void_p) for n in ("tokens", "embeds", "lengths", "logits", "hidden")]
+
 
 _STATUS = {1: "MAMBA_EINVAL", 2: "MAMBA_EUNSUPPORTED", 3: "MAMBA_EWORKSPACE", 4: "MAMBA_EHIP"}
 
@@ -373,3 +379,16 @@ class DecodeGraph:
             self.close()
         except Exception:
             pass
+
+
+def mamba_backbone_prefill_ex(dims: BackboneDims, weights: BackboneWeights, B: int, T: int, conv_state,
+                              ssm_state, workspace, tokens=None, embeds=None, lengths=None, logits=None,
+                              hidden=None, stream=None) -> None:
+    """Prefill variants: token ids [B, T] or raw input rows embeds [B, T, d_model]; optional
+    per-sequence lengths [B] int32 (right-padded ragged batch); logits [B, vocab] of each last
+    valid token and/or hidden [B, T, d_model] (norm_f at every position)."""
+    io = PrefillIO(_ptr(tokens), _ptr(embeds), _ptr(lengths), _ptr(logits), _ptr(hidden))
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(load_library().mamba_backbone_prefill_ex(
+        ctypes.byref(dims), ctypes.byref(weights), ctypes.byref(io), B, T, _ptr(conv_state),
+        _ptr(ssm_state), _ptr(workspace), ws_bytes, _stream(stream)))

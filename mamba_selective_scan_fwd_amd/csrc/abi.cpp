@@ -589,6 +589,56 @@ mamba_status mamba_backbone_prefill(const mamba_backbone_dims* dims,
   });
 }
 
+mamba_status mamba_backbone_prefill_ex(const mamba_backbone_dims* dims,
+                                       const mamba_backbone_weights* w, const mamba_prefill_io* io,
+                                       int B, int T, float* conv_state, float* ssm_state,
+                                       void* workspace, size_t workspace_bytes, void* stream) {
+  static const char* fn = "mamba_backbone_prefill_ex";
+  return guarded([&] {
+    check_backbone_dims(fn, dims);
+    if (!io) fail(MAMBA_EINVAL, fn, "io is NULL");
+    check_dim(fn, "B", B);
+    check_dim(fn, "T", T);
+    if (B == 0 || T == 0) return;
+    if (B > kMaxGridYZ) fail(MAMBA_EUNSUPPORTED, fn, "B = %d exceeds %d", B, kMaxGridYZ);
+    if ((int64_t)B * T > INT32_MAX / 2) fail(MAMBA_EUNSUPPORTED, fn, "B * T too large");
+    if (!io->tokens == !io->embeds) fail(MAMBA_EINVAL, fn, "exactly one of tokens and embeds must be given");
+    if (!io->logits && !io->hidden) fail(MAMBA_EINVAL, fn, "neither logits nor hidden is requested");
+    const mamba_backbone_dims& d = *dims;
+    const int64_t bt = (int64_t)B * T;
+    check_ptr(fn, "embeds", io->embeds, 4, false);
+    check_ptr(fn, "lengths", io->lengths, 4, false);
+    check_ptr(fn, "hidden", io->hidden, 4, false);
+    const size_t need = mamba::backbone_workspace_bytes(d, B, T);
+    // the shared checks want a logits buffer and a token array: stand in the ones present
+    const float* lg = io->logits ? io->logits : io->hidden;
+    const int32_t* tk = io->tokens ? io->tokens : reinterpret_cast<const int32_t*>(io->embeds);
+    check_backbone_call(fn, d, w, tk, io->tokens ? bt : bt * d.d_model, io->logits ? B : 0, conv_state,
+                        ssm_state, lg, workspace, workspace_bytes, need);
+    const Range rws = range("workspace", workspace, 1, (int64_t)need, (int64_t)need, 1);
+    const Range rhid = range("hidden", io->hidden, bt, d.d_model, d.d_model, 4);
+    const Range rlog = range("logits", io->logits, B, d.vocab, d.vocab, 4);
+    const Range rlen = range("lengths", io->lengths, 1, B, B, 4);
+    const Range remb = range("embeds", io->embeds, bt, d.d_model, d.d_model, 4);
+    const int64_t L = d.n_layers;
+    const Range rcs = range("conv_state", conv_state, L * B * d.d_inner, d.d_conv, d.d_conv, 4);
+    const Range rss = range("ssm_state", ssm_state, L * B * d.d_inner, d.d_state, d.d_state, 4);
+    check_disjoint(fn, rhid, {rws, rlog, rlen, remb, rcs, rss});
+    check_disjoint(fn, rws, {rlen, remb});
+    check_disjoint(fn, rlog, {rlen, remb});
+    check_disjoint(fn, rcs, {rlen, remb});
+    check_disjoint(fn, rss, {rlen, remb});
+    mamba::BackbonePrefillIO pio{};
+    pio.tokens = io->tokens;
+    pio.embeds = io->embeds;
+    pio.lengths = io->lengths;
+    pio.logits = io->logits;
+    pio.hidden = io->hidden;
+    check_hip(fn, mamba::run_backbone_prefill_io(d, *w, pio, B, T, conv_state, ssm_state, workspace,
+                                                 static_cast<hipStream_t>(stream)));
+  });
+}
+
 size_t mamba_backbone_decode_workspace_size(const mamba_backbone_dims* dims, int B) {
   if (!dims || B <= 0) return 0;
   return mamba::backbone_decode_workspace_bytes(*dims, B);

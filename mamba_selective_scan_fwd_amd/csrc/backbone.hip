@@ -55,6 +55,28 @@ __global__ void __launch_bounds__(256) rmsnorm_kernel(const float* __restrict__ 
   for (int c = threadIdx.x; c < Dm; c += 256) o[c] = from_f32<OT>(xr[c] * inv * (w ? w[c] : 1.0f));
 }
 
+// RMSNorm of each sequence's last valid position: row b * T + clamp(lengths[b], 1, T) - 1.
+template <typename OT>
+__global__ void __launch_bounds__(256) rmsnorm_last_kernel(const float* __restrict__ x,
+                                                           const int32_t* __restrict__ lengths,
+                                                           int T, const float* __restrict__ w,
+                                                           float eps, OT* __restrict__ out,
+                                                           int Dm) {
+  __shared__ float part[4];
+  const int b = blockIdx.x;
+  const int t = min(max(lengths[b], 1), T) - 1;
+  const float* xr = x + ((int64_t)b * T + t) * Dm;
+  float ss = 0.0f;
+  for (int c = threadIdx.x; c < Dm; c += 256) ss = fmaf(xr[c], xr[c], ss);
+  for (int m = 32; m >= 1; m /= 2) ss += __shfl_xor(ss, m);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  const float tot = part[0] + part[1] + part[2] + part[3];
+  const float inv = 1.0f / sqrtf(tot / (float)Dm + eps);
+  OT* o = out + (int64_t)b * Dm;
+  for (int c = threadIdx.x; c < Dm; c += 256) o[c] = from_f32<OT>(xr[c] * inv * (w ? w[c] : 1.0f));
+}
+
 // ------------------------------------------------------------------------- GEMM (MFMA)
 //
 // C[M, N] (+)= A[M, K] * W[N, K]^T with A f32 or bf16 (rounded to bf16 when staged), W bf16
@@ -300,6 +322,17 @@ hipError_t launch_rmsnorm(const float* x, int64_t x_row_stride, const float* w, 
   else
     rmsnorm_kernel<float><<<dim3((unsigned)rows), 256, 0, s>>>(x, x_row_stride, w, eps,
                                                                static_cast<float*>(out), Dm);
+  return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm_last(const float* x, const int32_t* lengths, int T, const float* w,
+                               float eps, void* out, bool out_bf16, int B, int Dm, hipStream_t s) {
+  if (out_bf16)
+    rmsnorm_last_kernel<bf16><<<dim3((unsigned)B), 256, 0, s>>>(x, lengths, T, w, eps,
+                                                                static_cast<bf16*>(out), Dm);
+  else
+    rmsnorm_last_kernel<float><<<dim3((unsigned)B), 256, 0, s>>>(x, lengths, T, w, eps,
+                                                                 static_cast<float*>(out), Dm);
   return hipGetLastError();
 }
 

@@ -51,6 +51,15 @@ size_t backbone_workspace_bytes(const mamba_backbone_dims& d, int B, int T) {
 hipError_t run_backbone_prefill(const mamba_backbone_dims& d, const mamba_backbone_weights& w,
                                 const int32_t* tokens, int B, int T, float* conv_state,
                                 float* ssm_state, float* logits, void* workspace, hipStream_t s) {
+  BackbonePrefillIO io{};
+  io.tokens = tokens;
+  io.logits = logits;
+  return run_backbone_prefill_io(d, w, io, B, T, conv_state, ssm_state, workspace, s);
+}
+
+hipError_t run_backbone_prefill_io(const mamba_backbone_dims& d, const mamba_backbone_weights& w,
+                                   const BackbonePrefillIO& io, int B, int T, float* conv_state,
+                                   float* ssm_state, void* workspace, hipStream_t s) {
   const BackboneLayout lay = backbone_layout(d, B, T);
   char* ws = static_cast<char*>(workspace);
   float* h = reinterpret_cast<float*>(ws + lay.h);
@@ -71,7 +80,9 @@ hipError_t run_backbone_prefill(const mamba_backbone_dims& d, const mamba_backbo
   const auto* dt_proj = static_cast<const bf16_storage*>(w.dt_proj);
   const auto* out_proj = static_cast<const bf16_storage*>(w.out_proj);
 
-  hipError_t e = launch_embed_gather(tokens, w.embed, h, bt, d.vocab, Dm, s);
+  // the residual stream starts at the embedding rows, or at the caller's raw inputs
+  hipError_t e = io.embeds ? hipMemcpyAsync(h, io.embeds, sizeof(float) * bt * Dm, hipMemcpyDeviceToDevice, s)
+                           : launch_embed_gather(io.tokens, w.embed, h, bt, d.vocab, Dm, s);
   if (e != hipSuccess) return e;
   for (int l = 0; l < d.n_layers; ++l) {
     // F1: normed activations, already bf16 for the in_proj GEMM
@@ -82,6 +93,7 @@ hipError_t run_backbone_prefill(const mamba_backbone_dims& d, const mamba_backbo
     // F4a: conv + SiLU over the x lane, carrying this layer's conv state
     ConvFwdArgs ca{proj, 2 * D, w.conv_w + (int64_t)l * D * K, w.conv_b + (int64_t)l * D,
                    conv_state + (int64_t)l * B * D * K, u, false, B, T, D, K};
+    ca.lengths = io.lengths;
     if ((e = launch_conv1d_fwd(ca, s)) != hipSuccess) return e;
     // F4b: xdbl = u @ x_proj^T   [bt, R + 2N]: dt lane | B | C
     if ((e = launch_gemm_bf16(u, false, D, x_proj + (int64_t)l * xw * D, D, xdbl, xw, (int)bt, xw, D,
@@ -94,15 +106,23 @@ hipError_t run_backbone_prefill(const mamba_backbone_dims& d, const mamba_backbo
                    xdbl + R, xdbl + R + N, xw, w.D_skip + (int64_t)l * D, proj + D, 2 * D,
                    ssm_state + (int64_t)l * B * D * N, ssm_state + (int64_t)l * B * D * N, y,
                    false, B, T, D, N, scan_ws};
+    sa.lengths = io.lengths;
     if ((e = launch_selective_scan_fwd(sa, s)) != hipSuccess) return e;
     // F5 + F6: h += y @ out_proj^T
     if ((e = launch_gemm_bf16(y, false, D, out_proj + (int64_t)l * Dm * D, D, h, Dm, (int)bt, Dm, D,
                               true, s)) != hipSuccess) return e;
   }
-  // norm_f on the last timestep of each sequence, then the tied head against the embedding
-  if ((e = launch_rmsnorm(h + (int64_t)(T - 1) * Dm, (int64_t)T * Dm, w.norm_f, d.eps, last, true, B,
-                          Dm, s)) != hipSuccess) return e;
-  return launch_gemm_bf16(last, true, Dm, w.embed, Dm, logits, d.vocab, B, d.vocab, Dm, false, s);
+  // norm_f at every position (the all-T output), and on each sequence's last (valid) token
+  // followed by the tied head against the embedding
+  if (io.hidden && (e = launch_rmsnorm(h, Dm, w.norm_f, d.eps, io.hidden, false, bt, Dm, s)) != hipSuccess)
+    return e;
+  if (!io.logits) return hipSuccess;
+  if (io.lengths)
+    e = launch_rmsnorm_last(h, io.lengths, T, w.norm_f, d.eps, last, true, B, Dm, s);
+  else
+    e = launch_rmsnorm(h + (int64_t)(T - 1) * Dm, (int64_t)T * Dm, w.norm_f, d.eps, last, true, B, Dm, s);
+  if (e != hipSuccess) return e;
+  return launch_gemm_bf16(last, true, Dm, w.embed, Dm, io.logits, d.vocab, B, d.vocab, Dm, false, s);
 }
 
 // ----------------------------------------------------------------------------- decode step

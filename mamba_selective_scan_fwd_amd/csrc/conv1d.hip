@@ -58,7 +58,7 @@ template <typename IO, int K, int V>
 __global__ void __launch_bounds__(256) conv1d_fwd_kernel(
     const IO* __restrict__ x, int64_t x_row_stride, const float* __restrict__ conv_w,
     const float* __restrict__ conv_b, float* __restrict__ conv_state, IO* __restrict__ u, int B,
-    int T, int D, int tile_t) {
+    int T, int D, int tile_t, const int32_t* __restrict__ lengths) {
   const int d0 = (blockIdx.x * blockDim.x + threadIdx.x) * V;
   const int b = blockIdx.y;
   const int t0 = blockIdx.z * tile_t;
@@ -137,11 +137,13 @@ __global__ void __launch_bounds__(256) conv1d_fwd_kernel(
   }
 
   if (t0 == 0 && st) {
-    // New state: X[T .. T+K-1]. Entries with index >= K are tokens T-K..T-1; the others
-    // (only when T < K) are the old state shifted left by T.
+    // New state: X[Tb .. Tb+K-1] with Tb this sequence's length (T unless lengths are given).
+    // Entries with index >= K are tokens Tb-K..Tb-1; the others (Tb < K) are the old state
+    // shifted left by Tb.
+    const int Tb = lengths ? min(max(lengths[b], 0), T) : T;
 #pragma unroll
     for (int k = 0; k < K; ++k) {
-      const int i = T + k;
+      const int i = Tb + k;
       float r[V];
       if (i >= K) {
         Vec<IO, V>::load(r, xb + (int64_t)(i - K) * x_row_stride);
@@ -204,7 +206,7 @@ static hipError_t launch_conv_fwd_kv(const ConvFwdArgs& a, hipStream_t s, int ti
   dim3 grid((lanes + threads - 1) / threads, a.B, tiles);
   conv1d_fwd_kernel<IO, K, V><<<grid, threads, 0, s>>>(
       static_cast<const IO*>(a.x), a.x_row_stride, a.conv_w, a.conv_b, a.conv_state,
-      static_cast<IO*>(a.u), a.B, a.T, a.D, tile_t);
+      static_cast<IO*>(a.u), a.B, a.T, a.D, tile_t, a.lengths);
   return hipGetLastError();
 }
 

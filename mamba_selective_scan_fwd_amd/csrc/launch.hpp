@@ -26,6 +26,9 @@ struct ConvFwdArgs {
   void* u;
   bool bf16;
   int B, T, D, K;
+  // per-sequence valid lengths (device, [B], clamped to [0, T]) or NULL: the new conv state
+  // is taken after each sequence's own last token
+  const int32_t* lengths = nullptr;
 };
 
 struct ConvStepArgs {
@@ -65,6 +68,9 @@ struct ScanFwdArgs {
   float* conv_state = nullptr;
   void* u_out = nullptr;
   int K = 0;
+  // per-sequence valid lengths (device, [B], clamped to [0, T]) or NULL: each sequence's
+  // states are taken after its own last token; y past it is not written
+  const int32_t* lengths = nullptr;
 };
 
 struct SsmStepArgs {
@@ -126,6 +132,10 @@ hipError_t launch_embed_gather(const int32_t* tokens, const void* E, float* out,
                                int vocab, int Dm, hipStream_t s);
 hipError_t launch_rmsnorm(const float* x, int64_t x_row_stride, const float* w, float eps,
                           void* out, bool out_bf16, int64_t rows, int Dm, hipStream_t s);
+// RMSNorm of row (b * T + clamp(lengths[b], 1, T) - 1) of x for b < B: each sequence's last
+// valid position.
+hipError_t launch_rmsnorm_last(const float* x, const int32_t* lengths, int T, const float* w,
+                               float eps, void* out, bool out_bf16, int B, int Dm, hipStream_t s);
 hipError_t launch_gemm_bf16(const void* A, bool a_bf16, int64_t lda, const void* W, int64_t ldw,
                             float* C, int64_t ldc, int M, int N, int K, bool accumulate,
                             hipStream_t s);
@@ -136,6 +146,18 @@ constexpr int64_t kSkinnyGemmMaxLds = 64 * 1024;
 hipError_t launch_conv1d_fwd(const ConvFwdArgs& a, hipStream_t s);
 
 size_t backbone_workspace_bytes(const mamba_backbone_dims& d, int B, int T);
+// Inputs and outputs of one backbone prefill: token ids or raw input rows, optional
+// per-sequence lengths, logits of each last valid token and/or norm_f rows of every position.
+struct BackbonePrefillIO {
+  const int32_t* tokens = nullptr;   // [B, T]
+  const float* embeds = nullptr;     // [B, T, d_model]
+  const int32_t* lengths = nullptr;  // [B]
+  float* logits = nullptr;           // [B, vocab]
+  float* hidden = nullptr;           // [B, T, d_model]
+};
+hipError_t run_backbone_prefill_io(const mamba_backbone_dims& d, const mamba_backbone_weights& w,
+                                   const BackbonePrefillIO& io, int B, int T, float* conv_state,
+                                   float* ssm_state, void* workspace, hipStream_t s);
 hipError_t run_backbone_prefill(const mamba_backbone_dims& d, const mamba_backbone_weights& w,
                                 const int32_t* tokens, int B, int T, float* conv_state,
                                 float* ssm_state, float* logits, void* workspace, hipStream_t s);

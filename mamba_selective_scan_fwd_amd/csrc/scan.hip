@@ -63,6 +63,7 @@ struct ScanParams {
   float* conv_state;       // [B][D][K] in/out, or NULL (zeros, not written)
   float* conv_ws;          // [B][D][K] copy of the incoming conv state (chunks > 1)
   void* u_out;             // [B][T][D] or NULL
+  const int32_t* lengths;  // [B] valid tokens per sequence (clamped to [0, T]) or NULL
   int64_t x_row_stride;
   int64_t bc_row_stride;
   int64_t z_row_stride;
@@ -129,7 +130,9 @@ scan_kernel(const ScanParams p) {
   const int c = blockIdx.z;
   const int N = p.N, D = p.D;
   const int t0 = c * p.chunk_t;
-  const int len = min(p.T, t0 + p.chunk_t) - t0;
+  // this sequence's length (ragged batches: each sequence stops at its own last token)
+  const int Tb = p.lengths ? min(max(p.lengths[b], 0), p.T) : p.T;
+  const int len = max(min(Tb, t0 + p.chunk_t) - t0, 0);  // 0: the chunk is past the end
   const int nblk = (len + kTB - 1) / kTB;
   const int64_t row0 = (int64_t)b * p.T + t0;  // first row of the chunk
   const int64_t bcs = p.bc_row_stride;
@@ -417,10 +420,13 @@ scan_kernel(const ScanParams p) {
     }
   };
 
-  // prologue: block 0 staged, block 1 in flight
-  load_block(0, std::integral_constant<int, 0>{});
-  stage_a(0, std::integral_constant<int, 0>{});
-  if (nblk > 1) load_block(1, std::integral_constant<int, 1>{});
+  // prologue: block 0 staged, block 1 in flight (an empty chunk loads nothing; its map is
+  // the identity and its state passes through)
+  if (nblk > 0) {
+    load_block(0, std::integral_constant<int, 0>{});
+    stage_a(0, std::integral_constant<int, 0>{});
+    if (nblk > 1) load_block(1, std::integral_constant<int, 1>{});
+  }
   __syncthreads();
   for (int k = 0; k < nblk; k += 2) {
     block(k, std::integral_constant<int, 0>{});
@@ -440,7 +446,7 @@ scan_kernel(const ScanParams p) {
       // new conv state X[T .. T+K-1]: x tokens T-K .. T-1, or (T < K) the old state shifted
       if (c == p.chunks - 1 && p.conv_state && g == 0) {
         for (int kk = 0; kk < K; ++kk) {
-          const int i = p.T + kk;
+          const int i = Tb + kk;
           p.conv_state[((int64_t)b * D + d) * K + kk] =
               i >= K ? to_f32(xin[((int64_t)b * p.T + i - K) * p.x_row_stride + d])
                      : (cs_old ? cs_old[((int64_t)b * D + d) * K + i] : 0.0f);
@@ -522,6 +528,7 @@ static hipError_t launch_scan_npk(const ScanFwdArgs& a, const ScanPlan& pl, hipS
   p.conv_b = a.conv_b;
   p.conv_state = a.conv_state;
   p.u_out = a.u_out;
+  p.lengths = a.lengths;
   p.x_row_stride = a.x_row_stride;
   p.bc_row_stride = a.bc_row_stride;
   p.z_row_stride = a.z_row_stride;

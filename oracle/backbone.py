@@ -46,18 +46,23 @@ def gemm(A, W, accum: str = "f64") -> np.ndarray:
     return bf16(A) @ bf16(W).T
 
 
-def prefill(w: dict, tokens: np.ndarray, n_layers: int, d_inner: int, d_state: int,
+def prefill(w: dict, tokens, n_layers: int, d_inner: int, d_state: int,
             dt_rank: int, vocab: int, eps: float, conv_state=None, ssm_state=None,
-            accum: str = "f64"):
-    """Returns (logits [B, vocab], conv_state [L,B,D,K], ssm_state [L,B,D,N], hidden [B,T,Dm]).
-    accum: the GEMMs' summation precision (see gemm)."""
+            accum: str = "f64", embeds=None):
+    """Returns (logits [B, vocab], conv_state [L,B,D,K], ssm_state [L,B,D,N], hidden [B,T,Dm]),
+    hidden being the residual stream before norm_f. embeds: [B, T, Dm] raw input rows used in
+    place of the embedding of `tokens` (the raw-input prefill). accum: the GEMMs' summation
+    precision (see gemm)."""
     def gemm_(A, W):
         return gemm(A, W, accum)
 
-    Bsz, T = tokens.shape
+    if embeds is not None:
+        h = np.array(embeds, np.float64)  # [B, T, Dm]
+    else:
+        h = np.asarray(w["embed"], np.float64)[tokens]
+    Bsz, T = h.shape[:2]
     D, N, R = d_inner, d_state, dt_rank
     K = w["conv_w"].shape[2]
-    h = np.asarray(w["embed"], np.float64)[tokens]  # [B, T, Dm]
     cs_all = np.zeros((n_layers, Bsz, D, K)) if conv_state is None else np.array(conv_state, np.float64)
     hs_all = np.zeros((n_layers, Bsz, D, N)) if ssm_state is None else np.array(ssm_state, np.float64)
     for l in range(n_layers):

@@ -101,3 +101,13 @@ def test_gemm_f32_accumulation_is_close():
     a = ob.gemm(A, Wm, "f32")
     r = ob.gemm(A, Wm)
     assert np.max(np.abs(a - r)) <= 1e-5 * np.sqrt(700) * np.max(np.abs(r)) and not np.array_equal(a, r)
+
+
+def test_prefill_from_embedding_rows_equals_token_prefill():
+    """The raw-input prefill started at the embedding rows of the tokens is the token prefill."""
+    s, w, tok = _tiny()
+    a = ob.prefill(w, tok, s.n_layers, s.D, s.N, s.dt_rank, s.vocab, s.eps)
+    b = ob.prefill(w, None, s.n_layers, s.D, s.N, s.dt_rank, s.vocab, s.eps,
+                   embeds=w["embed"].astype(np.float64)[tok])
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(x, y)

@@ -385,3 +385,85 @@ def test_backbone_decode_full_size():
         e, spread = rel_err(g_, r_), rel_err(a_, r_)
         _say(f"  {name}: gpu max-rel {e:.2e} | oracle f32-vs-f64 {spread:.2e}")
         assert np.isfinite(e) and e <= max(TOL_BF16, 3 * spread), name
+
+
+# ------------------------------------------------------------------ prefill variants
+
+def _variant_run(s, st, B, T, tokens=None, embeds=None, lengths=None, want_logits=True, want_hidden=True,
+                 states=None):
+    dims = _dims(s)
+    L = s.n_layers
+    if states is None:
+        cs = torch.zeros(L, B, s.D, s.K, device="cuda")
+        hs = torch.zeros(L, B, s.D, s.N, device="cuda")
+    else:
+        cs, hs = states[0].clone(), states[1].clone()
+    logits = torch.empty(B, s.vocab, device="cuda") if want_logits else None
+    hidden = torch.empty(B, T, s.d_model, device="cuda") if want_hidden else None
+    ws = torch.empty(m.mamba_backbone_workspace_size(dims, B, T), dtype=torch.uint8, device="cuda")
+    m.mamba_backbone_prefill_ex(dims, st, B, T, cs, hs, ws, tokens=tokens, embeds=embeds, lengths=lengths,
+                                logits=logits, hidden=hidden)
+    torch.cuda.synchronize()
+    return logits, hidden, cs, hs
+
+
+def test_backbone_prefill_hidden_all_positions():
+    """norm_f output at every position against the oracle, and the logits equal to the plain
+    prefill's."""
+    _say("case backbone prefill, all-position norm_f output")
+    s = SMALL
+    w = W.backbone_weights(s, seed=17)
+    tok = W.backbone_tokens(s, seed=17)
+    t, st = _upload(w)
+    tk = torch.from_numpy(tok).cuda()
+    lg, hid, cs, hs = _variant_run(s, st, s.B, s.T, tokens=tk)
+    lg0, cs0, hs0 = _gpu_prefill(s, t, st, tok)
+    assert np.array_equal(host(lg), lg0) and np.array_equal(host(hs), hs0)
+    _, _, _, h = ob.prefill(w, tok, s.n_layers, s.D, s.N, s.dt_rank, s.vocab, s.eps)
+    e = rel_err(host(hid), ob.rmsnorm(h, w["norm_f"], s.eps))
+    _say(f"  hidden max-rel {e:.2e}")
+    assert e <= TOL_BF16
+
+
+def test_backbone_prefill_from_embeds_equals_tokens():
+    """The raw-input prefill started at the tokens' embedding rows is the token prefill, bit
+    for bit."""
+    _say("case backbone prefill from raw input rows")
+    s = SMALL
+    w = W.backbone_weights(s, seed=18)
+    tok = W.backbone_tokens(s, seed=18)
+    t, st = _upload(w)
+    tk = torch.from_numpy(tok).cuda()
+    emb = dev(w["embed"][tok])
+    a = _variant_run(s, st, s.B, s.T, tokens=tk)
+    b = _variant_run(s, st, s.B, s.T, embeds=emb)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("T,lengths", [(70, [70, 33, 1]), (400, [400, 150, 0])])
+def test_backbone_ragged_batch_vs_oracle(T, lengths):
+    """Right-padded sequences of different lengths in one call: each one's logits and states
+    against the oracle run on that sequence alone (T = 400 runs the scan in several chunks; a
+    zero length leaves that sequence's states as they were)."""
+    _say(f"case backbone ragged batch T{T} lengths {lengths}")
+    s = W.BackboneShape("rag", n_layers=3, B=3, T=T, d_model=64, D=128, N=16, K=4, dt_rank=8, vocab=200,
+                        vocab_padded=256)
+    w = W.backbone_weights(s, seed=19)
+    tok = W.backbone_tokens(s, seed=19)
+    t, st = _upload(w)
+    g = torch.Generator(device="cuda").manual_seed(6)
+    cs0 = torch.randn(3, 3, s.D, s.K, device="cuda", generator=g) * 0.5
+    hs0 = torch.randn(3, 3, s.D, s.N, device="cuda", generator=g) * 0.5
+    lens = torch.tensor(lengths, dtype=torch.int32, device="cuda")
+    lg, _, cs, hs = _variant_run(s, st, 3, T, tokens=torch.from_numpy(tok).cuda(), lengths=lens,
+                                 want_hidden=False, states=(cs0, hs0))
+    for b, n in enumerate(lengths):
+        if n == 0:
+            assert torch.equal(cs[:, b], cs0[:, b]) and torch.equal(hs[:, b], hs0[:, b])
+            continue
+        rl, rcs, rhs, _ = ob.prefill(w, tok[b:b + 1, :n], 3, s.D, s.N, s.dt_rank, s.vocab, s.eps,
+                                     conv_state=host(cs0[:, b:b + 1]), ssm_state=host(hs0[:, b:b + 1]))
+        errs = [rel_err(host(lg[b:b + 1]), rl), rel_err(host(cs[:, b:b + 1]), rcs), rel_err(host(hs[:, b:b + 1]), rhs)]
+        _say(f"  sequence {b} (length {n}): logits/conv/ssm {[f'{e:.2e}' for e in errs]}")
+        assert max(errs) <= TOL_BF16, (b, errs)
