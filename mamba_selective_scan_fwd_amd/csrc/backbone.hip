@@ -149,7 +149,17 @@ __device__ __forceinline__ bf16x8 load_chunk_scalar(const AT* row, int k0, int K
 template <typename AT, int BM, int BN, int BK, int WGM, int WGN, bool VEC>
 __global__ void __launch_bounds__(64 * WGM * WGN) gemm_mfma_kernel(
     const AT* __restrict__ A, int64_t lda, const bf16* __restrict__ W, int64_t ldw,
-    float* __restrict__ C, int64_t ldc, int M, int N, int K, int accumulate) {
+    float* __restrict__ C, int64_t ldc, int M, int N, int K, int accumulate, int k_chunk,
+    int64_t c_split_stride) {
+  // split K (gridDim.z > 1): slice z covers k in [z * k_chunk, z * k_chunk + k_chunk) and
+  // writes its partial product to its own C plane (C + z * c_split_stride)
+  {
+    const int k0 = blockIdx.z * k_chunk;
+    A += k0;
+    W += k0;
+    K = min(K - k0, k_chunk);
+    C += blockIdx.z * c_split_stride;
+  }
   constexpr int NT = 64 * WGM * WGN;
   constexpr int WTM = BM / WGM, WTN = BN / WGN;  // wave tile
   constexpr int TM = WTM / 16, TN = WTN / 16;
@@ -338,14 +348,16 @@ hipError_t launch_rmsnorm_last(const float* x, const int32_t* lengths, int T, co
 
 template <typename AT, int BM, int BN, int BK, int WGM, int WGN>
 static hipError_t gemm_tile(const AT* A, int64_t lda, const bf16* W, int64_t ldw, float* C,
-                            int64_t ldc, int M, int N, int K, bool acc, bool vec, hipStream_t s) {
-  const dim3 grid((unsigned)((N + BN - 1) / BN), (unsigned)((M + BM - 1) / BM));
+                            int64_t ldc, int M, int N, int K, bool acc, bool vec, hipStream_t s,
+                            int ks = 1, int k_chunk = 0, int64_t c_split_stride = 0) {
+  if (ks <= 1) k_chunk = K;
+  const dim3 grid((unsigned)((N + BN - 1) / BN), (unsigned)((M + BM - 1) / BM), (unsigned)ks);
   if (vec)
     gemm_mfma_kernel<AT, BM, BN, BK, WGM, WGN, true><<<grid, 64 * WGM * WGN, 0, s>>>(
-        A, lda, W, ldw, C, ldc, M, N, K, acc ? 1 : 0);
+        A, lda, W, ldw, C, ldc, M, N, K, acc ? 1 : 0, k_chunk, c_split_stride);
   else
     gemm_mfma_kernel<AT, BM, BN, BK, WGM, WGN, false><<<grid, 64 * WGM * WGN, 0, s>>>(
-        A, lda, W, ldw, C, ldc, M, N, K, acc ? 1 : 0);
+        A, lda, W, ldw, C, ldc, M, N, K, acc ? 1 : 0, k_chunk, c_split_stride);
   return hipGetLastError();
 }
 
@@ -367,6 +379,67 @@ static hipError_t gemm_at(const AT* A, int64_t lda, const bf16* W, int64_t ldw, 
   if (N < 128) return gemm_tile<AT, 32, 80, 64, 2, 1>(A, lda, W, ldw, C, ldc, M, N, K, acc, vec, s);
   if (M <= 64) return gemm_tile<AT, 64, 32, 64, 2, 1>(A, lda, W, ldw, C, ldc, M, N, K, acc, vec, s);
   return gemm_tile<AT, 128, 128, 64, 2, 2>(A, lda, W, ldw, C, ldc, M, N, K, acc, vec, s);
+}
+
+// C[m, n] (+)= sum over the ks partial planes P[z, m, n] in order z = 0 .. ks-1.
+__global__ void __launch_bounds__(256) splitk_reduce_kernel(const float* __restrict__ P, int ks,
+                                                            float* __restrict__ C, int64_t ldc,
+                                                            int M, int N, int accumulate) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)M * N) return;
+  const int m = (int)(i / N), n = (int)(i % N);
+  float v = 0.0f;
+  for (int z = 0; z < ks; ++z) v += P[(int64_t)z * M * N + i];
+  float* cp = C + (int64_t)m * ldc + n;
+  *cp = accumulate ? *cp + v : v;
+}
+
+// Slices of K for a few-row product (a decode batch), so that streaming W is spread over
+// enough workgroups: about 256, each at least one 64-wide k-slab.
+// k-slices: whole 64-wide slabs per slice, as many slices as needed to cover K
+static int splitk_chunk(int K, int want) {
+  const int nslab = (K + 63) / 64;
+  return (nslab + want - 1) / want * 64;
+}
+
+int gemm_splitk_slices(int M, int N, int K) {
+  if (M > kSplitKMaxM || M <= kSkinnyMaxM || K % 8 != 0 || K < 128) return 1;
+  const int bm = N < 128 ? 32 : 64, bn = N < 128 ? 80 : 32;
+  const int64_t blocks = (int64_t)((N + bn - 1) / bn) * ((M + bm - 1) / bm);
+  const int want = (int)std::min<int64_t>(std::max<int64_t>(256 / std::max<int64_t>(blocks, 1), 1),
+                                          (K + 63) / 64);
+  const int chunk = splitk_chunk(K, want);
+  return (K + chunk - 1) / chunk;
+}
+
+hipError_t launch_gemm_bf16_splitk(const void* A, bool a_bf16, int64_t lda, const void* W,
+                                   int64_t ldw, float* C, int64_t ldc, int M, int N, int K,
+                                   bool accumulate, float* partial, hipStream_t s) {
+  const int ks = gemm_splitk_slices(M, N, K);
+  const int chunk = ks > 1 ? (K + ks - 1) / ks : K;
+  const int k_chunk = (chunk + 63) / 64 * 64;
+  const bool aligned = lda % 8 == 0 && ldw % 8 == 0 && reinterpret_cast<uintptr_t>(A) % 16 == 0 &&
+                       reinterpret_cast<uintptr_t>(W) % 16 == 0;
+  if (ks <= 1 || !aligned || M <= kSkinnyMaxM)
+    return launch_gemm_bf16(A, a_bf16, lda, W, ldw, C, ldc, M, N, K, accumulate, s);
+  const bf16* w = static_cast<const bf16*>(W);
+  const int64_t plane = (int64_t)M * N;
+  hipError_t e;
+  if (N < 128) {
+    e = a_bf16 ? gemm_tile<bf16, 32, 80, 64, 2, 1>(static_cast<const bf16*>(A), lda, w, ldw, partial, N, M, N, K,
+                                                   false, true, s, ks, k_chunk, plane)
+               : gemm_tile<float, 32, 80, 64, 2, 1>(static_cast<const float*>(A), lda, w, ldw, partial, N, M, N,
+                                                    K, false, true, s, ks, k_chunk, plane);
+  } else {
+    e = a_bf16 ? gemm_tile<bf16, 64, 32, 64, 2, 1>(static_cast<const bf16*>(A), lda, w, ldw, partial, N, M, N, K,
+                                                   false, true, s, ks, k_chunk, plane)
+               : gemm_tile<float, 64, 32, 64, 2, 1>(static_cast<const float*>(A), lda, w, ldw, partial, N, M, N,
+                                                    K, false, true, s, ks, k_chunk, plane);
+  }
+  if (e != hipSuccess) return e;
+  splitk_reduce_kernel<<<dim3((unsigned)((plane + 255) / 256)), 256, 0, s>>>(partial, ks, C, ldc, M, N,
+                                                                            accumulate ? 1 : 0);
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm_bf16(const void* A, bool a_bf16, int64_t lda, const void* W, int64_t ldw,

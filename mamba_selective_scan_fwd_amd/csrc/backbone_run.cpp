@@ -10,6 +10,8 @@
 // allocation, so it can be captured into a HIP graph like every other call.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include "../../include/mamba_ssm.h"
 #include "launch.hpp"
 
@@ -135,7 +137,7 @@ hipError_t run_backbone_prefill_io(const mamba_backbone_dims& d, const mamba_bac
 // decode steps continues one sequence.
 
 struct DecodeLayout {
-  size_t h, xn, proj, u, xdbl, dt, y, last, total;
+  size_t h, xn, proj, u, xdbl, dt, y, last, partial, total;
 };
 
 static DecodeLayout decode_layout(const mamba_backbone_dims& d, int B) {
@@ -155,6 +157,15 @@ static DecodeLayout decode_layout(const mamba_backbone_dims& d, int B) {
   l.dt = take((size_t)B * d.d_inner * 4);
   l.y = take((size_t)B * d.d_inner * 4);
   l.last = take((size_t)B * d.d_model * 2);
+  // split-K partial planes of the largest projection
+  size_t part = 0;
+  const int shapes[4][2] = {{2 * d.d_inner, d.d_model}, {(int)xw, d.d_inner}, {d.d_inner, d.dt_rank},
+                            {d.d_model, d.d_inner}};
+  for (const auto& nk : shapes) {
+    const int ks = gemm_splitk_slices(B, nk[0], nk[1]);
+    if (ks > 1) part = std::max(part, (size_t)ks * B * nk[0] * 4);
+  }
+  l.partial = take(part);
   l.total = off;
   return l;
 }
@@ -176,6 +187,7 @@ hipError_t run_backbone_decode(const mamba_backbone_dims& d, const mamba_backbon
   float* dt = reinterpret_cast<float*>(ws + lay.dt);
   float* y = reinterpret_cast<float*>(ws + lay.y);
   void* last = ws + lay.last;
+  float* partial = reinterpret_cast<float*>(ws + lay.partial);
 
   const int Dm = d.d_model, D = d.d_inner, N = d.d_state, K = d.d_conv, R = d.dt_rank;
   const int xw = R + 2 * N;
@@ -188,21 +200,21 @@ hipError_t run_backbone_decode(const mamba_backbone_dims& d, const mamba_backbon
   if (e != hipSuccess) return e;
   for (int l = 0; l < d.n_layers; ++l) {
     if ((e = launch_rmsnorm(h, Dm, w.norm_w + (int64_t)l * Dm, d.eps, xn, true, B, Dm, s)) != hipSuccess) return e;
-    if ((e = launch_gemm_bf16(xn, true, Dm, in_proj + (int64_t)l * 2 * D * Dm, Dm, proj, 2 * D, B, 2 * D, Dm,
-                              false, s)) != hipSuccess) return e;
+    if ((e = launch_gemm_bf16_splitk(xn, true, Dm, in_proj + (int64_t)l * 2 * D * Dm, Dm, proj, 2 * D, B,
+                                     2 * D, Dm, false, partial, s)) != hipSuccess) return e;
     ConvStepArgs ca{proj, 2 * D, w.conv_w + (int64_t)l * D * K, w.conv_b + (int64_t)l * D,
                     conv_state + (int64_t)l * B * D * K, u, false, 1, B, D, K};
     if ((e = launch_conv1d_step(ca, s)) != hipSuccess) return e;
-    if ((e = launch_gemm_bf16(u, false, D, x_proj + (int64_t)l * xw * D, D, xdbl, xw, B, xw, D, false, s)) !=
-        hipSuccess) return e;
-    if ((e = launch_gemm_bf16(xdbl, false, xw, dt_proj + (int64_t)l * D * R, R, dt, D, B, D, R, false, s)) !=
-        hipSuccess) return e;
+    if ((e = launch_gemm_bf16_splitk(u, false, D, x_proj + (int64_t)l * xw * D, D, xdbl, xw, B, xw, D, false,
+                                     partial, s)) != hipSuccess) return e;
+    if ((e = launch_gemm_bf16_splitk(xdbl, false, xw, dt_proj + (int64_t)l * D * R, R, dt, D, B, D, R, false,
+                                     partial, s)) != hipSuccess) return e;
     SsmStepArgs sa{u, dt, w.dt_bias + (int64_t)l * D, true, w.A_log + (int64_t)l * D * N, xdbl + R,
                    xdbl + R + N, xw, w.D_skip + (int64_t)l * D, proj + D, 2 * D,
                    ssm_state + (int64_t)l * B * D * N, y, false, 1, B, D, N};
     if ((e = launch_ssm_step(sa, s)) != hipSuccess) return e;
-    if ((e = launch_gemm_bf16(y, false, D, out_proj + (int64_t)l * Dm * D, D, h, Dm, B, Dm, D, true, s)) !=
-        hipSuccess) return e;
+    if ((e = launch_gemm_bf16_splitk(y, false, D, out_proj + (int64_t)l * Dm * D, D, h, Dm, B, Dm, D, true,
+                                     partial, s)) != hipSuccess) return e;
   }
   if ((e = launch_rmsnorm(h, Dm, w.norm_f, d.eps, last, true, B, Dm, s)) != hipSuccess) return e;
   return launch_gemm_bf16(last, true, Dm, w.embed, Dm, logits, d.vocab, B, d.vocab, Dm, false, s);

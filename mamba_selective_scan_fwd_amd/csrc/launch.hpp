@@ -142,6 +142,13 @@ hipError_t launch_gemm_bf16(const void* A, bool a_bf16, int64_t lda, const void*
 // Largest M the few-row GEMM takes, and its LDS budget for the staged rows (M * K floats).
 constexpr int kSkinnyGemmMaxM = 8;
 constexpr int64_t kSkinnyGemmMaxLds = 64 * 1024;
+// Split-K GEMM for a decode batch (M <= kSplitKMaxM rows): the number of K slices for a
+// shape, and the launcher, which needs gemm_splitk_slices(M, N, K) * M * N floats of scratch.
+constexpr int kSplitKMaxM = 64;
+int gemm_splitk_slices(int M, int N, int K);
+hipError_t launch_gemm_bf16_splitk(const void* A, bool a_bf16, int64_t lda, const void* W,
+                                   int64_t ldw, float* C, int64_t ldc, int M, int N, int K,
+                                   bool accumulate, float* partial, hipStream_t s);
 
 hipError_t launch_conv1d_fwd(const ConvFwdArgs& a, hipStream_t s);
 

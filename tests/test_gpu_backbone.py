@@ -467,3 +467,20 @@ def test_backbone_ragged_batch_vs_oracle(T, lengths):
         errs = [rel_err(host(lg[b:b + 1]), rl), rel_err(host(cs[:, b:b + 1]), rcs), rel_err(host(hs[:, b:b + 1]), rhs)]
         _say(f"  sequence {b} (length {n}): logits/conv/ssm {[f'{e:.2e}' for e in errs]}")
         assert max(errs) <= TOL_BF16, (b, errs)
+
+
+def test_backbone_decode_batch16_splitk_vs_oracle():
+    """A decode batch of 16 on a wider 2-layer stack (d_model 256, d_inner 512): the
+    projections run as split-K GEMMs (64 x 32 and 32 x 80 tiles, 2..8 K slices) with a fixed-
+    order reduction; logits and states after 4 decode steps against the oracle."""
+    _say("case backbone decode B16, split-K projections")
+    s = W.BackboneShape("wide", n_layers=2, B=16, T=12, d_model=256, D=512, N=16, K=4, dt_rank=16,
+                        vocab=300, vocab_padded=320)
+    w = W.backbone_weights(s, seed=20)
+    tok = W.backbone_tokens(s, seed=20)
+    t, st = _upload(w)
+    got, cs, hs = _prefill_then_decode(s, t, st, tok, 8, graph=True)
+    ref, rcs, rhs = _oracle_prefill_then_decode(s, w, tok, 8)
+    for i, (g_, r_) in enumerate(zip(got, ref)):
+        assert rel_err(g_, r_) <= TOL_BF16, i
+    _check_backbone("decode B16", (got[-1], cs, hs), (ref[-1], rcs, rhs))
