@@ -41,7 +41,7 @@ def parse_args(argv=None):
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--config", default="c1", choices=["c1", "c3", "c2", "c4", "c4d"])
+    p.add_argument("--config", default="c1", choices=["c1", "c3", "c2", "c4", "c4d", "c5"])
     p.add_argument("--path", default="auto", choices=["auto", "fused", "split"],
                    help="prefill: one fused mamba_conv_scan_fwd call, or mamba_conv1d_fwd then "
                         "mamba_selective_scan_fwd; auto = fused for f32 I/O, split for bf16 (where "
@@ -345,6 +345,112 @@ def bench_decode(args, shape):
     return result, None
 
 
+def m3_step_bytes(shape):
+    """The Mamba-3 SISO step: per (layer, sequence, head) the SSM state read and written
+    (8 hd ds), K, V and angle states read and written (8 (ds + hd + na)); per (layer,
+    sequence) the in_proj row read and the output written; per layer the parameters."""
+    L, B, nh, hd, ds, na = shape.L, shape.B, shape.nheads, shape.headdim, shape.d_state, shape.na
+    di = nh * hd
+    per_head = 8 * hd * ds + 8 * (ds + hd + na)
+    per_row = 4 * shape.width + 4 * di
+    per_layer = 4 * (nh + 2 * ds + 2 * nh * ds + nh + (di if shape.gate_norm else 0))
+    return L * B * nh * per_head + L * B * per_row + L * per_layer
+
+
+def bench_m3(args, shape):
+    import torch
+
+    import mamba_selective_scan_fwd_amd as m
+    import workloads as W
+
+    L, B = shape.L, shape.B
+    dev = torch.device("cuda:0")
+    P = W.m3_params(shape)
+    p = {k: (None if v is None else torch.from_numpy(v).to(dev)) for k, v in P.items()}
+    ring = 4  # distinct per-step in_proj rows, resident in HBM, used round-robin
+    print(f"[bench] generating {ring} Mamba-3 steps of in_proj rows L={L} B={B}", file=sys.stderr, flush=True)
+    rows = [torch.from_numpy(W.m3_proj(shape, step=r)).to(dev) for r in range(ring)]
+    st = {k: torch.from_numpy(v).to(dev) for k, v in W.m3_states(shape).items()}
+    out = torch.empty(L, B, shape.d_inner, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        if ev:
+            ev[0].record(stream)
+        m.mamba3_siso_step(rows[i % ring], p, shape.a_floor, st["ssm"], st["k"], st["v"], st["angle"], out,
+                           shape.ngroups, shape.na, stream=stream)
+        if ev:
+            ev[1].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [_events(torch) for _ in range(args.steps)]
+    t_start, t_end = _events(torch)
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(i, evs[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    step_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    ms_step = total_ms / args.steps
+    sb = m3_step_bytes(shape)
+    avg = sum(step_ms) / len(step_ms)
+    achieved = sb / (avg * 1e-3) / 1e9
+    result = dict(
+        metric=METRIC,
+        value=L * B / (ms_step * 1e-3),
+        unit="tokens/s/layer",
+        ms_per_step=ms_step,
+        dtype="f32",
+        config=dict(workload=f"{shape.name}: Mamba-3 SISO decode step (split, BC-norm, RoPE, trapezoidal "
+                             f"update, gated norm), {L} layers in one launch, B={B}, {shape.nheads} heads x "
+                             f"headdim {shape.headdim}, d_state {shape.d_state}, {shape.na} angles, f32",
+                    L=L, B=B, nheads=shape.nheads, headdim=shape.headdim, d_state=shape.d_state,
+                    ngroups=shape.ngroups, n_angles=shape.na, step_bytes=sb),
+        roofline=dict(bound="hbm", achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s",
+                      frac=achieved / HBM_PEAK_GBS, traffic=measured_traffic("mamba3.hip", shape.name),
+                      call="mamba3_siso_step", algorithmic_bytes=sb, avg_ms=avg),
+        calls={"mamba3_siso_step": dict(avg_us=avg * 1e3, min_us=min(step_ms) * 1e3,
+                                        gbs=achieved)},
+        layer_gbs=sb / (ms_step * 1e-3) / 1e9,
+    )
+    result["layer_hbm_frac"] = result["layer_gbs"] / HBM_PEAK_GBS
+    return result, dict(P=P)
+
+
+def cpu_baseline_m3(shape, data, budget_s):
+    """The f64 oracle on a bounded sample of the same step: (layer, sequence) pairs, one at a
+    time, until the time budget is spent; scaled to tokens/s/layer (one pair is one token of
+    one layer)."""
+    import time
+
+    import numpy as np
+
+    from oracle import mamba3 as o3
+    import workloads as W
+
+    P = data["P"]
+    kw = dict(nheads=shape.nheads, headdim=shape.headdim, d_state=shape.d_state,
+              ngroups=shape.ngroups, n_angles=shape.na, a_floor=shape.a_floor)
+    zero = {k: v[:1, :1] for k, v in W.m3_states(W.Mamba3Shape(
+        "one", L=1, B=1, nheads=shape.nheads, headdim=shape.headdim, d_state=shape.d_state,
+        ngroups=shape.ngroups, n_angles=shape.n_angles)).items()}
+    done, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < budget_s and done < shape.L * shape.B:
+        l, b = done % shape.L, done // shape.L
+        row = W.m3_proj(shape, pairs=[(l, b)])[None]
+        lp = {k: (None if v is None else v[l:l + 1]) for k, v in P.items() if k != "gate_norm_w"}
+        lp["gate_w"] = None if P["gate_norm_w"] is None else P["gate_norm_w"][l:l + 1]
+        o3.siso_step(row, lp, zero["ssm"], zero["k"], zero["v"], zero["angle"], **kw)
+        done += 1
+    dt = time.perf_counter() - t0
+    return dict(value=done / dt, unit="tokens/s/layer", cores=1, kind="oracle",
+                sample=f"{done} of the {shape.L * shape.B} (layer, sequence) pairs of one step, "
+                       f"each through the f64 numpy oracle ({dt:.1f} s)")
+
+
 def gemm_flops(M, N, K):
     return 2.0 * M * N * K
 
@@ -634,6 +740,8 @@ def main(argv=None):
         result, inp = bench_backbone(args, shape)
     elif args.config == "c4d":
         result, inp = bench_backbone_decode(args, W.C4)
+    elif args.config == "c5":
+        result, inp = bench_m3(args, shape)
     else:
         result, inp = bench_prefill(args, shape)
     cpu = None
@@ -641,6 +749,8 @@ def main(argv=None):
         print("[bench] timing the CPU oracle baseline", file=sys.stderr, flush=True)
         if args.config == "c4":
             cpu = cpu_baseline_backbone(shape, inp, args.cpu_seconds)
+        elif args.config == "c5":
+            cpu = cpu_baseline_m3(shape, inp, args.cpu_seconds)
         else:
             cpu = cpu_baseline_prefill(shape, inp, args.cpu_seconds)
     line = dict(

@@ -380,6 +380,52 @@ mamba_status mamba_backbone_decode_graph_create(const mamba_backbone_dims* dims,
 mamba_status mamba_graph_launch(mamba_graph* graph, void* stream);
 void mamba_graph_destroy(mamba_graph* graph);
 
+/* ---------------------------------------------------------------- Mamba-3 SISO decode step
+ *
+ * [mamba3_siso inference.rs] (mamba-rs 0.2.1), phases F3-F7 of every layer for one new token
+ * per sequence, given each layer's in_proj output row:
+ *   F3 split of the row into z | x | B | C | dt | A | trap | angles (the order of m3_split's
+ *      outputs), with dt = softplus(dt + dt_bias), A = -max(softplus(A), a_floor) and
+ *      lambda = sigmoid(trap);
+ *   F4 BC-norm (RMSNorm over d_state per group, eps 1e-5, [d_state] weight), the per-head bias
+ *      (head h reads group h / (nheads / ngroups)), the angle step
+ *      theta = angle_state + dt * angles and the rotation of adjacent B/C pairs (2i, 2i+1) by
+ *      theta[i] for i < n_angles;
+ *   F5 alpha = exp(dt A), beta = (1 - lambda) dt alpha, gamma = lambda dt;
+ *   F6 h[p][n] = alpha h[p][n] + beta v_prev[p] k_prev[n] + gamma x[p] k[n] (k, q the
+ *      rotated B and C; k_prev, v_prev the K and V states), y[p] = q . h[p] + D x[p];
+ *   F7 g = y silu(z), RMS-normalised per head and scaled by gate_norm_w when that is given.
+ * The K state then holds k, the V state x, the angle state theta.
+ *
+ *   proj         in   [L][B] rows, f32, proj_row_stride >= W floats apart, where
+ *                     W = 2 nheads headdim + 2 ngroups d_state + 3 nheads + n_angles.
+ *   params       in   per-layer f32 parameters (below); gate_norm_w may be NULL.
+ *   a_floor      in   the floor of -A.
+ *   ssm_state    in/out [L][B][nheads][headdim][d_state] f32, 16-byte aligned.
+ *   k_state      in/out [L][B][nheads][d_state] f32 (the previous rotated B).
+ *   v_state      in/out [L][B][nheads][headdim] f32 (the previous x).
+ *   angle_state  in/out [L][B][nheads][max(n_angles, 1)] f32.
+ *   out          out  [L][B][nheads * headdim] f32, the gated output (the input of out_proj).
+ * Limits: d_state a multiple of 4 in [4, 256], headdim in [1, 256], nheads a multiple of
+ * ngroups, 0 <= n_angles <= d_state / 2, L * B * nheads < 2^31 (MAMBA_EUNSUPPORTED or
+ * MAMBA_EINVAL otherwise). L or B = 0 is a no-op. Outputs must not overlap inputs or each
+ * other. Nothing is allocated or synchronized.
+ */
+typedef struct mamba3_siso_params {
+  const float* dt_bias;     /* [L][nheads] */
+  const float* b_norm_w;    /* [L][d_state] */
+  const float* c_norm_w;    /* [L][d_state] */
+  const float* b_bias;      /* [L][nheads][d_state] */
+  const float* c_bias;      /* [L][nheads][d_state] */
+  const float* D;           /* [L][nheads] */
+  const float* gate_norm_w; /* [L][nheads * headdim], or NULL for the plain silu gate */
+} mamba3_siso_params;
+mamba_status mamba3_siso_step(const float* proj, int64_t proj_row_stride,
+                              const mamba3_siso_params* params, float a_floor,
+                              float* ssm_state, float* k_state, float* v_state,
+                              float* angle_state, float* out, int L, int B, int nheads,
+                              int headdim, int d_state, int ngroups, int n_angles, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -16,6 +16,7 @@ __all__ = [
     "mamba_selective_scan_workspace_size", "mamba_conv1d_step", "mamba_ssm_step",
     "scan_workspace", "mamba_embed_gather", "mamba_rmsnorm", "mamba_gemm_bf16",
     "BackboneDims", "BackboneWeights", "mamba_backbone_workspace_size", "mamba_backbone_prefill",
+    "Mamba3SisoParams", "mamba3_siso_step",
 ]
 
 MAMBA_F32 = 0
@@ -52,6 +53,8 @@ symbols = {
                                             ctypes.POINTER(ctypes.c_void_p)], _I),
     "mamba_graph_launch": ([_P, _P], _I),
     "mamba_graph_destroy": ([_P], None),
+    "mamba3_siso_step": ([_P, _I64, _P, ctypes.c_float, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I,
+                          _I, _P], _I),
 }
 
 
@@ -67,6 +70,12 @@ class BackboneWeights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "embed", "norm_f", "norm_w", "in_proj", "conv_w", "conv_b", "x_proj", "dt_proj",
         "dt_bias", "A_log", "D_skip", "out_proj")]
+
+class Mamba3SisoParams(ctypes.Structure):
+    """mamba3_siso_params: device pointers of the layer-stacked Mamba-3 parameters."""
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "dt_bias", "b_norm_w", "c_norm_w", "b_bias", "c_bias", "D", "gate_norm_w")]
+
 
 class PrefillIO(ctypes.Structure):
     """mamba_prefill_io."""
@@ -392,3 +401,21 @@ def mamba_backbone_prefill_ex(dims: BackboneDims, weights: BackboneWeights, B: i
     _check(load_library().mamba_backbone_prefill_ex(
         ctypes.byref(dims), ctypes.byref(weights), ctypes.byref(io), B, T, _ptr(conv_state),
         _ptr(ssm_state), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+# ------------------------------------------------------------ Mamba-3 SISO decode step
+
+def mamba3_siso_step(proj, params: dict, a_floor: float, ssm_state, k_state, v_state, angle_state,
+                     out, ngroups: int, n_angles: int, stream=None) -> None:
+    """Phases F3-F7 of the Mamba-3 SISO step for L layers and B sequences. proj [L, B, >= W]
+    (rows may be strided); params: dict of f32 tensors dt_bias [L, nh], b_norm_w / c_norm_w
+    [L, ds], b_bias / c_bias [L, nh, ds], D [L, nh], gate_norm_w [L, nh * hd] or None;
+    ssm_state [L, B, nh, hd, ds], k_state [L, B, nh, ds], v_state [L, B, nh, hd],
+    angle_state [L, B, nh, max(na, 1)]; out [L, B, nh * hd]."""
+    L, Bsz, nh, hd, ds = ssm_state.shape
+    c = Mamba3SisoParams(*[_ptr(params.get(n)) for n in (
+        "dt_bias", "b_norm_w", "c_norm_w", "b_bias", "c_bias", "D", "gate_norm_w")])
+    _check(load_library().mamba3_siso_step(
+        _ptr(proj), _row_stride(proj, "proj"), ctypes.byref(c), float(a_floor), _ptr(ssm_state),
+        _ptr(k_state), _ptr(v_state), _ptr(angle_state), _ptr(out), L, Bsz, nh, hd, ds, ngroups,
+        n_angles, _stream(stream)))

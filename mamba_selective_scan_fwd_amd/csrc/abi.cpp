@@ -449,6 +449,72 @@ mamba_status mamba_decode_step(const void* x, int64_t x_row_stride, const float*
   });
 }
 
+mamba_status mamba3_siso_step(const float* proj, int64_t proj_row_stride,
+                              const mamba3_siso_params* params, float a_floor,
+                              float* ssm_state, float* k_state, float* v_state,
+                              float* angle_state, float* out, int L, int B, int nheads,
+                              int headdim, int d_state, int ngroups, int n_angles, void* stream) {
+  static const char* fn = "mamba3_siso_step";
+  return guarded([&] {
+    check_dim(fn, "L", L);
+    check_dim(fn, "B", B);
+    check_state_dim(fn, "nheads", nheads, 1 << 20);
+    check_state_dim(fn, "headdim", headdim, mamba::kM3MaxHeadDim);
+    check_state_dim(fn, "d_state", d_state, mamba::kM3MaxDState);
+    if (ngroups < 1) fail(MAMBA_EINVAL, fn, "ngroups = %d must be at least 1", ngroups);
+    if (d_state % 4 != 0) fail(MAMBA_EUNSUPPORTED, fn, "d_state = %d is not a multiple of 4", d_state);
+    if (nheads % ngroups != 0) fail(MAMBA_EINVAL, fn, "nheads = %d is not a multiple of ngroups = %d", nheads, ngroups);
+    if (n_angles < 0 || 2 * n_angles > d_state)
+      fail(MAMBA_EINVAL, fn, "n_angles = %d is outside [0, d_state / 2 = %d]", n_angles, d_state / 2);
+    const int64_t heads = (int64_t)L * B * nheads;
+    if (heads > mamba::kM3MaxBlocks) fail(MAMBA_EUNSUPPORTED, fn, "L*B*nheads = %lld exceeds %lld", (long long)heads, (long long)mamba::kM3MaxBlocks);
+    if (!params) fail(MAMBA_EINVAL, fn, "params is NULL");
+    if (heads == 0) return;
+    const int64_t di = (int64_t)nheads * headdim, gs = (int64_t)ngroups * d_state;
+    const int64_t W = 2 * di + 2 * gs + 3 * (int64_t)nheads + n_angles;
+    if (proj_row_stride < W) fail(MAMBA_EINVAL, fn, "proj_row_stride = %lld is less than the row width %lld", (long long)proj_row_stride, (long long)W);
+    if (proj_row_stride > kMaxRowStride) fail(MAMBA_EUNSUPPORTED, fn, "proj_row_stride = %lld exceeds %lld", (long long)proj_row_stride, (long long)kMaxRowStride);
+    check_ptr(fn, "proj", proj, 4, true);
+    check_ptr(fn, "params->dt_bias", params->dt_bias, 4, true);
+    check_ptr(fn, "params->b_norm_w", params->b_norm_w, 4, true);
+    check_ptr(fn, "params->c_norm_w", params->c_norm_w, 4, true);
+    check_ptr(fn, "params->b_bias", params->b_bias, 4, true);
+    check_ptr(fn, "params->c_bias", params->c_bias, 4, true);
+    check_ptr(fn, "params->D", params->D, 4, true);
+    check_ptr(fn, "params->gate_norm_w", params->gate_norm_w, 4, false);
+    check_ptr(fn, "ssm_state", ssm_state, 16, true);
+    check_ptr(fn, "k_state", k_state, 4, true);
+    check_ptr(fn, "v_state", v_state, 4, true);
+    check_ptr(fn, "angle_state", angle_state, 4, true);
+    check_ptr(fn, "out", out, 4, true);
+    const int64_t rows = (int64_t)L * B;
+    const int na1 = n_angles > 0 ? n_angles : 1;
+    const Range rp = range("proj", proj, rows, proj_row_stride, W, 4);
+    const Range r1 = range("params->dt_bias", params->dt_bias, L, nheads, nheads, 4);
+    const Range r2 = range("params->b_norm_w", params->b_norm_w, L, d_state, d_state, 4);
+    const Range r3 = range("params->c_norm_w", params->c_norm_w, L, d_state, d_state, 4);
+    const Range r4 = range("params->b_bias", params->b_bias, L, nheads * (int64_t)d_state, nheads * (int64_t)d_state, 4);
+    const Range r5 = range("params->c_bias", params->c_bias, L, nheads * (int64_t)d_state, nheads * (int64_t)d_state, 4);
+    const Range r6 = range("params->D", params->D, L, nheads, nheads, 4);
+    const Range r7 = range("params->gate_norm_w", params->gate_norm_w, L, di, di, 4);
+    const Range rh = range("ssm_state", ssm_state, heads * headdim, d_state, d_state, 4);
+    const Range rk = range("k_state", k_state, heads, d_state, d_state, 4);
+    const Range rv = range("v_state", v_state, heads, headdim, headdim, 4);
+    const Range ra = range("angle_state", angle_state, heads, na1, na1, 4);
+    const Range ro = range("out", out, rows, di, di, 4);
+    check_disjoint(fn, ro, {rp, r1, r2, r3, r4, r5, r6, r7, rh, rk, rv, ra});
+    check_disjoint(fn, rh, {rp, r1, r2, r3, r4, r5, r6, r7, rk, rv, ra});
+    check_disjoint(fn, rk, {rp, r1, r2, r3, r4, r5, r6, r7, rv, ra});
+    check_disjoint(fn, rv, {rp, r1, r2, r3, r4, r5, r6, r7, ra});
+    check_disjoint(fn, ra, {rp, r1, r2, r3, r4, r5, r6, r7});
+    mamba::M3StepArgs a{proj, proj_row_stride, params->dt_bias, params->b_norm_w, params->c_norm_w,
+                        params->b_bias, params->c_bias, params->D, params->gate_norm_w, a_floor,
+                        ssm_state, k_state, v_state, angle_state, na1, out, L, B, nheads, headdim,
+                        d_state, ngroups, n_angles};
+    check_hip(fn, mamba::launch_m3_siso_step(a, static_cast<hipStream_t>(stream)));
+  });
+}
+
 mamba_status mamba_embed_gather(const int32_t* tokens, const void* E, float* out, int64_t rows,
                                 int vocab, int d_model, void* stream) {
   static const char* fn = "mamba_embed_gather";

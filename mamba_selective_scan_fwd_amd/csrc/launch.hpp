@@ -128,6 +128,32 @@ struct DecodeStepArgs {
 };
 hipError_t launch_decode_step(const DecodeStepArgs& a, hipStream_t s);
 
+// Mamba-3 SISO decode step (phases F3-F7) for L layers and B sequences: one in_proj row per
+// (layer, sequence), per-layer parameters, the four states updated in place.
+constexpr int kM3MaxDState = 256;
+constexpr int kM3MaxHeadDim = 256;
+constexpr int64_t kM3MaxBlocks = 0x7fffffff;
+struct M3StepArgs {
+  const float* proj;        // [L][B] rows of proj_row_stride floats
+  int64_t proj_row_stride;
+  const float* dt_bias;     // [L][nh]
+  const float* b_norm_w;    // [L][ds]
+  const float* c_norm_w;    // [L][ds]
+  const float* b_bias;      // [L][nh][ds]
+  const float* c_bias;      // [L][nh][ds]
+  const float* D;           // [L][nh]
+  const float* gate_w;      // [L][nh * hd] or NULL (plain silu gate)
+  float a_floor;
+  float* ssm;               // [L][B][nh][hd][ds], 16-byte aligned
+  float* k_state;           // [L][B][nh][ds]
+  float* v_state;           // [L][B][nh][hd]
+  float* angle;             // [L][B][nh][angle_stride]
+  int angle_stride;         // max(na, 1)
+  float* out;               // [L][B][nh * hd]
+  int L, B, nh, hd, ds, ng, na;
+};
+hipError_t launch_m3_siso_step(const M3StepArgs& a, hipStream_t s);
+
 hipError_t launch_embed_gather(const int32_t* tokens, const void* E, float* out, int64_t rows,
                                int vocab, int Dm, hipStream_t s);
 hipError_t launch_rmsnorm(const float* x, int64_t x_row_stride, const float* w, float eps,

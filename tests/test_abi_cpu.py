@@ -20,7 +20,7 @@ FAKE = 0x7F0000000000  # a well-aligned address; never dereferenced (calls fail 
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(mamba_\w+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(mamba3?_\w+)\s*\(", text)))
 
 
 def test_library_exports_every_declared_symbol():
@@ -152,3 +152,46 @@ def test_errors_are_thread_local():
     th.join()
     assert seen["msg"] == ""
     assert "u is NULL" in m.mamba_last_error()
+
+
+def m3_call(**kw):
+    p = m.Mamba3SisoParams(*[FAKE + (i << 26) for i in range(1, 7)], None)
+    a = dict(proj=FAKE + (1 << 33), prs=None, params=p, a_floor=1e-4, h=FAKE + (1 << 34),
+             k=FAKE + (1 << 35), v=FAKE + (1 << 36), ang=FAKE + (1 << 37), out=FAKE + (1 << 38),
+             L=2, B=3, nh=4, hd=8, ds=16, ng=2, na=4, stream=None)
+    a.update(kw)
+    if a["prs"] is None:
+        a["prs"] = 2 * a["nh"] * a["hd"] + 2 * a["ng"] * a["ds"] + 3 * a["nh"] + a["na"]
+    st = m.load_library().mamba3_siso_step(
+        a["proj"], a["prs"], ctypes.byref(a["params"]) if a["params"] is not None else None,
+        ctypes.c_float(a["a_floor"]), a["h"], a["k"], a["v"], a["ang"], a["out"], a["L"], a["B"],
+        a["nh"], a["hd"], a["ds"], a["ng"], a["na"], a["stream"])
+    return st, m.mamba_last_error()
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(ds=18), EUNSUP, "multiple of 4"),
+    (dict(ds=260), EUNSUP, "d_state = 260"),
+    (dict(hd=0), EINVAL, "headdim = 0"),
+    (dict(hd=300), EUNSUP, "headdim = 300"),
+    (dict(ng=3), EINVAL, "not a multiple of ngroups"),
+    (dict(ng=0), EINVAL, "ngroups = 0"),
+    (dict(na=9), EINVAL, "n_angles = 9"),
+    (dict(na=-1), EINVAL, "n_angles = -1"),
+    (dict(prs=10), EINVAL, "proj_row_stride"),
+    (dict(params=None), EINVAL, "params is NULL"),
+    (dict(proj=None), EINVAL, "proj is NULL"),
+    (dict(h=FAKE + (1 << 34) + 4), EINVAL, "ssm_state"),
+    (dict(out=FAKE + (1 << 34)), EINVAL, "out overlaps ssm_state"),
+    (dict(k=FAKE + (1 << 34) + 64), EINVAL, "ssm_state overlaps k_state"),
+    (dict(L=-1), EINVAL, "L = -1"),
+])
+def test_mamba3_step_validation(kw, status, needle):
+    st, msg = m3_call(**kw)
+    assert st == status, msg
+    assert needle in msg and msg.startswith("mamba3_siso_step"), msg
+
+
+def test_mamba3_step_empty_is_noop():
+    st, msg = m3_call(L=0, proj=None, h=None, k=None, v=None, ang=None, out=None)
+    assert st == 0, msg

@@ -11,6 +11,8 @@ Workloads (one Mamba-1 layer unless stated):
   c2  L=24 B=64    D=1536  N=16 K=4  f32, T=1 x 1000 decode steps
   c3  B=8  T=4096  D=5120  N=16 K=4  bf16 I/O     (2.8b-shaped prefill layer)
   c4  24-layer 130m-shaped backbone, B=4, T=2048, d_model 768, vocab 50280
+  c5  Mamba-3 SISO decode step, L=24 B=64, 24 heads x headdim 64, d_state 128, 1 group,
+      64 RoPE angles, gated output norm (130m-shaped: d_model 768, d_inner 1536)
 
 Distributions: x, z, B, C ~ N(0, 1); dt_raw ~ N(0, 0.1^2); dt_bias is the inverse
 softplus of dt0 with dt0 log-uniform in [1e-3, 0.1]; A_log[d, n] = log(n + 1)
@@ -28,6 +30,7 @@ import numpy as np
 X, Z, BM, CM, DT, DT0, CONVW = 0, 1, 2, 3, 4, 5, 6
 ALOG_RAND, DSKIP_RAND, CONVB_RAND, STATE_RAND = 7, 8, 9, 16
 EMBED, W_IN, W_X, W_DT, W_OUT, TOKENS = 10, 11, 12, 13, 14, 15
+M3_PROJ, M3_PARAMS, M3_STATE = 20, 21, 22
 
 
 @dataclasses.dataclass(frozen=True)
@@ -76,8 +79,39 @@ C1 = PrefillShape("c1", B=1, T=2048, D=1536, d_model=768, dt_rank=48)
 C2 = DecodeShape("c2", L=24, B=64, D=1536)
 C3 = PrefillShape("c3", B=8, T=4096, D=5120, io="bf16", d_model=2560, dt_rank=160)
 C4 = BackboneShape("c4")
-CONFIGS = {"c0": C0, "c1": C1, "c2": C2, "c3": C3, "c4": C4}
-CONFIG_INDEX = {"c0": 0, "c1": 1, "c2": 2, "c3": 3, "c4": 4}
+
+
+@dataclasses.dataclass(frozen=True)
+class Mamba3Shape:
+    name: str
+    L: int
+    B: int
+    nheads: int
+    headdim: int
+    d_state: int
+    ngroups: int = 1
+    n_angles: int = -1  # -1: d_state / 2 (every pair rotated)
+    a_floor: float = 1e-4
+    gate_norm: bool = True
+    d_model: int = 0  # shape label only
+
+    @property
+    def na(self) -> int:
+        return self.d_state // 2 if self.n_angles < 0 else self.n_angles
+
+    @property
+    def d_inner(self) -> int:
+        return self.nheads * self.headdim
+
+    @property
+    def width(self) -> int:
+        """in_proj row width: z | x | B | C | dt | A | trap | angles."""
+        return 2 * self.d_inner + 2 * self.ngroups * self.d_state + 3 * self.nheads + self.na
+
+
+C5 = Mamba3Shape("c5", L=24, B=64, nheads=24, headdim=64, d_state=128, d_model=768)
+CONFIGS = {"c0": C0, "c1": C1, "c2": C2, "c3": C3, "c4": C4, "c5": C5}
+CONFIG_INDEX = {"c0": 0, "c1": 1, "c2": 2, "c3": 3, "c4": 4, "c5": 5}
 
 
 def rng(seed: int, cfg: int, tensor: int, layer: int = 0, step: int = 0) -> np.random.Generator:
@@ -283,3 +317,56 @@ def backbone_weights(shape: BackboneShape, seed: int = 0, cfg: int = 4) -> dict:
 def backbone_tokens(shape: BackboneShape, seed: int = 0, cfg: int = 4) -> np.ndarray:
     """Token ids uniform in [0, vocab), [B, T] int32."""
     return rng(seed, cfg, TOKENS).integers(0, shape.vocab, size=(shape.B, shape.T)).astype(np.int32)
+
+
+# ------------------------------------------------------- Mamba-3 SISO step (c5) inputs
+#
+# in_proj rows: z, x, B, C ~ N(0, 1); dt_raw ~ N(0, 0.1^2); a_raw ~ N(1, 1) (softplus around
+# 1.3); trap_raw ~ N(0, 1) (lambda mostly in 0.15 .. 0.85); angles ~ N(0, 1). Parameters:
+# dt_bias as Mamba-1 (inverse softplus of a log-uniform [1e-3, 0.1] draw, per head);
+# B/C norm weights and the gate-norm weight 1 + N(0, 0.1^2); B/C biases 1 + N(0, 0.1^2)
+# (Mamba-3 starts them at one); D ~ U(0.5, 1.5). States zero unless drawn (N(0, 1); angles
+# U(-pi, pi)).
+
+def m3_params(shape: Mamba3Shape, seed: int = 0, cfg: int = 5) -> dict:
+    L, nh, ds, di = shape.L, shape.nheads, shape.d_state, shape.d_inner
+    g = rng(seed, cfg, M3_PARAMS)
+    p = dict(
+        dt_bias=np.stack([dt_bias_init(nh, rng(seed, cfg, DT0, l))[0] for l in range(L)]),
+        b_norm_w=(1.0 + normal(g, (L, ds), 0.1)).astype(np.float32),
+        c_norm_w=(1.0 + normal(g, (L, ds), 0.1)).astype(np.float32),
+        b_bias=(1.0 + normal(g, (L, nh, ds), 0.1)).astype(np.float32),
+        c_bias=(1.0 + normal(g, (L, nh, ds), 0.1)).astype(np.float32),
+        D=g.uniform(0.5, 1.5, size=(L, nh)).astype(np.float32),
+        gate_norm_w=(1.0 + normal(g, (L, di), 0.1)).astype(np.float32) if shape.gate_norm else None,
+    )
+    return p
+
+
+def m3_proj(shape: Mamba3Shape, step: int = 0, seed: int = 0, cfg: int = 5, pairs=None) -> np.ndarray:
+    """in_proj rows [L, B, W] of one step (or only the listed (l, b) rows, [len(pairs), W])."""
+    di, gs, nh, na = shape.d_inner, shape.ngroups * shape.d_state, shape.nheads, shape.na
+    todo = pairs if pairs is not None else [(l, b) for l in range(shape.L) for b in range(shape.B)]
+    rows = np.empty((len(todo), shape.width), np.float32)
+    for r, (l, b) in enumerate(todo):
+        g = rng(seed, cfg, M3_PROJ, l * 100003 + b, step)
+        rows[r, :2 * di + 2 * gs] = normal(g, 2 * di + 2 * gs)
+        o = 2 * di + 2 * gs
+        rows[r, o:o + nh] = normal(g, nh, 0.1)
+        rows[r, o + nh:o + 2 * nh] = 1.0 + normal(g, nh)
+        rows[r, o + 2 * nh:o + 3 * nh] = normal(g, nh)
+        rows[r, o + 3 * nh:] = normal(g, na)
+    return rows if pairs is not None else rows.reshape(shape.L, shape.B, shape.width)
+
+
+def m3_states(shape: Mamba3Shape, seed: int = 0, cfg: int = 5, random: bool = False) -> dict:
+    """ssm [L, B, nh, hd, ds], k [L, B, nh, ds], v [L, B, nh, hd], angle [L, B, nh, max(na, 1)]."""
+    L, B, nh, hd, ds = shape.L, shape.B, shape.nheads, shape.headdim, shape.d_state
+    na1 = max(shape.na, 1)
+    shapes = dict(ssm=(L, B, nh, hd, ds), k=(L, B, nh, ds), v=(L, B, nh, hd), angle=(L, B, nh, na1))
+    if not random:
+        return {k: np.zeros(v, np.float32) for k, v in shapes.items()}
+    g = rng(seed, cfg, M3_STATE)
+    out = {k: normal(g, v) for k, v in shapes.items() if k != "angle"}
+    out["angle"] = g.uniform(-np.pi, np.pi, size=shapes["angle"]).astype(np.float32)
+    return out
