@@ -85,6 +85,12 @@ template <typename IO>
 __device__ __forceinline__ float load_at(const IO* row, uint32_t lane_off) {
   return to_f32(*reinterpret_cast<const IO*>(reinterpret_cast<const char*>(row) + lane_off));
 }
+// The same, returning the stored element unconverted: a prefetched value stays in its I/O
+// type until it is used, so the wait for the load sits at the use, not at the load.
+template <typename IO>
+__device__ __forceinline__ IO load_raw(const IO* row, uint32_t lane_off) {
+  return *reinterpret_cast<const IO*>(reinterpret_cast<const char*>(row) + lane_off);
+}
 
 // OUT = false: summary pass over chunks 0 .. chunks-2 (no y). OUT = true: the output pass.
 //
@@ -96,8 +102,12 @@ __device__ __forceinline__ float load_at(const IO* row, uint32_t lane_off) {
 // per-token item reads its K raw inputs (x rows t-K+1 .. t, the carried conv state before
 // the sequence start) and computes u itself (rounded to the I/O type, as a stored u would
 // be); KC = 4 is the compile-time 4-tap case, KC = kMaxConvK any K <= 8 at run time.
+#ifndef MAMBA_SCAN_WPE
+#define MAMBA_SCAN_WPE 5  // minimum waves per SIMD the register allocation must allow
+#endif
+
 template <typename IO, int NP, int CH, int W, bool OUT, bool GATE, int KC>
-__global__ void __launch_bounds__(kLanes * W) __attribute__((amdgpu_waves_per_eu(5)))
+__global__ void __launch_bounds__(kLanes * W) __attribute__((amdgpu_waves_per_eu(MAMBA_SCAN_WPE)))
 scan_kernel(const ScanParams p) {
   constexpr int H = kLanes / CH;     // state groups per wave
   constexpr int G = W * H;           // state groups per workgroup
@@ -258,7 +268,7 @@ scan_kernel(const ScanParams p) {
   // Loads are never predicated on the token: a token past the chunk re-reads the chunk's last
   // row (in bounds; such values are never used), so no load result is merged with an older
   // value and nothing waits on a load before its use.
-  float pf_dt[2], pf_u[2], pf_z[2], pf_bc[2][BC_PER_T];
+  IO pf_dt[2], pf_u[2], pf_z[2], pf_bc[2][BC_PER_T];  // stored values, converted at use
   float pf_x[2][KM];  // fused conv: the item's K raw inputs, oldest first
   float u_blk[2], g_blk[2];  // u and silu(z) of this thread's item, for the finish
   // fused conv, general case (the sequence start or a partial block): token tg of the
@@ -281,9 +291,9 @@ scan_kernel(const ScanParams p) {
     if (k * kTB + kTB <= len) {
       // full block: scalar row address + the thread's fixed byte offset
       const int64_t row = row0 + k * kTB + it_wave;
-      pf_dt[st] = load_at(dt + row * D, off_x);
+      pf_dt[st] = load_raw(dt + row * D, off_x);
       if constexpr (KC == 0) {
-        pf_u[st] = load_at(u + row * D, off_x);
+        pf_u[st] = load_raw(u + row * D, off_x);
       } else if (t0 + k * kTB >= K - 1) {
         // every tap of every item in the block is an x row: scalar rows, fixed lane offset
 #pragma unroll
@@ -292,21 +302,21 @@ scan_kernel(const ScanParams p) {
       } else {
         load_conv_inputs(k, st);
       }
-      if constexpr (OUT && GATE) pf_z[st] = load_at(z + row * p.z_row_stride, off_z);
+      if constexpr (OUT && GATE) pf_z[st] = load_raw(z + row * p.z_row_stride, off_z);
       const int64_t step = (int64_t)k * kTB * bcs;
 #pragma unroll
       for (int r = 0; r < BC_PER_T; ++r)
-        if (threadIdx.x + r * NT < kTB * BCW) pf_bc[st][r] = to_f32(bc_src[r][step]);  // whole waves
+        if (threadIdx.x + r * NT < kTB * BCW) pf_bc[st][r] = bc_src[r][step];  // whole waves
     } else {
       const int64_t row = row0 + min(k * kTB + it_wave + it_lane, len - 1);
-      pf_dt[st] = to_f32(dt[row * D + dic]);
-      if constexpr (KC == 0) pf_u[st] = to_f32(u[row * D + dic]);
+      pf_dt[st] = dt[row * D + dic];
+      if constexpr (KC == 0) pf_u[st] = u[row * D + dic];
       else load_conv_inputs(k, st);
-      if constexpr (OUT && GATE) pf_z[st] = to_f32(z[row * p.z_row_stride + dic]);
+      if constexpr (OUT && GATE) pf_z[st] = z[row * p.z_row_stride + dic];
 #pragma unroll
       for (int r = 0; r < BC_PER_T; ++r)
         if (threadIdx.x + r * NT < kTB * BCW)
-          pf_bc[st][r] = to_f32(bc_src[r][(int64_t)(min(k * kTB + bc_j[r], len - 1) - bc_j[r]) * bcs]);
+          pf_bc[st][r] = bc_src[r][(int64_t)(min(k * kTB + bc_j[r], len - 1) - bc_j[r]) * bcs];
     }
   };
 
@@ -320,23 +330,28 @@ scan_kernel(const ScanParams p) {
       for (int kk = 0; kk < KM; ++kk)
         if (kk < K) cv = fmaf(wk[kk], pf_x[st][kk], cv);
       const IO uo = from_f32<IO>(silu(cv));
-      pf_u[st] = to_f32(uo);
+      pf_u[st] = uo;
       if constexpr (OUT) {
         const int j = it_wave + it_lane;
         if (p.u_out && di < D && k * kTB + j < len)
           static_cast<IO*>(p.u_out)[(row0 + k * kTB + j) * D + di] = uo;
       }
     }
-    const float v = pf_dt[st] + bias;
+    const float v = to_f32(pf_dt[st]) + bias;
     const float delta = sp ? softplus(v) : v;
-    s_dd[st][it_wave + it_lane][ic] = make_float2(delta, delta * pf_u[st]);
-    u_blk[st] = pf_u[st];
-    if constexpr (OUT && GATE) g_blk[st] = silu(pf_z[st]);
+    const float uf = to_f32(pf_u[st]);
+    s_dd[st][it_wave + it_lane][ic] = make_float2(delta, delta * uf);
+    u_blk[st] = uf;
+    if constexpr (OUT && GATE) g_blk[st] = silu(to_f32(pf_z[st]));
+    // pin both values here: left to the compiler they sink to their use after the next
+    // block's loads, whose wait then covers those loads too
+    asm volatile("" : "+v"(u_blk[st]));
+    if constexpr (OUT && GATE) asm volatile("" : "+v"(g_blk[st]));
 #pragma unroll
     for (int r = 0; r < BC_PER_T; ++r) {
       const int i = threadIdx.x + r * NT;
       if (i < kTB * BCW)
-        s_bc[st][bc_j[r]][i % BCW] = (bc_use[r] && k * kTB + bc_j[r] < len) ? pf_bc[st][r] : 0.0f;
+        s_bc[st][bc_j[r]][i % BCW] = (bc_use[r] && k * kTB + bc_j[r] < len) ? to_f32(pf_bc[st][r]) : 0.0f;
     }
   };
 
@@ -395,6 +410,9 @@ scan_kernel(const ScanParams p) {
     constexpr int st = decltype(P)::value;  // == k & 1
     if (k + 1 < nblk) {
       stage_a(k + 1, std::integral_constant<int, st ^ 1>{});
+      // every use of block k+1's loads stays above the next loads: a use scheduled below
+      // them would have to wait for them as well (the load counter drains in order)
+      __builtin_amdgcn_sched_barrier(0);
       if (k + 2 < nblk) load_block(k + 2, P);
     }
     const int nj = min(kTB, len - k * kTB);
