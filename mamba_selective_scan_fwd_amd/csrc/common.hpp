@@ -28,16 +28,15 @@ __device__ __forceinline__ float silu(float z) {
   return z * __builtin_amdgcn_rcpf(1.0f + fast_exp(-z));
 }
 
-// log1p(e) for e in [0, 1], accurate to a few ulp: with w = 1 + e rounded, the factor
-// e / (w - 1) corrects the rounding of w (w - 1 is exact here), so the relative error is
-// that of the hardware log2 and reciprocal, not the absolute error of w. This is the
-// textbook compensated log1p (Goldberg, "What every computer scientist should know
-// about floating-point arithmetic", Theorem 4).
+// log1p(e) for e in [0, 1], accurate to a few ulp: w = 1 + e is rounded, and its rounding
+// error c = (w - 1) - e is exact (w - 1 is exact, and it is within a factor of two of e, or
+// zero). log(1 + e) = log(w - c) = log(w) - c / w + O(c^2), and since |c| <= 2^-24 the
+// first-order term -c stands for -c / w to well under an ulp of the result. For e below
+// 2^-25, w = 1 and the result is exactly e.
 __device__ __forceinline__ float log1p_small(float e) {
-  float w = 1.0f + e;
-  float dw = w - 1.0f;
-  float l = __builtin_amdgcn_logf(w) * kLn2;  // natural log of w
-  return dw == 0.0f ? e : l * (e * __builtin_amdgcn_rcpf(dw));
+  const float w = 1.0f + e;
+  const float c = (w - 1.0f) - e;
+  return __builtin_amdgcn_logf(w) * kLn2 - c;
 }
 
 // softplus(v) = log(1 + exp(v)) = max(v, 0) + log1p(exp(-|v|)), with no overflow.

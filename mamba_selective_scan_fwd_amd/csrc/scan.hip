@@ -163,12 +163,13 @@ scan_kernel(const ScanParams p) {
   const uint32_t off_x = ((uint32_t)it_lane * (uint32_t)D + (uint32_t)dic) * (uint32_t)sizeof(IO);
   const uint32_t off_z =
       ((uint32_t)it_lane * (uint32_t)p.z_row_stride + (uint32_t)dic) * (uint32_t)sizeof(IO);
+  const uint32_t off_y = ((uint32_t)it_lane * (uint32_t)D + (uint32_t)dic) * (uint32_t)sizeof(IO);
 
   float a2[S];
 #pragma unroll
   for (int s = 0; s < S; ++s) a2[s] = a_log2(p.A_log, dc, g * S + s, N);
   const float bias = p.dt_bias ? p.dt_bias[dic] : 0.0f;
-  const float dskip = p.D_skip ? p.D_skip[dic] : 0.0f;
+  float dskip = p.D_skip ? p.D_skip[dic] : 0.0f;
   const bool sp = p.softplus != 0;
   const bool dval = d < D;
 
@@ -433,10 +434,20 @@ scan_kernel(const ScanParams p) {
         float yv = part[0];
         yv = fmaf(dskip, u_blk[st], yv);
         if constexpr (GATE) yv *= g_blk[st];
-        if (di < D) static_cast<IO*>(p.y)[(row0 + k * kTB + j) * D + di] = from_f32<IO>(yv);
+        if (di < D) {
+          // scalar row of the wave's first token + the lane's fixed byte offset
+          IO* yrow = static_cast<IO*>(p.y) + (row0 + k * kTB + it_wave) * D;
+          *reinterpret_cast<IO*>(reinterpret_cast<char*>(yrow) + off_y) = from_f32<IO>(yv);
+        }
       }
     }
   };
+
+  // Wait for the start state and the skip weight here, once: their first uses are inside the
+  // block loop, where the wait would be a full drain of the load counter on every block.
+  asm volatile("" : "+v"(dskip));
+#pragma unroll
+  for (int s = 0; s < S; ++s) asm volatile("" : "+v"(h[s]));
 
   // prologue: block 0 staged, block 1 in flight (an empty chunk loads nothing; its map is
   // the identity and its state passes through)
