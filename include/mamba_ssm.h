@@ -350,6 +350,7 @@ mamba_status mamba_backbone_prefill_ex(const mamba_backbone_dims* dims,
  *   conv_state, ssm_state  in/out, layouts as mamba_backbone_prefill, updated in place.
  *   logits       out  [B, vocab] f32.
  *   workspace    at least mamba_backbone_decode_workspace_size(dims, B) bytes, 256-byte aligned.
+ * dt_rank + 2 d_state above 1024 is MAMBA_EUNSUPPORTED.
  * Nothing is allocated or synchronized: the call can be captured into a HIP graph.
  */
 size_t mamba_backbone_decode_workspace_size(const mamba_backbone_dims* dims, int B);

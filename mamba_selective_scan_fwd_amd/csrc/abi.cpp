@@ -718,6 +718,9 @@ static void check_decode_call(const char* fn, const mamba_backbone_dims* dims,
   check_dim(fn, "B", B);
   if (B == 0) fail(MAMBA_EINVAL, fn, "B = 0");
   if ((int64_t)B > kMaxGridYZ) fail(MAMBA_EUNSUPPORTED, fn, "B = %d exceeds %d", B, kMaxGridYZ);
+  if ((int64_t)dims->dt_rank + 2LL * dims->d_state > mamba::kDecodeMaxXProj)
+    fail(MAMBA_EUNSUPPORTED, fn, "dt_rank + 2 d_state = %lld exceeds %d", (long long)dims->dt_rank + 2LL * dims->d_state,
+         mamba::kDecodeMaxXProj);
   check_backbone_call(fn, *dims, w, tokens, B, B, conv_state, ssm_state, logits, workspace,
                       workspace_bytes, mamba::backbone_decode_workspace_bytes(*dims, B));
 }

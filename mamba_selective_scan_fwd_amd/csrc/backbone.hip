@@ -395,50 +395,224 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(const float* __restr
 }
 
 // Slices of K for a few-row product (a decode batch), so that streaming W is spread over
-// enough workgroups: about 256, each at least one 64-wide k-slab.
+// enough workgroups: about 512, each at least one 64-wide k-slab, and at most
+// kSplitKMaxSlices slices (their readers add the partial planes one by one).
 // k-slices: whole 64-wide slabs per slice, as many slices as needed to cover K
 static int splitk_chunk(int K, int want) {
   const int nslab = (K + 63) / 64;
   return (nslab + want - 1) / want * 64;
 }
 
+#ifndef MAMBA_SPLITK_TARGET
+#define MAMBA_SPLITK_TARGET 512  // workgroups a split-K product aims for
+#endif
+#ifndef MAMBA_SPLITK_MAX
+#define MAMBA_SPLITK_MAX kSplitKMaxSlices
+#endif
+
 int gemm_splitk_slices(int M, int N, int K) {
   if (M > kSplitKMaxM || M <= kSkinnyMaxM || K % 8 != 0 || K < 128) return 1;
   const int bm = N < 128 ? 32 : 64, bn = N < 128 ? 80 : 32;
   const int64_t blocks = (int64_t)((N + bn - 1) / bn) * ((M + bm - 1) / bm);
-  const int want = (int)std::min<int64_t>(std::max<int64_t>(256 / std::max<int64_t>(blocks, 1), 1),
-                                          (K + 63) / 64);
+  const int want = (int)std::min<int64_t>(
+      std::min<int64_t>(std::max<int64_t>(MAMBA_SPLITK_TARGET / std::max<int64_t>(blocks, 1), 1), (K + 63) / 64),
+      MAMBA_SPLITK_MAX);
   const int chunk = splitk_chunk(K, want);
   return (K + chunk - 1) / chunk;
 }
 
-hipError_t launch_gemm_bf16_splitk(const void* A, bool a_bf16, int64_t lda, const void* W,
-                                   int64_t ldw, float* C, int64_t ldc, int M, int N, int K,
-                                   bool accumulate, float* partial, hipStream_t s) {
+hipError_t launch_gemm_bf16_parts(const void* A, bool a_bf16, int64_t lda, const void* W,
+                                  int64_t ldw, float* C, int64_t ldc, int M, int N, int K,
+                                  bool accumulate, float* partial, PartsView* out, hipStream_t s) {
   const int ks = gemm_splitk_slices(M, N, K);
   const int chunk = ks > 1 ? (K + ks - 1) / ks : K;
   const int k_chunk = (chunk + 63) / 64 * 64;
   const bool aligned = lda % 8 == 0 && ldw % 8 == 0 && reinterpret_cast<uintptr_t>(A) % 16 == 0 &&
                        reinterpret_cast<uintptr_t>(W) % 16 == 0;
-  if (ks <= 1 || !aligned || M <= kSkinnyMaxM)
+  if (ks <= 1 || !aligned || M <= kSkinnyMaxM) {
+    // one product, written to (or added into) C
+    *out = accumulate ? PartsView{nullptr, 0, 0, 0} : PartsView{C, 1, 0, ldc};
     return launch_gemm_bf16(A, a_bf16, lda, W, ldw, C, ldc, M, N, K, accumulate, s);
+  }
   const bf16* w = static_cast<const bf16*>(W);
   const int64_t plane = (int64_t)M * N;
-  hipError_t e;
-  if (N < 128) {
-    e = a_bf16 ? gemm_tile<bf16, 32, 80, 64, 2, 1>(static_cast<const bf16*>(A), lda, w, ldw, partial, N, M, N, K,
-                                                   false, true, s, ks, k_chunk, plane)
-               : gemm_tile<float, 32, 80, 64, 2, 1>(static_cast<const float*>(A), lda, w, ldw, partial, N, M, N,
-                                                    K, false, true, s, ks, k_chunk, plane);
-  } else {
-    e = a_bf16 ? gemm_tile<bf16, 64, 32, 64, 2, 1>(static_cast<const bf16*>(A), lda, w, ldw, partial, N, M, N, K,
-                                                   false, true, s, ks, k_chunk, plane)
-               : gemm_tile<float, 64, 32, 64, 2, 1>(static_cast<const float*>(A), lda, w, ldw, partial, N, M, N,
-                                                    K, false, true, s, ks, k_chunk, plane);
-  }
-  if (e != hipSuccess) return e;
-  splitk_reduce_kernel<<<dim3((unsigned)((plane + 255) / 256)), 256, 0, s>>>(partial, ks, C, ldc, M, N,
+  *out = PartsView{partial, ks, plane, N};
+  if (N < 128)
+    return a_bf16 ? gemm_tile<bf16, 32, 80, 64, 2, 1>(static_cast<const bf16*>(A), lda, w, ldw, partial, N, M, N,
+                                                      K, false, true, s, ks, k_chunk, plane)
+                  : gemm_tile<float, 32, 80, 64, 2, 1>(static_cast<const float*>(A), lda, w, ldw, partial, N, M,
+                                                       N, K, false, true, s, ks, k_chunk, plane);
+  return a_bf16 ? gemm_tile<bf16, 64, 32, 64, 2, 1>(static_cast<const bf16*>(A), lda, w, ldw, partial, N, M, N,
+                                                    K, false, true, s, ks, k_chunk, plane)
+                : gemm_tile<float, 64, 32, 64, 2, 1>(static_cast<const float*>(A), lda, w, ldw, partial, N, M,
+                                                     N, K, false, true, s, ks, k_chunk, plane);
+}
+
+hipError_t launch_gemm_bf16_splitk(const void* A, bool a_bf16, int64_t lda, const void* W,
+                                   int64_t ldw, float* C, int64_t ldc, int M, int N, int K,
+                                   bool accumulate, float* partial, hipStream_t s) {
+  PartsView v;
+  hipError_t e = launch_gemm_bf16_parts(A, a_bf16, lda, W, ldw, C, ldc, M, N, K, accumulate, partial, &v, s);
+  if (e != hipSuccess || v.p != partial) return e;
+  const int64_t plane = (int64_t)M * N;
+  splitk_reduce_kernel<<<dim3((unsigned)((plane + 255) / 256)), 256, 0, s>>>(partial, v.ks, C, ldc, M, N,
                                                                             accumulate ? 1 : 0);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------- decode step with split-K consumers
+//
+// In the decode step the split-K partial planes are not reduced by a kernel of their own:
+// each consumer adds them up as it reads (PartsView::at, in slice order, so the values are
+// those the reduction kernel would have written).
+
+// h[r] += the out_proj partials (if any), then RMSNorm of the new h[r] (bf16 out). The
+// arithmetic is that of rmsnorm_kernel applied after a split-K reduction with accumulate.
+__global__ void __launch_bounds__(256) residual_rmsnorm_kernel(float* __restrict__ h, PartsView add,
+                                                               const float* __restrict__ w, float eps,
+                                                               bf16* __restrict__ out, int Dm) {
+  __shared__ float part[8];
+  const int64_t r = blockIdx.x;
+  float* hr = h + r * Dm;
+  float ss = 0.0f;
+  for (int c = threadIdx.x; c < Dm; c += 256) {
+    float v = hr[c];
+    if (add.ks > 0) {
+      v = v + add.at(r, c);
+      hr[c] = v;
+    }
+    ss = fmaf(v, v, ss);
+  }
+  for (int m = 32; m >= 1; m /= 2) ss += __shfl_xor(ss, m);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  const float tot = part[0] + part[1] + part[2] + part[3];
+  const float inv = 1.0f / sqrtf(tot / (float)Dm + eps);
+  bf16* o = out + r * Dm;
+  for (int c = threadIdx.x; c < Dm; c += 256) o[c] = (bf16)(hr[c] * inv * (w ? w[c] : 1.0f));
+}
+
+// Conv step on the x lane of the in_proj output (columns 0 .. D-1), the same arithmetic as
+// conv1d_step_kernel: shift the K-slot window, append x, taps from the oldest, SiLU.
+__global__ void __launch_bounds__(256) decode_conv_kernel(PartsView xin, const float* __restrict__ conv_w,
+                                                          const float* __restrict__ conv_b,
+                                                          float* __restrict__ conv_state,
+                                                          float* __restrict__ u, int D, int K) {
+  const int d = blockIdx.x * 256 + threadIdx.x;
+  const int b = blockIdx.y;
+  if (d >= D) return;
+  float* st = conv_state + ((int64_t)b * D + d) * K;
+  const float* w = conv_w + (int64_t)d * K;
+  float sv[kMaxConvK];
+  for (int k = 0; k + 1 < K; ++k) sv[k] = st[k + 1];
+  sv[K - 1] = xin.at(b, d);
+  float c = conv_b ? conv_b[d] : 0.0f;
+  for (int k = 0; k < K; ++k) c = fmaf(w[k], sv[k], c);
+  for (int k = 0; k < K; ++k) st[k] = sv[k];
+  u[(int64_t)b * D + d] = silu(c);
+}
+
+// SSM step of one layer with dt_proj folded in: the x_proj row of sequence b (dt low-rank
+// part | B | C, from its partial planes) is summed once into LDS; each channel's NQ lanes
+// then form dt = W_dt[d] . bf16(x[0 .. R)) (the projection's bf16 operands, f32 sums), and
+// go on as the SSM step (softplus(dt + bias), update, readout, D skip), with z from the
+// in_proj partials (columns zcol .. zcol + D - 1).
+template <int NQ, bool VEC4>
+__global__ void __launch_bounds__(256) decode_ssm_kernel(
+    const float* __restrict__ u, PartsView xd, const bf16* __restrict__ Wdt, int R,
+    const float* __restrict__ dt_bias, const float* __restrict__ A_log, const float* __restrict__ D_skip,
+    PartsView zin, int zcol, float* __restrict__ state, float* __restrict__ y, int D, int N) {
+  __shared__ float s_x[kDecodeMaxXProj];
+  const int b = blockIdx.y;
+  for (int i = threadIdx.x; i < R + 2 * N; i += 256) s_x[i] = xd.at(b, i);
+  __syncthreads();
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  const int d = t / NQ, q = t % NQ;
+  if (d >= D) return;  // whole NQ-lane groups drop out together
+
+  // lane q takes the contiguous columns [q * C, q * C + C) of W_dt's row d
+  float acc = 0.0f;
+  const bf16* wr = Wdt + (int64_t)d * R;
+  const int C = (R + NQ - 1) / NQ, r0 = q * C, r1 = min(R, r0 + C);
+  if (VEC4) {  // R a multiple of 4 NQ: C is a multiple of 4 and each run is 8-byte aligned
+    for (int r = r0; r < r1; r += 4) {
+      const uint2 wv = *reinterpret_cast<const uint2*>(wr + r);
+      acc = fmaf((float)(bf16)s_x[r], __uint_as_float(wv.x << 16), acc);
+      acc = fmaf((float)(bf16)s_x[r + 1], __uint_as_float(wv.x & 0xffff0000u), acc);
+      acc = fmaf((float)(bf16)s_x[r + 2], __uint_as_float(wv.y << 16), acc);
+      acc = fmaf((float)(bf16)s_x[r + 3], __uint_as_float(wv.y & 0xffff0000u), acc);
+    }
+  } else {
+    for (int r = r0; r < r1; ++r) acc = fmaf((float)(bf16)s_x[r], (float)wr[r], acc);
+  }
+#pragma unroll
+  for (int m = NQ / 2; m >= 1; m /= 2) acc += __shfl_xor(acc, m, NQ);
+
+  const int64_t ch = (int64_t)b * D + d;
+  const float uv = u[ch];
+  const float delta = softplus(acc + (dt_bias ? dt_bias[d] : 0.0f));
+  const float du = delta * uv;
+  float* hs = state + ch * N;
+  const float* al = A_log + (int64_t)d * N;
+  float part = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int n = 4 * q + j;
+    if (n < N) {
+      const float a2 = -__builtin_amdgcn_exp2f(al[n] * kLog2e) * kLog2e;
+      const float a = __builtin_amdgcn_exp2f(delta * a2);
+      const float hn = fmaf(a, hs[n], du * s_x[R + n]);
+      hs[n] = hn;
+      part = fmaf(s_x[R + N + n], hn, part);
+    }
+  }
+#pragma unroll
+  for (int m = NQ / 2; m >= 1; m /= 2) part += __shfl_xor(part, m, NQ);
+  if (q == 0) {
+    float yv = fmaf(D_skip ? D_skip[d] : 0.0f, uv, part);
+    yv *= silu(zin.at(b, zcol + d));
+    y[ch] = yv;
+  }
+}
+
+hipError_t launch_residual_rmsnorm(float* h, const PartsView& add, const float* w, float eps, void* out,
+                                   int rows, int Dm, hipStream_t s) {
+  residual_rmsnorm_kernel<<<dim3((unsigned)rows), 256, 0, s>>>(h, add, w, eps, static_cast<bf16*>(out), Dm);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_conv(const PartsView& xin, const float* conv_w, const float* conv_b,
+                              float* conv_state, float* u, int B, int D, int K, hipStream_t s) {
+  decode_conv_kernel<<<dim3((unsigned)((D + 255) / 256), (unsigned)B), 256, 0, s>>>(xin, conv_w, conv_b,
+                                                                                    conv_state, u, D, K);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_ssm(const float* u, const PartsView& xd, const void* Wdt, int R, const float* dt_bias,
+                             const float* A_log, const float* D_skip, const PartsView& zin, int zcol,
+                             float* state, float* y, int B, int D, int N, hipStream_t s) {
+  if (R + 2 * N > kDecodeMaxXProj || N > 64) return hipErrorInvalidValue;
+  const int q = (N + 3) / 4;
+  const int NQ = q <= 1 ? 1 : q <= 2 ? 2 : q <= 4 ? 4 : q <= 8 ? 8 : 16;
+  const dim3 grid((unsigned)(((int64_t)D * NQ + 255) / 256), (unsigned)B);
+  const bf16* w = static_cast<const bf16*>(Wdt);
+  // 8-byte loads of W_dt when every lane's run of columns is whole groups of four, aligned
+  const bool vec4 = R % (4 * NQ) == 0 && reinterpret_cast<uintptr_t>(Wdt) % 8 == 0;
+#define MAMBA_DECODE_SSM(NQV)                                                                         \
+  if (vec4)                                                                                           \
+    decode_ssm_kernel<NQV, true><<<grid, 256, 0, s>>>(u, xd, w, R, dt_bias, A_log, D_skip, zin, zcol, \
+                                                      state, y, D, N);                                \
+  else                                                                                                \
+    decode_ssm_kernel<NQV, false><<<grid, 256, 0, s>>>(u, xd, w, R, dt_bias, A_log, D_skip, zin, zcol, \
+                                                       state, y, D, N)
+  switch (NQ) {
+    case 1: MAMBA_DECODE_SSM(1); break;
+    case 2: MAMBA_DECODE_SSM(2); break;
+    case 4: MAMBA_DECODE_SSM(4); break;
+    case 8: MAMBA_DECODE_SSM(8); break;
+    default: MAMBA_DECODE_SSM(16); break;
+  }
+#undef MAMBA_DECODE_SSM
   return hipGetLastError();
 }
 

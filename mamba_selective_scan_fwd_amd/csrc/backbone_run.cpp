@@ -135,9 +135,14 @@ hipError_t run_backbone_prefill_io(const mamba_backbone_dims& d, const mamba_bac
 // the silu(z) gate (F10), out_proj (F11) and the residual (F12); then norm_f and the tied head
 // (gpu_lm.rs page). Same weights and state layout as the prefill, so a prefill followed by
 // decode steps continues one sequence.
+//
+// Six kernels per layer: RMSNorm with the previous layer's residual add, in_proj, the conv
+// step, x_proj, the SSM step (dt_proj, softplus, update, readout, skip, gate), out_proj. The
+// projections are split over K for the small batch; their partial planes are summed by the
+// kernels that read them (in slice order), not by a reduction kernel of their own.
 
 struct DecodeLayout {
-  size_t h, xn, proj, u, xdbl, dt, y, last, partial, total;
+  size_t h, xn, proj, u, xdbl, y, last, part_in, part_x, part_out, total;
 };
 
 static DecodeLayout decode_layout(const mamba_backbone_dims& d, int B) {
@@ -154,18 +159,18 @@ static DecodeLayout decode_layout(const mamba_backbone_dims& d, int B) {
   l.proj = take((size_t)B * 2 * d.d_inner * 4);
   l.u = take((size_t)B * d.d_inner * 4);
   l.xdbl = take((size_t)B * xw * 4);
-  l.dt = take((size_t)B * d.d_inner * 4);
   l.y = take((size_t)B * d.d_inner * 4);
   l.last = take((size_t)B * d.d_model * 2);
-  // split-K partial planes of the largest projection
-  size_t part = 0;
-  const int shapes[4][2] = {{2 * d.d_inner, d.d_model}, {(int)xw, d.d_inner}, {d.d_inner, d.dt_rank},
-                            {d.d_model, d.d_inner}};
-  for (const auto& nk : shapes) {
-    const int ks = gemm_splitk_slices(B, nk[0], nk[1]);
-    if (ks > 1) part = std::max(part, (size_t)ks * B * nk[0] * 4);
-  }
-  l.partial = take(part);
+  // split-K partial planes of in_proj (read by the conv step and, for z, by the SSM step),
+  // of x_proj (read by the SSM step) and of out_proj (read by the next RMSNorm): all three
+  // are live at once
+  auto parts = [&](int N, int K) {
+    const int ks = gemm_splitk_slices(B, N, K);
+    return ks > 1 ? (size_t)ks * B * N * 4 : 0;
+  };
+  l.part_in = take(parts(2 * d.d_inner, d.d_model));
+  l.part_x = take(parts((int)xw, d.d_inner));
+  l.part_out = take(parts(d.d_model, d.d_inner));
   l.total = off;
   return l;
 }
@@ -184,10 +189,11 @@ hipError_t run_backbone_decode(const mamba_backbone_dims& d, const mamba_backbon
   float* proj = reinterpret_cast<float*>(ws + lay.proj);
   float* u = reinterpret_cast<float*>(ws + lay.u);
   float* xdbl = reinterpret_cast<float*>(ws + lay.xdbl);
-  float* dt = reinterpret_cast<float*>(ws + lay.dt);
   float* y = reinterpret_cast<float*>(ws + lay.y);
   void* last = ws + lay.last;
-  float* partial = reinterpret_cast<float*>(ws + lay.partial);
+  float* part_in = reinterpret_cast<float*>(ws + lay.part_in);
+  float* part_x = reinterpret_cast<float*>(ws + lay.part_x);
+  float* part_out = reinterpret_cast<float*>(ws + lay.part_out);
 
   const int Dm = d.d_model, D = d.d_inner, N = d.d_state, K = d.d_conv, R = d.dt_rank;
   const int xw = R + 2 * N;
@@ -198,25 +204,30 @@ hipError_t run_backbone_decode(const mamba_backbone_dims& d, const mamba_backbon
 
   hipError_t e = launch_embed_gather(tokens, w.embed, h, B, d.vocab, Dm, s);
   if (e != hipSuccess) return e;
+  PartsView v_out{nullptr, 0, 0, 0};  // the previous layer's out_proj, not yet in h
   for (int l = 0; l < d.n_layers; ++l) {
-    if ((e = launch_rmsnorm(h, Dm, w.norm_w + (int64_t)l * Dm, d.eps, xn, true, B, Dm, s)) != hipSuccess) return e;
-    if ((e = launch_gemm_bf16_splitk(xn, true, Dm, in_proj + (int64_t)l * 2 * D * Dm, Dm, proj, 2 * D, B,
-                                     2 * D, Dm, false, partial, s)) != hipSuccess) return e;
-    ConvStepArgs ca{proj, 2 * D, w.conv_w + (int64_t)l * D * K, w.conv_b + (int64_t)l * D,
-                    conv_state + (int64_t)l * B * D * K, u, false, 1, B, D, K};
-    if ((e = launch_conv1d_step(ca, s)) != hipSuccess) return e;
-    if ((e = launch_gemm_bf16_splitk(u, false, D, x_proj + (int64_t)l * xw * D, D, xdbl, xw, B, xw, D, false,
-                                     partial, s)) != hipSuccess) return e;
-    if ((e = launch_gemm_bf16_splitk(xdbl, false, xw, dt_proj + (int64_t)l * D * R, R, dt, D, B, D, R, false,
-                                     partial, s)) != hipSuccess) return e;
-    SsmStepArgs sa{u, dt, w.dt_bias + (int64_t)l * D, true, w.A_log + (int64_t)l * D * N, xdbl + R,
-                   xdbl + R + N, xw, w.D_skip + (int64_t)l * D, proj + D, 2 * D,
-                   ssm_state + (int64_t)l * B * D * N, y, false, 1, B, D, N};
-    if ((e = launch_ssm_step(sa, s)) != hipSuccess) return e;
-    if ((e = launch_gemm_bf16_splitk(y, false, D, out_proj + (int64_t)l * Dm * D, D, h, Dm, B, Dm, D, true,
-                                     partial, s)) != hipSuccess) return e;
+    // F12 of the previous layer (residual) + F1
+    if ((e = launch_residual_rmsnorm(h, v_out, w.norm_w + (int64_t)l * Dm, d.eps, xn, B, Dm, s)) != hipSuccess)
+      return e;
+    PartsView v_in, v_x;
+    if ((e = launch_gemm_bf16_parts(xn, true, Dm, in_proj + (int64_t)l * 2 * D * Dm, Dm, proj, 2 * D, B, 2 * D,
+                                    Dm, false, part_in, &v_in, s)) != hipSuccess)
+      return e;
+    if ((e = launch_decode_conv(v_in, w.conv_w + (int64_t)l * D * K, w.conv_b + (int64_t)l * D,
+                                conv_state + (int64_t)l * B * D * K, u, B, D, K, s)) != hipSuccess)
+      return e;
+    if ((e = launch_gemm_bf16_parts(u, false, D, x_proj + (int64_t)l * xw * D, D, xdbl, xw, B, xw, D, false,
+                                    part_x, &v_x, s)) != hipSuccess)
+      return e;
+    if ((e = launch_decode_ssm(u, v_x, dt_proj + (int64_t)l * D * R, R, w.dt_bias + (int64_t)l * D,
+                               w.A_log + (int64_t)l * D * N, w.D_skip + (int64_t)l * D, v_in, D,
+                               ssm_state + (int64_t)l * B * D * N, y, B, D, N, s)) != hipSuccess)
+      return e;
+    if ((e = launch_gemm_bf16_parts(y, false, D, out_proj + (int64_t)l * Dm * D, D, h, Dm, B, Dm, D, true,
+                                    part_out, &v_out, s)) != hipSuccess)
+      return e;
   }
-  if ((e = launch_rmsnorm(h, Dm, w.norm_f, d.eps, last, true, B, Dm, s)) != hipSuccess) return e;
+  if ((e = launch_residual_rmsnorm(h, v_out, w.norm_f, d.eps, last, B, Dm, s)) != hipSuccess) return e;
   return launch_gemm_bf16(last, true, Dm, w.embed, Dm, logits, d.vocab, B, d.vocab, Dm, false, s);
 }
 

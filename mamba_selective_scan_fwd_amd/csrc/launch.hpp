@@ -171,7 +171,45 @@ constexpr int64_t kSkinnyGemmMaxLds = 64 * 1024;
 // Split-K GEMM for a decode batch (M <= kSplitKMaxM rows): the number of K slices for a
 // shape, and the launcher, which needs gemm_splitk_slices(M, N, K) * M * N floats of scratch.
 constexpr int kSplitKMaxM = 64;
+constexpr int kSplitKMaxSlices = 8;  // the readers of the partial planes add them one by one
 int gemm_splitk_slices(int M, int N, int K);
+
+// The result of a product that may be split over K: value(r, c) = sum over z < ks of
+// p[z * plane + r * ld + c], added in order z = 0, 1, ... (ks = 1, plane = 0 for a product
+// written whole; ks = 0 when it was added into its destination already).
+struct PartsView {
+  const float* p;
+  int ks;
+  int64_t plane, ld;
+  __host__ __device__ float at(int64_t r, int64_t c) const {
+    const float* q = p + r * ld + c;
+    float v = 0.0f;
+    int z = 0;
+    for (; z + 4 <= ks; z += 4) {  // four loads in flight, added in order
+      float t[4];
+      for (int i = 0; i < 4; ++i) t[i] = q[(z + i) * plane];
+      for (int i = 0; i < 4; ++i) v += t[i];
+    }
+    for (; z < ks; ++z) v += q[z * plane];
+    return v;
+  }
+};
+// C (+)= A W^T for a decode batch, left as split-K partial planes in `partial` (no reduction
+// kernel) or, when not split, written to (added into) C; *out describes where the result is.
+hipError_t launch_gemm_bf16_parts(const void* A, bool a_bf16, int64_t lda, const void* W,
+                                  int64_t ldw, float* C, int64_t ldc, int M, int N, int K,
+                                  bool accumulate, float* partial, PartsView* out, hipStream_t s);
+// Widest x_proj row (dt_rank + 2 d_state) the decode step's SSM kernel stages in LDS.
+constexpr int kDecodeMaxXProj = 1024;
+// Decode-step consumers of split-K results: residual add + RMSNorm, conv step on the x lane,
+// and the SSM step with dt_proj folded in.
+hipError_t launch_residual_rmsnorm(float* h, const PartsView& add, const float* w, float eps, void* out,
+                                   int rows, int Dm, hipStream_t s);
+hipError_t launch_decode_conv(const PartsView& xin, const float* conv_w, const float* conv_b,
+                              float* conv_state, float* u, int B, int D, int K, hipStream_t s);
+hipError_t launch_decode_ssm(const float* u, const PartsView& xd, const void* Wdt, int R, const float* dt_bias,
+                             const float* A_log, const float* D_skip, const PartsView& zin, int zcol,
+                             float* state, float* y, int B, int D, int N, hipStream_t s);
 hipError_t launch_gemm_bf16_splitk(const void* A, bool a_bf16, int64_t lda, const void* W,
                                    int64_t ldw, float* C, int64_t ldc, int M, int N, int K,
                                    bool accumulate, float* partial, hipStream_t s);
