@@ -494,6 +494,7 @@ __global__ void __launch_bounds__(256) residual_rmsnorm_kernel(float* __restrict
 
 // Conv step on the x lane of the in_proj output (columns 0 .. D-1), the same arithmetic as
 // conv1d_step_kernel: shift the K-slot window, append x, taps from the oldest, SiLU.
+template <bool K4>
 __global__ void __launch_bounds__(256) decode_conv_kernel(PartsView xin, const float* __restrict__ conv_w,
                                                           const float* __restrict__ conv_b,
                                                           float* __restrict__ conv_state,
@@ -503,12 +504,23 @@ __global__ void __launch_bounds__(256) decode_conv_kernel(PartsView xin, const f
   if (d >= D) return;
   float* st = conv_state + ((int64_t)b * D + d) * K;
   const float* w = conv_w + (int64_t)d * K;
-  float sv[kMaxConvK];
-  for (int k = 0; k + 1 < K; ++k) sv[k] = st[k + 1];
-  sv[K - 1] = xin.at(b, d);
+  const float xv = xin.at(b, d);
   float c = conv_b ? conv_b[d] : 0.0f;
-  for (int k = 0; k < K; ++k) c = fmaf(w[k], sv[k], c);
-  for (int k = 0; k < K; ++k) st[k] = sv[k];
+  if (K4) {  // the 4-slot window and taps as 16-byte accesses
+    const float4 v = *reinterpret_cast<const float4*>(st);
+    const float4 wv = *reinterpret_cast<const float4*>(w);
+    c = fmaf(wv.x, v.y, c);
+    c = fmaf(wv.y, v.z, c);
+    c = fmaf(wv.z, v.w, c);
+    c = fmaf(wv.w, xv, c);
+    *reinterpret_cast<float4*>(st) = make_float4(v.y, v.z, v.w, xv);
+  } else {
+    float sv[kMaxConvK];
+    for (int k = 0; k + 1 < K; ++k) sv[k] = st[k + 1];
+    sv[K - 1] = xv;
+    for (int k = 0; k < K; ++k) c = fmaf(w[k], sv[k], c);
+    for (int k = 0; k < K; ++k) st[k] = sv[k];
+  }
   u[(int64_t)b * D + d] = silu(c);
 }
 
@@ -555,15 +567,34 @@ __global__ void __launch_bounds__(256) decode_ssm_kernel(
   float* hs = state + ch * N;
   const float* al = A_log + (int64_t)d * N;
   float part = 0.0f;
+  if (VEC4 && N % 4 == 0) {
+    // four states per lane as one 16-byte access (N a multiple of 4: rows 16-byte aligned)
+    const int n0 = 4 * q;
+    if (n0 < N) {
+      const float4 hv = *reinterpret_cast<const float4*>(hs + n0);
+      const float4 av = *reinterpret_cast<const float4*>(al + n0);
+      const float hh[4] = {hv.x, hv.y, hv.z, hv.w}, aa[4] = {av.x, av.y, av.z, av.w};
+      float hn[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int n = 4 * q + j;
-    if (n < N) {
-      const float a2 = -__builtin_amdgcn_exp2f(al[n] * kLog2e) * kLog2e;
-      const float a = __builtin_amdgcn_exp2f(delta * a2);
-      const float hn = fmaf(a, hs[n], du * s_x[R + n]);
-      hs[n] = hn;
-      part = fmaf(s_x[R + N + n], hn, part);
+      for (int j = 0; j < 4; ++j) {
+        const float a2 = -__builtin_amdgcn_exp2f(aa[j] * kLog2e) * kLog2e;
+        const float a = __builtin_amdgcn_exp2f(delta * a2);
+        hn[j] = fmaf(a, hh[j], du * s_x[R + n0 + j]);
+        part = fmaf(s_x[R + N + n0 + j], hn[j], part);
+      }
+      *reinterpret_cast<float4*>(hs + n0) = make_float4(hn[0], hn[1], hn[2], hn[3]);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = 4 * q + j;
+      if (n < N) {
+        const float a2 = -__builtin_amdgcn_exp2f(al[n] * kLog2e) * kLog2e;
+        const float a = __builtin_amdgcn_exp2f(delta * a2);
+        const float hn = fmaf(a, hs[n], du * s_x[R + n]);
+        hs[n] = hn;
+        part = fmaf(s_x[R + N + n], hn, part);
+      }
     }
   }
 #pragma unroll
@@ -583,8 +614,11 @@ hipError_t launch_residual_rmsnorm(float* h, const PartsView& add, const float* 
 
 hipError_t launch_decode_conv(const PartsView& xin, const float* conv_w, const float* conv_b,
                               float* conv_state, float* u, int B, int D, int K, hipStream_t s) {
-  decode_conv_kernel<<<dim3((unsigned)((D + 255) / 256), (unsigned)B), 256, 0, s>>>(xin, conv_w, conv_b,
-                                                                                    conv_state, u, D, K);
+  const dim3 grid((unsigned)((D + 255) / 256), (unsigned)B);
+  if (K == 4 && ((reinterpret_cast<uintptr_t>(conv_w) | reinterpret_cast<uintptr_t>(conv_state)) & 15) == 0)
+    decode_conv_kernel<true><<<grid, 256, 0, s>>>(xin, conv_w, conv_b, conv_state, u, D, K);
+  else
+    decode_conv_kernel<false><<<grid, 256, 0, s>>>(xin, conv_w, conv_b, conv_state, u, D, K);
   return hipGetLastError();
 }
 
@@ -597,7 +631,8 @@ hipError_t launch_decode_ssm(const float* u, const PartsView& xd, const void* Wd
   const dim3 grid((unsigned)(((int64_t)D * NQ + 255) / 256), (unsigned)B);
   const bf16* w = static_cast<const bf16*>(Wdt);
   // 8-byte loads of W_dt when every lane's run of columns is whole groups of four, aligned
-  const bool vec4 = R % (4 * NQ) == 0 && reinterpret_cast<uintptr_t>(Wdt) % 8 == 0;
+  const bool vec4 = R % (4 * NQ) == 0 && reinterpret_cast<uintptr_t>(Wdt) % 8 == 0 && N % 4 == 0 &&
+                    ((reinterpret_cast<uintptr_t>(state) | reinterpret_cast<uintptr_t>(A_log)) & 15) == 0;
 #define MAMBA_DECODE_SSM(NQV)                                                                         \
   if (vec4)                                                                                           \
     decode_ssm_kernel<NQV, true><<<grid, 256, 0, s>>>(u, xd, w, R, dt_bias, A_log, D_skip, zin, zcol, \
