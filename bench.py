@@ -34,6 +34,11 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 METRIC = "selective-scan prefill tokens/s/layer (d_inner=1536/5120) + HBM GB/s % peak"
+# VALU issue rate without packed fp32: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz lane-slots/s
+VALU_SLOTS_PER_S = 256 * 4 * 16 * 2.4e9
+# the scan's minimal issue slots per (t, d, n): delta*A, exp2 (two slots), delta*u*B, the
+# state fma and the readout fma
+SCAN_SLOTS_PER_ELEMENT = 6
 
 
 def parse_args(argv=None):
@@ -227,6 +232,12 @@ def bench_prefill(args, shape):
         layer_gbs=lb / (ms_step * 1e-3) / 1e9,
     )
     result["layer_hbm_frac"] = result["layer_gbs"] / HBM_PEAK_GBS
+    # the arithmetic floor of the scan (one pass over B*T*D*N elements at the VALU issue rate)
+    # beside its HBM floor: the one that is higher bounds the layer
+    floor_s = B * T * D * N * SCAN_SLOTS_PER_ELEMENT / VALU_SLOTS_PER_S
+    result["valu_floor_us"] = floor_s * 1e6
+    result["hbm_floor_us"] = lb / (HBM_PEAK_GBS * 1e9) * 1e6
+    result["valu_frac"] = floor_s / (ms_step * 1e-3)
     return result, inp
 
 
@@ -760,7 +771,7 @@ def main(argv=None):
         data="synthetic", config=result["config"], roofline=result["roofline"],
         cpu_baseline=cpu, calls=result["calls"], layer_gbs=result["layer_gbs"],
         layer_hbm_frac=result["layer_hbm_frac"])
-    for extra in ("backbone_tokens_per_s", "layer_chain_us"):
+    for extra in ("backbone_tokens_per_s", "layer_chain_us", "valu_floor_us", "hbm_floor_us", "valu_frac"):
         if extra in result:
             line[extra] = result[extra]
     print(json.dumps(line), flush=True)
