@@ -471,8 +471,9 @@ def test_backbone_ragged_batch_vs_oracle(T, lengths):
 
 def test_backbone_decode_batch16_splitk_vs_oracle():
     """A decode batch of 16 on a wider 2-layer stack (d_model 256, d_inner 512): the
-    projections run as split-K GEMMs (64 x 32 and 32 x 80 tiles, 2..8 K slices) with a fixed-
-    order reduction; logits and states after 4 decode steps against the oracle."""
+    projections run as split-K GEMMs (64 x 32 and 32 x 80 tiles, 2..8 K slices) whose partial
+    planes are summed by the kernels that read them; logits and states after 4 decode steps
+    against the oracle."""
     _say("case backbone decode B16, split-K projections")
     s = W.BackboneShape("wide", n_layers=2, B=16, T=12, d_model=256, D=512, N=16, K=4, dt_rank=16,
                         vocab=300, vocab_padded=320)
@@ -484,3 +485,24 @@ def test_backbone_decode_batch16_splitk_vs_oracle():
     for i, (g_, r_) in enumerate(zip(got, ref)):
         assert rel_err(g_, r_) <= TOL_BF16, i
     _check_backbone("decode B16", (got[-1], cs, hs), (ref[-1], rcs, rhs))
+
+
+@pytest.mark.parametrize("K,N,R,B,Dm,D", [
+    (3, 24, 32, 12, 128, 256),  # 8 lanes per channel (6 busy), 16-byte paths, split-K
+    (2, 10, 12, 9, 128, 192),   # d_state not a multiple of 4: element-wise state and dt paths
+])
+def test_backbone_decode_odd_shapes_vs_oracle(K, N, R, B, Dm, D):
+    """Decode steps with a conv width other than 4, d_state 10 or 24 and dt_rank 12 or 32:
+    the general paths of the decode kernels (window shift, lanes per channel, dt projection)
+    against the oracle over 3 steps after a 5-token prefill."""
+    _say(f"case backbone decode K{K} N{N} R{R} B{B}")
+    s = W.BackboneShape(f"odd{K}{N}", n_layers=2, B=B, T=8, d_model=Dm, D=D, N=N, K=K, dt_rank=R,
+                        vocab=150, vocab_padded=160)
+    w = W.backbone_weights(s, seed=21)
+    tok = W.backbone_tokens(s, seed=21)
+    t, st = _upload(w)
+    got, cs, hs = _prefill_then_decode(s, t, st, tok, 5)
+    ref, rcs, rhs = _oracle_prefill_then_decode(s, w, tok, 5)
+    for i, (g_, r_) in enumerate(zip(got, ref)):
+        assert rel_err(g_, r_) <= TOL_BF16, i
+    _check_backbone(f"decode K{K} N{N}", (got[-1], cs, hs), (ref[-1], rcs, rhs))
