@@ -6,20 +6,23 @@
 // GpuMambaInference::new (A = -exp(A_log)). Softplus, A = -exp(A_log), the D skip and the
 // gate are all fused here: u, dt, z, B and C are read once and y is written once.
 //
-// Workgroup = 64 consecutive channels x all NP (padded) states, as kWaves waves. Wave q
-// owns states [q*S, (q+1)*S) of every channel (lanes run along d, S = NP / kWaves states
-// in registers per lane), so a channel's recurrence is split over the waves by state, not
-// by time: there is no rescan and the whole T of a chunk is walked once.
+// Workgroup = CH consecutive channels (32; 64 when N > 32) x all NP (padded) states, as W
+// waves. Each lane holds one channel and one group of S consecutive states in registers
+// (S = 2 at N = 16): lanes 0..CH-1 of a wave take one state group, the next CH lanes the
+// next. A channel's recurrence is thus split over lanes and waves by state, not by time:
+// there is no rescan and the whole T of a chunk is walked once.
 //
 // The per-token work that does not depend on the state is shared through LDS, in blocks of
-// kWaves tokens: in each block wave q computes delta (softplus) and delta*u for token q of
-// the block and silu(z) for the same token, and stages part of the block's B/C rows; every
-// wave then reads delta, delta*u and its states' B/C values for the block's tokens from LDS
-// and advances its S states, leaving its partial C.h per token in LDS; after the barrier
-// wave q adds the kWaves partials of token q, the D skip and the gate, and stores y. The
-// block buffers are double-buffered, so one barrier per block orders everything.
+// kTB = 8 tokens. In each block every thread owns one (token, channel) item: it computes
+// delta (softplus), delta*u and silu(z) for that item (and, with the conv fused, u itself
+// from its K raw inputs) and stages part of the block's B/C rows. Every lane then reads
+// delta, delta*u and its states' B/C values for the block's tokens from LDS, advances its S
+// states and leaves its partial C.h per token in LDS; after the barrier each item's owner
+// adds the partials of its item, the D skip and the gate, and stores y. The block buffers
+// are double-buffered, so one barrier per block orders everything, and the global loads of
+// a block are issued one block before their use.
 //
-// T parallelism: when B * ceil(D/64) workgroups cannot fill the chip, T is cut into chunks.
+// T parallelism: when B * ceil(D/CH) workgroups cannot fill the chip, T is cut into chunks.
 // A chunk acts on the state as h -> P*h + H per (b, d, n), P = exp(A * sum(delta)) and H the
 // state it reaches from h = 0. A summary pass computes (sum(delta), H) of every chunk but
 // the last; the output pass starts each chunk from the carried state folded through the
