@@ -146,19 +146,39 @@ __device__ __forceinline__ bf16x8 load_chunk_scalar(const AT* row, int k0, int K
   return r;
 }
 
+#ifndef MAMBA_GEMM_WPE
+#define MAMBA_GEMM_WPE 2  // waves per SIMD the register allocation must allow
+#endif
+
 template <typename AT, int BM, int BN, int BK, int WGM, int WGN, bool VEC>
-__global__ void __launch_bounds__(64 * WGM * WGN) gemm_mfma_kernel(
+__global__ void __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(MAMBA_GEMM_WPE)))
+gemm_mfma_kernel(
     const AT* __restrict__ A, int64_t lda, const bf16* __restrict__ W, int64_t ldw,
     float* __restrict__ C, int64_t ldc, int M, int N, int K, int accumulate, int k_chunk,
     int64_t c_split_stride) {
+  // XCD-aware tile order. Workgroups are handed to the 8 XCDs (each with its own L2) in
+  // round-robin order of their linear id, so neighbouring ids land on different L2s. Here
+  // each XCD takes one contiguous run of tiles instead, in (slice, m, n) order with n
+  // fastest: the tiles that share an A row block run on one XCD at about the same time, and
+  // the row block is fetched into that L2 once rather than once per XCD.
+  // (Split-K launches keep the plain order: their slices share no operand rows.)
+  int bx = blockIdx.x, by = blockIdx.y, bz = blockIdx.z;
+  if (gridDim.z == 1) {
+    const int gx = gridDim.x, G = gx * (int)gridDim.y;
+    const int L = blockIdx.x + gx * blockIdx.y;
+    const int xcd = L % 8, idx = L / 8, base = G / 8, rem = G % 8;
+    const int t = xcd * base + min(xcd, rem) + idx;  // a bijection of [0, G)
+    bx = t % gx;
+    by = t / gx;
+  }
   // split K (gridDim.z > 1): slice z covers k in [z * k_chunk, z * k_chunk + k_chunk) and
   // writes its partial product to its own C plane (C + z * c_split_stride)
   {
-    const int k0 = blockIdx.z * k_chunk;
+    const int k0 = bz * k_chunk;
     A += k0;
     W += k0;
     K = min(K - k0, k_chunk);
-    C += blockIdx.z * c_split_stride;
+    C += bz * c_split_stride;
   }
   constexpr int NT = 64 * WGM * WGN;
   constexpr int WTM = BM / WGM, WTN = BN / WGN;  // wave tile
@@ -174,21 +194,26 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_mfma_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WGN, wn = wave % WGN;
-  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+  const int m0 = by * BM, n0 = bx * BN;
 
-  bf16x8 ra[A_CH], rw[W_CH];
-  auto fetch = [&](int k0) {
+  // Two register sets of staged chunks: the loads of slab kt+2 are issued while slab kt is
+  // multiplied and slab kt+1 (loaded one iteration earlier) is written to LDS, so a load has
+  // a whole iteration to arrive. A tile entirely inside the operands skips the bounds checks.
+  bf16x8 ra[2][A_CH], rw[2][W_CH];
+  const bool full = VEC && m0 + BM <= M && n0 + BN <= N && K % BK == 0;
+  auto fetch = [&](int k0, auto SET) {
+    constexpr int st = decltype(SET)::value;
 #pragma unroll
     for (int i = 0; i < A_CH; ++i) {
       const int c = tid + i * NT, r = c / CPR, kc = (c % CPR) * 8;
       const int gm = m0 + r, gk = k0 + kc;
       if constexpr (VEC) {
         Chunk<AT> ch;
-        if (gm < M && gk < K) load_chunk<AT>(ch, A + (int64_t)gm * lda + gk);
+        if (full || (gm < M && gk < K)) load_chunk<AT>(ch, A + (int64_t)gm * lda + gk);
         else zero_chunk<AT>(ch);
-        ra[i] = to_bf16x8(ch);
+        ra[st][i] = to_bf16x8(ch);
       } else {
-        ra[i] = gm < M ? load_chunk_scalar(A + (int64_t)gm * lda, gk, K) : bf16x8{};
+        ra[st][i] = gm < M ? load_chunk_scalar(A + (int64_t)gm * lda, gk, K) : bf16x8{};
       }
     }
 #pragma unroll
@@ -197,24 +222,25 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_mfma_kernel(
       const int gn = n0 + r, gk = k0 + kc;
       if constexpr (VEC) {
         Chunk<bf16> ch;
-        if (gn < N && gk < K) load_chunk<bf16>(ch, W + (int64_t)gn * ldw + gk);
+        if (full || (gn < N && gk < K)) load_chunk<bf16>(ch, W + (int64_t)gn * ldw + gk);
         else zero_chunk<bf16>(ch);
-        rw[i] = to_bf16x8(ch);
+        rw[st][i] = to_bf16x8(ch);
       } else {
-        rw[i] = gn < N ? load_chunk_scalar(W + (int64_t)gn * ldw, gk, K) : bf16x8{};
+        rw[st][i] = gn < N ? load_chunk_scalar(W + (int64_t)gn * ldw, gk, K) : bf16x8{};
       }
     }
   };
-  auto stash = [&](int buf) {
+  auto stash = [&](int buf, auto SET) {
+    constexpr int st = decltype(SET)::value;
 #pragma unroll
     for (int i = 0; i < A_CH; ++i) {
       const int c = tid + i * NT;
-      *reinterpret_cast<bf16x8*>(&As[buf][(c / CPR) * LDK + (c % CPR) * 8]) = ra[i];
+      *reinterpret_cast<bf16x8*>(&As[buf][(c / CPR) * LDK + (c % CPR) * 8]) = ra[st][i];
     }
 #pragma unroll
     for (int i = 0; i < W_CH; ++i) {
       const int c = tid + i * NT;
-      *reinterpret_cast<bf16x8*>(&Ws[buf][(c / CPR) * LDK + (c % CPR) * 8]) = rw[i];
+      *reinterpret_cast<bf16x8*>(&Ws[buf][(c / CPR) * LDK + (c % CPR) * 8]) = rw[st][i];
     }
   };
 
@@ -224,14 +250,11 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_mfma_kernel(
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
   const int nk = (K + BK - 1) / BK;
-  fetch(0);
-  stash(0);
-  __syncthreads();
   const int frow = lane & 15, fk = (lane >> 4) * 8;
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) fetch((kt + 1) * BK);
+  auto multiply = [&](int buf) {
 #pragma unroll
     for (int kk = 0; kk < BK; kk += 32) {
       bf16x8 af[TM], bfr[TN];
@@ -247,8 +270,23 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_mfma_kernel(
         for (int j = 0; j < TN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
     }
-    if (kt + 1 < nk) stash(buf ^ 1);
+  };
+  // iteration kt: loads of slab kt+2 into set kt & 1, multiply LDS buffer kt & 1, write slab
+  // kt+1 (set (kt+1) & 1) into LDS buffer (kt+1) & 1, barrier
+  auto step = [&](int kt, auto SET) {
+    constexpr int st = decltype(SET)::value;  // == kt & 1
+    if (kt + 2 < nk) fetch((kt + 2) * BK, SET);
+    multiply(st);
+    if (kt + 1 < nk) stash(st ^ 1, std::integral_constant<int, st ^ 1>{});
     __syncthreads();
+  };
+  fetch(0, S0{});
+  if (nk > 1) fetch(BK, S1{});
+  stash(0, S0{});
+  __syncthreads();
+  for (int kt = 0; kt < nk; kt += 2) {
+    step(kt, S0{});
+    if (kt + 1 < nk) step(kt + 1, S1{});
   }
 
   // epilogue: lane holds rows 4*(lane/16)+0..3 of column lane%16 of each 16x16 tile
