@@ -48,4 +48,17 @@ __device__ __forceinline__ float softplus(float v) {
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
+// 16-byte load and store of data streamed through once (a state read and rewritten by one
+// step): marked non-temporal, so they do not push reused data (weights, shared rows) out of
+// the caches. p must be 16-byte aligned.
+__device__ __forceinline__ float4 load_stream4(const float* p) {
+  typedef float f4 __attribute__((ext_vector_type(4)));
+  const f4 v = __builtin_nontemporal_load(reinterpret_cast<const f4*>(p));
+  return make_float4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ void store_stream4(float* p, float4 v) {
+  typedef float f4 __attribute__((ext_vector_type(4)));
+  __builtin_nontemporal_store(f4{v.x, v.y, v.z, v.w}, reinterpret_cast<f4*>(p));
+}
+
 }  // namespace mamba

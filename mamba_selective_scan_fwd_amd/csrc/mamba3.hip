@@ -63,7 +63,7 @@ __global__ void __launch_bounds__(kThreads) m3_siso_step_kernel(const M3StepArgs
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int p = sub + u * RPB;
-    hv[u] = active && p < hd ? *reinterpret_cast<const float4*>(hs + (int64_t)p * ds + n0)
+    hv[u] = active && p < hd ? load_stream4(hs + (int64_t)p * ds + n0)
                              : make_float4(0.f, 0.f, 0.f, 0.f);
   }
 
@@ -144,7 +144,7 @@ __global__ void __launch_bounds__(kThreads) m3_siso_step_kernel(const M3StepArgs
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int p = p0 + sub + u * RPB;
-        hv[u] = active && p < hd ? *reinterpret_cast<const float4*>(hs + (int64_t)p * ds + n0)
+        hv[u] = active && p < hd ? load_stream4(hs + (int64_t)p * ds + n0)
                                  : make_float4(0.f, 0.f, 0.f, 0.f);
       }
     }
@@ -159,7 +159,7 @@ __global__ void __launch_bounds__(kThreads) m3_siso_step_kernel(const M3StepArgs
       hn.y = fmaf(alpha, hv[u].y, fmaf(kc[1], vp, xc[1] * xx));
       hn.z = fmaf(alpha, hv[u].z, fmaf(kc[2], vp, xc[2] * xx));
       hn.w = fmaf(alpha, hv[u].w, fmaf(kc[3], vp, xc[3] * xx));
-      if (on) *reinterpret_cast<float4*>(hs + (int64_t)p * ds + n0) = hn;
+      if (on) store_stream4(hs + (int64_t)p * ds + n0, hn);
       yp[u] = (qv[0] * hn.x + qv[1] * hn.y) + (qv[2] * hn.z + qv[3] * hn.w);
     }
 #pragma unroll

@@ -62,7 +62,7 @@ __global__ void __launch_bounds__(256) ssm_step_kernel(
 
   float h[4], alog[4], bv[4], cv[4];
   if constexpr (VEC) {
-    const float4 hv = *reinterpret_cast<const float4*>(hs + n0);
+    const float4 hv = load_stream4(hs + n0);
     const float4 av = *reinterpret_cast<const float4*>(al + n0);
     h[0] = hv.x; h[1] = hv.y; h[2] = hv.z; h[3] = hv.w;
     alog[0] = av.x; alog[1] = av.y; alog[2] = av.z; alog[3] = av.w;
@@ -85,7 +85,7 @@ __global__ void __launch_bounds__(256) ssm_step_kernel(
     part = fmaf(cv[j], h[j], part);
   }
   if constexpr (VEC) {
-    *reinterpret_cast<float4*>(hs + n0) = make_float4(h[0], h[1], h[2], h[3]);
+    store_stream4(hs + n0, make_float4(h[0], h[1], h[2], h[3]));
   } else {
 #pragma unroll
     for (int j = 0; j < 4; ++j)
@@ -185,11 +185,11 @@ __global__ void __launch_bounds__(256) decode_step_kernel(const DecodeStepArgs a
     const float xin = to_f32(static_cast<const IO*>(a.x)[(int64_t)lb * a.x_row_stride + d]);
     float c = cb;
     if (VEC && K == 4) {
-      const float4 sv = *reinterpret_cast<const float4*>(cst);
+      const float4 sv = load_stream4(cst);
       sreg[0] = sv.y; sreg[1] = sv.z; sreg[2] = sv.w; sreg[3] = xin;
 #pragma unroll
       for (int k = 0; k < 4; ++k) c = fmaf(wk[k], sreg[k], c);
-      if (q == 0) *reinterpret_cast<float4*>(cst) = make_float4(sreg[0], sreg[1], sreg[2], sreg[3]);
+      if (q == 0) store_stream4(cst, make_float4(sreg[0], sreg[1], sreg[2], sreg[3]));
     } else {
 #pragma unroll
       for (int k = 0; k < kMaxConvK; ++k) {
@@ -217,7 +217,7 @@ __global__ void __launch_bounds__(256) decode_step_kernel(const DecodeStepArgs a
     float* hs = a.ssm_state + ch * N;
     float h[4], bv[4], cv[4];
     if constexpr (VEC) {
-      const float4 hv = *reinterpret_cast<const float4*>(hs + n0);
+      const float4 hv = load_stream4(hs + n0);
       h[0] = hv.x; h[1] = hv.y; h[2] = hv.z; h[3] = hv.w;
     } else {
 #pragma unroll
@@ -233,7 +233,7 @@ __global__ void __launch_bounds__(256) decode_step_kernel(const DecodeStepArgs a
       part = fmaf(cv[j], h[j], part);
     }
     if constexpr (VEC) {
-      *reinterpret_cast<float4*>(hs + n0) = make_float4(h[0], h[1], h[2], h[3]);
+      store_stream4(hs + n0, make_float4(h[0], h[1], h[2], h[3]));
     } else {
 #pragma unroll
       for (int j = 0; j < 4; ++j)
