@@ -25,10 +25,13 @@ struct Vec {
     if constexpr (V == 1) {
       v[0] = to_f32(p[0]);
     } else if constexpr (sizeof(IO) == 4) {
-      const float4 f = *reinterpret_cast<const float4*>(p);
+      // x is read once here (non-temporal: it does not displace reused lines)
+      const float4 f = load_stream4(reinterpret_cast<const float*>(p));
       v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
     } else {
-      const uint2 r = *reinterpret_cast<const uint2*>(p);
+      typedef unsigned u2 __attribute__((ext_vector_type(2)));
+      const u2 rr = __builtin_nontemporal_load(reinterpret_cast<const u2*>(p));
+      const uint2 r = make_uint2(rr[0], rr[1]);
       v[0] = __uint_as_float(r.x << 16);
       v[1] = __uint_as_float(r.x & 0xffff0000u);
       v[2] = __uint_as_float(r.y << 16);
