@@ -41,9 +41,13 @@ __device__ __forceinline__ float log1p_small(float e) {
 
 // softplus(v) = log(1 + exp(v)) = max(v, 0) + log1p(exp(-|v|)), with no overflow.
 // At the dt-bias values of Mamba layers (v around -7..-2) a plain log(1 + exp(v)) in f32
-// loses most of its digits; the compensated log1p keeps the relative error near 1e-7.
+// loses most of its digits; the compensated log1p keeps the relative error near 1e-7. (The
+// log1p is written out here so that max(v, 0) - c and the log share one fma.)
 __device__ __forceinline__ float softplus(float v) {
-  return fmaxf(v, 0.0f) + log1p_small(fast_exp(-fabsf(v)));
+  const float e = fast_exp(-fabsf(v));
+  const float w = 1.0f + e;
+  const float c = (w - 1.0f) - e;  // the rounding error of w, exactly
+  return fmaf(__builtin_amdgcn_logf(w), kLn2, (v > 0.0f ? v : 0.0f) - c);
 }
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }

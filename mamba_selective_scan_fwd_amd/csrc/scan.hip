@@ -355,7 +355,8 @@ scan_kernel(const ScanParams p) {
     for (int r = 0; r < BC_PER_T; ++r) {
       const int i = threadIdx.x + r * NT;
       if (i < kTB * BCW)
-        s_bc[st][bc_j[r]][i % BCW] = (bc_use[r] && k * kTB + bc_j[r] < len) ? to_f32(pf_bc[st][r]) : 0.0f;
+        // (tokens past the chunk's end are never scanned, so only padded states need zeros)
+        s_bc[st][bc_j[r]][i % BCW] = bc_use[r] ? to_f32(pf_bc[st][r]) : 0.0f;
     }
   };
 
