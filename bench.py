@@ -15,7 +15,10 @@ backbone for 64 sequences (after a 64-token prefill), replayed from its captured
 
 Prints one JSON line. `value` is tokens/s/layer (batch tokens per step / step time);
 `roofline` covers the dominant kernel call, timed with HIP events on the stream it runs
-on; `cpu_baseline` is the f64 CPU oracle timed on the host on a bounded sample.
+on: for prefill the call holding the scan against the VALU issue rate (the scan is
+arithmetic-bound; its HBM rate is reported beside it), for the decode steps HBM, for the
+backbone prefill the GEMMs against bf16 MFMA. `cpu_baseline` is the f64 CPU oracle timed on
+the host on a bounded sample.
 """
 from __future__ import annotations
 
@@ -34,18 +37,29 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 METRIC = "selective-scan prefill tokens/s/layer (d_inner=1536/5120) + HBM GB/s % peak"
-# VALU issue rate without packed fp32: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz lane-slots/s
-VALU_SLOTS_PER_S = 256 * 4 * 16 * 2.4e9
-# the scan's minimal issue slots per (t, d, n): delta*A, exp2 (two slots), delta*u*B, the
-# state fma and the readout fma
-SCAN_SLOTS_PER_ELEMENT = 6
+# VALU issue rate: the published fp32 vector peak, 157.3 TFLOP/s, is 78.6 T fp32 FMAs/s:
+# 256 CUs x 128 FMA lanes per clock x 2.4 GHz. One slot = one lane of one full-rate fp32 op.
+# Plain (unpacked) fp32 ops reach this rate on gfx950: independent v_fma_f32 streams measured
+# 83% of it at 16 waves per SIMD, 68% at 5.
+VALU_SLOTS_PER_S = 256 * 128 * 2.4e9
+# v_exp_f32 issues at quarter rate: 4 slots (measured at 3.6-4 fma slots in a mixed stream)
+EXP_SLOTS = 4
+# the scan's minimal slots per (t, d, n): delta*A, exp2, delta*u*B, the state fma and the
+# readout fma
+SCAN_SLOTS_PER_ELEMENT = 4 + EXP_SLOTS
+# default warm-up steps per config, about 0.1 s of work each: from idle the GPU clock takes
+# tens of milliseconds of load to ramp up (the 130m layer call measured 44 us after 20 warm-up
+# steps, 40 us after 2000)
+DEFAULT_WARMUP = {"c1": 2000, "c3": 100, "c2": 1000, "c5": 200, "c4": 10, "c4d": 100}
 
 
 def parse_args(argv=None):
     p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
-    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=None,
+                   help="untimed steps before the timed ones (default: about 0.1 s of work for the "
+                        "config; the GPU clock ramps up over the first tens of milliseconds of load)")
     p.add_argument("--config", default="c1", choices=["c1", "c3", "c2", "c4", "c4d", "c5"])
     p.add_argument("--path", default="auto", choices=["auto", "fused", "split"],
                    help="prefill: one fused mamba_conv_scan_fwd call, or mamba_conv1d_fwd then "
@@ -123,6 +137,60 @@ def _events(torch):
     return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
 
+HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000  # hipEventDisableSystemFence (hip_runtime_api.h)
+_hip_rt = None
+
+
+def _hip():
+    """The HIP runtime the process already uses (torch loads it; same soname)."""
+    global _hip_rt
+    if _hip_rt is None:
+        import ctypes
+        rt = ctypes.CDLL("libamdhip64.so.7")
+        rt.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        rt.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        rt.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                           ctypes.c_void_p]
+        rt.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        _hip_rt = rt
+    return _hip_rt
+
+
+def _hip_ok(rc, what):
+    if rc != 0:
+        raise RuntimeError(f"{what} failed with HIP error {rc}")
+
+
+class TimingEvent:
+    """A HIP event used only for timing, created with hipEventDisableSystemFence. Recording a
+    default event (torch's) ends with a system-scope fence, a cache write-back and invalidate
+    that stalls the GPU between the calls it brackets: at the 130m layer three such events per
+    step added about 12 us to a 39 us call. Same interface as torch.cuda.Event."""
+
+    def __init__(self):
+        import ctypes
+        self._ct = ctypes
+        self.h = ctypes.c_void_p()
+        _hip_ok(_hip().hipEventCreateWithFlags(ctypes.byref(self.h), HIP_EVENT_DISABLE_SYSTEM_FENCE),
+                "hipEventCreateWithFlags")
+
+    def record(self, stream):
+        _hip_ok(_hip().hipEventRecord(self.h, self._ct.c_void_p(stream.cuda_stream)), "hipEventRecord")
+
+    def elapsed_time(self, other):
+        ms = self._ct.c_float()
+        _hip_ok(_hip().hipEventElapsedTime(self._ct.byref(ms), self.h, other.h), "hipEventElapsedTime")
+        return ms.value
+
+    def __del__(self):
+        if self.h:
+            _hip().hipEventDestroy(self.h)
+
+
+def _call_events(n):
+    return tuple(TimingEvent() for _ in range(n))
+
+
 def bench_prefill(args, shape):
     import numpy as np
     import torch
@@ -161,8 +229,6 @@ def bench_prefill(args, shape):
         if fused:
             m.mamba_conv_scan_fwd(x, p["conv_w"], p["conv_b"], conv_state, dt, p["dt_bias"], p["A_log"],
                                   Bm, Cm, p["D_skip"], z, ssm_state, ssm_state, y, workspace=ws, stream=stream)
-            if ev:
-                ev[1].record(stream)
         else:
             m.mamba_conv1d_fwd(x, p["conv_w"], p["conv_b"], conv_state, u, stream=stream)
             if ev:
@@ -170,7 +236,7 @@ def bench_prefill(args, shape):
             m.mamba_selective_scan_fwd(u, dt, p["dt_bias"], p["A_log"], Bm, Cm, p["D_skip"], z,
                                        ssm_state, ssm_state, y, workspace=ws, stream=stream)
         if ev:
-            ev[2].record(stream)
+            ev[-1].record(stream)
 
     for _ in range(args.warmup):
         step()
@@ -179,7 +245,7 @@ def bench_prefill(args, shape):
           f"{'fused' if fused else 'split'} path)", file=sys.stderr, flush=True)
 
     # per-call events over the timed region
-    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
+    evs = [_call_events(2 if fused else 3) for _ in range(args.steps)]
     t_start, t_end = _events(torch)
     torch.cuda.synchronize()
     t_start.record(stream)
@@ -194,7 +260,7 @@ def bench_prefill(args, shape):
     tokens = B * T
     if fused:
         lb = conv_scan_bytes(s, B, T, D, N, K)
-        call_ms = [e[0].elapsed_time(e[2]) for e in evs]
+        call_ms = [e[0].elapsed_time(e[1]) for e in evs]
         calls = {"mamba_conv_scan_fwd": dict(avg_ms=sum(call_ms) / len(call_ms), min_ms=min(call_ms),
                                              bytes=lb, kernel_file="scan.hip")}
     else:
@@ -208,10 +274,12 @@ def bench_prefill(args, shape):
             "mamba_selective_scan_fwd": dict(avg_ms=sum(scan_ms) / len(scan_ms), min_ms=min(scan_ms),
                                              bytes=sb, kernel_file="scan.hip"),
         }
-    dom_name = max(calls, key=lambda k: calls[k]["avg_ms"])
-    dom = calls[dom_name]
-    achieved = dom["bytes"] / (dom["avg_ms"] * 1e-3) / 1e9
-    traffic = measured_traffic(dom["kernel_file"], shape.name)
+    # the call holding the scan (the longest) is arithmetic-bound: its roofline is the VALU
+    # issue rate over the scan's algorithmic slots (one pass over the B*T*D*N elements)
+    scan_call = "mamba_conv_scan_fwd" if fused else "mamba_selective_scan_fwd"
+    traffic = measured_traffic(calls[scan_call]["kernel_file"], shape.name)
+    slots = B * T * D * N * SCAN_SLOTS_PER_ELEMENT
+    alu = slots / (calls[scan_call]["avg_ms"] * 1e-3) / 1e12
     result = dict(
         metric=METRIC,
         value=tokens / (ms_step * 1e-3),
@@ -224,17 +292,21 @@ def bench_prefill(args, shape):
                              f"), B={B} T={T} d_inner={D} d_state={N} d_conv={K} io={io}",
                     B=B, T=T, d_inner=D, d_state=N, d_conv=K, io_dtype=io, layer_bytes=lb,
                     path="fused" if fused else "split"),
-        roofline=dict(bound="hbm", achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s",
-                      frac=achieved / HBM_PEAK_GBS, traffic=traffic, call=dom_name,
-                      algorithmic_bytes=dom["bytes"], avg_ms=dom["avg_ms"]),
+        roofline=dict(bound="alu", achieved=alu, peak=VALU_SLOTS_PER_S / 1e12, unit="Tslot/s",
+                      frac=alu * 1e12 / VALU_SLOTS_PER_S, traffic=traffic, call=scan_call,
+                      algorithmic_slots=slots, algorithmic_bytes=calls[scan_call]["bytes"],
+                      avg_ms=calls[scan_call]["avg_ms"],
+                      hbm_achieved_gbs=calls[scan_call]["bytes"] / (calls[scan_call]["avg_ms"] * 1e-3) / 1e9,
+                      hbm_peak_gbs=HBM_PEAK_GBS,
+                      hbm_frac=calls[scan_call]["bytes"] / (calls[scan_call]["avg_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS),
         calls={k: dict(avg_us=v["avg_ms"] * 1e3, min_us=v["min_ms"] * 1e3,
                        gbs=v["bytes"] / (v["avg_ms"] * 1e-3) / 1e9) for k, v in calls.items()},
         layer_gbs=lb / (ms_step * 1e-3) / 1e9,
     )
     result["layer_hbm_frac"] = result["layer_gbs"] / HBM_PEAK_GBS
     # the arithmetic floor of the scan (one pass over B*T*D*N elements at the VALU issue rate)
-    # beside its HBM floor: the one that is higher bounds the layer
-    floor_s = B * T * D * N * SCAN_SLOTS_PER_ELEMENT / VALU_SLOTS_PER_S
+    # beside the layer's HBM floor: the one that is higher bounds the layer
+    floor_s = slots / VALU_SLOTS_PER_S
     result["valu_floor_us"] = floor_s * 1e6
     result["hbm_floor_us"] = lb / (HBM_PEAK_GBS * 1e9) * 1e6
     result["valu_frac"] = floor_s / (ms_step * 1e-3)
@@ -317,7 +389,7 @@ def bench_decode(args, shape):
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    evs = [_events(torch) for _ in range(args.steps)]
+    evs = [_call_events(2) for _ in range(args.steps)]
     t_start, t_end = _events(torch)
     t_start.record(stream)
     for i in range(args.steps):
@@ -396,7 +468,7 @@ def bench_m3(args, shape):
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    evs = [_events(torch) for _ in range(args.steps)]
+    evs = [_call_events(2) for _ in range(args.steps)]
     t_start, t_end = _events(torch)
     t_start.record(stream)
     for i in range(args.steps):
@@ -559,7 +631,7 @@ def bench_backbone(args, shape):
     for _, fn, _, _ in pieces:
         fn()
     torch.cuda.synchronize()
-    evs = [[_events(torch) for _ in pieces] for _ in range(reps)]
+    evs = [[_call_events(2) for _ in pieces] for _ in range(reps)]
     for r in range(reps):
         for (_, fn, _, _), (e0, e1) in zip(pieces, evs[r]):
             e0.record(stream)
@@ -723,7 +795,7 @@ def main(argv=None):
     args = parse_args(argv)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py: this build runs the hot path on one GPU only; --gpus {args.gpus} "
+        print(f"bench.py runs the hot path on one GPU only; --gpus {args.gpus} "
               f"(WORLD_SIZE={world}) is not supported. The work shards across GPUs by batch or "
               "d_inner with no communication; run one process per GPU on its own share.",
               file=sys.stderr)
@@ -744,6 +816,8 @@ def main(argv=None):
         torch.cuda.synchronize()
         print(json.dumps(dict(calibrate_copy_bytes=n * 4, launches=3)), flush=True)
         return
+    if args.warmup is None:
+        args.warmup = DEFAULT_WARMUP[args.config]
     shape = W.CONFIGS.get(args.config, W.C4)
     if args.config == "c2":
         result, inp = bench_decode(args, shape)

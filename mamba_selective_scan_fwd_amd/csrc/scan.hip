@@ -388,8 +388,9 @@ scan_kernel(const ScanParams p) {
     else sum_delta += o.dd.x;
   };
   // Token j+1's LDS reads are issued before token j's arithmetic (one token of look-ahead:
-  // the read latency hides behind a token of work); the scheduling barriers stop the compiler
-  // from hoisting further, which would cost more registers than it saves.
+  // the read latency hides behind a token of work). A full block is one straight-line
+  // region: the compiler pairs the reads of neighbouring tokens into wider LDS instructions
+  // and moves the decay factors of a token ahead of the previous token's state update.
   auto scan_block = [&](int st, int nj) {
     TokOps cur, nxt;
     read_token(st, 0, cur);
@@ -399,7 +400,6 @@ scan_kernel(const ScanParams p) {
         if (j + 1 < kTB) read_token(st, j + 1, nxt);
         scan_token(st, j, cur);
         cur = nxt;
-        __builtin_amdgcn_sched_barrier(0);
       }
     } else {
       for (int j = 0; j < nj; ++j) {
