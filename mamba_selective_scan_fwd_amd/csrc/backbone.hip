@@ -149,6 +149,9 @@ __device__ __forceinline__ bf16x8 load_chunk_scalar(const AT* row, int k0, int K
 #ifndef MAMBA_GEMM_WPE
 #define MAMBA_GEMM_WPE 2  // waves per SIMD the register allocation must allow
 #endif
+#ifndef MAMBA_GEMM_LDS_EPI
+#define MAMBA_GEMM_LDS_EPI 1  // write C through LDS as rows of float4 (1) or from the fragments (0)
+#endif
 
 template <typename AT, int BM, int BN, int BK, int WGM, int WGN, bool VEC>
 __global__ void __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(MAMBA_GEMM_WPE)))
@@ -188,8 +191,13 @@ gemm_mfma_kernel(
   constexpr int A_CH = BM * CPR / NT, W_CH = BN * CPR / NT;
   static_assert(TM * 16 == WTM && TN * 16 == WTN && BK % 32 == 0, "tile shape");
   static_assert(A_CH * NT == BM * CPR && W_CH * NT == BN * CPR, "staging split");
-  __shared__ __attribute__((aligned(16))) bf16 As[2][BM * LDK];
-  __shared__ __attribute__((aligned(16))) bf16 Ws[2][BN * LDK];
+  // staging buffers for A and W; after the last k-slab the same LDS holds the C tile
+  constexpr int LDC = BN + 4;  // (4 rows apart = 16 banks: the fragment writes do not collide)
+  constexpr int kStageBytes = 2 * (BM + BN) * LDK * (int)sizeof(bf16);
+  constexpr int kCBytes = MAMBA_GEMM_LDS_EPI ? BM * LDC * (int)sizeof(float) : 0;
+  __shared__ __attribute__((aligned(16))) char smem[kStageBytes > kCBytes ? kStageBytes : kCBytes];
+  auto As = reinterpret_cast<bf16(*)[BM * LDK]>(smem);
+  auto Ws = reinterpret_cast<bf16(*)[BN * LDK]>(smem + 2 * BM * LDK * sizeof(bf16));
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -291,6 +299,44 @@ gemm_mfma_kernel(
 
   // epilogue: lane holds rows 4*(lane/16)+0..3 of column lane%16 of each 16x16 tile
   const int ccol = lane & 15, crow = (lane >> 4) * 4;
+  if constexpr (MAMBA_GEMM_LDS_EPI != 0) {
+    // The tile goes to LDS in that layout (the last k-slab's barrier has freed the staging
+    // buffers), then back out as rows: each lane stores 16 contiguous bytes, a wave whole
+    // rows, instead of 4-byte stores that cover 64-byte pieces of 4 rows.
+    float* Cs = reinterpret_cast<float*>(smem);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          Cs[(wm * WTM + i * 16 + crow + r) * LDC + wn * WTN + j * 16 + ccol] = acc[i][j][r];
+    __syncthreads();
+    constexpr int V = BN / 4;  // float4 per tile row
+    const bool c_vec = ldc % 4 == 0 && reinterpret_cast<uintptr_t>(C) % 16 == 0;
+#pragma unroll 4
+    for (int idx = tid; idx < BM * V; idx += NT) {
+      const int r = idx / V, c4 = (idx % V) * 4;
+      const int gm = m0 + r, gn = n0 + c4;
+      if (gm >= M) continue;
+      const float4 v = *reinterpret_cast<const float4*>(&Cs[r * LDC + c4]);
+      float* cp = C + (int64_t)gm * ldc + gn;
+      if (c_vec && gn + 4 <= N) {
+        float4 o = v;
+        if (accumulate) {
+          const float4 old = *reinterpret_cast<const float4*>(cp);
+          o.x += old.x; o.y += old.y; o.z += old.z; o.w += old.w;
+        }
+        *reinterpret_cast<float4*>(cp) = o;
+      } else {
+        const float e[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (gn + q < N) cp[q] = accumulate ? cp[q] + e[q] : e[q];
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -484,6 +530,41 @@ hipError_t launch_gemm_bf16_parts(const void* A, bool a_bf16, int64_t lda, const
                                                     K, false, true, s, ks, k_chunk, plane)
                 : gemm_tile<float, 64, 32, 64, 2, 1>(static_cast<const float*>(A), lda, w, ldw, partial, N, M,
                                                      N, K, false, true, s, ks, k_chunk, plane);
+}
+
+// Many rows, few columns (x_proj's dt_rank + 2 d_state): 32 x 80 tiles leave too few
+// workgroups to stream A at full rate (M / 32 of them), so K is cut into slices: about 1024
+// workgroups, whole 64-wide k-slabs per slice, at most max_ks slices.
+int gemm_rows_ksplit(int M, int N, int K, int max_ks) {
+  if (N >= 128 || M <= kSplitKMaxM || K % 64 != 0) return 1;
+  const int64_t blocks = (int64_t)((N + 79) / 80) * ((M + 31) / 32);
+  const int want = (int)std::min<int64_t>(
+      std::min<int64_t>(std::max<int64_t>(1024 / std::max<int64_t>(blocks, 1), 1), K / 64),
+      std::min(max_ks, kSplitKMaxSlices));
+  if (want <= 1) return 1;
+  const int chunk = splitk_chunk(K, want);
+  return (K + chunk - 1) / chunk;
+}
+
+hipError_t launch_gemm_bf16_rows(const void* A, bool a_bf16, int64_t lda, const void* W,
+                                 int64_t ldw, float* C, int64_t ldc, int M, int N, int K,
+                                 bool accumulate, float* partial, int max_ks, hipStream_t s) {
+  const int ks = gemm_rows_ksplit(M, N, K, max_ks);
+  const bool aligned = lda % 8 == 0 && ldw % 8 == 0 && reinterpret_cast<uintptr_t>(A) % 16 == 0 &&
+                       reinterpret_cast<uintptr_t>(W) % 16 == 0;
+  if (ks <= 1 || !aligned) return launch_gemm_bf16(A, a_bf16, lda, W, ldw, C, ldc, M, N, K, accumulate, s);
+  const int k_chunk = splitk_chunk(K, ks);
+  const int64_t plane = (int64_t)M * N;
+  const bf16* w = static_cast<const bf16*>(W);
+  const hipError_t e =
+      a_bf16 ? gemm_tile<bf16, 32, 80, 64, 2, 1>(static_cast<const bf16*>(A), lda, w, ldw, partial, N, M, N, K,
+                                                 false, true, s, ks, k_chunk, plane)
+             : gemm_tile<float, 32, 80, 64, 2, 1>(static_cast<const float*>(A), lda, w, ldw, partial, N, M, N, K,
+                                                  false, true, s, ks, k_chunk, plane);
+  if (e != hipSuccess) return e;
+  splitk_reduce_kernel<<<dim3((unsigned)((plane + 255) / 256)), 256, 0, s>>>(partial, ks, C, ldc, M, N,
+                                                                            accumulate ? 1 : 0);
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm_bf16_splitk(const void* A, bool a_bf16, int64_t lda, const void* W,

@@ -210,6 +210,13 @@ hipError_t launch_decode_conv(const PartsView& xin, const float* conv_w, const f
 hipError_t launch_decode_ssm(const float* u, const PartsView& xd, const void* Wdt, int R, const float* dt_bias,
                              const float* A_log, const float* D_skip, const PartsView& zin, int zcol,
                              float* state, float* y, int B, int D, int N, hipStream_t s);
+// C (+)= A W^T for many rows and fewer than 128 columns (a prefill's x_proj): K split into
+// up to max_ks slices whose partial planes (ks * M * N floats of `partial`) are summed in
+// order into C by a second kernel; one plain product when splitting does not apply.
+int gemm_rows_ksplit(int M, int N, int K, int max_ks);
+hipError_t launch_gemm_bf16_rows(const void* A, bool a_bf16, int64_t lda, const void* W,
+                                 int64_t ldw, float* C, int64_t ldc, int M, int N, int K,
+                                 bool accumulate, float* partial, int max_ks, hipStream_t s);
 hipError_t launch_gemm_bf16_splitk(const void* A, bool a_bf16, int64_t lda, const void* W,
                                    int64_t ldw, float* C, int64_t ldc, int M, int N, int K,
                                    bool accumulate, float* partial, hipStream_t s);
