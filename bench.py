@@ -17,7 +17,8 @@ Prints one JSON line. `value` is tokens/s/layer (batch tokens per step / step ti
 `roofline` covers the dominant kernel call, timed with HIP events on the stream it runs
 on: for prefill the call holding the scan against the VALU issue rate (the scan is
 arithmetic-bound; its HBM rate is reported beside it), for the decode steps HBM, for the
-backbone prefill the GEMMs against bf16 MFMA. `cpu_baseline` is the f64 CPU oracle timed on
+backbone prefill the longest per-layer call (a GEMM against bf16 MFMA, the scan against the
+VALU rate). `cpu_baseline` is the f64 CPU oracle timed on
 the host on a bounded sample.
 """
 from __future__ import annotations
@@ -656,11 +657,21 @@ def bench_backbone(args, shape):
         roof = dict(bound="mfma", achieved=achieved, peak=MFMA_BF16_PEAK_TFLOPS, unit="TFLOP/s",
                     frac=achieved / MFMA_BF16_PEAK_TFLOPS, traffic=None, call=dom_name,
                     algorithmic_flops=flops, avg_ms=dom["avg_us"] * 1e-3)
+    elif "scan" in dom_name:
+        # the scan is arithmetic-bound, as in the single-layer prefill: VALU issue rate over
+        # one pass of B*T*D*N elements, with its HBM rate beside it
+        slots = B * T * D * N * SCAN_SLOTS_PER_ELEMENT
+        achieved = slots / (dom["avg_us"] * 1e-6) / 1e12
+        hbm = nbytes / (dom["avg_us"] * 1e-6) / 1e9
+        roof = dict(bound="alu", achieved=achieved, peak=VALU_SLOTS_PER_S / 1e12, unit="Tslot/s",
+                    frac=achieved * 1e12 / VALU_SLOTS_PER_S,
+                    traffic=measured_traffic("scan.hip", shape.name), call=dom_name,
+                    algorithmic_slots=slots, algorithmic_bytes=nbytes, avg_ms=dom["avg_us"] * 1e-3,
+                    hbm_achieved_gbs=hbm, hbm_peak_gbs=HBM_PEAK_GBS, hbm_frac=hbm / HBM_PEAK_GBS)
     else:
         achieved = nbytes / (dom["avg_us"] * 1e-6) / 1e9
-        kfile = "scan.hip" if "scan" in dom_name else "conv1d.hip"
         roof = dict(bound="hbm", achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s",
-                    frac=achieved / HBM_PEAK_GBS, traffic=measured_traffic(kfile, shape.name),
+                    frac=achieved / HBM_PEAK_GBS, traffic=measured_traffic("conv1d.hip", shape.name),
                     call=dom_name, algorithmic_bytes=nbytes, avg_ms=dom["avg_us"] * 1e-3)
     layer_us = sum(calls[k]["avg_us"] for k in per_layer)
     result = dict(
