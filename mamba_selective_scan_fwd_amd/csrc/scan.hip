@@ -290,27 +290,32 @@ scan_kernel(const ScanParams p) {
       }
     }
   };
+  // Row offsets (in elements, wave-uniform) of the next block to load: load_block is called
+  // once per block in block order, and each call advances them by one block, so a block's
+  // row addresses cost one scalar add per tensor rather than a 64-bit row multiply.
+  int64_t ld_xd = (row0 + it_wave) * D;                  // u, dt
+  int64_t ld_z = (row0 + it_wave) * p.z_row_stride;      // z
+  int64_t ld_x = (row0 + it_wave + 1 - K) * p.x_row_stride;  // oldest conv tap (fused conv)
+  int64_t ld_bc = 0;                                     // B/C, from the chunk's first row
   auto load_block = [&](int k, auto P) {
     constexpr int st = decltype(P)::value;
     if (k * kTB + kTB <= len) {
       // full block: scalar row address + the thread's fixed byte offset
-      const int64_t row = row0 + k * kTB + it_wave;
-      pf_dt[st] = load_raw(dt + row * D, off_x);
+      pf_dt[st] = load_raw(dt + ld_xd, off_x);
       if constexpr (KC == 0) {
-        pf_u[st] = load_raw(u + row * D, off_x);
+        pf_u[st] = load_raw(u + ld_xd, off_x);
       } else if (t0 + k * kTB >= K - 1) {
         // every tap of every item in the block is an x row: scalar rows, fixed lane offset
 #pragma unroll
         for (int kk = 0; kk < KM; ++kk)
-          if (kk < K) pf_x[st][kk] = load_at(xin + (row + 1 + kk - K) * p.x_row_stride, off_xx);
+          if (kk < K) pf_x[st][kk] = load_at(xin + ld_x + kk * p.x_row_stride, off_xx);
       } else {
         load_conv_inputs(k, st);
       }
-      if constexpr (OUT && GATE) pf_z[st] = load_raw(z + row * p.z_row_stride, off_z);
-      const int64_t step = (int64_t)k * kTB * bcs;
+      if constexpr (OUT && GATE) pf_z[st] = load_raw(z + ld_z, off_z);
 #pragma unroll
       for (int r = 0; r < BC_PER_T; ++r)
-        if (threadIdx.x + r * NT < kTB * BCW) pf_bc[st][r] = bc_src[r][step];  // whole waves
+        if (threadIdx.x + r * NT < kTB * BCW) pf_bc[st][r] = bc_src[r][ld_bc];  // whole waves
     } else {
       const int64_t row = row0 + min(k * kTB + it_wave + it_lane, len - 1);
       pf_dt[st] = dt[row * D + dic];
@@ -322,6 +327,10 @@ scan_kernel(const ScanParams p) {
         if (threadIdx.x + r * NT < kTB * BCW)
           pf_bc[st][r] = bc_src[r][(int64_t)(min(k * kTB + bc_j[r], len - 1) - bc_j[r]) * bcs];
     }
+    ld_xd += (int64_t)kTB * D;
+    ld_z += (int64_t)kTB * p.z_row_stride;
+    ld_x += (int64_t)kTB * p.x_row_stride;
+    ld_bc += (int64_t)kTB * bcs;
   };
 
   // stage A: delta and delta*u of this thread's item of block k into LDS, B/C of block k
@@ -410,6 +419,7 @@ scan_kernel(const ScanParams p) {
     }
   };
 
+  int64_t st_y = (row0 + it_wave) * D;  // y row offset of the block being finished
   // one block: stage A of block k+1, loads of block k+2, stage B of block k, barrier, finish
   auto block = [&](int k, auto P) {
     constexpr int st = decltype(P)::value;  // == k & 1
@@ -440,10 +450,11 @@ scan_kernel(const ScanParams p) {
         if constexpr (GATE) yv *= g_blk[st];
         if (di < D) {
           // scalar row of the wave's first token + the lane's fixed byte offset
-          IO* yrow = static_cast<IO*>(p.y) + (row0 + k * kTB + it_wave) * D;
+          IO* yrow = static_cast<IO*>(p.y) + st_y;
           *reinterpret_cast<IO*>(reinterpret_cast<char*>(yrow) + off_y) = from_f32<IO>(yv);
         }
       }
+      st_y += (int64_t)kTB * D;
     }
   };
 
