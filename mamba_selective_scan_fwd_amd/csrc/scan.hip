@@ -211,16 +211,24 @@ scan_kernel(const ScanParams p) {
         const int n = g * S + s;
         h[s] = n < N ? p.start_ws[((int64_t)b * N + n) * D + dc] : 0.0f;
       }
-      // predecessors in groups of kFold: all of a group's loads are issued before its fmas
+      // predecessors in groups of kFold: all of a group's loads are issued before its fmas.
+      // The lane's part of each index is formed once; per predecessor only a wave-uniform
+      // offset is added (one address add per load instead of a 64-bit index product).
       constexpr int kFold = S <= 2 ? 8 : (S <= 4 ? 4 : 1);
+      const float* sw_lane = p.sum_ws + (int64_t)b * p.chunks * D + dc;
+      const float* hw_lane[S];
+#pragma unroll
+      for (int s = 0; s < S; ++s)
+        hw_lane[s] = p.h_ws + ((int64_t)b * p.chunks * N + min(g * S + s, N - 1)) * D + dc;
+      const int64_t chunk_nd = (int64_t)N * D;  // h_ws distance between consecutive chunks
       for (int c0 = 0; c0 < c; c0 += kFold) {
         float sd[kFold], hv[kFold][S];
 #pragma unroll
         for (int f = 0; f < kFold; ++f) {
-          const int64_t bc_ = (int64_t)b * p.chunks + min(c0 + f, c - 1);
-          sd[f] = p.sum_ws[bc_ * D + dc];
+          const int64_t cc = min(c0 + f, c - 1);
+          sd[f] = sw_lane[cc * D];
 #pragma unroll
-          for (int s = 0; s < S; ++s) hv[f][s] = p.h_ws[(bc_ * N + min(g * S + s, N - 1)) * D + dc];
+          for (int s = 0; s < S; ++s) hv[f][s] = hw_lane[s][cc * chunk_nd];
         }
 #pragma unroll
         for (int f = 0; f < kFold; ++f) {
