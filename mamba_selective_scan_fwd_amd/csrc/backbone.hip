@@ -399,6 +399,64 @@ __global__ void __launch_bounds__(256) gemm_skinny_kernel(const AT* __restrict__
   }
 }
 
+// The same product with 16-byte weight loads (ldw and K multiples of 8, W 16-byte aligned):
+// a wave takes 8 columns, and lane l handles column l / 8 and the k-chunks (8 consecutive
+// k) l % 8, l % 8 + 8, ... of it, so each load instruction reads 128 contiguous bytes of 8
+// weight rows. The 8 lanes of a column add their partial sums with three xor-shuffles.
+template <typename AT>
+__global__ void __launch_bounds__(256) gemm_skinny_vec_kernel(const AT* __restrict__ A, int64_t lda,
+                                                              const bf16* __restrict__ W,
+                                                              int64_t ldw, float* __restrict__ C,
+                                                              int64_t ldc, int M, int N, int K,
+                                                              int accumulate) {
+  extern __shared__ float as[];  // M x K, bf16-rounded values held as f32
+  for (int r = 0; r < M; ++r)
+    for (int k = threadIdx.x; k < K; k += 256)
+      as[r * K + k] = to_f32(from_f32<bf16>(to_f32(A[(int64_t)r * lda + k])));
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = (blockIdx.x * 4 + wave) * 8 + (lane >> 3);
+  const int kq = lane & 7;
+  float part[kSkinnyMaxM];
+#pragma unroll
+  for (int r = 0; r < kSkinnyMaxM; ++r) part[r] = 0.0f;
+  if (n < N) {
+    const bf16* wr = W + (int64_t)n * ldw;
+#pragma unroll 4
+    for (int k0 = kq * 8; k0 < K; k0 += 64) {
+      const bf16x8 w8 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(wr + k0));
+      float wf[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) wf[i] = to_f32(w8[i]);
+#pragma unroll
+      for (int r = 0; r < kSkinnyMaxM; ++r) {
+        if (r < M) {
+          const float4 a0 = *reinterpret_cast<const float4*>(&as[r * K + k0]);
+          const float4 a1 = *reinterpret_cast<const float4*>(&as[r * K + k0 + 4]);
+          float v = part[r];
+          v = fmaf(a0.x, wf[0], v); v = fmaf(a0.y, wf[1], v);
+          v = fmaf(a0.z, wf[2], v); v = fmaf(a0.w, wf[3], v);
+          v = fmaf(a1.x, wf[4], v); v = fmaf(a1.y, wf[5], v);
+          v = fmaf(a1.z, wf[6], v); v = fmaf(a1.w, wf[7], v);
+          part[r] = v;
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < kSkinnyMaxM; ++r) {
+    if (r >= M) break;
+    float v = part[r];
+    v += __shfl_xor(v, 1);
+    v += __shfl_xor(v, 2);
+    v += __shfl_xor(v, 4);
+    if (kq == 0 && n < N) {
+      float* cp = C + (int64_t)r * ldc + n;
+      *cp = accumulate ? *cp + v : v;
+    }
+  }
+}
+
 // ------------------------------------------------------------------------- launchers
 
 hipError_t launch_embed_gather(const int32_t* tokens, const void* E, float* out, int64_t rows,
@@ -450,7 +508,11 @@ static hipError_t gemm_at(const AT* A, int64_t lda, const bf16* W, int64_t ldw, 
                           int64_t ldc, int M, int N, int K, bool acc, hipStream_t s) {
   if (M <= kSkinnyMaxM && (int64_t)M * K * 4 <= kSkinnyGemmMaxLds) {
     const unsigned blocks = (unsigned)((N + 31) / 32);
-    gemm_skinny_kernel<AT><<<blocks, 256, sizeof(float) * M * K, s>>>(A, lda, W, ldw, C, ldc, M, N, K,
+    if (K % 8 == 0 && ldw % 8 == 0 && reinterpret_cast<uintptr_t>(W) % 16 == 0)
+      gemm_skinny_vec_kernel<AT><<<blocks, 256, sizeof(float) * M * K, s>>>(A, lda, W, ldw, C, ldc, M, N,
+                                                                             K, acc ? 1 : 0);
+    else
+      gemm_skinny_kernel<AT><<<blocks, 256, sizeof(float) * M * K, s>>>(A, lda, W, ldw, C, ldc, M, N, K,
                                                                      acc ? 1 : 0);
     return hipGetLastError();
   }
