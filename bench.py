@@ -322,7 +322,44 @@ def bench_prefill(args, shape):
     result["valu_floor_us"] = floor_s * 1e6
     result["hbm_floor_us"] = lb / (HBM_PEAK_GBS * 1e9) * 1e6
     result["valu_frac"] = floor_s / (ms_step * 1e-3)
+    if B == 1:
+        result["vs_step_by_step"] = step_by_step_prefill(m, torch, x, z, dt, Bm, Cm, p, conv_state,
+                                                         ssm_state, stream, ms_step)
     return result, inp
+
+
+def step_by_step_prefill(m, torch, x, z, dt, Bm, Cm, p, conv_state, ssm_state, stream, prefill_ms):
+    """Context for the pages' claim that the parallel prefill is 10-40x faster than a
+    step-by-step prefill for T > 128 (they name no hardware): the same B = 1 layer run as T
+    single-token steps, one mamba_decode_step call per token launched from the host, timed
+    once as a whole, against one step of the parallel prefill on this GPU. Not part of
+    `value`."""
+    _, T, D = x.shape
+    K, N = conv_state.shape[-1], ssm_state.shape[-1]
+    cs = conv_state.clone().view(1, 1, D, K)
+    hs = ssm_state.clone().view(1, 1, D, N)
+    w, cb = p["conv_w"].view(1, D, K), p["conv_b"].view(1, D)
+    dtb, al, ds = p["dt_bias"].view(1, D), p["A_log"].view(1, D, N), p["D_skip"].view(1, D)
+    yt = torch.empty(1, 1, D, dtype=x.dtype, device=x.device)
+    rows = [tuple(a[0, t].view(1, 1, -1) for a in (x, dt, z, Bm, Cm)) for t in range(T)]
+
+    def run():
+        for xt, dtt, zt, bt, ct in rows:
+            m.mamba_decode_step(xt, w, cb, cs, dtt, dtb, al, bt, ct, ds, zt, hs, yt, stream=stream)
+
+    run()  # warm-up pass
+    torch.cuda.synchronize()
+    t0, t1 = _events(torch)
+    t0.record(stream)
+    run()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1)
+    return dict(step_by_step_ms=ms, prefill_ms=prefill_ms, speedup=ms / prefill_ms, tokens=T,
+                how=f"{T} mamba_decode_step calls (one token each, launched from the host) vs one "
+                    f"parallel prefill step",
+                pages_claim="parallel prefill 10-40x faster than step-by-step prefill for T > 128, "
+                            "no hardware stated (context only)")
 
 
 def cpu_baseline_prefill(shape, inp, budget_s):
@@ -867,7 +904,8 @@ def main(argv=None):
         data="synthetic", config=result["config"], roofline=result["roofline"],
         cpu_baseline=cpu, calls=result["calls"], layer_gbs=result["layer_gbs"],
         layer_hbm_frac=result["layer_hbm_frac"])
-    for extra in ("backbone_tokens_per_s", "layer_chain_us", "valu_floor_us", "hbm_floor_us", "valu_frac"):
+    for extra in ("backbone_tokens_per_s", "layer_chain_us", "valu_floor_us", "hbm_floor_us", "valu_frac",
+                  "vs_step_by_step"):
         if extra in result:
             line[extra] = result[extra]
     print(json.dumps(line), flush=True)
