@@ -528,10 +528,10 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Launch-plan constants (overridable at build time for tuning sweeps).
 #ifndef MAMBA_SCAN_TARGET_WAVES
-#define MAMBA_SCAN_TARGET_WAVES 4096  // ~4 waves per SIMD (256 CUs x 4 SIMDs)
+#define MAMBA_SCAN_TARGET_WAVES 6144  // ~6 waves per SIMD (256 CUs x 4 SIMDs)
 #endif
 #ifndef MAMBA_SCAN_MIN_CHUNK
-#define MAMBA_SCAN_MIN_CHUNK 64  // tokens per chunk, at least
+#define MAMBA_SCAN_MIN_CHUNK 88  // tokens per chunk, at least (11 blocks)
 #endif
 
 static int padded_n(int N) { return N <= 16 ? 16 : (N <= 32 ? 32 : 64); }
@@ -539,8 +539,12 @@ static int padded_n(int N) { return N <= 16 ? 16 : (N <= 32 ? 32 : 64); }
 ScanPlan plan_selective_scan(int B, int T, int D, int N) {
   ScanPlan p{1, T, 0};
   if (B <= 0 || T <= 0 || D <= 0 || N <= 0) return p;
+  // Chunks are added while the grid stays within the target (rounded down: a grid that
+  // already fills most of it runs as one chunk, since every extra chunk count adds a summary
+  // pass over the data), and no chunk is shorter than the minimum, where the chunk's fixed
+  // start (the fold of its predecessors' maps, the first loads) is no longer amortised.
   const int64_t waves_per_chunk = (int64_t)B * ((D + kCh - 1) / kCh) * kWaves;
-  int64_t chunks = (MAMBA_SCAN_TARGET_WAVES + waves_per_chunk - 1) / waves_per_chunk;
+  int64_t chunks = MAMBA_SCAN_TARGET_WAVES / waves_per_chunk;
   chunks = std::max<int64_t>(1, std::min<int64_t>(chunks, T / MAMBA_SCAN_MIN_CHUNK));
   // whole blocks of kTB tokens per chunk
   int chunk_t = (int)((T + chunks - 1) / chunks);
