@@ -91,6 +91,11 @@ RAGGED = [
     (2, 513, 96, 32, 3, "bf16"),
     (3, 257, 200, 16, 4, "bf16"),
     (1, 17, 1, 16, 4, "f32"),
+    # long chunk folds: 43 chunks of 96 tokens (up to 42 predecessor maps, in groups of 8),
+    # and 22 chunks with 64 states (8 per lane, predecessors folded one at a time)
+    (1, 4096, 64, 16, 4, "f32"),
+    (1, 4096, 64, 16, 4, "bf16"),
+    (1, 2048, 64, 64, 4, "f32"),
 ]
 
 
