@@ -717,17 +717,56 @@ __global__ void __launch_bounds__(256) decode_ssm_kernel(
     PartsView zin, int zcol, float* __restrict__ state, float* __restrict__ y, int D, int N) {
   __shared__ float s_x[kDecodeMaxXProj];
   const int b = blockIdx.y;
-  for (int i = threadIdx.x; i < R + 2 * N; i += 256) s_x[i] = xd.at(b, i);
-  __syncthreads();
   const int t = blockIdx.x * 256 + threadIdx.x;
   const int d = t / NQ, q = t % NQ;
+  const int dc = min(d, D - 1);  // (lanes past D load a valid row and drop out below)
+
+  // This lane's loads that do not depend on the x_proj row are issued before the row is
+  // staged, so their latency overlaps the staging (the barrier waits only for LDS work):
+  // its W_dt run, its four states and A_log entries (16-byte path), u and the parameters.
+  // Lane q takes the contiguous columns [q * C, q * C + C) of W_dt's row d.
+  const bf16* wr = Wdt + (int64_t)dc * R;
+  const int C = (R + NQ - 1) / NQ, r0 = q * C, r1 = min(R, r0 + C);
+  constexpr int kPreW = 4;  // W_dt runs of up to 16 columns are loaded up front
+  uint2 wpre[kPreW];
+  const bool pre_w = VEC4 && C <= 4 * kPreW;
+  if (pre_w) {
+#pragma unroll
+    for (int i = 0; i < kPreW; ++i)
+      wpre[i] = r0 + 4 * i < r1 ? *reinterpret_cast<const uint2*>(wr + r0 + 4 * i) : make_uint2(0, 0);
+  }
+  const int64_t ch = (int64_t)b * D + dc;
+  float* hs = state + ch * N;
+  const float* al = A_log + (int64_t)dc * N;
+  const int n0 = 4 * q;
+  const bool vec_state = VEC4 && N % 4 == 0;
+  float4 hv = make_float4(0.f, 0.f, 0.f, 0.f), av = hv;
+  if (vec_state && n0 < N) {
+    hv = *reinterpret_cast<const float4*>(hs + n0);
+    av = *reinterpret_cast<const float4*>(al + n0);
+  }
+  const float uv = u[ch];
+  const float bias = dt_bias ? dt_bias[dc] : 0.0f;
+  const float dskip = D_skip ? D_skip[dc] : 0.0f;
+
+  for (int i = threadIdx.x; i < R + 2 * N; i += 256) s_x[i] = xd.at(b, i);
+  __syncthreads();
   if (d >= D) return;  // whole NQ-lane groups drop out together
 
-  // lane q takes the contiguous columns [q * C, q * C + C) of W_dt's row d
   float acc = 0.0f;
-  const bf16* wr = Wdt + (int64_t)d * R;
-  const int C = (R + NQ - 1) / NQ, r0 = q * C, r1 = min(R, r0 + C);
-  if (VEC4) {  // R a multiple of 4 NQ: C is a multiple of 4 and each run is 8-byte aligned
+  if (pre_w) {
+#pragma unroll
+    for (int i = 0; i < kPreW; ++i) {
+      const int r = r0 + 4 * i;
+      if (r < r1) {
+        const uint2 wv = wpre[i];
+        acc = fmaf((float)(bf16)s_x[r], __uint_as_float(wv.x << 16), acc);
+        acc = fmaf((float)(bf16)s_x[r + 1], __uint_as_float(wv.x & 0xffff0000u), acc);
+        acc = fmaf((float)(bf16)s_x[r + 2], __uint_as_float(wv.y << 16), acc);
+        acc = fmaf((float)(bf16)s_x[r + 3], __uint_as_float(wv.y & 0xffff0000u), acc);
+      }
+    }
+  } else if (VEC4) {  // R a multiple of 4 NQ: C is a multiple of 4 and each run is 8-byte aligned
     for (int r = r0; r < r1; r += 4) {
       const uint2 wv = *reinterpret_cast<const uint2*>(wr + r);
       acc = fmaf((float)(bf16)s_x[r], __uint_as_float(wv.x << 16), acc);
@@ -741,19 +780,12 @@ __global__ void __launch_bounds__(256) decode_ssm_kernel(
 #pragma unroll
   for (int m = NQ / 2; m >= 1; m /= 2) acc += __shfl_xor(acc, m, NQ);
 
-  const int64_t ch = (int64_t)b * D + d;
-  const float uv = u[ch];
-  const float delta = softplus(acc + (dt_bias ? dt_bias[d] : 0.0f));
+  const float delta = softplus(acc + bias);
   const float du = delta * uv;
-  float* hs = state + ch * N;
-  const float* al = A_log + (int64_t)d * N;
   float part = 0.0f;
-  if (VEC4 && N % 4 == 0) {
+  if (vec_state) {
     // four states per lane as one 16-byte access (N a multiple of 4: rows 16-byte aligned)
-    const int n0 = 4 * q;
     if (n0 < N) {
-      const float4 hv = *reinterpret_cast<const float4*>(hs + n0);
-      const float4 av = *reinterpret_cast<const float4*>(al + n0);
       const float hh[4] = {hv.x, hv.y, hv.z, hv.w}, aa[4] = {av.x, av.y, av.z, av.w};
       float hn[4];
 #pragma unroll
@@ -781,7 +813,7 @@ __global__ void __launch_bounds__(256) decode_ssm_kernel(
 #pragma unroll
   for (int m = NQ / 2; m >= 1; m /= 2) part += __shfl_xor(part, m, NQ);
   if (q == 0) {
-    float yv = fmaf(D_skip ? D_skip[d] : 0.0f, uv, part);
+    float yv = fmaf(dskip, uv, part);
     yv *= silu(zin.at(b, zcol + d));
     y[ch] = yv;
   }
