@@ -191,6 +191,11 @@ class TimingEvent:
             _hip().hipEventDestroy(self.h)
 
 
+def _median(xs):
+    srt = sorted(xs)
+    return srt[len(srt) // 2]
+
+
 def _call_events(n):
     return tuple(TimingEvent() for _ in range(n))
 
@@ -274,17 +279,17 @@ def bench_prefill(args, shape):
         lb = conv_scan_bytes(s, B, T, D, N, K)
         call_ms = [e[0].elapsed_time(e[1]) for e in evs.values()]
         calls = {"mamba_conv_scan_fwd": dict(avg_ms=sum(call_ms) / len(call_ms), min_ms=min(call_ms),
-                                             bytes=lb, kernel_file="scan.hip")}
+                                             median_ms=_median(call_ms), bytes=lb, kernel_file="scan.hip")}
     else:
         cb, sb = conv_bytes(s, B, T, D, K), scan_bytes(s, B, T, D, N)
         lb = cb + sb
         conv_ms = [e[0].elapsed_time(e[1]) for e in evs.values()]
         scan_ms = [e[1].elapsed_time(e[2]) for e in evs.values()]
         calls = {
-            "mamba_conv1d_fwd": dict(avg_ms=sum(conv_ms) / len(conv_ms), min_ms=min(conv_ms), bytes=cb,
-                                     kernel_file="conv1d.hip"),
+            "mamba_conv1d_fwd": dict(avg_ms=sum(conv_ms) / len(conv_ms), min_ms=min(conv_ms),
+                                     median_ms=_median(conv_ms), bytes=cb, kernel_file="conv1d.hip"),
             "mamba_selective_scan_fwd": dict(avg_ms=sum(scan_ms) / len(scan_ms), min_ms=min(scan_ms),
-                                             bytes=sb, kernel_file="scan.hip"),
+                                             median_ms=_median(scan_ms), bytes=sb, kernel_file="scan.hip"),
         }
     # the call holding the scan (the longest) is arithmetic-bound: its roofline is the VALU
     # issue rate over the scan's algorithmic slots (one pass over the B*T*D*N elements)
@@ -311,7 +316,7 @@ def bench_prefill(args, shape):
                       hbm_achieved_gbs=calls[scan_call]["bytes"] / (calls[scan_call]["avg_ms"] * 1e-3) / 1e9,
                       hbm_peak_gbs=HBM_PEAK_GBS,
                       hbm_frac=calls[scan_call]["bytes"] / (calls[scan_call]["avg_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS),
-        calls={k: dict(avg_us=v["avg_ms"] * 1e3, min_us=v["min_ms"] * 1e3,
+        calls={k: dict(avg_us=v["avg_ms"] * 1e3, median_us=v["median_ms"] * 1e3, min_us=v["min_ms"] * 1e3,
                        gbs=v["bytes"] / (v["avg_ms"] * 1e-3) / 1e9) for k, v in calls.items()},
         layer_gbs=lb / (ms_step * 1e-3) / 1e9,
     )
@@ -322,42 +327,91 @@ def bench_prefill(args, shape):
     result["valu_floor_us"] = floor_s * 1e6
     result["hbm_floor_us"] = lb / (HBM_PEAK_GBS * 1e9) * 1e6
     result["valu_frac"] = floor_s / (ms_step * 1e-3)
+    if fused:
+        # the same call with the caches cold (the layer's 51 MB fit the 256 MB MALL)
+        avg, med, mn = cold_call_times(torch, lambda: step(), stream)
+        result["cold"] = dict(call=scan_call, avg_us=avg * 1e3, median_us=med * 1e3, min_us=mn * 1e3,
+                              hbm_gbs=lb / (avg * 1e-3) / 1e9,
+                              flush="512 MB written between repetitions, 20 repetitions")
     if B == 1:
         result["vs_step_by_step"] = step_by_step_prefill(m, torch, x, z, dt, Bm, Cm, p, conv_state,
-                                                         ssm_state, stream, ms_step)
+                                                         ssm_state, stream, (128, 512, 2048))
     return result, inp
 
 
-def step_by_step_prefill(m, torch, x, z, dt, Bm, Cm, p, conv_state, ssm_state, stream, prefill_ms):
+def cold_call_times(torch, fn, stream, reps=20, flush_bytes=512 << 20):
+    """Call times with the caches cold: before each repetition a scratch buffer of 512 MB
+    (twice the 256 MB MALL) is written, so the call's inputs come from HBM, not from the
+    last-level cache where back-to-back steps of a working set this small would find them.
+    Returns (avg, median, min) in ms."""
+    scratch = torch.empty(flush_bytes // 4, dtype=torch.float32, device="cuda")
+    times = []
+    for r in range(reps):
+        scratch.fill_(float(r))
+        e0, e1 = _call_events(2)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    del scratch
+    srt = sorted(times)
+    return sum(times) / len(times), srt[len(srt) // 2], srt[0]
+
+
+def step_by_step_prefill(m, torch, x, z, dt, Bm, Cm, p, conv_state, ssm_state, stream, lengths):
     """Context for the pages' claim that the parallel prefill is 10-40x faster than a
-    step-by-step prefill for T > 128 (they name no hardware): the same B = 1 layer run as T
-    single-token steps, one mamba_decode_step call per token launched from the host, timed
-    once as a whole, against one step of the parallel prefill on this GPU. Not part of
-    `value`."""
-    _, T, D = x.shape
+    step-by-step prefill for T > 128 (they name no hardware): the first T tokens of the same
+    B = 1 layer run as T single-token steps (one mamba_decode_step call per token, launched
+    from the host, timed as a whole) against one parallel prefill call over the same T
+    tokens (mamba_conv_scan_fwd, average of 20 back-to-back calls). Not part of `value`."""
+    _, Tmax, D = x.shape
     K, N = conv_state.shape[-1], ssm_state.shape[-1]
-    cs = conv_state.clone().view(1, 1, D, K)
-    hs = ssm_state.clone().view(1, 1, D, N)
     w, cb = p["conv_w"].view(1, D, K), p["conv_b"].view(1, D)
     dtb, al, ds = p["dt_bias"].view(1, D), p["A_log"].view(1, D, N), p["D_skip"].view(1, D)
-    yt = torch.empty(1, 1, D, dtype=x.dtype, device=x.device)
-    rows = [tuple(a[0, t].view(1, 1, -1) for a in (x, dt, z, Bm, Cm)) for t in range(T)]
+    out = {}
+    for T in lengths:
+        if T > Tmax:
+            continue
+        cs = conv_state.clone().view(1, 1, D, K)
+        hs = ssm_state.clone().view(1, 1, D, N)
+        yt = torch.empty(1, 1, D, dtype=x.dtype, device=x.device)
+        rows = [tuple(a[0, t].view(1, 1, -1) for a in (x, dt, z, Bm, Cm)) for t in range(T)]
 
-    def run():
-        for xt, dtt, zt, bt, ct in rows:
-            m.mamba_decode_step(xt, w, cb, cs, dtt, dtb, al, bt, ct, ds, zt, hs, yt, stream=stream)
+        def run():
+            for xt, dtt, zt, bt, ct in rows:
+                m.mamba_decode_step(xt, w, cb, cs, dtt, dtb, al, bt, ct, ds, zt, hs, yt, stream=stream)
 
-    run()  # warm-up pass
-    torch.cuda.synchronize()
-    t0, t1 = _events(torch)
-    t0.record(stream)
-    run()
-    t1.record(stream)
-    torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1)
-    return dict(step_by_step_ms=ms, prefill_ms=prefill_ms, speedup=ms / prefill_ms, tokens=T,
-                how=f"{T} mamba_decode_step calls (one token each, launched from the host) vs one "
-                    f"parallel prefill step",
+        run()  # warm-up pass
+        torch.cuda.synchronize()
+        t0, t1 = _events(torch)
+        t0.record(stream)
+        run()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        step_ms = t0.elapsed_time(t1)
+        # the parallel prefill over the same T tokens
+        xs, zs, dts, Bs, Cs = (a[:, :T].contiguous() for a in (x, z, dt, Bm, Cm))
+        cs2, hs2 = conv_state.clone(), ssm_state.clone()
+        ys = torch.empty_like(xs)
+        ws = m.scan_workspace(1, T, D, N)
+
+        def pre():
+            m.mamba_conv_scan_fwd(xs, p["conv_w"], p["conv_b"], cs2, dts, p["dt_bias"], p["A_log"], Bs, Cs,
+                                  p["D_skip"], zs, hs2, hs2, ys, workspace=ws, stream=stream)
+
+        for _ in range(20):
+            pre()
+        torch.cuda.synchronize()
+        t0.record(stream)
+        for _ in range(20):
+            pre()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        pre_ms = t0.elapsed_time(t1) / 20
+        out[str(T)] = dict(step_by_step_ms=step_ms, prefill_ms=pre_ms, speedup=step_ms / pre_ms)
+    return dict(by_T=out, how="T mamba_decode_step calls (one token each, launched from the host) vs one "
+                              "mamba_conv_scan_fwd call over the same T tokens",
                 pages_claim="parallel prefill 10-40x faster than step-by-step prefill for T > 128, "
                             "no hardware stated (context only)")
 
@@ -450,7 +504,8 @@ def bench_decode(args, shape):
     ms_step = total_ms / args.steps
     sb = decode_step_bytes(4, L, B, D, N, K)
     calls = {
-        "mamba_decode_step": dict(avg_ms=sum(step_ms) / len(step_ms), min_ms=min(step_ms), bytes=sb,
+        "mamba_decode_step": dict(avg_ms=sum(step_ms) / len(step_ms), min_ms=min(step_ms),
+                                  median_ms=_median(step_ms), bytes=sb,
                                   kernel_file="step.hip"),
     }
     dom_name = "mamba_decode_step"
@@ -469,11 +524,17 @@ def bench_decode(args, shape):
                       frac=achieved / HBM_PEAK_GBS,
                       traffic=measured_traffic(dom["kernel_file"], shape.name), call=dom_name,
                       algorithmic_bytes=dom["bytes"], avg_ms=dom["avg_ms"]),
-        calls={k: dict(avg_us=v["avg_ms"] * 1e3, min_us=v["min_ms"] * 1e3,
+        calls={k: dict(avg_us=v["avg_ms"] * 1e3, median_us=v["median_ms"] * 1e3, min_us=v["min_ms"] * 1e3,
                        gbs=v["bytes"] / (v["avg_ms"] * 1e-3) / 1e9) for k, v in calls.items()},
         layer_gbs=sb / (ms_step * 1e-3) / 1e9,
     )
     result["layer_hbm_frac"] = result["layer_gbs"] / HBM_PEAK_GBS
+    # the same call with the caches cold (the step's 419 MB exceed the MALL, but the states
+    # of the last step may still sit in it)
+    avg, med, mn = cold_call_times(torch, lambda: step(0), stream)
+    result["cold"] = dict(call=dom_name, avg_us=avg * 1e3, median_us=med * 1e3, min_us=mn * 1e3,
+                          hbm_gbs=sb / (avg * 1e-3) / 1e9,
+                          flush="512 MB written between repetitions, 20 repetitions")
     return result, None
 
 
@@ -544,7 +605,8 @@ def bench_m3(args, shape):
         roofline=dict(bound="hbm", achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s",
                       frac=achieved / HBM_PEAK_GBS, traffic=measured_traffic("mamba3.hip", shape.name),
                       call="mamba3_siso_step", algorithmic_bytes=sb, avg_ms=avg),
-        calls={"mamba3_siso_step": dict(avg_us=avg * 1e3, min_us=min(step_ms) * 1e3,
+        calls={"mamba3_siso_step": dict(avg_us=avg * 1e3, median_us=_median(step_ms) * 1e3,
+                                        min_us=min(step_ms) * 1e3,
                                         gbs=achieved)},
         layer_gbs=sb / (ms_step * 1e-3) / 1e9,
     )
@@ -691,7 +753,8 @@ def bench_backbone(args, shape):
     for i, (name, _, flops, nbytes) in enumerate(pieces):
         ms = [evs[r][i][0].elapsed_time(evs[r][i][1]) for r in range(reps)]
         avg = sum(ms) / len(ms)
-        c = dict(avg_us=avg * 1e3, min_us=min(ms) * 1e3, gbs=nbytes / (avg * 1e-3) / 1e9)
+        c = dict(avg_us=avg * 1e3, median_us=_median(ms) * 1e3, min_us=min(ms) * 1e3,
+                 gbs=nbytes / (avg * 1e-3) / 1e9)
         if flops:
             c["tflops"] = flops / (avg * 1e-3) / 1e12
         calls[name] = c
@@ -905,7 +968,7 @@ def main(argv=None):
         cpu_baseline=cpu, calls=result["calls"], layer_gbs=result["layer_gbs"],
         layer_hbm_frac=result["layer_hbm_frac"])
     for extra in ("backbone_tokens_per_s", "layer_chain_us", "valu_floor_us", "hbm_floor_us", "valu_frac",
-                  "vs_step_by_step"):
+                  "vs_step_by_step", "cold"):
         if extra in result:
             line[extra] = result[extra]
     print(json.dumps(line), flush=True)
