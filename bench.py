@@ -458,6 +458,39 @@ def cpu_baseline_prefill(shape, inp, budget_s):
                 sample=sample, seconds=elapsed)
 
 
+def cpu_baseline_decode(shape, budget_s):
+    """The f64 oracle's decode step (conv step, then SSM step) on a bounded sample of the
+    same workload: layer steps of all B sequences, timed one layer at a time on the host's
+    cores, whole steps repeated while within the budget (at most 20), scaled to a step of
+    L layers."""
+    import numpy as np
+
+    import workloads as W
+    from oracle import oracle
+
+    L, B = shape.L, shape.B
+    P = W.decode_params(shape)
+    f64 = lambda a: np.ascontiguousarray(a, dtype=np.float64)
+    layers, elapsed = 0, 0.0
+    while layers < 20 * L and elapsed < budget_s:  # whole steps repeated within the budget
+        l = layers % L
+        i = W.decode_step_inputs(shape, layers // L, layers=[l])
+        cs = np.zeros((B, shape.D, shape.K))
+        hs = np.zeros((B, shape.D, shape.N))
+        a = {k: f64(v[0]) for k, v in i.items()}
+        t0 = time.perf_counter()
+        u, _ = oracle.conv1d_step(a["x"], f64(P["conv_w"][l]), f64(P["conv_b"][l]), cs)
+        oracle.ssm_step(u, a["dt"], f64(P["A_log"][l]), a["Bm"], a["Cm"], f64(P["D_skip"][l]), a["z"],
+                        f64(P["dt_bias"][l]), hs)
+        elapsed += time.perf_counter() - t0
+        layers += 1
+    step_s = elapsed * L / layers
+    sample = (f"{layers // L} steps of all {L} layers (B={B})" if layers % L == 0 else
+              f"{layers} layer steps (B={B}), time scaled to a step of {L} layers")
+    return dict(value=L * B / step_s, unit="tokens/s/layer", cores=oracle.threads(), kind="oracle",
+                sample=sample, seconds=elapsed)
+
+
 def bench_decode(args, shape):
     import numpy as np
     import torch
@@ -952,10 +985,12 @@ def main(argv=None):
     else:
         result, inp = bench_prefill(args, shape)
     cpu = None
-    if not args.no_cpu_baseline and inp is not None:
+    if not args.no_cpu_baseline and (inp is not None or args.config == "c2"):
         print("[bench] timing the CPU oracle baseline", file=sys.stderr, flush=True)
         if args.config == "c4":
             cpu = cpu_baseline_backbone(shape, inp, args.cpu_seconds)
+        elif args.config == "c2":
+            cpu = cpu_baseline_decode(shape, args.cpu_seconds)
         elif args.config == "c5":
             cpu = cpu_baseline_m3(shape, inp, args.cpu_seconds)
         else:
