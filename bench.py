@@ -568,6 +568,34 @@ def bench_decode(args, shape):
     result["cold"] = dict(call=dom_name, avg_us=avg * 1e3, median_us=med * 1e3, min_us=mn * 1e3,
                           hbm_gbs=sb / (avg * 1e-3) / 1e9,
                           flush="512 MB written between repetitions, 20 repetitions")
+    # context: the same step as 2 L launches (conv step, then SSM step, one layer per call),
+    # the per-layer launch pattern of the pages' step chain, against the one fused launch
+    u = torch.empty(L, B, D, device=dev)
+    lp = [{k: v[l:l + 1] for k, v in p.items()} for l in range(L)]
+
+    def per_layer(i):
+        si = steps_in[i % ring]
+        for l in range(L):
+            q = lp[l]
+            m.mamba_conv1d_step(si["x"][l:l + 1], q["conv_w"], q["conv_b"], cs[l:l + 1], u[l:l + 1],
+                                stream=stream)
+            m.mamba_ssm_step(u[l:l + 1], si["dt"][l:l + 1], q["dt_bias"], q["A_log"], si["Bm"][l:l + 1],
+                             si["Cm"][l:l + 1], q["D_skip"], si["z"][l:l + 1], hs[l:l + 1], y[l:l + 1],
+                             stream=stream)
+
+    for i in range(5):
+        per_layer(i)
+    torch.cuda.synchronize()
+    reps = 20
+    t0, t1 = _events(torch)
+    t0.record(stream)
+    for i in range(reps):
+        per_layer(i)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    result["per_layer_launches"] = dict(step_us=t0.elapsed_time(t1) / reps * 1e3, launches_per_step=2 * L,
+                                        fused_step_us=ms_step * 1e3,
+                                        how="mamba_conv1d_step + mamba_ssm_step per layer (context)")
     return result, None
 
 
@@ -1003,7 +1031,7 @@ def main(argv=None):
         cpu_baseline=cpu, calls=result["calls"], layer_gbs=result["layer_gbs"],
         layer_hbm_frac=result["layer_hbm_frac"])
     for extra in ("backbone_tokens_per_s", "layer_chain_us", "valu_floor_us", "hbm_floor_us", "valu_frac",
-                  "vs_step_by_step", "cold"):
+                  "vs_step_by_step", "cold", "per_layer_launches"):
         if extra in result:
             line[extra] = result[extra]
     print(json.dumps(line), flush=True)
