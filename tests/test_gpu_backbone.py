@@ -83,6 +83,28 @@ def test_gemm_strided_operands():
     np.testing.assert_array_equal(out[:, N:], 7.0)
 
 
+@pytest.mark.parametrize("M,N,K,ldw,acc", [
+    (8, 520, 96, 96, True),      # 16-byte path at the row limit, last column group partly out
+    (5, 300, 64, 72, False),     # 16-byte path with a strided weight row (ldw > K)
+    (4, 77, 40, 44, False),      # ldw not a multiple of 8: the element-wise kernel
+])
+def test_gemm_few_rows_vector_and_fallback(M, N, K, ldw, acc):
+    """The few-row product (M <= 8) on its 16-byte weight path and on the element-wise path,
+    against the oracle; columns of C beyond N keep their values."""
+    _say(f"case gemm few rows M{M} N{N} K{K} ldw{ldw} acc={acc}")
+    g = np.random.default_rng(M * 31 + N + K)
+    A = g.normal(size=(M, K)).astype(np.float32)
+    Wbig = W.bf16_round(g.normal(size=(N, ldw)).astype(np.float32) * 0.05)
+    C0 = g.normal(size=(M, N + 3)).astype(np.float32)
+    C = dev(C0)
+    m.mamba_gemm_bf16(dev(A), _bf16_dev(Wbig), C, M=M, N=N, K=K, ldw=ldw, ldc=N + 3, accumulate=acc)
+    torch.cuda.synchronize()
+    out = host(C)
+    ref = ob.gemm(A, Wbig[:, :K]) + (C0[:, :N] if acc else 0.0)
+    assert rel_err(out[:, :N], ref) <= TOL_F32
+    np.testing.assert_array_equal(out[:, N:], C0[:, N:])
+
+
 def test_gemm_empty_is_noop():
     C = torch.full((4, 4), 3.0, device="cuda")
     A = torch.zeros(0, 16, device="cuda")
