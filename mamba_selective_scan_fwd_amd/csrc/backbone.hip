@@ -705,6 +705,81 @@ __global__ void __launch_bounds__(256) decode_conv_kernel(PartsView xin, const f
   u[(int64_t)b * D + d] = silu(c);
 }
 
+// Conv step and x_proj of one decode layer in one launch. Workgroup (s, g) takes the
+// kConvXC channels of slice s and up to kConvXRows sequences of group g: it runs the conv
+// step for them (the arithmetic of decode_conv_kernel: the same u and conv state bit for
+// bit), writes u for the SSM step and keeps bf16(u) in LDS, then forms the slice's share of
+// every x_proj column: part[s][b][n] = sum over the slice's channels c, in order, of
+// bf16(u[b][c]) * W_x[n][c] in f32 (the operands the MFMA product rounds to, f32 sums).
+// The SSM step adds the D / kConvXC planes in slice order. Needs D % kConvXC == 0 and 16-byte
+// aligned W_x rows.
+template <bool K4>
+__global__ void __launch_bounds__(256) decode_conv_xproj_kernel(
+    PartsView xin, const float* __restrict__ conv_w, const float* __restrict__ conv_b,
+    float* __restrict__ conv_state, float* __restrict__ u, const bf16* __restrict__ Wx, int xw,
+    float* __restrict__ part, int B, int D, int K) {
+  __shared__ float s_u[kConvXRows][kConvXC];
+  const int sl = blockIdx.x, d0 = sl * kConvXC;
+  const int b0 = blockIdx.y * kConvXRows;
+  const int rows = min(kConvXRows, B - b0);
+  for (int i = threadIdx.x; i < rows * kConvXC; i += 256) {
+    const int bl = i / kConvXC, c = i % kConvXC, b = b0 + bl, d = d0 + c;
+    float* st = conv_state + ((int64_t)b * D + d) * K;
+    const float* w = conv_w + (int64_t)d * K;
+    const float xv = xin.at(b, d);
+    float cv = conv_b ? conv_b[d] : 0.0f;
+    if (K4) {
+      const float4 v = *reinterpret_cast<const float4*>(st);
+      const float4 wv = *reinterpret_cast<const float4*>(w);
+      cv = fmaf(wv.x, v.y, cv);
+      cv = fmaf(wv.y, v.z, cv);
+      cv = fmaf(wv.z, v.w, cv);
+      cv = fmaf(wv.w, xv, cv);
+      *reinterpret_cast<float4*>(st) = make_float4(v.y, v.z, v.w, xv);
+    } else {
+      float sv[kMaxConvK];
+      for (int k = 0; k + 1 < K; ++k) sv[k] = st[k + 1];
+      sv[K - 1] = xv;
+      for (int k = 0; k < K; ++k) cv = fmaf(w[k], sv[k], cv);
+      for (int k = 0; k < K; ++k) st[k] = sv[k];
+    }
+    const float uv = silu(cv);
+    u[(int64_t)b * D + d] = uv;
+    s_u[bl][c] = to_f32(from_f32<bf16>(uv));
+  }
+  __syncthreads();
+  // the thread's outputs o = tid, tid + 256, ... advance together (independent chains); each
+  // output still sums its channels in order
+  const int64_t plane = (int64_t)B * xw;
+  const int nout = rows * xw;
+  for (int o0 = threadIdx.x; o0 < nout; o0 += kConvXOut * 256) {
+    float acc[kConvXOut];
+    const bf16* wr[kConvXOut];
+    int bl[kConvXOut];
+#pragma unroll
+    for (int j = 0; j < kConvXOut; ++j) {
+      const int o = min(o0 + j * 256, nout - 1);  // (clamped; results past nout are not stored)
+      bl[j] = o / xw;
+      wr[j] = Wx + (int64_t)(o % xw) * D + d0;
+      acc[j] = 0.0f;
+    }
+    for (int c = 0; c < kConvXC; c += 8) {
+      bf16x8 w8[kConvXOut];
+#pragma unroll
+      for (int j = 0; j < kConvXOut; ++j) w8[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(wr[j] + c));
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < kConvXOut; ++j) acc[j] = fmaf(s_u[bl[j]][c + i], to_f32(w8[j][i]), acc[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < kConvXOut; ++j) {
+      const int o = o0 + j * 256;
+      if (o < nout) part[(int64_t)sl * plane + (int64_t)(b0 + o / xw) * xw + o % xw] = acc[j];
+    }
+  }
+}
+
 // SSM step of one layer with dt_proj folded in: the x_proj row of sequence b (dt low-rank
 // part | B | C, from its partial planes) is summed once into LDS; each channel's NQ lanes
 // then form dt = W_dt[d] . bf16(x[0 .. R)) (the projection's bf16 operands, f32 sums), and
@@ -832,6 +907,22 @@ hipError_t launch_decode_conv(const PartsView& xin, const float* conv_w, const f
     decode_conv_kernel<true><<<grid, 256, 0, s>>>(xin, conv_w, conv_b, conv_state, u, D, K);
   else
     decode_conv_kernel<false><<<grid, 256, 0, s>>>(xin, conv_w, conv_b, conv_state, u, D, K);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_conv_xproj(const PartsView& xin, const float* conv_w, const float* conv_b,
+                                    float* conv_state, float* u, const void* Wx, int xw, float* part,
+                                    PartsView* out, int B, int D, int K, hipStream_t s) {
+  if (D % kConvXC != 0 || B > kSplitKMaxM || (reinterpret_cast<uintptr_t>(Wx) & 15) != 0)
+    return hipErrorInvalidValue;
+  const dim3 grid((unsigned)(D / kConvXC), (unsigned)((B + kConvXRows - 1) / kConvXRows));
+  const bf16* w = static_cast<const bf16*>(Wx);
+  if (K == 4 && ((reinterpret_cast<uintptr_t>(conv_w) | reinterpret_cast<uintptr_t>(conv_state)) & 15) == 0)
+    decode_conv_xproj_kernel<true><<<grid, 256, 0, s>>>(xin, conv_w, conv_b, conv_state, u, w, xw, part, B, D, K);
+  else
+    decode_conv_xproj_kernel<false><<<grid, 256, 0, s>>>(xin, conv_w, conv_b, conv_state, u, w, xw, part, B, D,
+                                                         K);
+  *out = PartsView{part, D / kConvXC, (int64_t)B * xw, xw};
   return hipGetLastError();
 }
 

@@ -170,7 +170,9 @@ static DecodeLayout decode_layout(const mamba_backbone_dims& d, int B) {
     return ks > 1 ? (size_t)ks * B * N * 4 : 0;
   };
   l.part_in = take(parts(2 * d.d_inner, d.d_model));
-  l.part_x = take(parts((int)xw, d.d_inner));
+  // (the fused conv step + x_proj leaves d_inner / kConvXC planes)
+  l.part_x = take(std::max(parts((int)xw, d.d_inner),
+                           d.d_inner % kConvXC == 0 ? (size_t)(d.d_inner / kConvXC) * B * xw * 4 : 0));
   l.part_out = take(parts(d.d_model, d.d_inner));
   l.total = off;
   return l;
@@ -205,6 +207,7 @@ hipError_t run_backbone_decode(const mamba_backbone_dims& d, const mamba_backbon
 
   hipError_t e = launch_embed_gather(tokens, w.embed, h, B, d.vocab, Dm, s);
   if (e != hipSuccess) return e;
+  const bool fuse_conv_x = D % kConvXC == 0 && B <= kSplitKMaxM;
   PartsView v_out{nullptr, 0, 0, 0};  // the previous layer's out_proj, not yet in h
   for (int l = 0; l < d.n_layers; ++l) {
     // F12 of the previous layer (residual) + F1
@@ -214,12 +217,21 @@ hipError_t run_backbone_decode(const mamba_backbone_dims& d, const mamba_backbon
     if ((e = launch_gemm_bf16_parts(xn, true, Dm, in_proj + (int64_t)l * 2 * D * Dm, Dm, proj, 2 * D, B, 2 * D,
                                     Dm, false, part_in, &v_in, s)) != hipSuccess)
       return e;
-    if ((e = launch_decode_conv(v_in, w.conv_w + (int64_t)l * D * K, w.conv_b + (int64_t)l * D,
-                                conv_state + (int64_t)l * B * D * K, u, B, D, K, s)) != hipSuccess)
-      return e;
-    if ((e = launch_gemm_bf16_parts(u, false, D, x_proj + (int64_t)l * xw * D, D, xdbl, xw, B, xw, D, false,
-                                    part_x, &v_x, s)) != hipSuccess)
-      return e;
+    const bf16_storage* wx = x_proj + (int64_t)l * xw * D;
+    if (fuse_conv_x && (reinterpret_cast<uintptr_t>(wx) & 15) == 0) {
+      // conv step and x_proj in one launch, x_proj left as per-slice partial planes
+      if ((e = launch_decode_conv_xproj(v_in, w.conv_w + (int64_t)l * D * K, w.conv_b + (int64_t)l * D,
+                                        conv_state + (int64_t)l * B * D * K, u, wx, xw, part_x, &v_x, B, D,
+                                        K, s)) != hipSuccess)
+        return e;
+    } else {
+      if ((e = launch_decode_conv(v_in, w.conv_w + (int64_t)l * D * K, w.conv_b + (int64_t)l * D,
+                                  conv_state + (int64_t)l * B * D * K, u, B, D, K, s)) != hipSuccess)
+        return e;
+      if ((e = launch_gemm_bf16_parts(u, false, D, wx, D, xdbl, xw, B, xw, D, false, part_x, &v_x, s)) !=
+          hipSuccess)
+        return e;
+    }
     if ((e = launch_decode_ssm(u, v_x, dt_proj + (int64_t)l * D * R, R, w.dt_bias + (int64_t)l * D,
                                w.A_log + (int64_t)l * D * N, w.D_skip + (int64_t)l * D, v_in, D,
                                ssm_state + (int64_t)l * B * D * N, y, B, D, N, s)) != hipSuccess)

@@ -207,6 +207,15 @@ hipError_t launch_residual_rmsnorm(float* h, const PartsView& add, const float* 
                                    int rows, int Dm, hipStream_t s);
 hipError_t launch_decode_conv(const PartsView& xin, const float* conv_w, const float* conv_b,
                               float* conv_state, float* u, int B, int D, int K, hipStream_t s);
+// Conv step + x_proj of a decode layer in one launch (D a multiple of kConvXC, B <= kSplitKMaxM,
+// 16-byte aligned W_x): u and the conv state as launch_decode_conv, and x_proj left as
+// D / kConvXC partial planes in `part` (*out describes them).
+constexpr int kConvXC = 64;     // channels per x_proj slice
+constexpr int kConvXRows = 4;   // sequences per workgroup
+constexpr int kConvXOut = 4;    // x_proj outputs a thread accumulates together
+hipError_t launch_decode_conv_xproj(const PartsView& xin, const float* conv_w, const float* conv_b,
+                                    float* conv_state, float* u, const void* Wx, int xw, float* part,
+                                    PartsView* out, int B, int D, int K, hipStream_t s);
 hipError_t launch_decode_ssm(const float* u, const PartsView& xd, const void* Wdt, int R, const float* dt_bias,
                              const float* A_log, const float* D_skip, const PartsView& zin, int zcol,
                              float* state, float* y, int B, int D, int N, hipStream_t s);
