@@ -58,3 +58,18 @@ def test_valu_floor_constants():
     assert bench.SCAN_SLOTS_PER_ELEMENT == 8
     floor_us = 8 * 4096 * 5120 * 16 * bench.SCAN_SLOTS_PER_ELEMENT / bench.VALU_SLOTS_PER_S * 1e6
     assert floor_us == pytest.approx(273.07, rel=1e-4)
+
+
+def test_cpu_baseline_decode_small_shape():
+    """The decode step's CPU oracle baseline on a small shape: whole steps within the budget,
+    tokens/s/layer = L * B / (time of one step of L layers)."""
+    s = W.DecodeShape("tiny", L=3, B=2, D=32, N=8, K=4)
+    r = bench.cpu_baseline_decode(s, budget_s=0.5)
+    assert r["kind"] == "oracle" and r["unit"] == "tokens/s/layer"
+    assert r["value"] > 0 and r["cores"] >= 1 and r["seconds"] > 0
+    assert "layers" in r["sample"] or "steps" in r["sample"]
+
+
+def test_median_of_sampled_call_times():
+    assert bench._median([3.0, 1.0, 2.0]) == 2.0
+    assert bench._median([4.0, 1.0, 3.0, 2.0]) == 3.0
