@@ -523,6 +523,10 @@ static hipError_t gemm_at(const AT* A, int64_t lda, const bf16* W, int64_t ldw, 
   // tiles, one column tile, so that the grid still covers the chip. Few rows (a decode step's
   // batch): 64 x 32 tiles, so that streaming the weights is spread over more workgroups.
   if (N < 128) return gemm_tile<AT, 32, 80, 64, 2, 1>(A, lda, W, ldw, C, ldc, M, N, K, acc, vec, s);
+  // (very wide outputs with few rows, the tied head of a decode batch: 64 x 64 tiles, which
+  // read the weights once per 64 columns with four waves)
+  if (M <= 64 && N >= 8192)
+    return gemm_tile<AT, 64, 64, 64, 2, 2>(A, lda, W, ldw, C, ldc, M, N, K, acc, vec, s);
   if (M <= 64) return gemm_tile<AT, 64, 32, 64, 2, 1>(A, lda, W, ldw, C, ldc, M, N, K, acc, vec, s);
   return gemm_tile<AT, 128, 128, 64, 2, 2>(A, lda, W, ldw, C, ldc, M, N, K, acc, vec, s);
 }
