@@ -513,6 +513,7 @@ def test_backbone_decode_batch16_splitk_vs_oracle():
     (3, 24, 32, 12, 128, 256),  # 8 lanes per channel (6 busy), 16-byte paths, split-K
     (2, 10, 12, 9, 128, 192),   # d_state not a multiple of 4: element-wise state and dt paths
     (4, 16, 16, 72, 128, 256),  # a batch above the split-K limit: whole products, one plane
+    (4, 16, 16, 5, 128, 160),   # d_inner not a multiple of 64: conv step and x_proj as two launches
 ])
 def test_backbone_decode_odd_shapes_vs_oracle(K, N, R, B, Dm, D):
     """Decode steps with a conv width other than 4, d_state 10 or 24 and dt_rank 12 or 32:
