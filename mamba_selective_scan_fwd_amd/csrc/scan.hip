@@ -26,7 +26,8 @@
 // A chunk acts on the state as h -> P*h + H per (b, d, n), P = exp(A * sum(delta)) and H the
 // state it reaches from h = 0. A summary pass computes (sum(delta), H) of every chunk but
 // the last; the output pass starts each chunk from the carried state folded through the
-// maps of the chunks before it (few chunks, so each workgroup folds them itself).
+// maps of the chunks before it (at most MAMBA_SCAN_MAX_CHUNKS chunks, so each workgroup folds
+// them itself).
 #include <algorithm>
 #include <type_traits>
 
@@ -533,6 +534,9 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 #ifndef MAMBA_SCAN_MIN_CHUNK
 #define MAMBA_SCAN_MIN_CHUNK 88  // tokens per chunk, at least (11 blocks)
 #endif
+#ifndef MAMBA_SCAN_MAX_CHUNKS
+#define MAMBA_SCAN_MAX_CHUNKS 64  // each output workgroup folds up to this many - 1 chunk maps
+#endif
 
 static int padded_n(int N) { return N <= 16 ? 16 : (N <= 32 ? 32 : 64); }
 
@@ -546,6 +550,9 @@ ScanPlan plan_selective_scan(int B, int T, int D, int N) {
   const int64_t waves_per_chunk = (int64_t)B * ((D + kCh - 1) / kCh) * kWaves;
   int64_t chunks = MAMBA_SCAN_TARGET_WAVES / waves_per_chunk;
   chunks = std::max<int64_t>(1, std::min<int64_t>(chunks, T / MAMBA_SCAN_MIN_CHUNK));
+  // the fold of the chunk maps before a chunk is sequential in the chunk count, so the count
+  // is capped: a very long sequence over few channels gets longer chunks instead
+  chunks = std::min<int64_t>(chunks, MAMBA_SCAN_MAX_CHUNKS);
   // whole blocks of kTB tokens per chunk
   int chunk_t = (int)((T + chunks - 1) / chunks);
   chunk_t = (chunk_t + kTB - 1) / kTB * kTB;
