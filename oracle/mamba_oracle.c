@@ -21,9 +21,11 @@
  *
  * Parity pins for every function here live in tests/test_oracle_pins.py.
  */
+#define _POSIX_C_SOURCE 199309L /* clock_gettime */
 #include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
+#include <time.h>
 #ifdef _OPENMP
 #include <omp.h>
 #endif
@@ -193,4 +195,36 @@ void oracle_ssm_step(const double* u, const double* dt, const double* dt_bias, i
     acc += (D_skip ? D_skip[d] : 0.0) * ut;
     y[(int64_t)b * D + d] = z ? acc * silu(z[(int64_t)b * z_row_stride + d]) : acc;
   }
+}
+
+/*
+ * CPU-baseline timing, no arithmetic of its own: the wall time in seconds of
+ * oracle_conv1d_fwd followed by oracle_selective_scan_fwd on the given arrays (the conv
+ * writes u, which the scan reads), measured with the monotonic clock around the two calls
+ * only, with the channel loops on `threads` OpenMP threads (0 = the default team).
+ */
+double oracle_time_conv_scan(const double* x, int64_t x_row_stride, const double* conv_w,
+                             const double* conv_b, double* conv_state, double* u,
+                             const double* dt, const double* dt_bias, int delta_softplus,
+                             const double* A_log, const double* Bm, const double* Cm,
+                             int64_t bc_row_stride, const double* D_skip, const double* z,
+                             int64_t z_row_stride, const double* ssm_state_in,
+                             double* ssm_state_out, double* y, int B, int T, int D, int N, int K,
+                             int threads) {
+#ifdef _OPENMP
+  const int saved = omp_get_max_threads();
+  if (threads > 0) omp_set_num_threads(threads);
+#else
+  (void)threads;
+#endif
+  struct timespec t0, t1;
+  clock_gettime(CLOCK_MONOTONIC, &t0);
+  oracle_conv1d_fwd(x, x_row_stride, conv_w, conv_b, conv_state, u, B, T, D, K);
+  oracle_selective_scan_fwd(u, dt, dt_bias, delta_softplus, A_log, Bm, Cm, bc_row_stride, D_skip,
+                            z, z_row_stride, ssm_state_in, ssm_state_out, y, B, T, D, N);
+  clock_gettime(CLOCK_MONOTONIC, &t1);
+#ifdef _OPENMP
+  omp_set_num_threads(saved);
+#endif
+  return (double)(t1.tv_sec - t0.tv_sec) + 1e-9 * (double)(t1.tv_nsec - t0.tv_nsec);
 }

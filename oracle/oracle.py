@@ -67,6 +67,9 @@ def lib() -> ctypes.CDLL:
         L.oracle_silu.restype = ctypes.c_double
         L.oracle_threads.argtypes = []
         L.oracle_threads.restype = ctypes.c_int
+        L.oracle_time_conv_scan.argtypes = [P, I64, P, P, P, P, P, P, I, P, P, P, I64, P, P, I64,
+                                            P, P, P, I, I, I, I, I, I]
+        L.oracle_time_conv_scan.restype = ctypes.c_double
         _lib = L
     return _lib
 
@@ -177,3 +180,46 @@ def ssm_step(u, dt, A_log, Bm, Cm, D_skip, z, dt_bias, ssm_state, delta_softplus
                           _p(Bm), _p(Cm), Bm.shape[1], _p(_f64(D_skip)), _p(zz), zrow, _p(st),
                           _p(y), Bsz, D, N)
     return y, st
+
+
+class ConvScanTimer:
+    """CPU-baseline timing of the prefill layer (conv + SiLU, then the scan) on fixed inputs.
+
+    The inputs are converted to contiguous f64 once, here; each ``run`` calls the C timing
+    entry, which times only the two oracle calls with the monotonic clock, on ``threads``
+    OpenMP threads (0: the default team). Arguments follow conv1d_fwd and selective_scan_fwd;
+    x carries the channel lane in columns 0..D-1 of its rows, Bm and Cm share one row length.
+    """
+
+    def __init__(self, x, conv_w, conv_b, conv_state, dt, dt_bias, A_log, Bm, Cm, D_skip, z,
+                 ssm_state=None, delta_softplus=True):
+        self.x = _f64(x)
+        self.w = _f64(conv_w)
+        self.D, self.K = self.w.shape
+        self.B, self.T, self.xrow = self.x.shape
+        self.conv_b = _f64(conv_b)
+        self.st0 = None if conv_state is None else _f64(conv_state)
+        self.dt = _f64(dt)
+        self.dt_bias = _f64(dt_bias)
+        self.A = _f64(A_log)
+        self.N = self.A.shape[1]
+        self.Bm = _f64(Bm)
+        self.Cm = _f64(Cm)
+        self.D_skip = _f64(D_skip)
+        self.z = _f64(z)
+        self.zrow = 0 if self.z is None else self.z.shape[2]
+        self.h0 = None if ssm_state is None else _f64(ssm_state)
+        self.softplus = int(bool(delta_softplus))
+        self.u = np.zeros((self.B, self.T, self.D), np.float64)
+        self.y = np.zeros((self.B, self.T, self.D), np.float64)
+        self.h1 = np.zeros((self.B, self.D, self.N), np.float64)
+
+    def run(self, threads: int = 0) -> float:
+        """One timed pass; returns the seconds the two oracle calls took."""
+        st = None if self.st0 is None else self.st0.copy()
+        return float(lib().oracle_time_conv_scan(
+            _p(self.x), self.xrow, _p(self.w), _p(self.conv_b), _p(st), _p(self.u), _p(self.dt),
+            _p(self.dt_bias), self.softplus, _p(self.A), _p(self.Bm), _p(self.Cm),
+            self.Bm.shape[2], _p(self.D_skip), _p(self.z), self.zrow, _p(self.h0), _p(self.h1),
+            _p(self.y), self.B, self.T, self.D, self.N, self.K, int(threads)))
+
