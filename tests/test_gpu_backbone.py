@@ -241,16 +241,61 @@ def _normwise(g, r):
     return float(np.linalg.norm(np.asarray(g, np.float64) - r) / max(np.linalg.norm(r), 1e-30))
 
 
-def test_backbone_full_size_24_layers():
-    """The whole 24-layer backbone on sequence 0 of the batch-4 workload (sequences are
-    independent). Across 24 layers the bf16 rounding of activations at every GEMM input turns
-    any difference in summation order into different rounding decisions, which then add up
-    layer after layer: the oracle itself moves by several 1e-2 when its GEMMs sum the same
-    bf16 products in f32 instead of f64. The bar is three times that spread, measured here
-    between the two oracle evaluations, per output and per metric (max-abs-rel and normwise);
-    the 2e-2 bar itself is met at one layer (test above) and on the three-layer stack."""
+def _layer_slice(w, l):
+    """Layer l of a layer-stacked weight dict, as a one-layer stack (embedding and norm_f kept)."""
+    return {k: (v[l:l + 1] if v.ndim >= 2 and k != "embed" else v) for k, v in w.items()}
+
+
+def test_backbone_full_size_per_layer():
+    """Every layer of the 24-layer 130m backbone at its full shapes (B 4, T 2048), on every
+    sequence, at the bf16 bar. The oracle runs the stack layer by layer in f64; the GPU runs
+    layer l alone (mamba_backbone_prefill_ex over a one-layer stack, raw input rows) from the
+    oracle's residual stream entering that layer, so each layer is held to 2e-2 on its own:
+    its output residual stream (through norm_f, at every position), its conv and SSM states,
+    and the head's logits of the last token, per sequence."""
+    s0 = W.C4
+    s1 = W.BackboneShape("c4-layer", n_layers=1)
+    B, T = s0.B, s0.T
+    _say(f"case backbone full size, per layer: L{s0.n_layers} B{B} T{T} Dm{s0.d_model}")
+    w = W.backbone_weights(s0)
+    tok = W.backbone_tokens(s0)
+    h = np.asarray(w["embed"], np.float64)[tok]
+    worst = {}
+    failures = []
+    for l in range(s0.n_layers):
+        wl = _layer_slice(w, l)
+        lg, cs, hs, h_next = ob.prefill(wl, None, 1, s0.D, s0.N, s0.dt_rank, s0.vocab, s0.eps, embeds=h)
+        t, st = _upload(wl)
+        g_lg, g_hid, g_cs, g_hs = _variant_run(s1, st, B, T, embeds=dev(h))
+        g_lg, g_hid, g_cs, g_hs = host(g_lg), host(g_hid), host(g_cs), host(g_hs)
+        ref_hid = ob.rmsnorm(h_next, w["norm_f"], s0.eps)
+        errs = {}
+        for b in range(B):
+            for name, g_, r_ in (("hidden", g_hid[b], ref_hid[b]), ("logits", g_lg[b], lg[b]),
+                                 ("conv_state", g_cs[0, b], cs[0, b]), ("ssm_state", g_hs[0, b], hs[0, b])):
+                e = rel_err(g_, r_)
+                errs[name] = max(errs.get(name, 0.0), e)
+                if not (np.isfinite(e) and e <= TOL_BF16):
+                    failures.append((l, b, name, e))
+        for k, v in errs.items():
+            worst[k] = max(worst.get(k, 0.0), v)
+        _say(f"  layer {l:2d}: " + " ".join(f"{k} {v:.2e}" for k, v in errs.items()))
+        h = h_next
+        del t, st
+    _say("  worst over layers and sequences: " + " ".join(f"{k} {v:.2e}" for k, v in worst.items()))
+    assert not failures, failures[:10]
+
+
+def test_backbone_full_size_24_layers_drift():
+    """Drift report for the 24-layer stack end to end (sequence 0; sequences are
+    independent): the per-layer bar is held above, and here the layers are chained on each
+    side. bf16 rounding of activations at every GEMM input turns any difference in
+    summation order into different rounding decisions, which add up over depth: the oracle
+    itself moves when its GEMMs sum the same bf16 products in f32 instead of f64 (about 1e-2
+    normwise, 4e-2 to 2e-1 max-abs-rel). Printed: the GPU's error and that spread, max-abs-rel
+    and normwise. Asserted: finite outputs and a normwise error within the bf16 bar, 2e-2."""
     s = W.C4
-    _say(f"case backbone full size L{s.n_layers} T{s.T} Dm{s.d_model}, batch element 0 of {s.B}")
+    _say(f"case backbone full size L{s.n_layers} T{s.T} Dm{s.d_model}, end to end, sequence 0 of {s.B}")
     w = W.backbone_weights(s)
     tok = W.backbone_tokens(s)
     t, st = _upload(w)
@@ -263,8 +308,8 @@ def test_backbone_full_size_24_layers():
         s_max, s_nw = rel_err(a, r), _normwise(a, r)
         _say(f"  {name}: gpu max-rel {e_max:.2e} normwise {e_nw:.2e} | oracle f32-vs-f64 "
              f"max-rel {s_max:.2e} normwise {s_nw:.2e}")
-        assert np.isfinite(e_max) and e_max <= max(TOL_BF16, 3 * s_max), name
-        assert e_nw <= max(TOL_BF16, 3 * s_nw), name
+        assert np.isfinite(g).all(), name
+        assert e_nw <= TOL_BF16, name
 
 
 # ------------------------------------------------------------------ decode steps of the backbone
@@ -388,14 +433,73 @@ def test_backbone_decode_graph_replays_equal_eager():
     graph.close()
 
 
-def test_backbone_decode_full_size():
-    """The 130m shapes (24 layers, vocab 50280), B = 4: prefill 24 tokens, then 4 decode steps
-    from the captured graph, against the oracle. The bar is three times the spread between
-    the oracle's f64 and f32 GEMM summations (as for the 24-layer prefill), and at least the
-    bf16 bar."""
+def test_backbone_decode_full_size_per_layer():
+    """One decode step of every layer of the 130m backbone at its full shapes (vocab 50280),
+    B = 4, after a 24-token prefill, each layer held to the bf16 bar on its own. The oracle
+    runs the prefill and the step layer by layer. The GPU step takes token ids, so layer l is
+    fed the oracle's residual row entering it through the embedding: rows 0..B-1 of the
+    table are replaced by those rows, rounded to bf16 (the table's type), and the tokens are
+    0..B-1. The oracle evaluates the same one-layer step from the same table and the same
+    states (the oracle's, after the prefill, rounded to f32 as the GPU holds them); compared
+    per sequence: the new conv and SSM states and the logits (norm_f and the head over that
+    table)."""
+    s0 = W.C4
+    B, n_pre, L = 4, 24, s0.n_layers
+    s1 = W.BackboneShape("c4-decode-layer", n_layers=1, B=B, T=1)
+    _say(f"case backbone decode full shapes, per layer: L{L} B{B}, {n_pre}-token prefill + 1 step")
+    w = W.backbone_weights(s0)
+    tok = W.backbone_tokens(s0)[:B, :n_pre + 1]
+    _, cs_all, hs_all, _ = ob.prefill(w, tok[:, :n_pre], L, s0.D, s0.N, s0.dt_rank, s0.vocab, s0.eps)
+    dims = _dims(s1)
+    wsd = torch.empty(m.mamba_backbone_decode_workspace_size(dims, B), dtype=torch.uint8, device="cuda")
+    ids = np.arange(B, dtype=np.int32)[:, None]
+    step_tok = torch.from_numpy(ids[:, 0].copy()).cuda()
+    h = np.asarray(w["embed"], np.float64)[tok[:, n_pre:n_pre + 1]]  # [B, 1, Dm]
+    failures = []
+    worst = {}
+    for l in range(L):
+        cs_in = cs_all[l:l + 1].astype(np.float32).astype(np.float64)
+        hs_in = hs_all[l:l + 1].astype(np.float32).astype(np.float64)
+        wl = _layer_slice(w, l)
+        table = np.array(w["embed"], np.float32)
+        table[:B] = ob.bf16(h[:, 0])
+        wl["embed"] = table
+        lg, cs1, hs1, _ = ob.prefill(wl, ids, 1, s0.D, s0.N, s0.dt_rank, s0.vocab, s0.eps,
+                                     conv_state=cs_in, ssm_state=hs_in)
+        t, st = _upload(wl)
+        cs_g, hs_g = dev(cs_in), dev(hs_in)
+        lg_g = torch.empty(B, s0.vocab, device="cuda")
+        m.mamba_backbone_decode_step(dims, st, step_tok, cs_g, hs_g, lg_g, wsd)
+        torch.cuda.synchronize()
+        g_lg, g_cs, g_hs = host(lg_g), host(cs_g), host(hs_g)
+        errs = {}
+        for b in range(B):
+            for name, g_, r_ in (("logits", g_lg[b], lg[b]), ("conv_state", g_cs[0, b], cs1[0, b]),
+                                 ("ssm_state", g_hs[0, b], hs1[0, b])):
+                e = rel_err(g_, r_)
+                errs[name] = max(errs.get(name, 0.0), e)
+                if not (np.isfinite(e) and e <= TOL_BF16):
+                    failures.append((l, b, name, e))
+        for k, v in errs.items():
+            worst[k] = max(worst.get(k, 0.0), v)
+        _say(f"  layer {l:2d}: " + " ".join(f"{k} {v:.2e}" for k, v in errs.items()))
+        # the oracle's own chain continues from its unrounded residual stream
+        h = ob.prefill(_layer_slice(w, l), None, 1, s0.D, s0.N, s0.dt_rank, s0.vocab, s0.eps,
+                       conv_state=cs_all[l:l + 1], ssm_state=hs_all[l:l + 1], embeds=h)[3]
+        del t, st
+    _say("  worst over layers and sequences: " + " ".join(f"{k} {v:.2e}" for k, v in worst.items()))
+    assert not failures, failures[:10]
+
+
+def test_backbone_decode_full_size_drift():
+    """Drift report for the chained 24-layer decode (the per-layer bar is held above): the
+    130m shapes, B = 4, a 24-token prefill and then 4 decode steps from the captured graph,
+    against the oracle. Printed: the GPU's error and the oracle's own spread between f64 and
+    f32 GEMM summation, max-abs-rel and normwise. Asserted: finite outputs and a normwise
+    error within the bf16 bar, 2e-2."""
     s0 = W.C4
     s = W.BackboneShape("c4-decode", n_layers=24, B=4, T=28)
-    _say("case backbone decode full shapes L24 B4, 24 + 4 tokens, graph")
+    _say("case backbone decode full shapes L24 B4, 24 + 4 tokens, graph, drift")
     w = W.backbone_weights(s0)
     tok = W.backbone_tokens(s0)[:, :28]
     t, st = _upload(w)
@@ -405,8 +509,11 @@ def test_backbone_decode_full_size():
     for name, g_, r_, a_ in (("logits", got[-1], ref[-1], alt[-1]), ("conv_state", cs, rcs, acs),
                              ("ssm_state", hs, rhs, ahs)):
         e, spread = rel_err(g_, r_), rel_err(a_, r_)
-        _say(f"  {name}: gpu max-rel {e:.2e} | oracle f32-vs-f64 {spread:.2e}")
-        assert np.isfinite(e) and e <= max(TOL_BF16, 3 * spread), name
+        e_nw, s_nw = _normwise(g_, r_), _normwise(a_, r_)
+        _say(f"  {name}: gpu max-rel {e:.2e} normwise {e_nw:.2e} | oracle f32-vs-f64 max-rel "
+             f"{spread:.2e} normwise {s_nw:.2e}")
+        assert np.isfinite(g_).all(), name
+        assert e_nw <= TOL_BF16, name
 
 
 # ------------------------------------------------------------------ prefill variants
