@@ -154,6 +154,31 @@ mamba_status mamba_conv_scan_fwd(const void* x, int64_t x_row_stride, const floa
                                  void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * mamba_conv_scan_fwd for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc. Same arguments, results and
+ * errors as mamba_conv_scan_fwd without the workspace pair: the chunk summaries go to a fixed
+ * scratch array inside the library (16 MiB per GPU, held from the library's first use on that
+ * GPU until the process ends). Every shape with d_state <= 53 fits; a shape whose workspace
+ * (mamba_selective_scan_workspace_size) exceeds 16 MiB fails with MAMBA_EWORKSPACE before
+ * anything is enqueued. The call allocates nothing: it neither calls hipMalloc nor lets a
+ * library allocate.
+ * All calls on one GPU share its scratch, which keeps whatever the last call left there (every
+ * call writes the parts it reads before reading them). Calls whose work may overlap on one GPU
+ * (on different streams, or from different threads without ordering) race on the scratch and
+ * must not be issued; calls ordered on one stream are safe. The current device must be the
+ * one the stream and the buffers belong to.
+ */
+mamba_status mamba_conv_scan_fwd_noalloc(const void* x, int64_t x_row_stride, const float* conv_w,
+                                         const float* conv_b, float* conv_state, const void* dt,
+                                         const float* dt_bias, int delta_softplus,
+                                         const float* A_log, const void* Bm, const void* Cm,
+                                         int64_t bc_row_stride, const float* D_skip,
+                                         const void* z, int64_t z_row_stride,
+                                         const float* ssm_state_in, float* ssm_state_out, void* u,
+                                         void* y, mamba_dtype io_dtype, int B, int T, int D, int K,
+                                         int N, void* stream);
+
+/*
  * One decode step of the conv for L independent layers in one launch.
  * [inference.rs] step chain F4 (one-token conv on the d_conv-slot shift register, state
  * mutated in place) + F4b (SiLU), fused as in the mixed chain's conv-step-with-SiLU

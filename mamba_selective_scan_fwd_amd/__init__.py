@@ -39,6 +39,8 @@ symbols = {
                         _I, _I, _P], _I),
     "mamba_conv_scan_fwd": ([_P, _I64, _P, _P, _P, _P, _P, _I, _P, _P, _P, _I64, _P, _P, _I64, _P, _P,
                              _P, _P, _I, _I, _I, _I, _I, _I, _P, _SZ, _P], _I),
+    "mamba_conv_scan_fwd_noalloc": ([_P, _I64, _P, _P, _P, _P, _P, _I, _P, _P, _P, _I64, _P, _P, _I64,
+                                     _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P], _I),
     "mamba_decode_step": ([_P, _I64, _P, _P, _P, _P, _P, _I, _P, _P, _P, _I64, _P, _P, _I64, _P, _P,
                            _P, _I, _I, _I, _I, _I, _I, _P], _I),
     "mamba_embed_gather": ([_P, _P, _P, _I64, _I, _I, _P], _I),
@@ -235,6 +237,26 @@ def mamba_conv_scan_fwd(x, conv_w, conv_b, conv_state, dt, dt_bias, A_log, Bm, C
         int(bool(delta_softplus)), _ptr(A_log), _ptr(Bm), _ptr(Cm), bcs, _ptr(D_skip), _ptr(z), zs,
         _ptr(ssm_state_in), _ptr(ssm_state_out), _ptr(u), _ptr(y), _io_dtype(y), Bsz, T, D, K, N,
         _ptr(workspace), wsb, _stream(stream)))
+
+
+def mamba_conv_scan_fwd_noalloc(x, conv_w, conv_b, conv_state, dt, dt_bias, A_log, Bm, Cm, D_skip, z,
+                                ssm_state_in, ssm_state_out, y, u=None, delta_softplus=True,
+                                stream=None) -> None:
+    """mamba_conv_scan_fwd without a workspace: the library's fixed scratch stands in for it.
+    Arguments as mamba_conv_scan_fwd."""
+    Bsz, T, D = y.shape
+    K = conv_w.shape[1]
+    N = A_log.shape[1]
+    xs = _row_stride(x, "x")
+    bcs = _row_stride(Bm, "Bm")
+    if _row_stride(Cm, "Cm") != bcs:
+        raise ValueError("Bm and Cm must share one row stride")
+    zs = _row_stride(z, "z") if z is not None else 0
+    _check(load_library().mamba_conv_scan_fwd_noalloc(
+        _ptr(x), xs, _ptr(conv_w), _ptr(conv_b), _ptr(conv_state), _ptr(dt), _ptr(dt_bias),
+        int(bool(delta_softplus)), _ptr(A_log), _ptr(Bm), _ptr(Cm), bcs, _ptr(D_skip), _ptr(z), zs,
+        _ptr(ssm_state_in), _ptr(ssm_state_out), _ptr(u), _ptr(y), _io_dtype(y), Bsz, T, D, K, N,
+        _stream(stream)))
 
 
 def mamba_conv1d_step(x, conv_w, conv_b, conv_state, u, stream=None) -> None:

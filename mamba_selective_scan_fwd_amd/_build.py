@@ -16,8 +16,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmamba_ssm.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
-SOURCES = ["abi.cpp", "backbone_run.cpp", "backbone.hip", "conv1d.hip", "mamba3.hip", "scan.hip",
-           "step.hip"]
+SOURCES = ["abi.cpp", "backbone_run.cpp", "backbone.hip", "conv1d.hip", "mamba3.hip", "noalloc.hip",
+           "scan.hip", "step.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

@@ -217,6 +217,105 @@ mamba_status mamba_selective_scan_fwd(const void* u, const void* dt, const float
   });
 }
 
+}  // extern "C"
+
+namespace {
+
+// mamba_conv_scan_fwd's checks and launch, shared with its no-allocation variant; fn names
+// the entry point in error messages.
+void conv_scan_fwd(const char* fn, const void* x, int64_t x_row_stride, const float* conv_w,
+                   const float* conv_b, float* conv_state, const void* dt, const float* dt_bias,
+                   int delta_softplus, const float* A_log, const void* Bm, const void* Cm,
+                   int64_t bc_row_stride, const float* D_skip, const void* z,
+                   int64_t z_row_stride, const float* ssm_state_in, float* ssm_state_out, void* u,
+                   void* y, mamba_dtype io_dtype, int B, int T, int D, int K, int N,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+  check_dtype(fn, io_dtype);
+  check_dim(fn, "B", B);
+  check_dim(fn, "T", T);
+  check_dim(fn, "D", D);
+  check_state_dim(fn, "K", K, kMaxK);
+  check_state_dim(fn, "N", N, kMaxN);
+  if (B > kMaxGridYZ) fail(MAMBA_EUNSUPPORTED, fn, "B = %d exceeds %d", B, kMaxGridYZ);
+  if (B == 0 || D == 0) return;
+  const size_t es = elem_size(io_dtype);
+  check_ptr(fn, "ssm_state_in", ssm_state_in, 4, false);
+  check_ptr(fn, "ssm_state_out", ssm_state_out, 4, false);
+  check_ptr(fn, "conv_state", conv_state, 4, false);
+  const int64_t nstate = (int64_t)B * D * N;
+  const Range rsi = range("ssm_state_in", ssm_state_in, 1, nstate, nstate, 4);
+  const Range rso = range("ssm_state_out", ssm_state_out, 1, nstate, nstate, 4);
+  const Range rcs = range("conv_state", conv_state, (int64_t)B * D, K, K, 4);
+  if (ssm_state_in != ssm_state_out) check_disjoint(fn, rso, {rsi});
+  check_disjoint(fn, rcs, {rsi, rso});
+  if (T == 0) {  // both states pass through (the conv state is unchanged)
+    check_hip(fn, mamba::launch_selective_scan_fwd(
+                      mamba::ScanFwdArgs{nullptr, nullptr, dt_bias, delta_softplus != 0, A_log, Bm,
+                                         Cm, bc_row_stride, D_skip, z, z_row_stride, ssm_state_in,
+                                         ssm_state_out, y, io_dtype == MAMBA_BF16, B, T, D, N,
+                                         workspace},
+                      static_cast<hipStream_t>(stream)));
+    return;
+  }
+  if (x_row_stride < D) fail(MAMBA_EINVAL, fn, "x_row_stride = %lld is less than D = %d", (long long)x_row_stride, D);
+  if (bc_row_stride < N) fail(MAMBA_EINVAL, fn, "bc_row_stride = %lld is less than N = %d", (long long)bc_row_stride, N);
+  if (z && z_row_stride < D) fail(MAMBA_EINVAL, fn, "z_row_stride = %lld is less than D = %d", (long long)z_row_stride, D);
+  if (D > kMaxRowStride || x_row_stride > kMaxRowStride || (z && z_row_stride > kMaxRowStride))
+    fail(MAMBA_EUNSUPPORTED, fn, "D or a row stride exceeds %lld elements", (long long)kMaxRowStride);
+  check_ptr(fn, "x", x, es, true);
+  check_ptr(fn, "conv_w", conv_w, 4, true);
+  check_ptr(fn, "conv_b", conv_b, 4, false);
+  check_ptr(fn, "dt", dt, es, true);
+  check_ptr(fn, "dt_bias", dt_bias, 4, false);
+  check_ptr(fn, "A_log", A_log, 4, true);
+  check_ptr(fn, "Bm", Bm, es, true);
+  check_ptr(fn, "Cm", Cm, es, true);
+  check_ptr(fn, "D_skip", D_skip, 4, false);
+  check_ptr(fn, "z", z, es, false);
+  check_ptr(fn, "u", u, es, false);
+  check_ptr(fn, "y", y, es, true);
+  const size_t need = mamba::plan_selective_scan(B, T, D, N).workspace_bytes;
+  if (need > 0) {
+    if (!workspace) fail(MAMBA_EWORKSPACE, fn, "workspace is NULL but %zu bytes are required", need);
+    if (workspace_bytes < need) fail(MAMBA_EWORKSPACE, fn, "workspace_bytes = %zu but %zu are required", workspace_bytes, need);
+    if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) fail(MAMBA_EINVAL, fn, "workspace is not 256-byte aligned");
+  }
+  const int64_t rows = (int64_t)B * T;
+  const Range rx = range("x", x, rows, x_row_stride, D, es);
+  const Range rw = range("conv_w", conv_w, D, K, K, 4);
+  const Range rb = range("conv_b", conv_b, 1, D, D, 4);
+  const Range rdt = range("dt", dt, rows, D, D, es);
+  const Range rdb = range("dt_bias", dt_bias, 1, D, D, 4);
+  const Range ra = range("A_log", A_log, D, N, N, 4);
+  const Range rB = range("Bm", Bm, rows, bc_row_stride, N, es);
+  const Range rC = range("Cm", Cm, rows, bc_row_stride, N, es);
+  const Range rD = range("D_skip", D_skip, 1, D, D, 4);
+  const Range rz = range("z", z, rows, z_row_stride, D, es);
+  const Range rws = range("workspace", need ? workspace : nullptr, 1, (int64_t)need, (int64_t)need, 1);
+  const Range ru = range("u", u, rows, D, D, es);
+  const Range ry = range("y", y, rows, D, D, es);
+  check_disjoint(fn, ry, {rx, rw, rb, rcs, rdt, rdb, ra, rB, rC, rD, rz, rsi, rso, rws, ru});
+  check_disjoint(fn, ru, {rx, rw, rb, rcs, rdt, rdb, ra, rB, rC, rD, rz, rsi, rso, rws});
+  check_disjoint(fn, rso, {rx, rw, rb, rdt, rdb, ra, rB, rC, rD, rz, rws});
+  check_disjoint(fn, rcs, {rx, rw, rb, rdt, rdb, ra, rB, rC, rD, rz, rws});
+  check_disjoint(fn, rws, {rx, rw, rb, rdt, rdb, ra, rB, rC, rD, rz, rsi});
+  mamba::ScanFwdArgs a{nullptr, dt, dt_bias, delta_softplus != 0, A_log, Bm, Cm, bc_row_stride,
+                       D_skip, z, z_row_stride, ssm_state_in, ssm_state_out, y,
+                       io_dtype == MAMBA_BF16, B, T, D, N, workspace};
+  a.x = x;
+  a.x_row_stride = x_row_stride;
+  a.conv_w = conv_w;
+  a.conv_b = conv_b;
+  a.conv_state = conv_state;
+  a.u_out = u;
+  a.K = K;
+  check_hip(fn, mamba::launch_selective_scan_fwd(a, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
 mamba_status mamba_conv_scan_fwd(const void* x, int64_t x_row_stride, const float* conv_w,
                                  const float* conv_b, float* conv_state, const void* dt,
                                  const float* dt_bias, int delta_softplus, const float* A_log,
@@ -225,88 +324,41 @@ mamba_status mamba_conv_scan_fwd(const void* x, int64_t x_row_stride, const floa
                                  const float* ssm_state_in, float* ssm_state_out, void* u, void* y,
                                  mamba_dtype io_dtype, int B, int T, int D, int K, int N,
                                  void* workspace, size_t workspace_bytes, void* stream) {
-  static const char* fn = "mamba_conv_scan_fwd";
   return guarded([&] {
-    check_dtype(fn, io_dtype);
+    conv_scan_fwd("mamba_conv_scan_fwd", x, x_row_stride, conv_w, conv_b, conv_state, dt, dt_bias,
+                  delta_softplus, A_log, Bm, Cm, bc_row_stride, D_skip, z, z_row_stride,
+                  ssm_state_in, ssm_state_out, u, y, io_dtype, B, T, D, K, N, workspace,
+                  workspace_bytes, stream);
+  });
+}
+
+mamba_status mamba_conv_scan_fwd_noalloc(const void* x, int64_t x_row_stride, const float* conv_w,
+                                         const float* conv_b, float* conv_state, const void* dt,
+                                         const float* dt_bias, int delta_softplus,
+                                         const float* A_log, const void* Bm, const void* Cm,
+                                         int64_t bc_row_stride, const float* D_skip,
+                                         const void* z, int64_t z_row_stride,
+                                         const float* ssm_state_in, float* ssm_state_out, void* u,
+                                         void* y, mamba_dtype io_dtype, int B, int T, int D, int K,
+                                         int N, void* stream) {
+  static const char* fn = "mamba_conv_scan_fwd_noalloc";
+  return guarded([&] {
     check_dim(fn, "B", B);
     check_dim(fn, "T", T);
     check_dim(fn, "D", D);
-    check_state_dim(fn, "K", K, kMaxK);
     check_state_dim(fn, "N", N, kMaxN);
-    if (B > kMaxGridYZ) fail(MAMBA_EUNSUPPORTED, fn, "B = %d exceeds %d", B, kMaxGridYZ);
-    if (B == 0 || D == 0) return;
-    const size_t es = elem_size(io_dtype);
-    check_ptr(fn, "ssm_state_in", ssm_state_in, 4, false);
-    check_ptr(fn, "ssm_state_out", ssm_state_out, 4, false);
-    check_ptr(fn, "conv_state", conv_state, 4, false);
-    const int64_t nstate = (int64_t)B * D * N;
-    const Range rsi = range("ssm_state_in", ssm_state_in, 1, nstate, nstate, 4);
-    const Range rso = range("ssm_state_out", ssm_state_out, 1, nstate, nstate, 4);
-    const Range rcs = range("conv_state", conv_state, (int64_t)B * D, K, K, 4);
-    if (ssm_state_in != ssm_state_out) check_disjoint(fn, rso, {rsi});
-    check_disjoint(fn, rcs, {rsi, rso});
-    if (T == 0) {  // both states pass through (the conv state is unchanged)
-      check_hip(fn, mamba::launch_selective_scan_fwd(
-                        mamba::ScanFwdArgs{nullptr, nullptr, dt_bias, delta_softplus != 0, A_log, Bm,
-                                           Cm, bc_row_stride, D_skip, z, z_row_stride, ssm_state_in,
-                                           ssm_state_out, y, io_dtype == MAMBA_BF16, B, T, D, N,
-                                           workspace},
-                        static_cast<hipStream_t>(stream)));
-      return;
-    }
-    if (x_row_stride < D) fail(MAMBA_EINVAL, fn, "x_row_stride = %lld is less than D = %d", (long long)x_row_stride, D);
-    if (bc_row_stride < N) fail(MAMBA_EINVAL, fn, "bc_row_stride = %lld is less than N = %d", (long long)bc_row_stride, N);
-    if (z && z_row_stride < D) fail(MAMBA_EINVAL, fn, "z_row_stride = %lld is less than D = %d", (long long)z_row_stride, D);
-    if (D > kMaxRowStride || x_row_stride > kMaxRowStride || (z && z_row_stride > kMaxRowStride))
-      fail(MAMBA_EUNSUPPORTED, fn, "D or a row stride exceeds %lld elements", (long long)kMaxRowStride);
-    check_ptr(fn, "x", x, es, true);
-    check_ptr(fn, "conv_w", conv_w, 4, true);
-    check_ptr(fn, "conv_b", conv_b, 4, false);
-    check_ptr(fn, "dt", dt, es, true);
-    check_ptr(fn, "dt_bias", dt_bias, 4, false);
-    check_ptr(fn, "A_log", A_log, 4, true);
-    check_ptr(fn, "Bm", Bm, es, true);
-    check_ptr(fn, "Cm", Cm, es, true);
-    check_ptr(fn, "D_skip", D_skip, 4, false);
-    check_ptr(fn, "z", z, es, false);
-    check_ptr(fn, "u", u, es, false);
-    check_ptr(fn, "y", y, es, true);
+    void* ws = nullptr;
     const size_t need = mamba::plan_selective_scan(B, T, D, N).workspace_bytes;
-    if (need > 0) {
-      if (!workspace) fail(MAMBA_EWORKSPACE, fn, "workspace is NULL but %zu bytes are required", need);
-      if (workspace_bytes < need) fail(MAMBA_EWORKSPACE, fn, "workspace_bytes = %zu but %zu are required", workspace_bytes, need);
-      if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) fail(MAMBA_EINVAL, fn, "workspace is not 256-byte aligned");
-    }
-    const int64_t rows = (int64_t)B * T;
-    const Range rx = range("x", x, rows, x_row_stride, D, es);
-    const Range rw = range("conv_w", conv_w, D, K, K, 4);
-    const Range rb = range("conv_b", conv_b, 1, D, D, 4);
-    const Range rdt = range("dt", dt, rows, D, D, es);
-    const Range rdb = range("dt_bias", dt_bias, 1, D, D, 4);
-    const Range ra = range("A_log", A_log, D, N, N, 4);
-    const Range rB = range("Bm", Bm, rows, bc_row_stride, N, es);
-    const Range rC = range("Cm", Cm, rows, bc_row_stride, N, es);
-    const Range rD = range("D_skip", D_skip, 1, D, D, 4);
-    const Range rz = range("z", z, rows, z_row_stride, D, es);
-    const Range rws = range("workspace", need ? workspace : nullptr, 1, (int64_t)need, (int64_t)need, 1);
-    const Range ru = range("u", u, rows, D, D, es);
-    const Range ry = range("y", y, rows, D, D, es);
-    check_disjoint(fn, ry, {rx, rw, rb, rcs, rdt, rdb, ra, rB, rC, rD, rz, rsi, rso, rws, ru});
-    check_disjoint(fn, ru, {rx, rw, rb, rcs, rdt, rdb, ra, rB, rC, rD, rz, rsi, rso, rws});
-    check_disjoint(fn, rso, {rx, rw, rb, rdt, rdb, ra, rB, rC, rD, rz, rws});
-    check_disjoint(fn, rcs, {rx, rw, rb, rdt, rdb, ra, rB, rC, rD, rz, rws});
-    check_disjoint(fn, rws, {rx, rw, rb, rdt, rdb, ra, rB, rC, rD, rz, rsi});
-    mamba::ScanFwdArgs a{nullptr, dt, dt_bias, delta_softplus != 0, A_log, Bm, Cm, bc_row_stride,
-                         D_skip, z, z_row_stride, ssm_state_in, ssm_state_out, y,
-                         io_dtype == MAMBA_BF16, B, T, D, N, workspace};
-    a.x = x;
-    a.x_row_stride = x_row_stride;
-    a.conv_w = conv_w;
-    a.conv_b = conv_b;
-    a.conv_state = conv_state;
-    a.u_out = u;
-    a.K = K;
-    check_hip(fn, mamba::launch_selective_scan_fwd(a, static_cast<hipStream_t>(stream)));
+    if (need > mamba::kNoAllocScratchBytes)
+      fail(MAMBA_EWORKSPACE, fn,
+           "this shape needs %zu bytes of scratch, more than the %zu of the library's fixed "
+           "scratch; call mamba_conv_scan_fwd with a workspace instead",
+           need, mamba::kNoAllocScratchBytes);
+    if (need > 0) check_hip(fn, mamba::noalloc_scratch(&ws));
+    conv_scan_fwd(fn, x, x_row_stride, conv_w, conv_b, conv_state, dt, dt_bias, delta_softplus,
+                  A_log, Bm, Cm, bc_row_stride, D_skip, z, z_row_stride, ssm_state_in,
+                  ssm_state_out, u, y, io_dtype, B, T, D, K, N, ws, need > 0 ? mamba::kNoAllocScratchBytes : 0,
+                  stream);
   });
 }
 

@@ -101,6 +101,16 @@ struct ScanPlan {
 
 ScanPlan plan_selective_scan(int B, int T, int D, int N);
 
+// Size of the library's fixed device scratch (noalloc.hip), the workspace of the entry points
+// that allocate nothing. The scan planner makes more than one chunk only while B * d_inner is
+// at most 24576, with B * chunks * d_inner at most 49152, so its workspace is bounded by
+// 983040 + 294912 * d_state bytes: every shape with d_state <= 53 fits.
+constexpr size_t kNoAllocScratchBytes = size_t(16) << 20;
+
+// The fixed scratch's device address on the current device, looked up on the first call per
+// device and kept.
+hipError_t noalloc_scratch(void** out);
+
 // Largest conv width the kernels take.
 constexpr int kMaxConvK = 8;
 

@@ -195,3 +195,20 @@ def test_mamba3_step_validation(kw, status, needle):
 def test_mamba3_step_empty_is_noop():
     st, msg = m3_call(L=0, proj=None, h=None, k=None, v=None, ang=None, out=None)
     assert st == 0, msg
+
+
+def test_noalloc_rejects_a_shape_beyond_its_scratch():
+    """The no-allocation conv + scan refuses, before any HIP call, a shape whose scan workspace
+    exceeds the library's fixed 16 MiB scratch (d_state 64 over 24576 channels in 2 chunks
+    needs 19857408 bytes), and says which call to use instead."""
+    lib = m.load_library()
+    B, T, D, K, N = 1, 176, 24576, 4, 64
+    need = lib.mamba_selective_scan_workspace_size(B, T, D, N)
+    assert need == 19857408 > (16 << 20)
+    st = lib.mamba_conv_scan_fwd_noalloc(
+        FAKE, D, FAKE, None, None, FAKE, None, 1, FAKE, FAKE, FAKE, 2 * N, None, None, 0,
+        None, None, None, FAKE, F32, B, T, D, K, N, None)
+    assert st == EWS
+    msg = m.mamba_last_error()
+    assert "mamba_conv_scan_fwd_noalloc" in msg and "19857408" in msg and str(16 << 20) in msg
+    assert "mamba_conv_scan_fwd with a workspace" in msg
