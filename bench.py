@@ -52,6 +52,29 @@ SCAN_SLOTS_PER_ELEMENT = 4 + EXP_SLOTS
 # tens of milliseconds of load to ramp up (the 130m layer call measured 44 us after 20 warm-up
 # steps, 40 us after 2000)
 DEFAULT_WARMUP = {"c1": 2000, "c3": 100, "c2": 1000, "c5": 200, "c4": 10, "c4d": 100}
+# whatever --warmup asks for, the untimed warm-up lasts at least this long: a few warm-up
+# steps of a 40 us call leave the GPU clock where idle left it
+MIN_WARMUP_S = 0.3
+
+
+def warm_up(torch, step, n, settle=None):
+    """n untimed warm-up steps (step(i), i = 0..n-1), then more untimed steps (settle(), or
+    step(i) for the following i) in batches of 32 until MIN_WARMUP_S of wall time has passed
+    since the first. Returns (steps run, seconds)."""
+    t0 = time.perf_counter()
+    for i in range(n):
+        step(i)
+    torch.cuda.synchronize()
+    i = n
+    while time.perf_counter() - t0 < MIN_WARMUP_S:
+        for _ in range(32):
+            if settle is None:
+                step(i)
+            else:
+                settle()
+            i += 1
+        torch.cuda.synchronize()
+    return i, time.perf_counter() - t0
 
 
 def parse_args(argv=None):
@@ -258,10 +281,8 @@ def bench_prefill(args, shape):
         if ev:
             ev[-1].record(stream)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    print(f"[bench] warmup done ({args.warmup} steps); timing {args.steps} steps ("
+    warm_steps, warm_s = warm_up(torch, lambda i: step(), args.warmup)
+    print(f"[bench] warmup done ({warm_steps} steps, {warm_s:.2f} s); timing {args.steps} steps ("
           f"{'fused' if fused else 'split'} path)", file=sys.stderr, flush=True)
 
     # per-call events over the timed region
@@ -344,6 +365,7 @@ def bench_prefill(args, shape):
     if B == 1:
         result["vs_step_by_step"] = step_by_step_prefill(m, torch, x, z, dt, Bm, Cm, p, conv_state,
                                                          ssm_state, stream, (128, 512, 2048))
+    result["warmup_run"] = dict(steps=warm_steps, seconds=round(warm_s, 3))
     return result, inp
 
 
@@ -362,6 +384,7 @@ def second_leg_c3(args, W):
     torch.cuda.empty_cache()
     rl = r["roofline"]
     return dict(workload=r["config"]["workload"], steps=a.steps, warmup=a.warmup,
+                warmup_run=r["warmup_run"],
                 ms_per_step=r["ms_per_step"], value=r["value"], unit=r["unit"],
                 calls=r["calls"], layer_gbs=r["layer_gbs"], layer_hbm_frac=r["layer_hbm_frac"],
                 scan_roofline=dict(bound=rl["bound"], achieved=rl["achieved"], peak=rl["peak"],
@@ -557,9 +580,7 @@ def bench_decode(args, shape):
         if ev:
             ev[1].record(stream)
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
+    warm_steps, warm_s = warm_up(torch, step, args.warmup)
     evs = _sampled_events(args.steps, args.event_every, 2)
     t_start, t_end = _events(torch)
     t_start.record(stream)
@@ -631,6 +652,7 @@ def bench_decode(args, shape):
     result["per_layer_launches"] = dict(step_us=t0.elapsed_time(t1) / reps * 1e3, launches_per_step=2 * L,
                                         fused_step_us=ms_step * 1e3,
                                         how="mamba_conv1d_step + mamba_ssm_step per layer (context)")
+    result["warmup_run"] = dict(steps=warm_steps, seconds=round(warm_s, 3))
     return result, None
 
 
@@ -671,9 +693,7 @@ def bench_m3(args, shape):
         if ev:
             ev[1].record(stream)
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
+    warm_steps, warm_s = warm_up(torch, step, args.warmup)
     evs = _sampled_events(args.steps, args.event_every, 2)
     t_start, t_end = _events(torch)
     t_start.record(stream)
@@ -707,6 +727,7 @@ def bench_m3(args, shape):
         layer_gbs=sb / (ms_step * 1e-3) / 1e9,
     )
     result["layer_hbm_frac"] = result["layer_gbs"] / HBM_PEAK_GBS
+    result["warmup_run"] = dict(steps=warm_steps, seconds=round(warm_s, 3))
     return result, dict(P=P)
 
 
@@ -779,10 +800,8 @@ def bench_backbone(args, shape):
     def step():
         m.mamba_backbone_prefill(dims, wst, tokens, cs, hs, logits, ws, stream=stream)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    print(f"[bench] warmup done ({args.warmup} steps); timing {args.steps} steps", file=sys.stderr,
+    warm_steps, warm_s = warm_up(torch, lambda i: step(), args.warmup)
+    print(f"[bench] warmup done ({warm_steps} steps, {warm_s:.2f} s); timing {args.steps} steps", file=sys.stderr,
           flush=True)
     t_start, t_end = _events(torch)
     t_start.record(stream)
@@ -900,6 +919,7 @@ def bench_backbone(args, shape):
         layer_gbs=None,
         layer_hbm_frac=None,
     )
+    result["warmup_run"] = dict(steps=warm_steps, seconds=round(warm_s, 3))
     return result, dict(weights=w, tokens=tok_np)
 
 
@@ -939,10 +959,13 @@ def bench_backbone_decode(args, shape):
         step_tok.copy_(tok[:, pos[0]])
         pos[0] += 1
 
-    for _ in range(args.warmup):
+    def warm(i):
         next_tokens()
         graph.launch(stream)
-    torch.cuda.synchronize()
+
+    # beyond the counted warm-up steps the graph replays on the same tokens (the token buffer
+    # holds only the counted steps)
+    warm_steps, warm_s = warm_up(torch, warm, args.warmup, settle=lambda: graph.launch(stream))
     t0, t1 = _events(torch)
     t0.record(stream)
     for _ in range(args.steps):
@@ -983,6 +1006,7 @@ def bench_backbone_decode(args, shape):
         layer_gbs=None,
         layer_hbm_frac=None,
     )
+    result["warmup_run"] = dict(steps=warm_steps, seconds=round(warm_s, 3))
     return result, None
 
 
@@ -1069,7 +1093,7 @@ def main(argv=None):
         cpu_baseline=cpu, calls=result["calls"], layer_gbs=result["layer_gbs"],
         layer_hbm_frac=result["layer_hbm_frac"])
     for extra in ("backbone_tokens_per_s", "layer_chain_us", "valu_floor_us", "hbm_floor_us", "valu_frac",
-                  "vs_step_by_step", "cold", "per_layer_launches"):
+                  "vs_step_by_step", "cold", "per_layer_launches", "warmup_run"):
         if extra in result:
             line[extra] = result[extra]
     if c3 is not None:
