@@ -11,6 +11,7 @@
 // Precision: GEMM operands are bf16 (weights stored bf16; activations rounded to bf16 as they
 // enter the GEMM), products accumulate in f32, everything else is f32.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.hpp"
 #include "launch.hpp"
@@ -149,6 +150,34 @@ __device__ __forceinline__ bf16x8 load_chunk_scalar(const AT* row, int k0, int K
 #ifndef MAMBA_GEMM_WPE
 #define MAMBA_GEMM_WPE 2  // waves per SIMD the register allocation must allow
 #endif
+// 32 x 32 MFMA tiles where the wave tile allows (1) or 16 x 16 everywhere (0)
+#ifndef MAMBA_GEMM_MFMA32
+#define MAMBA_GEMM_MFMA32 1
+#endif
+// XOR-swizzled LDS rows for the staged tiles (1) or rows padded by 8 elements (0)
+#ifndef MAMBA_GEMM_SWZ
+#define MAMBA_GEMM_SWZ 1
+#endif
+// register sets of staged chunks: 2 (slab kt+2 loads while kt multiplies) or 1 (kt+1)
+#ifndef MAMBA_GEMM_SETS
+#define MAMBA_GEMM_SETS 2
+#endif
+// the large-output tile: BM x BN x BK as WGM x WGN waves
+#ifndef MAMBA_GEMM_BM
+#define MAMBA_GEMM_BM 128
+#endif
+#ifndef MAMBA_GEMM_BN
+#define MAMBA_GEMM_BN 128
+#endif
+#ifndef MAMBA_GEMM_BK
+#define MAMBA_GEMM_BK 64
+#endif
+#ifndef MAMBA_GEMM_WGM
+#define MAMBA_GEMM_WGM 2
+#endif
+#ifndef MAMBA_GEMM_WGN
+#define MAMBA_GEMM_WGN 2
+#endif
 #ifndef MAMBA_GEMM_LDS_EPI
 #define MAMBA_GEMM_LDS_EPI 1  // write C through LDS as rows of float4 (1) or from the fragments (0)
 #endif
@@ -161,18 +190,30 @@ gemm_mfma_kernel(
     int64_t c_split_stride) {
   // XCD-aware tile order. Workgroups are handed to the 8 XCDs (each with its own L2) in
   // round-robin order of their linear id, so neighbouring ids land on different L2s. Here
-  // each XCD takes one contiguous run of tiles instead, in (slice, m, n) order with n
-  // fastest: the tiles that share an A row block run on one XCD at about the same time, and
-  // the row block is fetched into that L2 once rather than once per XCD.
+  // each XCD takes one contiguous run of tiles instead, and the runs follow a grouped
+  // order: the column tiles are cut into groups of up to 8, and within a group the tiles go
+  // row block by row block (n fastest). The tiles one XCD has in flight then cover a few row
+  // blocks of A and at most 8 column blocks of W, which fit its L2 together; with plain
+  // row-major order they would span every column block, and W (4.7 MB for in_proj) would be
+  // fetched again for each row block.
   // (Split-K launches keep the plain order: their slices share no operand rows.)
   int bx = blockIdx.x, by = blockIdx.y, bz = blockIdx.z;
   if (gridDim.z == 1) {
-    const int gx = gridDim.x, G = gx * (int)gridDim.y;
+    const int gx = gridDim.x, gy = gridDim.y, G = gx * gy;
     const int L = blockIdx.x + gx * blockIdx.y;
     const int xcd = L % 8, idx = L / 8, base = G / 8, rem = G % 8;
     const int t = xcd * base + min(xcd, rem) + idx;  // a bijection of [0, G)
-    bx = t % gx;
-    by = t / gx;
+    constexpr int kGroupN = 8;
+    const int full = (gx / kGroupN) * kGroupN * gy;  // tiles in whole groups
+    if (t < full) {
+      const int g = t / (kGroupN * gy), r = t % (kGroupN * gy);
+      by = r / kGroupN;
+      bx = g * kGroupN + r % kGroupN;
+    } else {
+      const int w = gx % kGroupN, r = t - full;  // the last, narrower group
+      by = r / w;
+      bx = gx - w + r % w;
+    }
   }
   // split K (gridDim.z > 1): slice z covers k in [z * k_chunk, z * k_chunk + k_chunk) and
   // writes its partial product to its own C plane (C + z * c_split_stride)
@@ -185,16 +226,30 @@ gemm_mfma_kernel(
   }
   constexpr int NT = 64 * WGM * WGN;
   constexpr int WTM = BM / WGM, WTN = BN / WGN;  // wave tile
-  constexpr int TM = WTM / 16, TN = WTN / 16;
-  constexpr int LDK = BK + 8;
+  // MFMA tile: 32 x 32 (v_mfma_f32_32x32x16_bf16, 16 k per step) when the wave tile is made
+  // of whole 32 x 32 tiles, else 16 x 16 (v_mfma_f32_16x16x32_bf16, 32 k per step)
+  constexpr int MT = MAMBA_GEMM_MFMA32 && WTM % 32 == 0 && WTN % 32 == 0 ? 32 : 16;
+  constexpr int KSTEP = MT == 32 ? 16 : 32;
+  constexpr int TM = WTM / MT, TN = WTN / MT;
+  // LDS row layout of the staged tiles. With kSwz, rows are BK elements (no pad) and the
+  // 16-byte chunk kc of row r sits at chunk kc ^ swz(r), swz(r) = (r ^ r >> 3) & 7: the 16
+  // rows a fragment read touches (and each pair of rows a 16-lane group writes) then fall on
+  // distinct bank groups for 32 or 64 four-byte banks. Without it, rows are padded by 8.
+  constexpr bool kSwz = MAMBA_GEMM_SWZ != 0 && BK == 64;
+  constexpr int LDK = kSwz ? BK : BK + 8;
+  auto swz = [](int r) { return kSwz ? (r ^ (r >> 3)) & 7 : 0; };
   constexpr int CPR = BK / 8;  // chunks per row
   constexpr int A_CH = BM * CPR / NT, W_CH = BN * CPR / NT;
-  static_assert(TM * 16 == WTM && TN * 16 == WTN && BK % 32 == 0, "tile shape");
+  static_assert(TM * MT == WTM && TN * MT == WTN && BK % 32 == 0, "tile shape");
   static_assert(A_CH * NT == BM * CPR && W_CH * NT == BN * CPR, "staging split");
+  static_assert(A_CH <= 32 && W_CH <= 32, "chunk masks");
   // staging buffers for A and W; after the last k-slab the same LDS holds the C tile
   constexpr int LDC = BN + 4;  // (4 rows apart = 16 banks: the fragment writes do not collide)
   constexpr int kStageBytes = 2 * (BM + BN) * LDK * (int)sizeof(bf16);
-  constexpr int kCBytes = MAMBA_GEMM_LDS_EPI ? BM * LDC * (int)sizeof(float) : 0;
+  // the C tile leaves through LDS in kParts passes of BM / kParts rows (one wave row per
+  // pass when the whole tile would need more LDS than the staging buffers)
+  constexpr int kParts = BM * LDC * (int)sizeof(float) > kStageBytes ? WGM : 1;
+  constexpr int kCBytes = MAMBA_GEMM_LDS_EPI ? BM / kParts * LDC * (int)sizeof(float) : 0;
   __shared__ __attribute__((aligned(16))) char smem[kStageBytes > kCBytes ? kStageBytes : kCBytes];
   auto As = reinterpret_cast<bf16(*)[BM * LDK]>(smem);
   auto Ws = reinterpret_cast<bf16(*)[BN * LDK]>(smem + 2 * BM * LDK * sizeof(bf16));
@@ -204,22 +259,34 @@ gemm_mfma_kernel(
   const int wm = wave / WGN, wn = wave % WGN;
   const int m0 = by * BM, n0 = bx * BN;
 
-  // Two register sets of staged chunks: the loads of slab kt+2 are issued while slab kt is
-  // multiplied and slab kt+1 (loaded one iteration earlier) is written to LDS, so a load has
-  // a whole iteration to arrive. A tile entirely inside the operands skips the bounds checks.
-  bf16x8 ra[2][A_CH], rw[2][W_CH];
+  // Register sets of staged chunks. With two, the loads of slab kt+2 are issued while slab
+  // kt is multiplied and slab kt+1 (loaded one iteration earlier) is written to LDS, so a
+  // load has a whole iteration to arrive. On the 16-byte path every chunk load is issued
+  // unconditionally (a chunk outside the operands reads an in-bounds address and is zeroed
+  // when written to LDS), and chunks stay as loaded (f32 A is rounded to bf16 only then):
+  // a load under a branch, or a use right after it, would make the wave wait for every load
+  // in flight, the prefetch included. A tile entirely inside the operands skips the checks.
+  constexpr int NSET = MAMBA_GEMM_SETS;
+  using ARaw = std::conditional_t<VEC, Chunk<AT>, bf16x8>;
+  using WRaw = std::conditional_t<VEC, Chunk<bf16>, bf16x8>;
+  ARaw ra[NSET][A_CH];
+  WRaw rw[NSET][W_CH];
+  uint32_t va[NSET] = {}, vw[NSET] = {};  // 16-byte path: bit i set when chunk i is inside
   const bool full = VEC && m0 + BM <= M && n0 + BN <= N && K % BK == 0;
   auto fetch = [&](int k0, auto SET) {
     constexpr int st = decltype(SET)::value;
+    if constexpr (VEC) {
+      va[st] = 0;
+      vw[st] = 0;
+    }
 #pragma unroll
     for (int i = 0; i < A_CH; ++i) {
       const int c = tid + i * NT, r = c / CPR, kc = (c % CPR) * 8;
       const int gm = m0 + r, gk = k0 + kc;
       if constexpr (VEC) {
-        Chunk<AT> ch;
-        if (full || (gm < M && gk < K)) load_chunk<AT>(ch, A + (int64_t)gm * lda + gk);
-        else zero_chunk<AT>(ch);
-        ra[st][i] = to_bf16x8(ch);
+        const bool ok = full || (gm < M && gk < K);
+        load_chunk<AT>(ra[st][i], A + (int64_t)min(gm, M - 1) * lda + (ok ? gk : 0));
+        va[st] |= (uint32_t)ok << i;
       } else {
         ra[st][i] = gm < M ? load_chunk_scalar(A + (int64_t)gm * lda, gk, K) : bf16x8{};
       }
@@ -229,10 +296,9 @@ gemm_mfma_kernel(
       const int c = tid + i * NT, r = c / CPR, kc = (c % CPR) * 8;
       const int gn = n0 + r, gk = k0 + kc;
       if constexpr (VEC) {
-        Chunk<bf16> ch;
-        if (full || (gn < N && gk < K)) load_chunk<bf16>(ch, W + (int64_t)gn * ldw + gk);
-        else zero_chunk<bf16>(ch);
-        rw[st][i] = to_bf16x8(ch);
+        const bool ok = full || (gn < N && gk < K);
+        load_chunk<bf16>(rw[st][i], W + (int64_t)min(gn, N - 1) * ldw + (ok ? gk : 0));
+        vw[st] |= (uint32_t)ok << i;
       } else {
         rw[st][i] = gn < N ? load_chunk_scalar(W + (int64_t)gn * ldw, gk, K) : bf16x8{};
       }
@@ -243,81 +309,143 @@ gemm_mfma_kernel(
 #pragma unroll
     for (int i = 0; i < A_CH; ++i) {
       const int c = tid + i * NT;
-      *reinterpret_cast<bf16x8*>(&As[buf][(c / CPR) * LDK + (c % CPR) * 8]) = ra[st][i];
+      const int r = c / CPR;
+      bf16x8 v;
+      if constexpr (VEC) {
+        v = to_bf16x8(ra[st][i]);
+        if (!((va[st] >> i) & 1u)) v = bf16x8{};
+      } else {
+        v = ra[st][i];
+      }
+      *reinterpret_cast<bf16x8*>(&As[buf][r * LDK + ((c % CPR) ^ swz(r)) * 8]) = v;
     }
 #pragma unroll
     for (int i = 0; i < W_CH; ++i) {
       const int c = tid + i * NT;
-      *reinterpret_cast<bf16x8*>(&Ws[buf][(c / CPR) * LDK + (c % CPR) * 8]) = rw[st][i];
+      const int r = c / CPR;
+      bf16x8 v;
+      if constexpr (VEC) {
+        v = to_bf16x8(rw[st][i]);
+        if (!((vw[st] >> i) & 1u)) v = bf16x8{};
+      } else {
+        v = rw[st][i];
+      }
+      *reinterpret_cast<bf16x8*>(&Ws[buf][r * LDK + ((c % CPR) ^ swz(r)) * 8]) = v;
     }
   };
 
-  f32x4 acc[TM][TN];
+  typedef float f32x16 __attribute__((ext_vector_type(16)));
+  using AccT = std::conditional_t<MT == 32, f32x16, f32x4>;
+  constexpr int NR = MT == 32 ? 16 : 4;  // accumulator registers per lane and tile
+  AccT acc[TM][TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int r = 0; r < NR; ++r) acc[i][j][r] = 0.0f;
 
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
   const int nk = (K + BK - 1) / BK;
-  const int frow = lane & 15, fk = (lane >> 4) * 8;
+  // fragment of lane l: row l % MT of the tile, 8 consecutive k at 8 * (l / MT)
+  const int frow = lane & (MT - 1), fk = (lane / MT) * 8;
   auto multiply = [&](int buf) {
 #pragma unroll
-    for (int kk = 0; kk < BK; kk += 32) {
+    for (int kk = 0; kk < BK; kk += KSTEP) {
       bf16x8 af[TM], bfr[TN];
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
-        af[i] = *reinterpret_cast<const bf16x8*>(&As[buf][(wm * WTM + i * 16 + frow) * LDK + kk + fk]);
+      for (int i = 0; i < TM; ++i) {
+        const int r = wm * WTM + i * MT + frow;
+        af[i] = *reinterpret_cast<const bf16x8*>(&As[buf][r * LDK + (((kk + fk) >> 3) ^ swz(r)) * 8]);
+      }
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
-        bfr[j] = *reinterpret_cast<const bf16x8*>(&Ws[buf][(wn * WTN + j * 16 + frow) * LDK + kk + fk]);
+      for (int j = 0; j < TN; ++j) {
+        const int r = wn * WTN + j * MT + frow;
+        bfr[j] = *reinterpret_cast<const bf16x8*>(&Ws[buf][r * LDK + (((kk + fk) >> 3) ^ swz(r)) * 8]);
+      }
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+          if constexpr (MT == 32)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+          else
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
     }
   };
   // iteration kt: loads of slab kt+2 into set kt & 1, multiply LDS buffer kt & 1, write slab
   // kt+1 (set (kt+1) & 1) into LDS buffer (kt+1) & 1, barrier
   auto step = [&](int kt, auto SET) {
     constexpr int st = decltype(SET)::value;  // == kt & 1
-    if (kt + 2 < nk) fetch((kt + 2) * BK, SET);
-    multiply(st);
-    if (kt + 1 < nk) stash(st ^ 1, std::integral_constant<int, st ^ 1>{});
+    if constexpr (NSET == 2) {
+      if (kt + 2 < nk) fetch((kt + 2) * BK, SET);
+      multiply(st);
+      if (kt + 1 < nk) stash(st ^ 1, std::integral_constant<int, st ^ 1>{});
+    } else {
+      // one register set: slab kt+1 is loaded while slab kt is multiplied
+      if (kt + 1 < nk) fetch((kt + 1) * BK, S0{});
+      multiply(st);
+      if (kt + 1 < nk) stash(st ^ 1, S0{});
+    }
     __syncthreads();
   };
   fetch(0, S0{});
-  if (nk > 1) fetch(BK, S1{});
+  if constexpr (NSET == 2) {
+    if (nk > 1) fetch(BK, S1{});
+  }
   stash(0, S0{});
   __syncthreads();
-  for (int kt = 0; kt < nk; kt += 2) {
+  // Steady state first: while both slabs of an iteration pair still load a later slab, the
+  // fetches carry no condition, so the load counter is known at every point of the loop and
+  // each stash waits only for its own slab, not for the prefetch behind it.
+  int kt0 = 0;
+  if constexpr (NSET == 2) {
+    for (; kt0 + 3 < nk; kt0 += 2) {
+      fetch((kt0 + 2) * BK, S0{});
+      multiply(0);
+      stash(1, S1{});
+      __syncthreads();
+      fetch((kt0 + 3) * BK, S1{});
+      multiply(1);
+      stash(0, S0{});
+      __syncthreads();
+    }
+  }
+  for (int kt = kt0; kt < nk; kt += 2) {
     step(kt, S0{});
     if (kt + 1 < nk) step(kt + 1, S1{});
   }
 
-  // epilogue: lane holds rows 4*(lane/16)+0..3 of column lane%16 of each 16x16 tile
-  const int ccol = lane & 15, crow = (lane >> 4) * 4;
+  // epilogue. Accumulator register r of lane l holds, in a 16 x 16 tile, row 4*(l/16) + r of
+  // column l % 16; in a 32 x 32 tile, row 8*(r/4) + 4*(l/32) + r%4 of column l % 32.
+  const int ccol = lane & (MT - 1), crow = (lane / MT) * 4;
+  auto acc_row = [&](int r) { return MT == 32 ? 8 * (r >> 2) + crow + (r & 3) : crow + r; };
   if constexpr (MAMBA_GEMM_LDS_EPI != 0) {
     // The tile goes to LDS in that layout (the last k-slab's barrier has freed the staging
     // buffers), then back out as rows: each lane stores 16 contiguous bytes, a wave whole
     // rows, instead of 4-byte stores that cover 64-byte pieces of 4 rows.
     float* Cs = reinterpret_cast<float*>(smem);
+    constexpr int PR = BM / kParts;  // tile rows per pass
+    for (int part = 0; part < kParts; ++part) {
+    if (part > 0) __syncthreads();  // the previous pass's rows have been read
+    if (kParts == 1 || wm == part) {
+      const int rbase = kParts == 1 ? wm * WTM : 0;
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+      for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
+        for (int j = 0; j < TN; ++j)
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          Cs[(wm * WTM + i * 16 + crow + r) * LDC + wn * WTN + j * 16 + ccol] = acc[i][j][r];
+          for (int r = 0; r < NR; ++r)
+            Cs[(rbase + i * MT + acc_row(r)) * LDC + wn * WTN + j * MT + ccol] = acc[i][j][r];
+    }
     __syncthreads();
     constexpr int V = BN / 4;  // float4 per tile row
     const bool c_vec = ldc % 4 == 0 && reinterpret_cast<uintptr_t>(C) % 16 == 0;
 #pragma unroll 4
-    for (int idx = tid; idx < BM * V; idx += NT) {
+    for (int idx = tid; idx < PR * V; idx += NT) {
       const int r = idx / V, c4 = (idx % V) * 4;
-      const int gm = m0 + r, gn = n0 + c4;
+      const int gm = m0 + part * PR + r, gn = n0 + c4;
       if (gm >= M) continue;
       const float4 v = *reinterpret_cast<const float4*>(&Cs[r * LDC + c4]);
       float* cp = C + (int64_t)gm * ldc + gn;
@@ -335,17 +463,18 @@ gemm_mfma_kernel(
           if (gn + q < N) cp[q] = accumulate ? cp[q] + e[q] : e[q];
       }
     }
+    }
     return;
   }
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
-      const int gn = n0 + wn * WTN + j * 16 + ccol;
+      const int gn = n0 + wn * WTN + j * MT + ccol;
       if (gn >= N) continue;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int gm = m0 + wm * WTM + i * 16 + crow + r;
+      for (int r = 0; r < NR; ++r) {
+        const int gm = m0 + wm * WTM + i * MT + acc_row(r);
         if (gm >= M) continue;
         float* cp = C + (int64_t)gm * ldc + gn;
         *cp = accumulate ? *cp + acc[i][j][r] : acc[i][j][r];
@@ -517,7 +646,8 @@ static hipError_t gemm_at(const AT* A, int64_t lda, const bf16* W, int64_t ldw, 
     return hipGetLastError();
   }
   // 16-byte chunk loads need every row start and the K extent on 8-element boundaries
-  const bool vec = K % 8 == 0 && lda % 8 == 0 && ldw % 8 == 0 &&
+  // (and K >= 8: on that path a chunk outside the operands still reads 16 in-bounds bytes)
+  const bool vec = K >= 8 && K % 8 == 0 && lda % 8 == 0 && ldw % 8 == 0 &&
                    reinterpret_cast<uintptr_t>(A) % 16 == 0 && reinterpret_cast<uintptr_t>(W) % 16 == 0;
   // Wide outputs: 128 x 128 tiles, 2 x 2 waves. Narrow ones (x_proj's 80 columns): 32 x 80
   // tiles, one column tile, so that the grid still covers the chip. Few rows (a decode step's
@@ -528,7 +658,8 @@ static hipError_t gemm_at(const AT* A, int64_t lda, const bf16* W, int64_t ldw, 
   if (M <= 64 && N >= 8192)
     return gemm_tile<AT, 64, 64, 64, 2, 2>(A, lda, W, ldw, C, ldc, M, N, K, acc, vec, s);
   if (M <= 64) return gemm_tile<AT, 64, 32, 64, 2, 1>(A, lda, W, ldw, C, ldc, M, N, K, acc, vec, s);
-  return gemm_tile<AT, 128, 128, 64, 2, 2>(A, lda, W, ldw, C, ldc, M, N, K, acc, vec, s);
+  return gemm_tile<AT, MAMBA_GEMM_BM, MAMBA_GEMM_BN, MAMBA_GEMM_BK, MAMBA_GEMM_WGM, MAMBA_GEMM_WGN>(
+      A, lda, W, ldw, C, ldc, M, N, K, acc, vec, s);
 }
 
 // C[m, n] (+)= sum over the ks partial planes P[z, m, n] in order z = 0 .. ks-1.
