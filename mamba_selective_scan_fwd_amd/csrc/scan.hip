@@ -117,13 +117,16 @@ scan_kernel(const ScanParams p) {
   constexpr int G = W * H;           // state groups per workgroup
   constexpr int S = NP / G;          // states per lane
   constexpr int NT = kLanes * W;
-  constexpr int BCW = 2 * NP;        // staged B/C row: per group [B(S) | C(S)]
+  // staged B/C row: per group [B(S) | C(S)]; the summary pass stages B alone, per group B(S)
+  constexpr int BCS = OUT ? 2 * S : S;  // slots per group
+  constexpr int BCW = G * BCS;
   static_assert(S >= 1 && S * G == NP, "state split");
   static_assert(kTB * CH == NT, "one per-token item per thread and block");
 
   __shared__ float2 s_dd[2][kTB][CH];  // (delta, delta*u)
   __shared__ __attribute__((aligned(16))) float s_bc[2][kTB][BCW];
   __shared__ float s_yp[OUT ? 2 : 1][OUT ? kTB : 1][G][CH];  // partial C.h per group
+  __shared__ float s_sd[OUT ? 1 : kTB][CH];  // summary pass: sum of delta per token residue
 
   const int lane = threadIdx.x & (kLanes - 1);
   // wave index, explicitly wave-uniform so that row arithmetic stays scalar
@@ -262,7 +265,8 @@ scan_kernel(const ScanParams p) {
   }
 
   // ---- B/C staging: thread i < kTB * BCW stages entry i of a block (token i / BCW, slot
-  // i % BCW; the slots of group g are [B(gS..gS+S) | C(gS..gS+S)]).
+  // i % BCW; the slots of group g are [B(gS..gS+S) | C(gS..gS+S)], or B(gS..gS+S) alone in
+  // the summary pass, which reads no C).
   constexpr int BC_PER_T = (kTB * BCW + NT - 1) / NT;
   const IO* bc_src[BC_PER_T];  // this thread's B or C entry, token bc_j of the chunk's block 0
   int bc_j[BC_PER_T];
@@ -270,11 +274,11 @@ scan_kernel(const ScanParams p) {
 #pragma unroll
   for (int r = 0; r < BC_PER_T; ++r) {
     const int i = threadIdx.x + r * NT;
-    const int slot = i % BCW, w = slot % (2 * S);
+    const int slot = i % BCW, w = slot % BCS;
     const bool isC = w >= S;
-    const int n = slot / (2 * S) * S + (isC ? w - S : w);
+    const int n = slot / BCS * S + (isC ? w - S : w);
     bc_j[r] = i / BCW;
-    bc_use[r] = i < kTB * BCW && n < N && (OUT || !isC);
+    bc_use[r] = i < kTB * BCW && n < N;
     bc_src[r] = static_cast<const IO*>(isC ? p.Cm : p.Bm) + (row0 + bc_j[r]) * bcs + min(n, N - 1);
   }
 
@@ -342,6 +346,7 @@ scan_kernel(const ScanParams p) {
     ld_bc += (int64_t)kTB * bcs;
   };
 
+  float sum_delta = 0.0f;  // summary pass: this item's share of the chunk's sum of delta
   // stage A: delta and delta*u of this thread's item of block k into LDS, B/C of block k
   auto stage_a = [&](int k, auto P) {
     constexpr int st = decltype(P)::value;
@@ -363,6 +368,9 @@ scan_kernel(const ScanParams p) {
     const float delta = sp ? softplus(v) : v;
     const float uf = to_f32(pf_u[st]);
     s_dd[st][it_wave + it_lane][ic] = make_float2(delta, delta * uf);
+    // summary pass: the chunk's sum of delta, per item (token residue j of channel ic); the
+    // residues are added at the end
+    if constexpr (!OUT) sum_delta += k * kTB + it_wave + it_lane < len ? delta : 0.0f;
     u_blk[st] = uf;
     if constexpr (OUT && GATE) g_blk[st] = silu(to_f32(pf_z[st]));
     // pin both values here: left to the compiler they sink to their use after the next
@@ -378,7 +386,6 @@ scan_kernel(const ScanParams p) {
     }
   };
 
-  float sum_delta = 0.0f;
   // stage B: the LDS operands of one token (delta, delta*u, and this group's B and C)
   struct TokOps {
     float2 dd;
@@ -386,7 +393,7 @@ scan_kernel(const ScanParams p) {
   };
   auto read_token = [&](int st, int j, TokOps& o) {
     o.dd = s_dd[st][j][ch];
-    const float* bcr = &s_bc[st][j][g * 2 * S];
+    const float* bcr = &s_bc[st][j][g * BCS];
 #pragma unroll
     for (int s = 0; s < S; ++s) {
       o.bv[s] = bcr[s];
@@ -403,7 +410,6 @@ scan_kernel(const ScanParams p) {
       if constexpr (OUT) acc = s == 0 ? o.cv[0] * h[0] : fmaf(o.cv[s], h[s], acc);
     }
     if constexpr (OUT) s_yp[st][j][g][ch] = acc;
-    else sum_delta += o.dd.x;
   };
   // Token j+1's LDS reads are issued before token j's arithmetic (one token of look-ahead:
   // the read latency hides behind a token of work). A full block is one straight-line
@@ -486,6 +492,10 @@ scan_kernel(const ScanParams p) {
     if (k + 1 < nblk) block(k + 1, std::integral_constant<int, 1>{});
   }
 
+  if constexpr (!OUT) {
+    s_sd[it_wave + it_lane][ic] = sum_delta;
+    __syncthreads();
+  }
   if (!dval) return;
   if constexpr (OUT) {
     if (c == p.chunks - 1 && p.state_out) {
@@ -508,7 +518,13 @@ scan_kernel(const ScanParams p) {
     }
   } else {
     const int64_t bc_ = (int64_t)b * p.chunks + c;
-    if (g == 0) p.sum_ws[bc_ * D + d] = sum_delta;
+    if (g == 0) {
+      // the chunk's sum of delta: the kTB token residues of channel ch, in residue order
+      float sd = 0.0f;
+#pragma unroll
+      for (int j = 0; j < kTB; ++j) sd += s_sd[j][ch];
+      p.sum_ws[bc_ * D + d] = sd;
+    }
 #pragma unroll
     for (int s = 0; s < S; ++s) {
       const int n = g * S + s;
