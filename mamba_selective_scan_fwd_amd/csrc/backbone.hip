@@ -96,6 +96,18 @@ __global__ void __launch_bounds__(256) rmsnorm_last_kernel(const float* __restri
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+// 16 bytes from global memory straight into LDS: lane l's bytes land at lds + 16 l (the LDS
+// address is the wave's; gfx950 global_load_lds_dwordx4). The builtin exists only for the
+// device target, so the host pass of a kernel that calls it sees an empty body.
+__device__ __forceinline__ void load_lds16(const void* g, void* lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds(g, lds, 16, 0, 0);
+#else
+  (void)g;
+  (void)lds;
+#endif
+}
+
 template <typename AT>
 struct Chunk;  // 8 consecutive elements of a row, as loaded
 template <>
@@ -150,6 +162,10 @@ __device__ __forceinline__ bf16x8 load_chunk_scalar(const AT* row, int k0, int K
 #ifndef MAMBA_GEMM_WPE
 #define MAMBA_GEMM_WPE 2  // waves per SIMD the register allocation must allow
 #endif
+// large bf16-A products stage their slabs straight into LDS (1) or through registers (0)
+#ifndef MAMBA_GEMM_DL
+#define MAMBA_GEMM_DL 1
+#endif
 // 32 x 32 MFMA tiles where the wave tile allows (1) or 16 x 16 everywhere (0)
 #ifndef MAMBA_GEMM_MFMA32
 #define MAMBA_GEMM_MFMA32 1
@@ -182,7 +198,7 @@ __device__ __forceinline__ bf16x8 load_chunk_scalar(const AT* row, int k0, int K
 #define MAMBA_GEMM_LDS_EPI 1  // write C through LDS as rows of float4 (1) or from the fragments (0)
 #endif
 
-template <typename AT, int BM, int BN, int BK, int WGM, int WGN, bool VEC>
+template <typename AT, int BM, int BN, int BK, int WGM, int WGN, bool VEC, bool DL>
 __global__ void __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(MAMBA_GEMM_WPE)))
 gemm_mfma_kernel(
     const AT* __restrict__ A, int64_t lda, const bf16* __restrict__ W, int64_t ldw,
@@ -235,7 +251,8 @@ gemm_mfma_kernel(
   // 16-byte chunk kc of row r sits at chunk kc ^ swz(r), swz(r) = (r ^ r >> 3) & 7: the 16
   // rows a fragment read touches (and each pair of rows a 16-lane group writes) then fall on
   // distinct bank groups for 32 or 64 four-byte banks. Without it, rows are padded by 8.
-  constexpr bool kSwz = MAMBA_GEMM_SWZ != 0 && BK == 64;
+  constexpr bool kSwz = (MAMBA_GEMM_SWZ != 0 || DL) && BK == 64;
+  static_assert(!DL || (VEC && BK == 64 && std::is_same_v<AT, bf16>), "direct LDS staging: bf16 A, 64-k slabs");
   constexpr int LDK = kSwz ? BK : BK + 8;
   auto swz = [](int r) { return kSwz ? (r ^ (r >> 3)) & 7 : 0; };
   constexpr int CPR = BK / 8;  // chunks per row
@@ -390,12 +407,49 @@ gemm_mfma_kernel(
     }
     __syncthreads();
   };
-  fetch(0, S0{});
-  if constexpr (NSET == 2) {
-    if (nk > 1) fetch(BK, S1{});
+  if constexpr (!DL) {
+    fetch(0, S0{});
+    if constexpr (NSET == 2) {
+      if (nk > 1) fetch(BK, S1{});
+    }
+    stash(0, S0{});
+    __syncthreads();
   }
-  stash(0, S0{});
-  __syncthreads();
+  if constexpr (DL) {
+    // Direct staging: each wave moves 1 KB pieces of the next slab from global memory
+    // straight into LDS (global_load_lds_dwordx4: lane l's 16 bytes land at the piece's
+    // base + 16 l), so no register staging and no LDS store instruction is spent on them.
+    // The LDS slot order is the swizzled layout, so lane l of piece i loads the chunk that
+    // belongs in slot 64 i + l. Rows past M (N) read the last row; their products are never
+    // stored. K is a whole number of slabs on this path.
+    constexpr int NW = WGM * WGN;
+    constexpr int PA = BM / 8 / NW, PW = BN / 8 / NW;  // 1 KB pieces per wave and tile
+    static_assert(PA * NW * 8 == BM && PW * NW * 8 == BN, "piece split");
+    auto issue = [&](int k0, int buf) {
+#pragma unroll
+      for (int j = 0; j < PA; ++j) {
+        const int i = wave * PA + j, sl = i * 64 + lane, r = sl >> 3, kc = (sl & 7) ^ swz(r);
+        load_lds16(A + (int64_t)min(m0 + r, M - 1) * lda + k0 + 8 * kc, &As[buf][i * 512]);
+      }
+#pragma unroll
+      for (int j = 0; j < PW; ++j) {
+        const int i = wave * PW + j, sl = i * 64 + lane, r = sl >> 3, kc = (sl & 7) ^ swz(r);
+        load_lds16(W + (int64_t)min(n0 + r, N - 1) * ldw + k0 + 8 * kc, &Ws[buf][i * 512]);
+      }
+    };
+    // the slab's pieces have landed (vector memory counter at zero), then every wave may read
+    auto landed = [&]() {
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+      __syncthreads();
+    };
+    issue(0, 0);
+    landed();
+    for (int kt = 0; kt < nk; ++kt) {
+      if (kt + 1 < nk) issue((kt + 1) * BK, (kt + 1) & 1);
+      multiply(kt & 1);
+      landed();
+    }
+  } else {
   // Steady state first: while both slabs of an iteration pair still load a later slab, the
   // fetches carry no condition, so the load counter is known at every point of the loop and
   // each stash waits only for its own slab, not for the prefetch behind it.
@@ -415,6 +469,7 @@ gemm_mfma_kernel(
   for (int kt = kt0; kt < nk; kt += 2) {
     step(kt, S0{});
     if (kt + 1 < nk) step(kt + 1, S1{});
+  }
   }
 
   // epilogue. Accumulator register r of lane l holds, in a 16 x 16 tile, row 4*(l/16) + r of
@@ -620,14 +675,21 @@ hipError_t launch_rmsnorm_last(const float* x, const int32_t* lengths, int T, co
 template <typename AT, int BM, int BN, int BK, int WGM, int WGN>
 static hipError_t gemm_tile(const AT* A, int64_t lda, const bf16* W, int64_t ldw, float* C,
                             int64_t ldc, int M, int N, int K, bool acc, bool vec, hipStream_t s,
-                            int ks = 1, int k_chunk = 0, int64_t c_split_stride = 0) {
+                            int ks = 1, int k_chunk = 0, int64_t c_split_stride = 0, bool dl = false) {
   if (ks <= 1) k_chunk = K;
   const dim3 grid((unsigned)((N + BN - 1) / BN), (unsigned)((M + BM - 1) / BM), (unsigned)ks);
+  if constexpr (std::is_same_v<AT, bf16> && BK == 64) {
+    if (dl && vec && ks <= 1 && K % BK == 0) {
+      gemm_mfma_kernel<AT, BM, BN, BK, WGM, WGN, true, true><<<grid, 64 * WGM * WGN, 0, s>>>(
+          A, lda, W, ldw, C, ldc, M, N, K, acc ? 1 : 0, k_chunk, c_split_stride);
+      return hipGetLastError();
+    }
+  }
   if (vec)
-    gemm_mfma_kernel<AT, BM, BN, BK, WGM, WGN, true><<<grid, 64 * WGM * WGN, 0, s>>>(
+    gemm_mfma_kernel<AT, BM, BN, BK, WGM, WGN, true, false><<<grid, 64 * WGM * WGN, 0, s>>>(
         A, lda, W, ldw, C, ldc, M, N, K, acc ? 1 : 0, k_chunk, c_split_stride);
   else
-    gemm_mfma_kernel<AT, BM, BN, BK, WGM, WGN, false><<<grid, 64 * WGM * WGN, 0, s>>>(
+    gemm_mfma_kernel<AT, BM, BN, BK, WGM, WGN, false, false><<<grid, 64 * WGM * WGN, 0, s>>>(
         A, lda, W, ldw, C, ldc, M, N, K, acc ? 1 : 0, k_chunk, c_split_stride);
   return hipGetLastError();
 }
@@ -658,8 +720,9 @@ static hipError_t gemm_at(const AT* A, int64_t lda, const bf16* W, int64_t ldw, 
   if (M <= 64 && N >= 8192)
     return gemm_tile<AT, 64, 64, 64, 2, 2>(A, lda, W, ldw, C, ldc, M, N, K, acc, vec, s);
   if (M <= 64) return gemm_tile<AT, 64, 32, 64, 2, 1>(A, lda, W, ldw, C, ldc, M, N, K, acc, vec, s);
+  // (bf16 A with whole 64-k slabs stages straight into LDS)
   return gemm_tile<AT, MAMBA_GEMM_BM, MAMBA_GEMM_BN, MAMBA_GEMM_BK, MAMBA_GEMM_WGM, MAMBA_GEMM_WGN>(
-      A, lda, W, ldw, C, ldc, M, N, K, acc, vec, s);
+      A, lda, W, ldw, C, ldc, M, N, K, acc, vec, s, 1, 0, 0, MAMBA_GEMM_DL != 0);
 }
 
 // C[m, n] (+)= sum over the ks partial planes P[z, m, n] in order z = 0 .. ks-1.
