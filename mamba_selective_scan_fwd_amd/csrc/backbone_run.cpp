@@ -110,9 +110,12 @@ hipError_t run_backbone_prefill_io(const mamba_backbone_dims& d, const mamba_bac
                    ssm_state + (int64_t)l * B * D * N, ssm_state + (int64_t)l * B * D * N, y,
                    false, B, T, D, N, scan_ws};
     sa.lengths = io.lengths;
+    // y leaves the scan as bf16: out_proj rounds its operand to bf16 anyway (the same RNE
+    // rounding), and a bf16 A is half the bytes and stages straight into LDS
+    sa.y_bf16 = true;
     if ((e = launch_selective_scan_fwd(sa, s)) != hipSuccess) return e;
     // F5 + F6: h += y @ out_proj^T
-    if ((e = launch_gemm_bf16(y, false, D, out_proj + (int64_t)l * Dm * D, D, h, Dm, (int)bt, Dm, D,
+    if ((e = launch_gemm_bf16(y, true, D, out_proj + (int64_t)l * Dm * D, D, h, Dm, (int)bt, Dm, D,
                               true, s)) != hipSuccess) return e;
   }
   // norm_f at every position (the all-T output), and on each sequence's last (valid) token

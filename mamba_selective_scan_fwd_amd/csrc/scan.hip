@@ -74,6 +74,7 @@ struct ScanParams {
   int B, T, D, N, K;
   int chunk_t, chunks;
   int softplus;
+  int y_bf16;  // f32 I/O only: y stored as bf16 (the operand type of the product that reads it)
 };
 
 // A * log2(e) for A = -exp(A_log) of state n (0 for padded states: decay 1, and their B and
@@ -464,9 +465,15 @@ scan_kernel(const ScanParams p) {
         yv = fmaf(dskip, u_blk[st], yv);
         if constexpr (GATE) yv *= g_blk[st];
         if (di < D) {
-          // scalar row of the wave's first token + the lane's fixed byte offset
-          IO* yrow = static_cast<IO*>(p.y) + st_y;
-          *reinterpret_cast<IO*>(reinterpret_cast<char*>(yrow) + off_y) = from_f32<IO>(yv);
+          if (std::is_same_v<IO, float> && p.y_bf16) {
+            // same element offsets at half the width
+            bf16* yrow = static_cast<bf16*>(p.y) + st_y;
+            *reinterpret_cast<bf16*>(reinterpret_cast<char*>(yrow) + off_y / 2) = from_f32<bf16>(yv);
+          } else {
+            // scalar row of the wave's first token + the lane's fixed byte offset
+            IO* yrow = static_cast<IO*>(p.y) + st_y;
+            *reinterpret_cast<IO*>(reinterpret_cast<char*>(yrow) + off_y) = from_f32<IO>(yv);
+          }
         }
       }
       st_y += (int64_t)kTB * D;
@@ -619,6 +626,7 @@ static hipError_t launch_scan_npk(const ScanFwdArgs& a, const ScanPlan& pl, hipS
   p.chunk_t = pl.chunk_t;
   p.chunks = pl.chunks;
   p.softplus = a.delta_softplus ? 1 : 0;
+  p.y_bf16 = a.y_bf16 && !a.bf16 ? 1 : 0;
   const unsigned gx = (unsigned)((a.D + CH - 1) / CH);
   if (pl.chunks > 1) {
     char* ws = static_cast<char*>(a.workspace);
