@@ -71,8 +71,8 @@ struct ScanFwdArgs {
   // per-sequence valid lengths (device, [B], clamped to [0, T]) or NULL: each sequence's
   // states are taken after its own last token; y past it is not written
   const int32_t* lengths = nullptr;
-  // f32 I/O only: y stored as bf16 (rounded to nearest even), for a consumer that reads it as
-  // a bf16 operand (the backbone's out_proj)
+  // f32 I/O with u as an input only: y stored as bf16 (rounded to nearest even), for a
+  // consumer that reads it as a bf16 operand (the backbone's out_proj)
   bool y_bf16 = false;
 };
 

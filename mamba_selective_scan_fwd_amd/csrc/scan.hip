@@ -465,7 +465,9 @@ scan_kernel(const ScanParams p) {
         yv = fmaf(dskip, u_blk[st], yv);
         if constexpr (GATE) yv *= g_blk[st];
         if (di < D) {
-          if (std::is_same_v<IO, float> && p.y_bf16) {
+          // (a bf16 y from f32 I/O is taken only with u as an input: the backbone's scan; the
+          // fused-conv kernels keep their register budget for the conv)
+          if (std::is_same_v<IO, float> && KC == 0 && p.y_bf16) {
             // same element offsets at half the width
             bf16* yrow = static_cast<bf16*>(p.y) + st_y;
             *reinterpret_cast<bf16*>(reinterpret_cast<char*>(yrow) + off_y / 2) = from_f32<bf16>(yv);
@@ -626,7 +628,7 @@ static hipError_t launch_scan_npk(const ScanFwdArgs& a, const ScanPlan& pl, hipS
   p.chunk_t = pl.chunk_t;
   p.chunks = pl.chunks;
   p.softplus = a.delta_softplus ? 1 : 0;
-  p.y_bf16 = a.y_bf16 && !a.bf16 ? 1 : 0;
+  p.y_bf16 = a.y_bf16 && !a.bf16 && !a.x ? 1 : 0;
   const unsigned gx = (unsigned)((a.D + CH - 1) / CH);
   if (pl.chunks > 1) {
     char* ws = static_cast<char*>(a.workspace);
