@@ -476,7 +476,11 @@ gemm_mfma_kernel(
   // column l % 16; in a 32 x 32 tile, row 8*(r/4) + 4*(l/32) + r%4 of column l % 32.
   const int ccol = lane & (MT - 1), crow = (lane / MT) * 4;
   auto acc_row = [&](int r) { return MT == 32 ? 8 * (r >> 2) + crow + (r & 3) : crow + r; };
-  if constexpr (MAMBA_GEMM_LDS_EPI != 0) {
+  // A product that adds into C (out_proj's residual) goes through LDS: the tile is read and
+  // written back as whole rows. A plain store goes out straight from the fragments (4-byte
+  // stores, whole 64- or 128-byte row pieces per instruction), which measured faster for
+  // in_proj and dt_proj and slower when C is read first.
+  if (MAMBA_GEMM_LDS_EPI != 0 && accumulate) {
     // The tile goes to LDS in that layout (the last k-slab's barrier has freed the staging
     // buffers), then back out as rows: each lane stores 16 contiguous bytes, a wave whole
     // rows, instead of 4-byte stores that cover 64-byte pieces of 4 rows.
