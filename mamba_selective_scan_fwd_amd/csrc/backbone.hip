@@ -56,6 +56,50 @@ __global__ void __launch_bounds__(256) rmsnorm_kernel(const float* __restrict__ 
   for (int c = threadIdx.x; c < Dm; c += 256) o[c] = from_f32<OT>(xr[c] * inv * (w ? w[c] : 1.0f));
 }
 
+// The same per-row arithmetic with one wave per row, for many rows (a prefill's bt rows):
+// lane l plays the four threads w * 64 + l of rmsnorm_kernel's block, keeping their running
+// sums apart and reducing each over the wave in the same order, so the result is the same bit
+// for bit; the row stays in registers, so it is read once. Rows up to kNormWaveMaxK * 256.
+constexpr int kNormWaveMaxK = 8;
+template <typename OT, int KMAX>
+__global__ void __launch_bounds__(256) rmsnorm_rows_kernel(const float* __restrict__ x, int64_t x_row_stride,
+                                                           const float* __restrict__ w, float eps,
+                                                           OT* __restrict__ out, int64_t rows, int Dm) {
+  const int lane = threadIdx.x & 63;
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= rows) return;  // whole waves
+  const float* xr = x + r * x_row_stride;
+  float v[4][KMAX];
+  float ss[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    ss[q] = 0.0f;
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) {
+      const int c = q * 64 + lane + 256 * k;
+      v[q][k] = c < Dm ? xr[c] : 0.0f;
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k)
+      if (q * 64 + lane + 256 * k < Dm) ss[q] = fmaf(v[q][k], v[q][k], ss[q]);
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    for (int m = 32; m >= 1; m /= 2) ss[q] += __shfl_xor(ss[q], m);
+  const float tot = ss[0] + ss[1] + ss[2] + ss[3];
+  const float inv = 1.0f / sqrtf(tot / (float)Dm + eps);
+  OT* o = out + r * Dm;
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) {
+      const int c = q * 64 + lane + 256 * k;
+      if (c < Dm) o[c] = from_f32<OT>(v[q][k] * inv * (w ? w[c] : 1.0f));
+    }
+}
+
 // RMSNorm of each sequence's last valid position: row b * T + clamp(lengths[b], 1, T) - 1.
 template <typename OT>
 __global__ void __launch_bounds__(256) rmsnorm_last_kernel(const float* __restrict__ x,
@@ -656,6 +700,24 @@ hipError_t launch_embed_gather(const int32_t* tokens, const void* E, float* out,
 
 hipError_t launch_rmsnorm(const float* x, int64_t x_row_stride, const float* w, float eps,
                           void* out, bool out_bf16, int64_t rows, int Dm, hipStream_t s) {
+  // many rows of at most 3 * 256 (or 8 * 256) elements: one wave per row
+  if (rows >= 1024 && Dm <= kNormWaveMaxK * 256) {
+    const dim3 grid((unsigned)((rows + 3) / 4));
+#define MAMBA_NORM_ROWS(KM)                                                                             \
+  if (out_bf16)                                                                                         \
+    rmsnorm_rows_kernel<bf16, KM><<<grid, 256, 0, s>>>(x, x_row_stride, w, eps, static_cast<bf16*>(out), \
+                                                       rows, Dm);                                       \
+  else                                                                                                  \
+    rmsnorm_rows_kernel<float, KM><<<grid, 256, 0, s>>>(x, x_row_stride, w, eps, static_cast<float*>(out), \
+                                                        rows, Dm)
+    if (Dm <= 3 * 256) {
+      MAMBA_NORM_ROWS(3);
+    } else {
+      MAMBA_NORM_ROWS(kNormWaveMaxK);
+    }
+#undef MAMBA_NORM_ROWS
+    return hipGetLastError();
+  }
   if (out_bf16)
     rmsnorm_kernel<bf16><<<dim3((unsigned)rows), 256, 0, s>>>(x, x_row_stride, w, eps,
                                                               static_cast<bf16*>(out), Dm);

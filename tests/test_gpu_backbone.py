@@ -130,6 +130,27 @@ def test_rmsnorm_vs_oracle(Dm, out):
     assert err <= (TOL_BF16 if out == "bf16" else TOL_F32)
 
 
+@pytest.mark.parametrize("Dm,out", [(768, "bf16"), (768, "f32"), (1000, "f32"), (2048, "bf16")])
+def test_rmsnorm_many_rows_same_bits(Dm, out):
+    """A prefill's many rows take the one-wave-per-row kernel: its rows equal, bit for bit,
+    the block-per-row kernel's (the same sums in the same order), and the oracle."""
+    _say(f"case rmsnorm many rows Dm{Dm} out={out}")
+    g = np.random.default_rng(Dm + 7)
+    rows = 1100
+    x = (g.normal(size=(rows, Dm)) * 2).astype(np.float32)
+    wv = g.normal(size=Dm).astype(np.float32)
+    dt = torch.bfloat16 if out == "bf16" else torch.float32
+    xd, wd = dev(x), dev(wv)
+    o_all = torch.empty(rows, Dm, device="cuda", dtype=dt)
+    m.mamba_rmsnorm(xd, wd, 1e-5, o_all)           # >= 1024 rows: one wave per row
+    o_few = torch.empty(40, Dm, device="cuda", dtype=dt)
+    m.mamba_rmsnorm(xd[1000:1040], wd, 1e-5, o_few)  # 40 rows: one block per row
+    torch.cuda.synchronize()
+    assert torch.equal(o_all[1000:1040], o_few)
+    ref = ob.rmsnorm(x, wv, 1e-5)
+    assert rel_err(host(o_all), ob.bf16(ref) if out == "bf16" else ref) <= (TOL_BF16 if out == "bf16" else TOL_F32)
+
+
 def test_rmsnorm_strided_rows():
     """The last-timestep gather: rows T * Dm apart."""
     B, T, Dm = 3, 5, 64
