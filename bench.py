@@ -825,6 +825,8 @@ def bench_backbone(args, shape):
     last = torch.empty(B, Dm, dtype=torch.bfloat16, device=dev)
     lg2 = torch.empty(B, shape.vocab, device=dev)
     sws = m.scan_workspace(B, T, D, N)
+    xdt_n = m.mamba_xproj_dtproj_workspace_size(bt, D, R, N)
+    xdt_ws = torch.empty(xdt_n, dtype=torch.uint8, device=dev) if xdt_n else None
     cs0 = torch.zeros(B, D, K, device=dev)
     hs0 = torch.zeros(B, D, N, device=dev)
     proj3 = proj.view(B, T, 2 * D)
@@ -839,11 +841,11 @@ def bench_backbone(args, shape):
         ("conv1d_fwd", lambda: m.mamba_conv1d_fwd(proj3[..., :D], t["conv_w"][0], t["conv_b"][0], cs0, u,
                                                   stream=stream),
          None, conv_bytes(4, B, T, D, K)),
-        ("gemm x_proj", lambda: m.mamba_gemm_bf16(u.view(bt, D), t["x_proj"][0], xdbl, stream=stream),
-         gemm_flops(bt, xw, D), 4 * bt * D + 2 * xw * D + 4 * bt * xw),
-        ("gemm dt_proj", lambda: m.mamba_gemm_bf16(xdbl, t["dt_proj"][0], dtb.view(bt, D), K=R, lda=xw,
-                                                   stream=stream),
-         gemm_flops(bt, D, R), 4 * bt * R + 2 * D * R + 4 * bt * D),
+        # x_proj split over K, then one kernel that sums its partial planes and applies dt_proj
+        ("x_proj + dt_proj", lambda: m.mamba_xproj_dtproj(u.view(bt, D), t["x_proj"][0], t["dt_proj"][0], xdbl,
+                                                          dtb.view(bt, D), workspace=xdt_ws, stream=stream),
+         gemm_flops(bt, xw, D) + gemm_flops(bt, D, R),
+         4 * bt * D + 2 * xw * D + 4 * bt * xw + 2 * D * R + 4 * bt * D),
         ("selective_scan_fwd", lambda: m.mamba_selective_scan_fwd(
             u, dtb, t["dt_bias"][0], t["A_log"][0], xdbl3[..., R:R + N], xdbl3[..., R + N:],
             t["D_skip"][0], proj3[..., D:], hs0, hs0, y, workspace=sws, stream=stream),
@@ -874,7 +876,7 @@ def bench_backbone(args, shape):
         if flops:
             c["tflops"] = flops / (avg * 1e-3) / 1e12
         calls[name] = c
-    per_layer = ("rmsnorm", "gemm in_proj", "conv1d_fwd", "gemm x_proj", "gemm dt_proj",
+    per_layer = ("rmsnorm", "gemm in_proj", "conv1d_fwd", "x_proj + dt_proj",
                  "selective_scan_fwd", "gemm out_proj")
     dom_name = max(per_layer, key=lambda k: calls[k]["avg_us"])
     dom = calls[dom_name]

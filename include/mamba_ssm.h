@@ -281,6 +281,30 @@ mamba_status mamba_gemm_bf16(const void* A, mamba_dtype a_dtype, int64_t lda, co
                              int64_t ldw, float* C, int64_t ldc, int M, int N, int K,
                              int accumulate, void* stream);
 
+/*
+ * The two projections between the conv and the scan of a prefill layer ([prefill.rs]
+ * prefill_body F4b and F4c: x_proj of the conv output u gives the dt lane, B and C; the
+ * low-rank dt lane goes through dt_proj to give the per-channel dt before its softplus):
+ *   xdbl[M, xw]     = u[M, d_inner] * W_x[xw, d_inner]^T          (xw = dt_rank + 2 d_state:
+ *                     columns dt lane | B | C)
+ *   dt[M, d_inner]  = xdbl[:, 0:dt_rank] * W_dt[d_inner, dt_rank]^T  (no bias: the scan adds
+ *                     dt_bias before its softplus)
+ * u f32, rows ldu apart; W_x and W_dt bf16 in the nn.Linear layout, contiguous rows; xdbl
+ * and dt f32, contiguous. Operands are rounded to bf16 (RNE) as they enter each product
+ * (u, and the dt lane of xdbl as computed in f32), with f32 accumulation, as mamba_gemm_bf16
+ * does; x_proj is split over d_inner and its partial sums added in a fixed order, so the
+ * values do not depend on timing. workspace: at least
+ * mamba_xproj_dtproj_workspace_size(M, d_inner, dt_rank, d_state) bytes (the split's
+ * partial planes; may be NULL when that is 0). Errors: MAMBA_EINVAL for negative sizes or
+ * leading dimensions below d_inner, MAMBA_EWORKSPACE for a missing or short workspace; xdbl,
+ * dt and the workspace must not overlap each other or the inputs. M == 0 is a no-op.
+ */
+size_t mamba_xproj_dtproj_workspace_size(int M, int d_inner, int dt_rank, int d_state);
+mamba_status mamba_xproj_dtproj(const float* u, int64_t ldu, const void* W_x, const void* W_dt,
+                                float* xdbl, float* dt, int M, int d_inner, int dt_rank,
+                                int d_state, void* workspace, size_t workspace_bytes,
+                                void* stream);
+
 typedef struct mamba_backbone_dims {
   int n_layers;      /* 24 for the 130m shape */
   int d_model;       /* 768 */

@@ -15,6 +15,7 @@ __all__ = [
     "mamba_version", "mamba_last_error", "mamba_conv1d_fwd", "mamba_selective_scan_fwd",
     "mamba_selective_scan_workspace_size", "mamba_conv1d_step", "mamba_ssm_step",
     "scan_workspace", "mamba_embed_gather", "mamba_rmsnorm", "mamba_gemm_bf16",
+    "mamba_xproj_dtproj_workspace_size", "mamba_xproj_dtproj",
     "BackboneDims", "BackboneWeights", "mamba_backbone_workspace_size", "mamba_backbone_prefill",
     "Mamba3SisoParams", "mamba3_siso_step",
 ]
@@ -46,6 +47,8 @@ symbols = {
     "mamba_embed_gather": ([_P, _P, _P, _I64, _I, _I, _P], _I),
     "mamba_rmsnorm": ([_P, _I64, _P, ctypes.c_float, _P, _I, _I64, _I, _P], _I),
     "mamba_gemm_bf16": ([_P, _I, _I64, _P, _I64, _P, _I64, _I, _I, _I, _I, _P], _I),
+    "mamba_xproj_dtproj_workspace_size": ([_I, _I, _I, _I], _SZ),
+    "mamba_xproj_dtproj": ([_P, _I64, _P, _P, _P, _P, _I, _I, _I, _I, _P, _SZ, _P], _I),
     "mamba_backbone_workspace_size": ([_P, _I, _I], _SZ),
     "mamba_backbone_prefill": ([_P, _P, _P, _I, _I, _P, _P, _P, _P, _SZ, _P], _I),
     "mamba_backbone_prefill_ex": ([_P, _P, _P, _I, _I, _P, _P, _P, _SZ, _P], _I),
@@ -335,6 +338,29 @@ def mamba_gemm_bf16(A, W, C, accumulate=False, M=None, N=None, K=None, lda=None,
     ldc = C.stride(0) if ldc is None else ldc
     _check(load_library().mamba_gemm_bf16(_ptr(A), _io_dtype(A), lda, _ptr(W), ldw, _ptr(C), ldc, M,
                                           N, K, int(bool(accumulate)), _stream(stream)))
+
+
+def mamba_xproj_dtproj_workspace_size(M: int, d_inner: int, dt_rank: int, d_state: int) -> int:
+    return int(load_library().mamba_xproj_dtproj_workspace_size(M, d_inner, dt_rank, d_state))
+
+
+def mamba_xproj_dtproj(u, W_x, W_dt, xdbl, dt, workspace=None, M=None, ldu=None, stream=None) -> None:
+    """xdbl = u @ W_x^T and dt = xdbl[:, :dt_rank] @ W_dt^T (bf16 operands, f32 sums).
+    u: [M, >= d_inner] f32 rows; W_x [dt_rank + 2 d_state, d_inner] and W_dt [d_inner, dt_rank]
+    bf16; xdbl [M, dt_rank + 2 d_state] and dt [M, d_inner] f32; workspace a device buffer of
+    mamba_xproj_dtproj_workspace_size bytes, or None (allocated here when needed)."""
+    import torch
+    d_inner, dt_rank = W_dt.shape
+    d_state = (W_x.shape[0] - dt_rank) // 2
+    M = u.shape[0] if M is None else M
+    ldu = u.stride(0) if ldu is None else ldu
+    need = mamba_xproj_dtproj_workspace_size(M, d_inner, dt_rank, d_state)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=u.device)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load_library().mamba_xproj_dtproj(_ptr(u), ldu, _ptr(W_x), _ptr(W_dt), _ptr(xdbl), _ptr(dt), M,
+                                             d_inner, dt_rank, d_state, _ptr(workspace), nbytes,
+                                             _stream(stream)))
 
 
 def mamba_backbone_workspace_size(dims: BackboneDims, B: int, T: int) -> int:

@@ -629,6 +629,60 @@ mamba_status mamba_gemm_bf16(const void* A, mamba_dtype a_dtype, int64_t lda, co
   });
 }
 
+// x_proj's K split as the backbone prefill runs it: at most d_inner / xw slices, so that the
+// partial planes fit in one [M, d_inner] buffer
+static size_t xproj_dtproj_ws(int M, int D, int R, int N) {
+  const int xw = R + 2 * N;
+  const int ks = mamba::gemm_rows_ksplit(M, xw, D, std::max(D / xw, 1));
+  return ks > 1 ? (size_t)ks * (size_t)M * (size_t)xw * sizeof(float) : 0;
+}
+
+size_t mamba_xproj_dtproj_workspace_size(int M, int d_inner, int dt_rank, int d_state) {
+  if (M <= 0 || d_inner <= 0 || dt_rank <= 0 || d_state < 0) return 0;
+  return xproj_dtproj_ws(M, d_inner, dt_rank, d_state);
+}
+
+mamba_status mamba_xproj_dtproj(const float* u, int64_t ldu, const void* W_x, const void* W_dt,
+                                float* xdbl, float* dt, int M, int d_inner, int dt_rank,
+                                int d_state, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  static const char* fn = "mamba_xproj_dtproj";
+  return guarded([&] {
+    check_dim(fn, "M", M);
+    check_dim(fn, "d_inner", d_inner);
+    check_dim(fn, "dt_rank", dt_rank);
+    check_dim(fn, "d_state", d_state);
+    if (M == 0) return;
+    if (d_inner == 0 || dt_rank == 0) fail(MAMBA_EINVAL, fn, "d_inner and dt_rank must be positive");
+    if (ldu < d_inner) fail(MAMBA_EINVAL, fn, "ldu = %lld is less than d_inner = %d", (long long)ldu, d_inner);
+    if (M > 65535 * 16) fail(MAMBA_EUNSUPPORTED, fn, "M = %d exceeds %d", M, 65535 * 16);
+    const int xw = dt_rank + 2 * d_state;
+    const size_t need = xproj_dtproj_ws(M, d_inner, dt_rank, d_state);
+    if (need) {
+      if (!workspace) fail(MAMBA_EWORKSPACE, fn, "workspace is NULL but %zu bytes are required", need);
+      if (workspace_bytes < need) fail(MAMBA_EWORKSPACE, fn, "workspace_bytes = %zu but %zu are required", workspace_bytes, need);
+      check_ptr(fn, "workspace", workspace, 4, true);
+    }
+    check_ptr(fn, "u", u, 4, true);
+    check_ptr(fn, "W_x", W_x, 2, true);
+    check_ptr(fn, "W_dt", W_dt, 2, true);
+    check_ptr(fn, "xdbl", xdbl, 4, true);
+    check_ptr(fn, "dt", dt, 4, true);
+    const Range ins[] = {range("u", u, M, ldu, d_inner, 4), range("W_x", W_x, xw, d_inner, d_inner, 2),
+                         range("W_dt", W_dt, d_inner, dt_rank, dt_rank, 2)};
+    const Range rx = range("xdbl", xdbl, M, xw, xw, 4), rd = range("dt", dt, M, d_inner, d_inner, 4);
+    check_disjoint(fn, rx, {ins[0], ins[1], ins[2], rd});
+    check_disjoint(fn, rd, {ins[0], ins[1], ins[2]});
+    if (need) {
+      const Range rw = range("workspace", workspace, 1, need, need, 1);
+      check_disjoint(fn, rw, {ins[0], ins[1], ins[2], rx, rd});
+    }
+    check_hip(fn, mamba::launch_xproj_dtproj(u, ldu, W_x, xdbl, xw, W_dt, dt_rank, dt, M, d_inner,
+                                             static_cast<float*>(workspace), std::max(d_inner / xw, 1),
+                                             static_cast<hipStream_t>(stream)));
+  });
+}
+
 static void check_backbone_dims(const char* fn, const mamba_backbone_dims* d) {
   if (!d) fail(MAMBA_EINVAL, fn, "dims is NULL");
   if (d->n_layers < 0) fail(MAMBA_EINVAL, fn, "n_layers = %d is negative", d->n_layers);

@@ -893,6 +893,158 @@ hipError_t launch_gemm_bf16_rows(const void* A, bool a_bf16, int64_t lda, const 
   return hipGetLastError();
 }
 
+// x_proj's partial planes summed and dt_proj applied, in one launch (prefill.rs page,
+// `prefill_body` stages F4b, the x_proj GEMM, and F4c, the gather of the dt columns and the
+// dt_proj GEMM ahead of the softplus, which the scan applies). A workgroup takes 16 rows
+// and 1/CS of the D output columns; the CS workgroups of a row block run on one XCD (same
+// blockIdx % 8), so all but the first find the partial planes in that XCD's L2.
+//  1. each row of xdbl (dt lane | B | C) is the sum of the ks partial planes, added in slice
+//     order from zero exactly as the reduction kernel above adds them; the column split 0
+//     writes the rows out for the scan; every split keeps the dt lane in LDS as bf16 (RNE,
+//     the rounding the GEMM applies when it stages an f32 operand), zero-padded to 64 k;
+//  2. dt = dt_lane @ W_dt^T by v_mfma_f32_16x16x32_bf16 tiles with W_dt as the first operand
+//     (lane l: output column n0 + l % 16, k = 8 (l / 16) + 0..7) and the staged rows as the
+//     second, so that the result register r of lane l is dt[m0 + l % 16][n0 + 4 (l / 16) + r].
+//     Each wave takes a quarter of the workgroup's columns, G tiles at a time, and passes
+//     the 16 x 16G block through LDS so that it leaves as row runs of 64 G bytes (stored
+//     straight from the fragments, each store instruction would cover 16 rows x 64 bytes:
+//     17.5 against 14.9 us at the 130m prefill). W_dt chunks past dt_rank are zero (their
+//     loads read the row's first chunk instead, in bounds). The first group of W_dt
+//     fragments is loaded before the planes are summed.
+// Requires dt_rank % 8 == 0 and <= 64, D % (64 CS) == 0, xw % 4 == 0, 16-byte aligned buffers.
+#ifndef MAMBA_XDT_FUSE
+#define MAMBA_XDT_FUSE 1  // x_proj's reduction and dt_proj in one kernel (1) or two launches (0)
+#endif
+#ifndef MAMBA_XDT_SPLIT
+#define MAMBA_XDT_SPLIT 4  // column splits per row block
+#endif
+constexpr int kXdtRows = 16;
+constexpr int kXdtMaxRank = 64;
+#ifndef MAMBA_XDT_GROUP
+#define MAMBA_XDT_GROUP 6
+#endif
+constexpr int kXdtGroup = MAMBA_XDT_GROUP;  // W_dt tiles whose fragments a wave loads together
+
+__global__ void __launch_bounds__(256) xproj_sum_dtproj_kernel(const float* __restrict__ P, int ks,
+                                                               int64_t plane, float* __restrict__ xdbl,
+                                                               int xw, const bf16* __restrict__ Wdt, int R,
+                                                               float* __restrict__ dt, int D, int M, int CS) {
+  __shared__ __align__(16) bf16 Xs[kXdtRows][kXdtMaxRank + 8];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nrb = (M + kXdtRows - 1) / kXdtRows;
+  const int b = blockIdx.x, hi = b / 8, cs = hi % CS, rb = (hi / CS) * 8 + b % 8;
+  if (rb >= nrb) return;  // the grid is whole groups of 8 row blocks
+  const int m0 = rb * kXdtRows;
+  const int fr = lane & 15, fc = lane >> 4;
+  const bool v0 = 8 * fc < R, v1 = 32 + 8 * fc < R, two = R > 32;
+  const int k0 = v0 ? 8 * fc : 0, k1 = v1 ? 32 + 8 * fc : 0;
+  // 16-column tiles per wave, their first, and groups of them
+  const int nt = D / (64 * CS), t_beg = (cs * 4 + wave) * nt, ng = (nt + kXdtGroup - 1) / kXdtGroup;
+  // W_dt fragments of a group of tiles (indexes past the last tile reload the last one)
+  uint4 wa[kXdtGroup], wb[kXdtGroup];
+  auto fetch = [&](int g) {
+#pragma unroll
+    for (int i = 0; i < kXdtGroup; ++i) {
+      const int t = min(g * kXdtGroup + i, nt - 1);
+      const bf16* wr = Wdt + (int64_t)((t_beg + t) * 16 + fr) * R;
+      wa[i] = *reinterpret_cast<const uint4*>(wr + k0);
+      wb[i] = *reinterpret_cast<const uint4*>(wr + k1);
+    }
+  };
+  fetch(0);
+
+  const int qw = cs == 0 ? xw / 4 : R / 4;  // float4 columns this split sums: all, or the dt lane
+  for (int q = tid; q < kXdtRows * qw; q += 256) {
+    const int r = q / qw, c = 4 * (q % qw);
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (m0 + r < M) {
+      const float* p = P + (int64_t)(m0 + r) * xw + c;
+      int z = 0;
+      for (; z + 4 <= ks; z += 4) {  // four loads in flight, added in slice order
+        float4 t[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) t[i] = *reinterpret_cast<const float4*>(p + (z + i) * plane);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          v.x += t[i].x; v.y += t[i].y; v.z += t[i].z; v.w += t[i].w;
+        }
+      }
+      for (; z < ks; ++z) {
+        const float4 t = *reinterpret_cast<const float4*>(p + z * plane);
+        v.x += t.x; v.y += t.y; v.z += t.z; v.w += t.w;
+      }
+      if (cs == 0) *reinterpret_cast<float4*>(xdbl + (int64_t)(m0 + r) * xw + c) = v;
+    }
+    if (c < R) {
+      Xs[r][c] = (bf16)v.x; Xs[r][c + 1] = (bf16)v.y; Xs[r][c + 2] = (bf16)v.z; Xs[r][c + 3] = (bf16)v.w;
+    }
+  }
+  for (int i = tid; i < kXdtRows * (kXdtMaxRank - R); i += 256)
+    Xs[i / (kXdtMaxRank - R)][R + i % (kXdtMaxRank - R)] = (bf16)0.0f;
+  __syncthreads();
+
+  const bf16x8 x0 = *reinterpret_cast<const bf16x8*>(&Xs[fr][8 * fc]);
+  const bf16x8 x1 = *reinterpret_cast<const bf16x8*>(&Xs[fr][32 + 8 * fc]);
+  // each wave's 16 x 16G block of dt is staged in LDS and leaves in row order
+  constexpr int TP = 16 * kXdtGroup + 4;  // staged row pitch, floats
+  __shared__ __align__(16) float Ts[4][kXdtRows * TP];
+  float* tw = Ts[wave];
+  auto group = [&](const uint4* ca, const uint4* cb, int g) {
+#pragma unroll
+    for (int i = 0; i < kXdtGroup; ++i) {
+      const int t = g * kXdtGroup + i;
+      const bf16x8 w0 = v0 ? __builtin_bit_cast(bf16x8, ca[i]) : bf16x8{};
+      const bf16x8 w1 = v1 ? __builtin_bit_cast(bf16x8, cb[i]) : bf16x8{};
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w0, x0, acc, 0, 0, 0);
+      if (two) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w1, x1, acc, 0, 0, 0);
+      *reinterpret_cast<f32x4*>(&tw[fr * TP + 16 * i + 4 * fc]) = acc;
+    }
+    // the wave's 16 x 16G block back in row order (LDS operations of one wave run in issue
+    // order): each store instruction covers runs of whole rows
+    const int valid = min(kXdtGroup, nt - g * kXdtGroup) * 4;  // float4 columns that exist
+#pragma unroll
+    for (int j = 0; j < kXdtGroup; ++j) {
+      const int idx = j * 64 + lane, r = idx / (4 * kXdtGroup), c4 = idx % (4 * kXdtGroup);
+      const f32x4 v = *reinterpret_cast<const f32x4*>(&tw[r * TP + 4 * c4]);
+      if (m0 + r < M && c4 < valid)
+        *reinterpret_cast<f32x4*>(dt + (int64_t)(m0 + r) * D + (t_beg + g * kXdtGroup) * 16 + 4 * c4) = v;
+    }
+  };
+  for (int g = 0; g < ng; ++g) {
+    if (g > 0) fetch(g);
+    group(wa, wb, g);
+  }
+}
+
+hipError_t launch_xproj_dtproj(const float* u, int64_t ldu, const void* Wx, float* xdbl, int xw,
+                               const void* Wdt, int R, float* dt, int M, int D, float* partial,
+                               int max_ks, hipStream_t s) {
+  const int ks = gemm_rows_ksplit(M, xw, D, max_ks);
+  auto a16 = [](const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; };
+  const bool fuse = MAMBA_XDT_FUSE && ks > 1 && ldu % 8 == 0 && D % 8 == 0 && a16(u) && a16(Wx) &&
+                    a16(Wdt) && a16(xdbl) && a16(dt) && a16(partial) && R % 8 == 0 && R > 0 &&
+                    R <= kXdtMaxRank && D % 64 == 0 && xw % 4 == 0;
+  hipError_t e;
+  if (!fuse) {
+    if ((e = launch_gemm_bf16_rows(u, false, ldu, Wx, D, xdbl, xw, M, xw, D, false, partial, max_ks, s)) !=
+        hipSuccess)
+      return e;
+    return launch_gemm_bf16(xdbl, false, xw, Wdt, R, dt, D, M, D, R, false, s);
+  }
+  const int k_chunk = splitk_chunk(D, ks);
+  const int64_t plane = (int64_t)M * xw;
+  if ((e = gemm_tile<float, 32, 80, 64, 2, 1>(u, ldu, static_cast<const bf16*>(Wx), D, partial, xw, M, xw, D,
+                                              false, true, s, ks, k_chunk, plane)) != hipSuccess)
+    return e;
+  int cs = MAMBA_XDT_SPLIT;
+  while (cs > 1 && D % (64 * cs) != 0) --cs;
+  const int64_t nrb = (M + kXdtRows - 1) / kXdtRows;
+  xproj_sum_dtproj_kernel<<<dim3((unsigned)((nrb + 7) / 8 * 8 * cs)), 256, 0, s>>>(
+      partial, ks, plane, xdbl, xw, static_cast<const bf16*>(Wdt), R, dt, D, M, cs);
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm_bf16_splitk(const void* A, bool a_bf16, int64_t lda, const void* W,
                                    int64_t ldw, float* C, int64_t ldc, int M, int N, int K,
                                    bool accumulate, float* partial, hipStream_t s) {

@@ -99,11 +99,10 @@ hipError_t run_backbone_prefill_io(const mamba_backbone_dims& d, const mamba_bac
     if ((e = launch_conv1d_fwd(ca, s)) != hipSuccess) return e;
     // F4b: xdbl = u @ x_proj^T   [bt, R + 2N]: dt lane | B | C. Split over K, its partial
     // planes in y, which is free until the scan writes it
-    if ((e = launch_gemm_bf16_rows(u, false, D, x_proj + (int64_t)l * xw * D, D, xdbl, xw, (int)bt, xw, D,
-                                   false, y, D / xw, s)) != hipSuccess) return e;
-    // F4c: dt = xdbl[:, :R] @ dt_proj^T   [bt, D]  (bias applied in the scan)
-    if ((e = launch_gemm_bf16(xdbl, false, xw, dt_proj + (int64_t)l * D * R, R, dt, D, (int)bt, D, R,
-                              false, s)) != hipSuccess) return e;
+    // F4c: dt = xdbl[:, :R] @ dt_proj^T   [bt, D]  (bias applied in the scan), in the
+    // kernel that sums x_proj's planes
+    if ((e = launch_xproj_dtproj(u, D, x_proj + (int64_t)l * xw * D, xdbl, xw, dt_proj + (int64_t)l * D * R, R,
+                                 dt, (int)bt, D, y, D / xw, s)) != hipSuccess) return e;
     // F4d: the scan, B/C read in place from xdbl, the gate from the z lane of proj
     ScanFwdArgs sa{u, dt, w.dt_bias + (int64_t)l * D, true, w.A_log + (int64_t)l * D * N,
                    xdbl + R, xdbl + R + N, xw, w.D_skip + (int64_t)l * D, proj + D, 2 * D,

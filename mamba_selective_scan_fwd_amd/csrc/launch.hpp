@@ -239,6 +239,13 @@ int gemm_rows_ksplit(int M, int N, int K, int max_ks);
 hipError_t launch_gemm_bf16_rows(const void* A, bool a_bf16, int64_t lda, const void* W,
                                  int64_t ldw, float* C, int64_t ldc, int M, int N, int K,
                                  bool accumulate, float* partial, int max_ks, hipStream_t s);
+// A prefill's x_proj and dt_proj: xdbl = u @ W_x^T ([M, xw], dt lane | B | C) and
+// dt = xdbl[:, :R] @ W_dt^T ([M, D], bias left to the scan); x_proj split over K as
+// launch_gemm_bf16_rows does (partial planes in `partial`), its planes summed and dt_proj
+// applied by one kernel where the shapes allow, else the two products one after the other.
+hipError_t launch_xproj_dtproj(const float* u, int64_t ldu, const void* Wx, float* xdbl, int xw,
+                               const void* Wdt, int R, float* dt, int M, int D, float* partial,
+                               int max_ks, hipStream_t s);
 hipError_t launch_gemm_bf16_splitk(const void* A, bool a_bf16, int64_t lda, const void* W,
                                    int64_t ldw, float* C, int64_t ldc, int M, int N, int K,
                                    bool accumulate, float* partial, hipStream_t s);

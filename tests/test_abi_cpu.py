@@ -212,3 +212,40 @@ def test_noalloc_rejects_a_shape_beyond_its_scratch():
     msg = m.mamba_last_error()
     assert "mamba_conv_scan_fwd_noalloc" in msg and "19857408" in msg and str(16 << 20) in msg
     assert "mamba_conv_scan_fwd with a workspace" in msg
+
+
+def test_xproj_dtproj_workspace_size():
+    """x_proj's K split as the backbone prefill runs it: the 130m layer (8192 rows, d_inner
+    1536, 80 output columns) takes 4 slices of 384, whose partial planes are 4 x 8192 x 80
+    floats; a decode-sized M and a d_inner that is not whole 64-wide slabs take no split."""
+    lib = m.load_library()
+    assert lib.mamba_xproj_dtproj_workspace_size(8192, 1536, 48, 16) == 4 * 8192 * 80 * 4
+    assert lib.mamba_xproj_dtproj_workspace_size(40, 1536, 48, 16) == 0
+    assert lib.mamba_xproj_dtproj_workspace_size(8192, 1000, 48, 16) == 0
+    assert lib.mamba_xproj_dtproj_workspace_size(-1, 1536, 48, 16) == 0
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(M=-1), EINVAL, "M = -1"),
+    (dict(ldu=1000), EINVAL, "ldu = 1000"),
+    (dict(ws=None), EWS, "workspace is NULL"),
+    (dict(wsb=100), EWS, "workspace_bytes = 100"),
+    (dict(xdbl=FAKE + 64), EINVAL, "xdbl overlaps u"),
+    (dict(dt=FAKE + (1 << 32) + 64), EINVAL, "xdbl overlaps dt"),
+    (dict(u=FAKE + 2), EINVAL, "aligned"),
+])
+def test_xproj_dtproj_validation(kw, status, needle):
+    lib = m.load_library()
+    M, D, R, N = 8192, 1536, 48, 16
+    a = dict(u=FAKE, ldu=D, wx=FAKE + (1 << 30), wdt=FAKE + (1 << 31), xdbl=FAKE + (1 << 32),
+             dt=FAKE + (1 << 33), M=M, ws=FAKE + (1 << 34), wsb=1 << 30)
+    a.update(kw)
+    st = lib.mamba_xproj_dtproj(a["u"], a["ldu"], a["wx"], a["wdt"], a["xdbl"], a["dt"], a["M"], D, R, N,
+                                a["ws"], a["wsb"], None)
+    assert st == status
+    assert needle in m.mamba_last_error()
+
+
+def test_xproj_dtproj_empty_is_noop():
+    lib = m.load_library()
+    assert lib.mamba_xproj_dtproj(None, 0, None, None, None, None, 0, 1536, 48, 16, None, 0, None) == 0

@@ -115,6 +115,64 @@ def test_gemm_empty_is_noop():
 
 # ------------------------------------------------------------------ RMSNorm, embedding
 
+# x_proj then dt_proj of a prefill layer: (M, d_inner, dt_rank, d_state). The split-K sum
+# and dt_proj run as one kernel for the first four (the 130m layer; a ragged row count; a
+# narrow layer whose column split is 2; dt_rank 56, so the second 32-wide k step is part
+# zero); the last three take the two-product path (dt_rank beyond 64; few rows, no split;
+# d_inner not whole 64-wide slabs).
+XDT_CASES = [(8192, 1536, 48, 16), (1000, 1536, 48, 16), (210, 128, 8, 16), (300, 512, 56, 16),
+             (500, 640, 80, 16), (40, 1536, 48, 16), (333, 1000, 48, 16)]
+
+
+@pytest.mark.parametrize("M,D,R,N", XDT_CASES)
+def test_xproj_dtproj_vs_oracle(M, D, R, N):
+    """xdbl against the oracle's bf16-operand product at the f32 bar. dt_proj rounds the dt
+    lane of xdbl to bf16 as it enters: to make that rounding the same on both sides, each dt
+    lane column of W_x has one nonzero, a power of two, so the lane is bf16(u) times a power
+    of two, exact in f32 and in f64 alike (the B and C columns are dense). dt then meets the
+    f32 bar against the oracle's dt_proj of its own xdbl; a wrong row, column or k index in
+    either product shows as an O(1) error."""
+    _say(f"case xproj_dtproj M{M} D{D} R{R} N{N}")
+    xw = R + 2 * N
+    g = np.random.default_rng(M + 3 * D + 7 * R)
+    u = g.normal(size=(M, D)).astype(np.float32)
+    Wx = W.bf16_round(g.normal(size=(xw, D)).astype(np.float32) * 0.05)
+    Wx[:R] = 0.0
+    cols = g.permutation(D)[:R]
+    Wx[np.arange(R), cols] = np.exp2(g.integers(-3, 2, size=R)) * g.choice([-1.0, 1.0], size=R)
+    Wdt = W.bf16_round(g.normal(size=(D, R)).astype(np.float32) * 0.1)
+    xdbl = torch.full((M, xw), float("nan"), device="cuda")
+    dt = torch.full((M, D), float("nan"), device="cuda")
+    m.mamba_xproj_dtproj(dev(u), _bf16_dev(Wx), _bf16_dev(Wdt), xdbl, dt)
+    torch.cuda.synchronize()
+    ref_x = ob.gemm(u, Wx)
+    ref_dt = ob.gemm(ref_x[:, :R], Wdt)
+    ex, ed = rel_err(host(xdbl), ref_x), rel_err(host(dt), ref_dt)
+    _say(f"  err xdbl {ex:.2e} dt {ed:.2e}")
+    assert ex <= TOL_F32 and ed <= TOL_F32
+
+
+def test_xproj_dtproj_strided_u():
+    """u as the x lane of a wider row (the conv output is contiguous in the backbone; the
+    ABI takes any row stride that is a multiple of 8 on the fused path)."""
+    M, D, R, N = 700, 1536, 48, 16
+    xw = R + 2 * N
+    g = np.random.default_rng(5)
+    u = g.normal(size=(M, 2 * D)).astype(np.float32)
+    Wx = W.bf16_round(g.normal(size=(xw, D)).astype(np.float32) * 0.05)
+    Wx[:R] = 0.0
+    Wx[np.arange(R), g.permutation(D)[:R]] = 0.5
+    Wdt = W.bf16_round(g.normal(size=(D, R)).astype(np.float32) * 0.1)
+    xdbl = torch.empty(M, xw, device="cuda")
+    dt = torch.empty(M, D, device="cuda")
+    ud = dev(u)
+    m.mamba_xproj_dtproj(ud[:, :D], _bf16_dev(Wx), _bf16_dev(Wdt), xdbl, dt)
+    torch.cuda.synchronize()
+    ref_x = ob.gemm(u[:, :D], Wx)
+    assert rel_err(host(xdbl), ref_x) <= TOL_F32
+    assert rel_err(host(dt), ob.gemm(ref_x[:, :R], Wdt)) <= TOL_F32
+
+
 @pytest.mark.parametrize("Dm,out", [(768, "f32"), (768, "bf16"), (100, "f32"), (2049, "f32")])
 def test_rmsnorm_vs_oracle(Dm, out):
     _say(f"case rmsnorm Dm{Dm} out={out}")
