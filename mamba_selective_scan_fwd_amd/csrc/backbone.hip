@@ -238,6 +238,9 @@ __device__ __forceinline__ bf16x8 load_chunk_scalar(const AT* row, int k0, int K
 #ifndef MAMBA_GEMM_WGN
 #define MAMBA_GEMM_WGN 2
 #endif
+#ifndef MAMBA_GEMM_CPRE
+#define MAMBA_GEMM_CPRE 1  // load the old C tile of an accumulating product before the k loop
+#endif
 #ifndef MAMBA_GEMM_LDS_EPI
 #define MAMBA_GEMM_LDS_EPI 1  // write C through LDS as rows of float4 (1) or from the fragments (0)
 #endif
@@ -406,6 +409,25 @@ gemm_mfma_kernel(
 #pragma unroll
       for (int r = 0; r < NR; ++r) acc[i][j][r] = 0.0f;
 
+  // Adding into C (out_proj's residual add) reads the old C tile in the epilogue. When the
+  // tile leaves in one pass and a thread's share is at most 12 float4, those reads are
+  // issued here, before the first k-slab, in the epilogue's own element order (rows and
+  // columns clamped into C; the values of clamped slots are never stored), so that their
+  // latency is spent under the k loop instead of after it.
+  constexpr int V4 = BN / 4;  // float4 per tile row
+  constexpr int kPre = MAMBA_GEMM_CPRE && MAMBA_GEMM_LDS_EPI && kParts == 1 && (BM * V4) % NT == 0 &&
+                               BM * V4 / NT <= 12 ? BM * V4 / NT : 0;
+  float4 cpre[kPre > 0 ? kPre : 1];
+  const bool pre = kPre > 0 && accumulate && N % 4 == 0 && ldc % 4 == 0 &&
+                   reinterpret_cast<uintptr_t>(C) % 16 == 0;
+  if (pre) {
+#pragma unroll
+    for (int q = 0; q < kPre; ++q) {
+      const int idx = tid + q * NT, r = idx / V4, c4 = (idx % V4) * 4;
+      cpre[q] = *reinterpret_cast<const float4*>(C + (int64_t)min(m0 + r, M - 1) * ldc + min(n0 + c4, N - 4));
+    }
+  }
+
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
   const int nk = (K + BK - 1) / BK;
@@ -544,6 +566,18 @@ gemm_mfma_kernel(
     }
     __syncthreads();
     constexpr int V = BN / 4;  // float4 per tile row
+    if (pre) {
+#pragma unroll
+      for (int q = 0; q < kPre; ++q) {
+        const int idx = tid + q * NT, r = idx / V, c4 = (idx % V) * 4;
+        const int gm = m0 + r, gn = n0 + c4;
+        const float4 v = *reinterpret_cast<const float4*>(&Cs[r * LDC + c4]);
+        if (gm < M && gn < N)
+          *reinterpret_cast<float4*>(C + (int64_t)gm * ldc + gn) =
+              make_float4(v.x + cpre[q].x, v.y + cpre[q].y, v.z + cpre[q].z, v.w + cpre[q].w);
+      }
+      return;
+    }
     const bool c_vec = ldc % 4 == 0 && reinterpret_cast<uintptr_t>(C) % 16 == 0;
 #pragma unroll 4
     for (int idx = tid; idx < PR * V; idx += NT) {
@@ -786,6 +820,14 @@ static hipError_t gemm_at(const AT* A, int64_t lda, const bf16* W, int64_t ldw, 
   if (M <= 64 && N >= 8192)
     return gemm_tile<AT, 64, 64, 64, 2, 2>(A, lda, W, ldw, C, ldc, M, N, K, acc, vec, s);
   if (M <= 64) return gemm_tile<AT, 64, 32, 64, 2, 1>(A, lda, W, ldw, C, ldc, M, N, K, acc, vec, s);
+  // Many rows, at most 1024 columns (out_proj at a prefill's row count): 128 x 128 tiles
+  // would give M/128 x N/128 workgroups, 1.5 per CU for the 130m out_proj at 8192 rows;
+  // 128 x 96 tiles (4 x 1 waves of 32 x 96, 32 x 32 MFMA) give 2 per CU, and their C tile is
+  // small enough for the early read of the old C when the product adds into it. At the
+  // 130m prefill: 37 us in the layer chain against 44 us for 128 x 128.
+  if (N <= 1024 && M >= 4096)
+    return gemm_tile<AT, 128, 96, 64, 4, 1>(A, lda, W, ldw, C, ldc, M, N, K, acc, vec, s, 1, 0, 0,
+                                            MAMBA_GEMM_DL != 0);
   // (bf16 A with whole 64-k slabs stages straight into LDS)
   return gemm_tile<AT, MAMBA_GEMM_BM, MAMBA_GEMM_BN, MAMBA_GEMM_BK, MAMBA_GEMM_WGM, MAMBA_GEMM_WGN>(
       A, lda, W, ldw, C, ldc, M, N, K, acc, vec, s, 1, 0, 0, MAMBA_GEMM_DL != 0);

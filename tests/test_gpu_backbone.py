@@ -46,6 +46,8 @@ GEMM_CASES = [
     (64, 768, 1536, "f32", True),      # a decode step's out_proj + residual
     (40, 1536, 48, "f32", False),      # dt_proj at B = 40
     (64, 50280, 768, "bf16", False),   # the head at B = 64
+    (4100, 768, 1536, "bf16", True),   # out_proj + residual at a prefill's row count, ragged M
+    (4096, 1000, 256, "f32", False),   # many rows, a narrow ragged N
 ]
 
 
