@@ -838,14 +838,13 @@ def bench_backbone(args, shape):
          None, 4 * bt * Dm + 2 * bt * Dm + 4 * Dm),
         ("gemm in_proj", lambda: m.mamba_gemm_bf16(xn, t["in_proj"][0], proj, stream=stream),
          gemm_flops(bt, 2 * D, Dm), 2 * bt * Dm + 2 * 2 * D * Dm + 4 * bt * 2 * D),
-        ("conv1d_fwd", lambda: m.mamba_conv1d_fwd(proj3[..., :D], t["conv_w"][0], t["conv_b"][0], cs0, u,
-                                                  stream=stream),
-         None, conv_bytes(4, B, T, D, K)),
-        # x_proj split over K, then one kernel that sums its partial planes and applies dt_proj
-        ("x_proj + dt_proj", lambda: m.mamba_xproj_dtproj(u.view(bt, D), t["x_proj"][0], t["dt_proj"][0], xdbl,
-                                                          dtb.view(bt, D), workspace=xdt_ws, stream=stream),
+        # the conv inside x_proj's split product, then one kernel that sums its partial planes
+        # and applies dt_proj
+        ("conv + x_proj + dt_proj", lambda: m.mamba_conv_xproj_dtproj(
+            proj3[..., :D], t["conv_w"][0], t["conv_b"][0], cs0, u, t["x_proj"][0], t["dt_proj"][0], xdbl,
+            dtb.view(bt, D), workspace=xdt_ws, stream=stream),
          gemm_flops(bt, xw, D) + gemm_flops(bt, D, R),
-         4 * bt * D + 2 * xw * D + 4 * bt * xw + 2 * D * R + 4 * bt * D),
+         conv_bytes(4, B, T, D, K) + 2 * xw * D + 4 * bt * xw + 2 * D * R + 4 * bt * D),
         ("selective_scan_fwd", lambda: m.mamba_selective_scan_fwd(
             u, dtb, t["dt_bias"][0], t["A_log"][0], xdbl3[..., R:R + N], xdbl3[..., R + N:],
             t["D_skip"][0], proj3[..., D:], hs0, hs0, y, workspace=sws, stream=stream),
@@ -876,8 +875,7 @@ def bench_backbone(args, shape):
         if flops:
             c["tflops"] = flops / (avg * 1e-3) / 1e12
         calls[name] = c
-    per_layer = ("rmsnorm", "gemm in_proj", "conv1d_fwd", "x_proj + dt_proj",
-                 "selective_scan_fwd", "gemm out_proj")
+    per_layer = ("rmsnorm", "gemm in_proj", "conv + x_proj + dt_proj", "selective_scan_fwd", "gemm out_proj")
     dom_name = max(per_layer, key=lambda k: calls[k]["avg_us"])
     dom = calls[dom_name]
     flops, nbytes = next((f, b) for n, _, f, b in pieces if n == dom_name)

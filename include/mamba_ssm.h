@@ -305,6 +305,28 @@ mamba_status mamba_xproj_dtproj(const float* u, int64_t ldu, const void* W_x, co
                                 int d_state, void* workspace, size_t workspace_bytes,
                                 void* stream);
 
+/*
+ * Stages F4a-F4c of a prefill layer in one call ([prefill.rs] prefill_body F4a, F4b, F4c):
+ * the conv + SiLU of mamba_conv1d_fwd over f32 rows, then x_proj of its output u and dt_proj
+ * of the dt lane as mamba_xproj_dtproj with M = B*T. u and the conv state come out as
+ * mamba_conv1d_fwd leaves them (same bits); xdbl and dt as mamba_xproj_dtproj computes them.
+ * Where d_conv == 4 and d_inner is a multiple of 64 the conv runs inside x_proj's product
+ * (u is still stored, for the scan).
+ *   x, x_row_stride, conv_w, conv_b, conv_state, u   as mamba_conv1d_fwd with MAMBA_F32.
+ *   lengths      in   [B] int32 valid tokens per sequence (device, clamped to [0, T]), or
+ *                     NULL (all T): the new conv state is taken after each sequence's own
+ *                     last valid token.
+ *   W_x, W_dt, xdbl, dt   as mamba_xproj_dtproj.
+ *   workspace    mamba_xproj_dtproj_workspace_size(B*T, d_inner, dt_rank, d_state) bytes.
+ * Errors as the two calls; every output must be disjoint from every input and each other.
+ */
+mamba_status mamba_conv_xproj_dtproj(const float* x, int64_t x_row_stride, const float* conv_w,
+                                     const float* conv_b, float* conv_state,
+                                     const int32_t* lengths, float* u, const void* W_x,
+                                     const void* W_dt, float* xdbl, float* dt, int B, int T,
+                                     int d_inner, int d_conv, int dt_rank, int d_state,
+                                     void* workspace, size_t workspace_bytes, void* stream);
+
 typedef struct mamba_backbone_dims {
   int n_layers;      /* 24 for the 130m shape */
   int d_model;       /* 768 */

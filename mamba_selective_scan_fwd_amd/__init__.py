@@ -15,7 +15,7 @@ __all__ = [
     "mamba_version", "mamba_last_error", "mamba_conv1d_fwd", "mamba_selective_scan_fwd",
     "mamba_selective_scan_workspace_size", "mamba_conv1d_step", "mamba_ssm_step",
     "scan_workspace", "mamba_embed_gather", "mamba_rmsnorm", "mamba_gemm_bf16",
-    "mamba_xproj_dtproj_workspace_size", "mamba_xproj_dtproj",
+    "mamba_xproj_dtproj_workspace_size", "mamba_xproj_dtproj", "mamba_conv_xproj_dtproj",
     "BackboneDims", "BackboneWeights", "mamba_backbone_workspace_size", "mamba_backbone_prefill",
     "Mamba3SisoParams", "mamba3_siso_step",
 ]
@@ -49,6 +49,8 @@ symbols = {
     "mamba_gemm_bf16": ([_P, _I, _I64, _P, _I64, _P, _I64, _I, _I, _I, _I, _P], _I),
     "mamba_xproj_dtproj_workspace_size": ([_I, _I, _I, _I], _SZ),
     "mamba_xproj_dtproj": ([_P, _I64, _P, _P, _P, _P, _I, _I, _I, _I, _P, _SZ, _P], _I),
+    "mamba_conv_xproj_dtproj": ([_P, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _SZ,
+                                 _P], _I),
     "mamba_backbone_workspace_size": ([_P, _I, _I], _SZ),
     "mamba_backbone_prefill": ([_P, _P, _P, _I, _I, _P, _P, _P, _P, _SZ, _P], _I),
     "mamba_backbone_prefill_ex": ([_P, _P, _P, _I, _I, _P, _P, _P, _SZ, _P], _I),
@@ -361,6 +363,27 @@ def mamba_xproj_dtproj(u, W_x, W_dt, xdbl, dt, workspace=None, M=None, ldu=None,
     _check(load_library().mamba_xproj_dtproj(_ptr(u), ldu, _ptr(W_x), _ptr(W_dt), _ptr(xdbl), _ptr(dt), M,
                                              d_inner, dt_rank, d_state, _ptr(workspace), nbytes,
                                              _stream(stream)))
+
+
+def mamba_conv_xproj_dtproj(x, conv_w, conv_b, conv_state, u, W_x, W_dt, xdbl, dt, lengths=None,
+                            workspace=None, stream=None) -> None:
+    """u = silu(conv(x)) (conv state carried), xdbl = u @ W_x^T, dt = xdbl[:, :dt_rank] @ W_dt^T.
+    x: [B, T, >= d_inner] f32 view (row stride as it is); conv_w [d_inner, d_conv]; conv_b
+    [d_inner] or None; conv_state [B, d_inner, d_conv] or None; u [B, T, d_inner]; W_x, W_dt
+    bf16; xdbl [B*T, dt_rank + 2 d_state]; dt [B*T, d_inner]; lengths [B] int32 or None."""
+    import torch
+    B, T = x.shape[0], x.shape[1]
+    d_inner, d_conv = conv_w.shape
+    dt_rank = W_dt.shape[1]
+    d_state = (W_x.shape[0] - dt_rank) // 2
+    need = mamba_xproj_dtproj_workspace_size(B * T, d_inner, dt_rank, d_state)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load_library().mamba_conv_xproj_dtproj(
+        _ptr(x), _row_stride(x, "x"), _ptr(conv_w), _ptr(conv_b), _ptr(conv_state), _ptr(lengths), _ptr(u),
+        _ptr(W_x), _ptr(W_dt), _ptr(xdbl), _ptr(dt), B, T, d_inner, d_conv, dt_rank, d_state, _ptr(workspace),
+        nbytes, _stream(stream)))
 
 
 def mamba_backbone_workspace_size(dims: BackboneDims, B: int, T: int) -> int:

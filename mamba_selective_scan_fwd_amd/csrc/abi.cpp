@@ -683,6 +683,69 @@ mamba_status mamba_xproj_dtproj(const float* u, int64_t ldu, const void* W_x, co
   });
 }
 
+mamba_status mamba_conv_xproj_dtproj(const float* x, int64_t x_row_stride, const float* conv_w,
+                                     const float* conv_b, float* conv_state,
+                                     const int32_t* lengths, float* u, const void* W_x,
+                                     const void* W_dt, float* xdbl, float* dt, int B, int T,
+                                     int d_inner, int d_conv, int dt_rank, int d_state,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+  static const char* fn = "mamba_conv_xproj_dtproj";
+  return guarded([&] {
+    check_dim(fn, "B", B);
+    check_dim(fn, "T", T);
+    check_dim(fn, "d_inner", d_inner);
+    check_dim(fn, "dt_rank", dt_rank);
+    check_dim(fn, "d_state", d_state);
+    check_state_dim(fn, "d_conv", d_conv, kMaxK);
+    if (B > kMaxGridYZ) fail(MAMBA_EUNSUPPORTED, fn, "B = %d exceeds %d", B, kMaxGridYZ);
+    const int64_t rows = (int64_t)B * T;
+    if (rows == 0) return;
+    if (d_inner == 0 || dt_rank == 0) fail(MAMBA_EINVAL, fn, "d_inner and dt_rank must be positive");
+    if (rows > 65535 * 16) fail(MAMBA_EUNSUPPORTED, fn, "B * T = %lld exceeds %d", (long long)rows, 65535 * 16);
+    if (x_row_stride < d_inner) fail(MAMBA_EINVAL, fn, "x_row_stride = %lld is less than d_inner = %d", (long long)x_row_stride, d_inner);
+    if (x_row_stride > kMaxRowStride) fail(MAMBA_EUNSUPPORTED, fn, "x_row_stride = %lld exceeds %lld", (long long)x_row_stride, (long long)kMaxRowStride);
+    const int xw = dt_rank + 2 * d_state;
+    const int M = (int)rows;
+    const size_t need = xproj_dtproj_ws(M, d_inner, dt_rank, d_state);
+    if (need) {
+      if (!workspace) fail(MAMBA_EWORKSPACE, fn, "workspace is NULL but %zu bytes are required", need);
+      if (workspace_bytes < need) fail(MAMBA_EWORKSPACE, fn, "workspace_bytes = %zu but %zu are required", workspace_bytes, need);
+      check_ptr(fn, "workspace", workspace, 4, true);
+    }
+    check_ptr(fn, "x", x, 4, true);
+    check_ptr(fn, "conv_w", conv_w, 4, true);
+    check_ptr(fn, "conv_b", conv_b, 4, false);
+    check_ptr(fn, "conv_state", conv_state, 4, false);
+    check_ptr(fn, "lengths", lengths, 4, false);
+    check_ptr(fn, "u", u, 4, true);
+    check_ptr(fn, "W_x", W_x, 2, true);
+    check_ptr(fn, "W_dt", W_dt, 2, true);
+    check_ptr(fn, "xdbl", xdbl, 4, true);
+    check_ptr(fn, "dt", dt, 4, true);
+    const Range rx = range("x", x, rows, x_row_stride, d_inner, 4);
+    const Range rcw = range("conv_w", conv_w, d_inner, d_conv, d_conv, 4);
+    const Range rcb = range("conv_b", conv_b, 1, d_inner, d_inner, 4);
+    const Range rl = range("lengths", lengths, 1, B, B, 4);
+    const Range rwx = range("W_x", W_x, xw, d_inner, d_inner, 2);
+    const Range rwd = range("W_dt", W_dt, d_inner, dt_rank, dt_rank, 2);
+    const Range rs = range("conv_state", conv_state, (int64_t)B * d_inner, d_conv, d_conv, 4);
+    const Range ru = range("u", u, rows, d_inner, d_inner, 4);
+    const Range rxd = range("xdbl", xdbl, rows, xw, xw, 4);
+    const Range rd = range("dt", dt, rows, d_inner, d_inner, 4);
+    const Range rw = range("workspace", need ? workspace : nullptr, 1, (int64_t)need, (int64_t)need, 1);
+    check_disjoint(fn, rs, {rx, rcw, rcb, rl, rwx, rwd});
+    check_disjoint(fn, ru, {rx, rcw, rcb, rl, rwx, rwd, rs});
+    check_disjoint(fn, rxd, {rx, rcw, rcb, rl, rwx, rwd, rs, ru});
+    check_disjoint(fn, rd, {rx, rcw, rcb, rl, rwx, rwd, rs, ru, rxd});
+    check_disjoint(fn, rw, {rx, rcw, rcb, rl, rwx, rwd, rs, ru, rxd, rd});
+    mamba::ConvFwdArgs a{x, x_row_stride, conv_w, conv_b, conv_state, u, false, B, T, d_inner, d_conv};
+    a.lengths = lengths;
+    check_hip(fn, mamba::launch_conv_xproj_dtproj(a, W_x, xdbl, xw, W_dt, dt_rank, dt,
+                                                  static_cast<float*>(workspace), std::max(d_inner / xw, 1),
+                                                  static_cast<hipStream_t>(stream)));
+  });
+}
+
 static void check_backbone_dims(const char* fn, const mamba_backbone_dims* d) {
   if (!d) fail(MAMBA_EINVAL, fn, "dims is NULL");
   if (d->n_layers < 0) fail(MAMBA_EINVAL, fn, "n_layers = %d is negative", d->n_layers);

@@ -957,6 +957,9 @@ hipError_t launch_gemm_bf16_rows(const void* A, bool a_bf16, int64_t lda, const 
 #ifndef MAMBA_XDT_FUSE
 #define MAMBA_XDT_FUSE 1  // x_proj's reduction and dt_proj in one kernel (1) or two launches (0)
 #endif
+#ifndef MAMBA_CONV_XPROJ
+#define MAMBA_CONV_XPROJ 1  // the prefill's conv and x_proj in one kernel (1) or two launches (0)
+#endif
 #ifndef MAMBA_XDT_SPLIT
 #define MAMBA_XDT_SPLIT 4  // column splits per row block
 #endif
@@ -1059,32 +1062,242 @@ __global__ void __launch_bounds__(256) xproj_sum_dtproj_kernel(const float* __re
   }
 }
 
-hipError_t launch_xproj_dtproj(const float* u, int64_t ldu, const void* Wx, float* xdbl, int xw,
-                               const void* Wdt, int R, float* dt, int M, int D, float* partial,
-                               int max_ks, hipStream_t s) {
-  const int ks = gemm_rows_ksplit(M, xw, D, max_ks);
+// x_proj's ks partial planes (ks * M * xw floats at `partial`) -> xdbl and dt: one kernel
+// when the shapes allow, else the in-order reduction and the dt_proj product.
+static hipError_t finish_xproj_dtproj(const float* partial, int ks, float* xdbl, int xw, const void* Wdt,
+                                      int R, float* dt, int M, int D, hipStream_t s) {
   auto a16 = [](const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; };
-  const bool fuse = MAMBA_XDT_FUSE && ks > 1 && ldu % 8 == 0 && D % 8 == 0 && a16(u) && a16(Wx) &&
-                    a16(Wdt) && a16(xdbl) && a16(dt) && a16(partial) && R % 8 == 0 && R > 0 &&
-                    R <= kXdtMaxRank && D % 64 == 0 && xw % 4 == 0;
-  hipError_t e;
+  const int64_t plane = (int64_t)M * xw;
+  const bool fuse = MAMBA_XDT_FUSE && a16(Wdt) && a16(xdbl) && a16(dt) && a16(partial) && R % 8 == 0 &&
+                    R > 0 && R <= kXdtMaxRank && D % 64 == 0 && xw % 4 == 0;
   if (!fuse) {
-    if ((e = launch_gemm_bf16_rows(u, false, ldu, Wx, D, xdbl, xw, M, xw, D, false, partial, max_ks, s)) !=
-        hipSuccess)
-      return e;
+    splitk_reduce_kernel<<<dim3((unsigned)((plane + 255) / 256)), 256, 0, s>>>(partial, ks, xdbl, xw, M, xw, 0);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
     return launch_gemm_bf16(xdbl, false, xw, Wdt, R, dt, D, M, D, R, false, s);
   }
-  const int k_chunk = splitk_chunk(D, ks);
-  const int64_t plane = (int64_t)M * xw;
-  if ((e = gemm_tile<float, 32, 80, 64, 2, 1>(u, ldu, static_cast<const bf16*>(Wx), D, partial, xw, M, xw, D,
-                                              false, true, s, ks, k_chunk, plane)) != hipSuccess)
-    return e;
   int cs = MAMBA_XDT_SPLIT;
   while (cs > 1 && D % (64 * cs) != 0) --cs;
   const int64_t nrb = (M + kXdtRows - 1) / kXdtRows;
   xproj_sum_dtproj_kernel<<<dim3((unsigned)((nrb + 7) / 8 * 8 * cs)), 256, 0, s>>>(
       partial, ks, plane, xdbl, xw, static_cast<const bf16*>(Wdt), R, dt, D, M, cs);
   return hipGetLastError();
+}
+
+hipError_t launch_xproj_dtproj(const float* u, int64_t ldu, const void* Wx, float* xdbl, int xw,
+                               const void* Wdt, int R, float* dt, int M, int D, float* partial,
+                               int max_ks, hipStream_t s) {
+  const int ks = gemm_rows_ksplit(M, xw, D, max_ks);
+  auto a16 = [](const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; };
+  if (ks <= 1 || ldu % 8 != 0 || D % 8 != 0 || !a16(u) || !a16(Wx)) {
+    hipError_t e = launch_gemm_bf16_rows(u, false, ldu, Wx, D, xdbl, xw, M, xw, D, false, partial, max_ks, s);
+    if (e != hipSuccess) return e;
+    return launch_gemm_bf16(xdbl, false, xw, Wdt, R, dt, D, M, D, R, false, s);
+  }
+  const int k_chunk = splitk_chunk(D, ks);
+  const int64_t plane = (int64_t)M * xw;
+  const hipError_t e = gemm_tile<float, 32, 80, 64, 2, 1>(u, ldu, static_cast<const bf16*>(Wx), D, partial, xw,
+                                                          M, xw, D, false, true, s, ks, k_chunk, plane);
+  if (e != hipSuccess) return e;
+  return finish_xproj_dtproj(partial, ks, xdbl, xw, Wdt, R, dt, M, D, s);
+}
+
+// ------------------------------------------------------- conv + x_proj of a prefill layer
+//
+// prefill.rs page, prefill_body stages F4a (the causal depthwise conv + SiLU over the x lane
+// of in_proj's output, carrying the conv state) and F4b (the x_proj GEMM), in one kernel
+// whose output is x_proj's split-K partial planes, as the split GEMM leaves them, plus u.
+// A workgroup takes 32 tokens of one sequence and one K slice of the channels (the slices
+// of the split GEMM), in 64-channel slabs:
+//  - lane l of wave q takes channel l of the slab and tokens 8 q .. 8 q + 7, and loads the
+//    11 x rows their taps reach itself (256-byte row pieces per wave; the rows shared with
+//    the neighbouring wave come from L1/L2); the rows of the next two slabs are in flight
+//    while a slab is computed;
+//  - u = silu(conv) is formed with the taps added in the order of conv1d_fwd_kernel, so u
+//    has the same bits; it is stored for the scan and kept in LDS as bf16 (RNE, the
+//    rounding x_proj applies to its operand), double-buffered, so a slab takes one barrier;
+//  - the slab goes into the 32 x xw partial product by v_mfma_f32_16x16x32_bf16 tiles
+//    (the slab order and k steps of the split GEMM's 32 x 80 tiles). Wave q takes column
+//    tiles q and q + 4 for both token tiles, so each W_x fragment is loaded once per
+//    workgroup (with two waves per column tile it was loaded twice: 36.7 against 31.6 us
+//    at the 130m prefill).
+// Workgroup (b, first token block, slice) is the only reader of sequence b's old conv state
+// for the slice's channels, and at its end the only writer of the new one (X[Tb .. Tb+K-1]
+// of X = [old state, x], Tb the sequence's length), as in conv1d_fwd_kernel. Its loop is a
+// copy of its own (FIRST), in which the window rows before the sequence start come from the
+// state, so that the other workgroups' loads carry no condition.
+constexpr int kCxRows = 32;   // tokens per workgroup
+constexpr int kCxK = 4;       // conv taps on this path
+constexpr int kCxMaxN = 80;   // x_proj columns: at most 5 tiles of 16
+
+template <bool FIRST>
+__device__ __forceinline__ void conv_xproj_body(
+    const float* __restrict__ xb, int64_t ldx, const float* __restrict__ conv_w,
+    const float* __restrict__ conv_b, const float* __restrict__ st_old, float* __restrict__ ub,
+    const bf16* __restrict__ Wx, int xw, f32x4 (&acc)[2][2], bf16* As, int t0, int T, int D, int c_beg,
+    int nslab) {
+  constexpr int SL = 64, W = kCxK - 1 + 8, AP = SL + 8;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r0 = wave * 8;
+  const int ntn = (xw + 15) / 16;
+  const int fr = lane & 15, fq = lane >> 4;
+  const float* bsrc = conv_b ? conv_b : conv_w;
+  // window of slab sl: x rows t0 + r0 - 3 + j (the state before the sequence start);
+  // nwin holds the next slab's, nwin2 (two slabs ahead) the one after
+  float nwin[W], nwin2[W];
+  auto load_window = [&](float (&dst)[W], int sl) {
+    const int c = c_beg + sl * SL + lane;
+#pragma unroll
+    for (int j = 0; j < W; ++j) {
+      const int tt = t0 + r0 - (kCxK - 1) + j;
+      if (FIRST && tt < 0)
+        dst[j] = st_old ? st_old[(int64_t)c * kCxK + kCxK + tt] : 0.0f;
+      else
+        dst[j] = xb[(int64_t)min(tt, T - 1) * ldx + c];
+    }
+  };
+  float4 wnext = *reinterpret_cast<const float4*>(conv_w + (int64_t)(c_beg + lane) * kCxK);
+  float bnext = bsrc[c_beg + lane];
+  load_window(nwin, 0);
+  load_window(nwin2, min(1, nslab - 1));
+  for (int sl = 0; sl < nslab; ++sl) {
+    const int c0 = c_beg + sl * SL;
+    float win[W];
+#pragma unroll
+    for (int j = 0; j < W; ++j) win[j] = nwin[j];
+#pragma unroll
+    for (int j = 0; j < W; ++j) nwin[j] = nwin2[j];
+    const float4 wt = wnext;
+    const float bias = conv_b ? bnext : 0.0f;
+    // W_x fragments of this slab: wave q takes column tiles q and q + 4 (when it exists) for
+    // both token tiles, so each tile's fragments are loaded once per workgroup; column
+    // 16 n + l % 16 (the last column for n >= xw, never stored), k = 8 (l / 16) + 32 kstep
+    uint4 wf[2][2];
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2)
+      wf[0][k2] = *reinterpret_cast<const uint4*>(Wx + (int64_t)min(16 * wave + fr, xw - 1) * D + c0 + 8 * fq +
+                                                  32 * k2);
+    if (wave + 4 < ntn) {
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2)
+        wf[1][k2] = *reinterpret_cast<const uint4*>(Wx + (int64_t)min(16 * (wave + 4) + fr, xw - 1) * D + c0 +
+                                                    8 * fq + 32 * k2);
+    }
+    {
+      const int sn = min(sl + 1, nslab - 1);
+      wnext = *reinterpret_cast<const float4*>(conv_w + (int64_t)(c_beg + sn * SL + lane) * kCxK);
+      bnext = bsrc[c_beg + sn * SL + lane];
+      load_window(nwin2, min(sl + 2, nslab - 1));
+    }
+    bf16* as = As + (sl & 1) * kCxRows * AP;
+    const float w[kCxK] = {wt.x, wt.y, wt.z, wt.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float c = bias;
+#pragma unroll
+      for (int k = 0; k < kCxK; ++k) c = fmaf(w[k], win[i + k], c);
+      const float uv = silu(c);
+      if (t0 + r0 + i < T) ub[(int64_t)(t0 + r0 + i) * D + c0 + lane] = uv;
+      as[(r0 + i) * AP + lane] = (bf16)uv;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2) {
+      bf16x8 a[2];
+#pragma unroll
+      for (int m = 0; m < 2; ++m) a[m] = *reinterpret_cast<const bf16x8*>(&as[(16 * m + fr) * AP + 32 * k2 + 8 * fq]);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        if (wave + 4 * i < ntn)
+#pragma unroll
+          for (int m = 0; m < 2; ++m)
+            acc[i][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[m], __builtin_bit_cast(bf16x8, wf[i][k2]),
+                                                                acc[i][m], 0, 0, 0);
+    }
+  }
+}
+
+__global__ void __launch_bounds__(256) conv_xproj_kernel(
+    const float* __restrict__ x, int64_t ldx, const float* __restrict__ conv_w,
+    const float* __restrict__ conv_b, float* __restrict__ conv_state, const int32_t* __restrict__ lengths,
+    float* __restrict__ u, const bf16* __restrict__ Wx, int xw, float* __restrict__ P, int64_t plane, int T,
+    int D, int k_chunk, int ntb) {
+  __shared__ __align__(16) bf16 As[2 * kCxRows * (64 + 8)];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int b = blockIdx.x / ntb, tb = blockIdx.x % ntb, zs = blockIdx.y;
+  const int t0 = tb * kCxRows;
+  const int c_beg = zs * k_chunk, c_end = min(D, c_beg + k_chunk);
+  const int nslab = (c_end - c_beg) / 64;
+  const float* xb = x + (int64_t)b * T * ldx;
+  float* ub = u + (int64_t)b * T * D;
+  const float* st_old = conv_state ? conv_state + (int64_t)b * D * kCxK : nullptr;
+  f32x4 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int m = 0; m < 2; ++m) acc[i][m] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (t0 == 0)
+    conv_xproj_body<true>(xb, ldx, conv_w, conv_b, st_old, ub, Wx, xw, acc, As, t0, T, D, c_beg, nslab);
+  else
+    conv_xproj_body<false>(xb, ldx, conv_w, conv_b, st_old, ub, Wx, xw, acc, As, t0, T, D, c_beg, nslab);
+  // register r of lane l of tile (i, m) holds token 16 m + 4 (l / 16) + r, column
+  // 16 (wave + 4 i) + l % 16
+  const int fr = lane & 15, fq = lane >> 4;
+  float* pz = P + zs * plane + ((int64_t)b * T + t0) * xw;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int n = 16 * (wave + 4 * i) + fr;
+    if (n >= xw) continue;
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int tr = 16 * m + 4 * fq + r;
+        if (t0 + tr < T) pz[(int64_t)tr * xw + n] = acc[i][m][r];
+      }
+  }
+  if (t0 == 0 && conv_state) {
+    // every read of the old state has returned before its thread reached the last barrier
+    const int Tb = lengths ? min(max(lengths[b], 0), T) : T;
+    float* st = conv_state + (int64_t)b * D * kCxK;
+    for (int c = c_beg + tid; c < c_end; c += 256) {
+      float v[kCxK];
+#pragma unroll
+      for (int k = 0; k < kCxK; ++k) {
+        const int i = Tb + k;
+        v[k] = i >= kCxK ? xb[(int64_t)(i - kCxK) * ldx + c] : st[(int64_t)c * kCxK + i];
+      }
+#pragma unroll
+      for (int k = 0; k < kCxK; ++k) st[(int64_t)c * kCxK + k] = v[k];
+    }
+  }
+}
+
+hipError_t launch_conv_xproj_dtproj(const ConvFwdArgs& ca, const void* Wx, float* xdbl, int xw,
+                                    const void* Wdt, int R, float* dt, float* partial, int max_ks,
+                                    hipStream_t s) {
+  const int D = ca.D, T = ca.T;
+  const int M = ca.B * T;
+  const int ks = gemm_rows_ksplit(M, xw, D, max_ks);
+  auto a16 = [](const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; };
+  const bool fuse = MAMBA_CONV_XPROJ && ks > 1 && ca.K == kCxK && !ca.bf16 && D % 64 == 0 &&
+                    xw <= kCxMaxN && ca.x_row_stride % 4 == 0 && a16(ca.x) && a16(ca.conv_w) && a16(Wx) &&
+                    a16(partial);
+  hipError_t e;
+  if (!fuse) {
+    if ((e = launch_conv1d_fwd(ca, s)) != hipSuccess) return e;
+    return launch_xproj_dtproj(static_cast<const float*>(ca.u), D, Wx, xdbl, xw, Wdt, R, dt, M, D, partial,
+                               max_ks, s);
+  }
+  const int k_chunk = splitk_chunk(D, ks);
+  const int ntb = (T + kCxRows - 1) / kCxRows;
+  const int64_t plane = (int64_t)M * xw;
+  conv_xproj_kernel<<<dim3((unsigned)(ca.B * ntb), (unsigned)ks), 256, 0, s>>>(
+      static_cast<const float*>(ca.x), ca.x_row_stride, ca.conv_w, ca.conv_b, ca.conv_state, ca.lengths,
+      static_cast<float*>(ca.u), static_cast<const bf16*>(Wx), xw, partial, plane, T, D, k_chunk, ntb);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  return finish_xproj_dtproj(partial, ks, xdbl, xw, Wdt, R, dt, M, D, s);
 }
 
 hipError_t launch_gemm_bf16_splitk(const void* A, bool a_bf16, int64_t lda, const void* W,

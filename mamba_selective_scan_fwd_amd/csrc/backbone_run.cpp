@@ -92,17 +92,16 @@ hipError_t run_backbone_prefill_io(const mamba_backbone_dims& d, const mamba_bac
     // F2: proj = xn @ in_proj^T   [bt, 2D]: x lane | z lane
     if ((e = launch_gemm_bf16(xn, true, Dm, in_proj + (int64_t)l * 2 * D * Dm, Dm, proj, 2 * D, (int)bt,
                               2 * D, Dm, false, s)) != hipSuccess) return e;
-    // F4a: conv + SiLU over the x lane, carrying this layer's conv state
-    ConvFwdArgs ca{proj, 2 * D, w.conv_w + (int64_t)l * D * K, w.conv_b + (int64_t)l * D,
-                   conv_state + (int64_t)l * B * D * K, u, false, B, T, D, K};
-    ca.lengths = io.lengths;
-    if ((e = launch_conv1d_fwd(ca, s)) != hipSuccess) return e;
-    // F4b: xdbl = u @ x_proj^T   [bt, R + 2N]: dt lane | B | C. Split over K, its partial
+    // F4a: conv + SiLU over the x lane, carrying this layer's conv state, computed inside
+    // F4b: xdbl = u @ x_proj^T   [bt, R + 2N]: dt lane | B | C, split over K, its partial
     // planes in y, which is free until the scan writes it
     // F4c: dt = xdbl[:, :R] @ dt_proj^T   [bt, D]  (bias applied in the scan), in the
     // kernel that sums x_proj's planes
-    if ((e = launch_xproj_dtproj(u, D, x_proj + (int64_t)l * xw * D, xdbl, xw, dt_proj + (int64_t)l * D * R, R,
-                                 dt, (int)bt, D, y, D / xw, s)) != hipSuccess) return e;
+    ConvFwdArgs ca{proj, 2 * D, w.conv_w + (int64_t)l * D * K, w.conv_b + (int64_t)l * D,
+                   conv_state + (int64_t)l * B * D * K, u, false, B, T, D, K};
+    ca.lengths = io.lengths;
+    if ((e = launch_conv_xproj_dtproj(ca, x_proj + (int64_t)l * xw * D, xdbl, xw, dt_proj + (int64_t)l * D * R,
+                                      R, dt, y, D / xw, s)) != hipSuccess) return e;
     // F4d: the scan, B/C read in place from xdbl, the gate from the z lane of proj
     ScanFwdArgs sa{u, dt, w.dt_bias + (int64_t)l * D, true, w.A_log + (int64_t)l * D * N,
                    xdbl + R, xdbl + R + N, xw, w.D_skip + (int64_t)l * D, proj + D, 2 * D,

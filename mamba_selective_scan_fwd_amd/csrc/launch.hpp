@@ -246,6 +246,12 @@ hipError_t launch_gemm_bf16_rows(const void* A, bool a_bf16, int64_t lda, const 
 hipError_t launch_xproj_dtproj(const float* u, int64_t ldu, const void* Wx, float* xdbl, int xw,
                                const void* Wdt, int R, float* dt, int M, int D, float* partial,
                                int max_ks, hipStream_t s);
+// The conv (as launch_conv1d_fwd with a.u f32) followed by launch_xproj_dtproj of its u,
+// with the conv computed inside x_proj's split product where the shapes allow (K == 4, f32,
+// d_inner a multiple of 64, xw <= 80): u and the conv state as the conv kernel leaves them.
+hipError_t launch_conv_xproj_dtproj(const ConvFwdArgs& a, const void* Wx, float* xdbl, int xw,
+                                    const void* Wdt, int R, float* dt, float* partial, int max_ks,
+                                    hipStream_t s);
 hipError_t launch_gemm_bf16_splitk(const void* A, bool a_bf16, int64_t lda, const void* W,
                                    int64_t ldw, float* C, int64_t ldc, int M, int N, int K,
                                    bool accumulate, float* partial, hipStream_t s);

@@ -249,3 +249,25 @@ def test_xproj_dtproj_validation(kw, status, needle):
 def test_xproj_dtproj_empty_is_noop():
     lib = m.load_library()
     assert lib.mamba_xproj_dtproj(None, 0, None, None, None, None, 0, 1536, 48, 16, None, 0, None) == 0
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(T=-1), EINVAL, "T = -1"),
+    (dict(K=9), EUNSUP, "d_conv = 9"),
+    (dict(xs=1000), EINVAL, "x_row_stride = 1000"),
+    (dict(ws=None), EWS, "workspace is NULL"),
+    (dict(u=FAKE + 64), EINVAL, "u overlaps x"),
+    (dict(st=FAKE + (1 << 35) + 4), EINVAL, "dt overlaps conv_state"),
+    (dict(xdbl=FAKE + (1 << 34) + 64), EINVAL, "workspace overlaps xdbl"),
+])
+def test_conv_xproj_dtproj_validation(kw, status, needle):
+    lib = m.load_library()
+    Bsz, T, D, R, N = 4, 2048, 1536, 48, 16
+    a = dict(x=FAKE, xs=2 * D, st=FAKE + (1 << 29), u=FAKE + (1 << 30), xdbl=FAKE + (1 << 32),
+             dt=FAKE + (1 << 35), T=T, K=4, ws=FAKE + (1 << 34), wsb=1 << 30)
+    a.update(kw)
+    st = lib.mamba_conv_xproj_dtproj(a["x"], a["xs"], FAKE + (1 << 28), None, a["st"], None, a["u"],
+                                     FAKE + (1 << 31), FAKE + (1 << 33), a["xdbl"], a["dt"], Bsz, a["T"], D,
+                                     a["K"], R, N, a["ws"], a["wsb"], None)
+    assert st == status
+    assert needle in m.mamba_last_error()

@@ -15,6 +15,7 @@ import torch
 import mamba_selective_scan_fwd_amd as m
 import workloads as W
 from oracle import backbone as ob
+from oracle import oracle
 from tests.parity_util import TOL_BF16, TOL_F32, dev, host, rel_err
 
 pytestmark = pytest.mark.gpu
@@ -173,6 +174,108 @@ def test_xproj_dtproj_strided_u():
     ref_x = ob.gemm(u[:, :D], Wx)
     assert rel_err(host(xdbl), ref_x) <= TOL_F32
     assert rel_err(host(dt), ob.gemm(ref_x[:, :R], Wdt)) <= TOL_F32
+
+
+# conv + x_proj + dt_proj of a prefill layer: (B, T, d_inner, d_conv, dt_rank, d_state,
+# lengths). The conv runs inside x_proj's product for the first four: the 130m layer; a
+# ragged T (70 = 2 x 32 + 6); 40 sequences of 2 tokens, where every workgroup holds a
+# sequence start and the taps reach into the state; ragged lengths. The last two take the
+# conv kernel and the split product: d_conv 3; few rows (no K split).
+CXD_CASES = [(4, 2048, 1536, 4, 48, 16, None), (3, 70, 128, 4, 8, 16, None), (40, 2, 512, 4, 16, 16, None),
+             (3, 70, 256, 4, 16, 16, [70, 33, 1]), (2, 300, 256, 3, 16, 16, None), (2, 5, 128, 4, 8, 16, None)]
+
+
+def _cxd_inputs(Bsz, T, D, K, R, N, seed):
+    g = np.random.default_rng(seed)
+    xw = R + 2 * N
+    x = g.normal(size=(Bsz, T, 2 * D)).astype(np.float32)   # x lane of an in_proj row: columns 0..D-1
+    cw = (g.normal(size=(D, K)) * 0.5).astype(np.float32)
+    cb = (g.normal(size=D) * 0.1).astype(np.float32)
+    cs = g.normal(size=(Bsz, D, K)).astype(np.float32)
+    Wx = W.bf16_round(g.normal(size=(xw, D)).astype(np.float32) * 0.05)
+    Wdt = W.bf16_round(g.normal(size=(D, R)).astype(np.float32) * 0.1)
+    return x, cw, cb, cs, Wx, Wdt
+
+
+def _cxd_run(fused, x, cw, cb, cs, Wx, Wdt, lengths=None):
+    Bsz, T, _ = x.shape
+    D, K = cw.shape
+    R = Wdt.shape[1]
+    xw = Wx.shape[0]
+    xd = dev(x)
+    csd = dev(cs)
+    u = torch.full((Bsz, T, D), float("nan"), device="cuda")
+    xdbl = torch.full((Bsz * T, xw), float("nan"), device="cuda")
+    dt = torch.full((Bsz * T, D), float("nan"), device="cuda")
+    wx, wdt = _bf16_dev(Wx), _bf16_dev(Wdt)
+    if fused:
+        ln = None if lengths is None else torch.tensor(lengths, dtype=torch.int32, device="cuda")
+        m.mamba_conv_xproj_dtproj(xd[..., :D], dev(cw), dev(cb), csd, u, wx, wdt, xdbl, dt, lengths=ln)
+    else:
+        m.mamba_conv1d_fwd(xd[..., :D], dev(cw), dev(cb), csd, u)
+        m.mamba_xproj_dtproj(u.view(Bsz * T, D), wx, wdt, xdbl, dt)
+    torch.cuda.synchronize()
+    return host(u), host(csd), host(xdbl), host(dt)
+
+
+@pytest.mark.parametrize("case", [c for c in CXD_CASES if c[6] is None],
+                         ids=lambda c: "B{}T{}D{}K{}R{}".format(*c[:5]))
+def test_conv_xproj_dtproj_equals_two_calls(case):
+    """The one-call F4a-F4c leaves u, the conv state, xdbl and dt bit for bit as the conv
+    call followed by mamba_xproj_dtproj (same tap order, same bf16 operands, same slab and
+    k-step order of the MFMA sums, same in-order sum of the planes). (The conv call takes no
+    per-sequence lengths: that case is checked against the oracle only.)"""
+    Bsz, T, D, K, R, N, lengths = case
+    _say(f"case conv_xproj_dtproj == two calls B{Bsz} T{T} D{D} K{K} R{R} N{N}")
+    ins = _cxd_inputs(Bsz, T, D, K, R, N, seed=Bsz * 1000 + T + D)
+    a = _cxd_run(True, *ins)
+    b = _cxd_run(False, *ins)
+    for name, ga, gb in zip(("u", "conv_state", "xdbl", "dt"), a, b):
+        assert np.array_equal(ga, gb), f"{name} differs from the two-call path"
+
+
+@pytest.mark.parametrize("case", CXD_CASES, ids=lambda c: "B{}T{}D{}K{}R{}".format(*c[:5]))
+def test_conv_xproj_dtproj_vs_oracle(case):
+    """u against the oracle's conv at the f32 bar, and the new conv state exactly (its
+    entries are copies of x or of the old state; with lengths, the oracle's state after each
+    sequence's prefix).
+
+    xdbl and dt: u enters x_proj rounded to bf16, and where u lies next to a rounding
+    midpoint the GPU's f32 u and the oracle's f64 u round to neighbouring bf16 values, one
+    ulp apart (at most 2^-7 |u|). As in the x_proj test, each dt lane column of W_x has a
+    single power-of-two entry, so a dt lane value is a rounded u times a power of two and
+    differs from the oracle's by at most 2^-7 of itself: that is its bar. A B or C value
+    moves by at most 2^-7 |u| |w| per such term; its bar allows two at the largest |u| and
+    |w|, over the RMS of the reference. dt moves by at most 2^-7 |lane| |w_dt| per dt lane
+    entry; its bar allows two in the same way. The bars come from the oracle's values and
+    the weights only. The two-call test above pins these outputs bit for bit to calls whose
+    own tests hold them to 1e-4."""
+    Bsz, T, D, K, R, N, lengths = case
+    _say(f"case conv_xproj_dtproj vs oracle B{Bsz} T{T} D{D} K{K} R{R} N{N} lengths={lengths}")
+    x, cw, cb, cs, Wx, Wdt = _cxd_inputs(Bsz, T, D, K, R, N, seed=Bsz * 1000 + T + D + 1)
+    g = np.random.default_rng(D + R)
+    Wx[:R] = 0.0
+    Wx[np.arange(R), g.permutation(D)[:R]] = np.exp2(g.integers(-3, 2, size=R)) * g.choice([-1.0, 1.0], size=R)
+    u, st, xdbl, dt = _cxd_run(True, x, cw, cb, cs, Wx, Wdt, lengths)
+    ref_u, ref_st = oracle.conv1d_fwd(x, cw, cb, cs)
+    if lengths is not None:
+        for bi, tb in enumerate(lengths):
+            if tb < T:
+                _, st_b = oracle.conv1d_fwd(x[bi:bi + 1, :tb], cw, cb, cs[bi:bi + 1])
+                ref_st[bi] = st_b[0]
+    assert rel_err(u, ref_u) <= TOL_F32
+    assert np.array_equal(st, ref_st.astype(np.float32)), "conv state"
+    ref_x = ob.gemm(ref_u.reshape(Bsz * T, D), Wx)
+    ref_dt = ob.gemm(ref_x[:, :R], Wdt)
+    rms = lambda a: float(np.sqrt(np.mean(np.square(a))))
+    umax = float(np.abs(ref_u).max())
+    tol_lane = 2.0 ** -7
+    tol_bc = 2 * 2.0 ** -7 * umax * float(np.abs(Wx[R:]).max()) / rms(ref_x[:, R:])
+    tol_dt = 2 * 2.0 ** -7 * float(np.abs(ref_x[:, :R]).max()) * float(np.abs(Wdt).max()) / rms(ref_dt)
+    el, ebc, ed = rel_err(xdbl[:, :R], ref_x[:, :R]), rel_err(xdbl[:, R:], ref_x[:, R:]), rel_err(dt, ref_dt)
+    _say(f"  err dt lane {el:.2e} (bar {tol_lane:.1e}) B|C {ebc:.2e} (bar {tol_bc:.1e}) dt {ed:.2e} "
+         f"(bar {tol_dt:.1e})")
+    assert el <= tol_lane and ebc <= tol_bc and ed <= tol_dt
 
 
 @pytest.mark.parametrize("Dm,out", [(768, "f32"), (768, "bf16"), (100, "f32"), (2049, "f32")])

@@ -68,3 +68,22 @@ def test_decode_step_kernel_does_not_spill():
     assert hits
     for name, u in hits.items():
         assert u.get("scratch") == 0, f"{name} spills {u.get('scratch')} bytes per lane"
+
+
+# backbone kernels of the 130m prefill: the in_proj / out_proj tiles with direct LDS staging,
+# the fused conv + x_proj, and the kernel that sums x_proj's planes and applies dt_proj
+HOT_BACKBONE = {
+    "in_proj 128x128 tiles": "_ZN5mamba16gemm_mfma_kernelIDF16bLi128ELi128ELi64ELi2ELi2ELb1ELb1E",
+    "out_proj 128x96 tiles": "_ZN5mamba16gemm_mfma_kernelIDF16bLi128ELi96ELi64ELi4ELi1ELb1ELb1E",
+    "conv + x_proj": "_ZN5mamba17conv_xproj_kernel",
+    "x_proj sum + dt_proj": "_ZN5mamba23xproj_sum_dtproj_kernel",
+}
+
+
+def test_hot_backbone_kernels_do_not_spill():
+    use = resource_usage("backbone.hip")
+    for what, prefix in HOT_BACKBONE.items():
+        hits = {k: v for k, v in use.items() if k.startswith(prefix)}
+        assert hits, f"{what}: kernel {prefix} not found"
+        for name, u in hits.items():
+            assert u.get("scratch") == 0, f"{what} ({name}) spills {u.get('scratch')} bytes per lane"
