@@ -937,7 +937,7 @@ hipError_t launch_gemm_bf16_rows(const void* A, bool a_bf16, int64_t lda, const 
 
 // x_proj's partial planes summed and dt_proj applied, in one launch (prefill.rs page,
 // `prefill_body` stages F4b, the x_proj GEMM, and F4c, the gather of the dt columns and the
-// dt_proj GEMM ahead of the softplus, which the scan applies). A workgroup takes 16 rows
+// dt_proj GEMM ahead of the softplus, which the scan applies). A workgroup takes 16 MT rows
 // and 1/CS of the D output columns; the CS workgroups of a row block run on one XCD (same
 // blockIdx % 8), so all but the first find the partial planes in that XCD's L2.
 //  1. each row of xdbl (dt lane | B | C) is the sum of the ks partial planes, added in slice
@@ -947,12 +947,13 @@ hipError_t launch_gemm_bf16_rows(const void* A, bool a_bf16, int64_t lda, const 
 //  2. dt = dt_lane @ W_dt^T by v_mfma_f32_16x16x32_bf16 tiles with W_dt as the first operand
 //     (lane l: output column n0 + l % 16, k = 8 (l / 16) + 0..7) and the staged rows as the
 //     second, so that the result register r of lane l is dt[m0 + l % 16][n0 + 4 (l / 16) + r].
-//     Each wave takes a quarter of the workgroup's columns, G tiles at a time, and passes
-//     the 16 x 16G block through LDS so that it leaves as row runs of 64 G bytes (stored
-//     straight from the fragments, each store instruction would cover 16 rows x 64 bytes:
-//     17.5 against 14.9 us at the 130m prefill). W_dt chunks past dt_rank are zero (their
-//     loads read the row's first chunk instead, in bounds). The first group of W_dt
-//     fragments is loaded before the planes are summed.
+//     Each wave takes a quarter of the workgroup's columns, G tiles at a time, whose W_dt
+//     fragments serve all MT row tiles, and passes each 16 x 16G block through LDS so that
+//     it leaves as row runs of 64 G bytes (stored straight from the fragments, each store
+//     instruction would cover 16 rows x 64 bytes: 17.5 against 14.9 us at the 130m
+//     prefill). W_dt chunks past dt_rank are zero (their loads read the row's first chunk
+//     instead, in bounds). The first group of W_dt fragments is loaded before the planes
+//     are summed.
 // Requires dt_rank % 8 == 0 and <= 64, D % (64 CS) == 0, xw % 4 == 0, 16-byte aligned buffers.
 #ifndef MAMBA_XDT_FUSE
 #define MAMBA_XDT_FUSE 1  // x_proj's reduction and dt_proj in one kernel (1) or two launches (0)
@@ -961,12 +962,16 @@ hipError_t launch_gemm_bf16_rows(const void* A, bool a_bf16, int64_t lda, const 
 #define MAMBA_CONV_XPROJ 1  // the prefill's conv and x_proj in one kernel (1) or two launches (0)
 #endif
 #ifndef MAMBA_XDT_SPLIT
-#define MAMBA_XDT_SPLIT 4  // column splits per row block
+#define MAMBA_XDT_SPLIT 6  // column splits per row block
 #endif
-constexpr int kXdtRows = 16;
+#ifndef MAMBA_XDT_MT
+#define MAMBA_XDT_MT 4  // 16-row MFMA tiles per workgroup
+#endif
+constexpr int kXdtMT = MAMBA_XDT_MT;
+constexpr int kXdtRows = 16 * kXdtMT;
 constexpr int kXdtMaxRank = 64;
 #ifndef MAMBA_XDT_GROUP
-#define MAMBA_XDT_GROUP 6
+#define MAMBA_XDT_GROUP 4
 #endif
 constexpr int kXdtGroup = MAMBA_XDT_GROUP;  // W_dt tiles whose fragments a wave loads together
 
@@ -1028,32 +1033,36 @@ __global__ void __launch_bounds__(256) xproj_sum_dtproj_kernel(const float* __re
     Xs[i / (kXdtMaxRank - R)][R + i % (kXdtMaxRank - R)] = (bf16)0.0f;
   __syncthreads();
 
-  const bf16x8 x0 = *reinterpret_cast<const bf16x8*>(&Xs[fr][8 * fc]);
-  const bf16x8 x1 = *reinterpret_cast<const bf16x8*>(&Xs[fr][32 + 8 * fc]);
-  // each wave's 16 x 16G block of dt is staged in LDS and leaves in row order
+  // each wave's 16 x 16G blocks of dt, one row tile at a time, are staged in LDS and leave
+  // in row order; the W_dt fragments serve every row tile of the workgroup
   constexpr int TP = 16 * kXdtGroup + 4;  // staged row pitch, floats
-  __shared__ __align__(16) float Ts[4][kXdtRows * TP];
+  __shared__ __align__(16) float Ts[4][16 * TP];
   float* tw = Ts[wave];
   auto group = [&](const uint4* ca, const uint4* cb, int g) {
-#pragma unroll
-    for (int i = 0; i < kXdtGroup; ++i) {
-      const int t = g * kXdtGroup + i;
-      const bf16x8 w0 = v0 ? __builtin_bit_cast(bf16x8, ca[i]) : bf16x8{};
-      const bf16x8 w1 = v1 ? __builtin_bit_cast(bf16x8, cb[i]) : bf16x8{};
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w0, x0, acc, 0, 0, 0);
-      if (two) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w1, x1, acc, 0, 0, 0);
-      *reinterpret_cast<f32x4*>(&tw[fr * TP + 16 * i + 4 * fc]) = acc;
-    }
-    // the wave's 16 x 16G block back in row order (LDS operations of one wave run in issue
-    // order): each store instruction covers runs of whole rows
     const int valid = min(kXdtGroup, nt - g * kXdtGroup) * 4;  // float4 columns that exist
 #pragma unroll
-    for (int j = 0; j < kXdtGroup; ++j) {
-      const int idx = j * 64 + lane, r = idx / (4 * kXdtGroup), c4 = idx % (4 * kXdtGroup);
-      const f32x4 v = *reinterpret_cast<const f32x4*>(&tw[r * TP + 4 * c4]);
-      if (m0 + r < M && c4 < valid)
-        *reinterpret_cast<f32x4*>(dt + (int64_t)(m0 + r) * D + (t_beg + g * kXdtGroup) * 16 + 4 * c4) = v;
+    for (int mt = 0; mt < kXdtMT; ++mt) {
+      const bf16x8 x0 = *reinterpret_cast<const bf16x8*>(&Xs[16 * mt + fr][8 * fc]);
+      const bf16x8 x1 = *reinterpret_cast<const bf16x8*>(&Xs[16 * mt + fr][32 + 8 * fc]);
+#pragma unroll
+      for (int i = 0; i < kXdtGroup; ++i) {
+        const bf16x8 w0 = v0 ? __builtin_bit_cast(bf16x8, ca[i]) : bf16x8{};
+        const bf16x8 w1 = v1 ? __builtin_bit_cast(bf16x8, cb[i]) : bf16x8{};
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w0, x0, acc, 0, 0, 0);
+        if (two) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w1, x1, acc, 0, 0, 0);
+        *reinterpret_cast<f32x4*>(&tw[fr * TP + 16 * i + 4 * fc]) = acc;
+      }
+      // the wave's 16 x 16G block back in row order (LDS operations of one wave run in
+      // issue order): each store instruction covers runs of whole rows
+#pragma unroll
+      for (int j = 0; j < kXdtGroup; ++j) {
+        const int idx = j * 64 + lane, r = idx / (4 * kXdtGroup), c4 = idx % (4 * kXdtGroup);
+        const f32x4 v = *reinterpret_cast<const f32x4*>(&tw[r * TP + 4 * c4]);
+        const int row = m0 + 16 * mt + r;
+        if (row < M && c4 < valid)
+          *reinterpret_cast<f32x4*>(dt + (int64_t)row * D + (t_beg + g * kXdtGroup) * 16 + 4 * c4) = v;
+      }
     }
   };
   for (int g = 0; g < ng; ++g) {
