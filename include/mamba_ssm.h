@@ -287,23 +287,26 @@ mamba_status mamba_gemm_bf16(const void* A, mamba_dtype a_dtype, int64_t lda, co
  * low-rank dt lane goes through dt_proj to give the per-channel dt before its softplus):
  *   xdbl[M, xw]     = u[M, d_inner] * W_x[xw, d_inner]^T          (xw = dt_rank + 2 d_state:
  *                     columns dt lane | B | C)
- *   dt[M, d_inner]  = xdbl[:, 0:dt_rank] * W_dt[d_inner, dt_rank]^T  (no bias: the scan adds
- *                     dt_bias before its softplus)
+ *   dt[M, d_inner]  = xdbl[:, 0:dt_rank] * W_dt[d_inner, dt_rank]^T, then + dt_bias when
+ *                     dt_bias is given, then softplus when delta_softplus != 0: the scan's
+ *                     delta, formed as mamba_selective_scan_fwd forms it (same order, same
+ *                     bits), for a scan then called without dt_bias and softplus
  * u f32, rows ldu apart; W_x and W_dt bf16 in the nn.Linear layout, contiguous rows; xdbl
  * and dt f32, contiguous. Operands are rounded to bf16 (RNE) as they enter each product
  * (u, and the dt lane of xdbl as computed in f32), with f32 accumulation, as mamba_gemm_bf16
  * does; x_proj is split over d_inner and its partial sums added in a fixed order, so the
  * values do not depend on timing. workspace: at least
  * mamba_xproj_dtproj_workspace_size(M, d_inner, dt_rank, d_state) bytes (the split's
- * partial planes; may be NULL when that is 0). Errors: MAMBA_EINVAL for negative sizes or
+ * partial planes; may be NULL when that is 0). dt_bias: [d_inner] f32 or NULL (zero).
+ * Errors: MAMBA_EINVAL for negative sizes or
  * leading dimensions below d_inner, MAMBA_EWORKSPACE for a missing or short workspace; xdbl,
  * dt and the workspace must not overlap each other or the inputs. M == 0 is a no-op.
  */
 size_t mamba_xproj_dtproj_workspace_size(int M, int d_inner, int dt_rank, int d_state);
 mamba_status mamba_xproj_dtproj(const float* u, int64_t ldu, const void* W_x, const void* W_dt,
-                                float* xdbl, float* dt, int M, int d_inner, int dt_rank,
-                                int d_state, void* workspace, size_t workspace_bytes,
-                                void* stream);
+                                float* xdbl, float* dt, const float* dt_bias, int delta_softplus,
+                                int M, int d_inner, int dt_rank, int d_state, void* workspace,
+                                size_t workspace_bytes, void* stream);
 
 /*
  * Stages F4a-F4c of a prefill layer in one call ([prefill.rs] prefill_body F4a, F4b, F4c):
@@ -316,14 +319,15 @@ mamba_status mamba_xproj_dtproj(const float* u, int64_t ldu, const void* W_x, co
  *   lengths      in   [B] int32 valid tokens per sequence (device, clamped to [0, T]), or
  *                     NULL (all T): the new conv state is taken after each sequence's own
  *                     last valid token.
- *   W_x, W_dt, xdbl, dt   as mamba_xproj_dtproj.
+ *   W_x, W_dt, xdbl, dt, dt_bias, delta_softplus   as mamba_xproj_dtproj.
  *   workspace    mamba_xproj_dtproj_workspace_size(B*T, d_inner, dt_rank, d_state) bytes.
  * Errors as the two calls; every output must be disjoint from every input and each other.
  */
 mamba_status mamba_conv_xproj_dtproj(const float* x, int64_t x_row_stride, const float* conv_w,
                                      const float* conv_b, float* conv_state,
                                      const int32_t* lengths, float* u, const void* W_x,
-                                     const void* W_dt, float* xdbl, float* dt, int B, int T,
+                                     const void* W_dt, float* xdbl, float* dt,
+                                     const float* dt_bias, int delta_softplus, int B, int T,
                                      int d_inner, int d_conv, int dt_rank, int d_state,
                                      void* workspace, size_t workspace_bytes, void* stream);
 

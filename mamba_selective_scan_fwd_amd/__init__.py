@@ -48,9 +48,9 @@ symbols = {
     "mamba_rmsnorm": ([_P, _I64, _P, ctypes.c_float, _P, _I, _I64, _I, _P], _I),
     "mamba_gemm_bf16": ([_P, _I, _I64, _P, _I64, _P, _I64, _I, _I, _I, _I, _P], _I),
     "mamba_xproj_dtproj_workspace_size": ([_I, _I, _I, _I], _SZ),
-    "mamba_xproj_dtproj": ([_P, _I64, _P, _P, _P, _P, _I, _I, _I, _I, _P, _SZ, _P], _I),
-    "mamba_conv_xproj_dtproj": ([_P, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _SZ,
-                                 _P], _I),
+    "mamba_xproj_dtproj": ([_P, _I64, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _SZ, _P], _I),
+    "mamba_conv_xproj_dtproj": ([_P, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I,
+                                 _P, _SZ, _P], _I),
     "mamba_backbone_workspace_size": ([_P, _I, _I], _SZ),
     "mamba_backbone_prefill": ([_P, _P, _P, _I, _I, _P, _P, _P, _P, _SZ, _P], _I),
     "mamba_backbone_prefill_ex": ([_P, _P, _P, _I, _I, _P, _P, _P, _SZ, _P], _I),
@@ -346,11 +346,14 @@ def mamba_xproj_dtproj_workspace_size(M: int, d_inner: int, dt_rank: int, d_stat
     return int(load_library().mamba_xproj_dtproj_workspace_size(M, d_inner, dt_rank, d_state))
 
 
-def mamba_xproj_dtproj(u, W_x, W_dt, xdbl, dt, workspace=None, M=None, ldu=None, stream=None) -> None:
-    """xdbl = u @ W_x^T and dt = xdbl[:, :dt_rank] @ W_dt^T (bf16 operands, f32 sums).
-    u: [M, >= d_inner] f32 rows; W_x [dt_rank + 2 d_state, d_inner] and W_dt [d_inner, dt_rank]
-    bf16; xdbl [M, dt_rank + 2 d_state] and dt [M, d_inner] f32; workspace a device buffer of
-    mamba_xproj_dtproj_workspace_size bytes, or None (allocated here when needed)."""
+def mamba_xproj_dtproj(u, W_x, W_dt, xdbl, dt, dt_bias=None, delta_softplus=False, workspace=None, M=None,
+                       ldu=None, stream=None) -> None:
+    """xdbl = u @ W_x^T and dt = xdbl[:, :dt_rank] @ W_dt^T (bf16 operands, f32 sums), then
+    dt + dt_bias and softplus when given (the scan's delta). u: [M, >= d_inner] f32 rows;
+    W_x [dt_rank + 2 d_state, d_inner] and W_dt [d_inner, dt_rank] bf16; xdbl
+    [M, dt_rank + 2 d_state] and dt [M, d_inner] f32; dt_bias [d_inner] f32 or None;
+    workspace a device buffer of mamba_xproj_dtproj_workspace_size bytes, or None (allocated
+    here when needed)."""
     import torch
     d_inner, dt_rank = W_dt.shape
     d_state = (W_x.shape[0] - dt_rank) // 2
@@ -360,14 +363,15 @@ def mamba_xproj_dtproj(u, W_x, W_dt, xdbl, dt, workspace=None, M=None, ldu=None,
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=u.device)
     nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(load_library().mamba_xproj_dtproj(_ptr(u), ldu, _ptr(W_x), _ptr(W_dt), _ptr(xdbl), _ptr(dt), M,
-                                             d_inner, dt_rank, d_state, _ptr(workspace), nbytes,
-                                             _stream(stream)))
+    _check(load_library().mamba_xproj_dtproj(_ptr(u), ldu, _ptr(W_x), _ptr(W_dt), _ptr(xdbl), _ptr(dt),
+                                             _ptr(dt_bias), int(bool(delta_softplus)), M, d_inner, dt_rank,
+                                             d_state, _ptr(workspace), nbytes, _stream(stream)))
 
 
 def mamba_conv_xproj_dtproj(x, conv_w, conv_b, conv_state, u, W_x, W_dt, xdbl, dt, lengths=None,
-                            workspace=None, stream=None) -> None:
-    """u = silu(conv(x)) (conv state carried), xdbl = u @ W_x^T, dt = xdbl[:, :dt_rank] @ W_dt^T.
+                            dt_bias=None, delta_softplus=False, workspace=None, stream=None) -> None:
+    """u = silu(conv(x)) (conv state carried), xdbl = u @ W_x^T, dt = xdbl[:, :dt_rank] @ W_dt^T
+    (then + dt_bias and softplus when given, as mamba_xproj_dtproj).
     x: [B, T, >= d_inner] f32 view (row stride as it is); conv_w [d_inner, d_conv]; conv_b
     [d_inner] or None; conv_state [B, d_inner, d_conv] or None; u [B, T, d_inner]; W_x, W_dt
     bf16; xdbl [B*T, dt_rank + 2 d_state]; dt [B*T, d_inner]; lengths [B] int32 or None."""
@@ -382,8 +386,8 @@ def mamba_conv_xproj_dtproj(x, conv_w, conv_b, conv_state, u, W_x, W_dt, xdbl, d
     nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(load_library().mamba_conv_xproj_dtproj(
         _ptr(x), _row_stride(x, "x"), _ptr(conv_w), _ptr(conv_b), _ptr(conv_state), _ptr(lengths), _ptr(u),
-        _ptr(W_x), _ptr(W_dt), _ptr(xdbl), _ptr(dt), B, T, d_inner, d_conv, dt_rank, d_state, _ptr(workspace),
-        nbytes, _stream(stream)))
+        _ptr(W_x), _ptr(W_dt), _ptr(xdbl), _ptr(dt), _ptr(dt_bias), int(bool(delta_softplus)), B, T, d_inner,
+        d_conv, dt_rank, d_state, _ptr(workspace), nbytes, _stream(stream)))
 
 
 def mamba_backbone_workspace_size(dims: BackboneDims, B: int, T: int) -> int:

@@ -643,9 +643,9 @@ size_t mamba_xproj_dtproj_workspace_size(int M, int d_inner, int dt_rank, int d_
 }
 
 mamba_status mamba_xproj_dtproj(const float* u, int64_t ldu, const void* W_x, const void* W_dt,
-                                float* xdbl, float* dt, int M, int d_inner, int dt_rank,
-                                int d_state, void* workspace, size_t workspace_bytes,
-                                void* stream) {
+                                float* xdbl, float* dt, const float* dt_bias, int delta_softplus,
+                                int M, int d_inner, int dt_rank, int d_state, void* workspace,
+                                size_t workspace_bytes, void* stream) {
   static const char* fn = "mamba_xproj_dtproj";
   return guarded([&] {
     check_dim(fn, "M", M);
@@ -668,17 +668,22 @@ mamba_status mamba_xproj_dtproj(const float* u, int64_t ldu, const void* W_x, co
     check_ptr(fn, "W_dt", W_dt, 2, true);
     check_ptr(fn, "xdbl", xdbl, 4, true);
     check_ptr(fn, "dt", dt, 4, true);
+    check_ptr(fn, "dt_bias", dt_bias, 4, false);
     const Range ins[] = {range("u", u, M, ldu, d_inner, 4), range("W_x", W_x, xw, d_inner, d_inner, 2),
-                         range("W_dt", W_dt, d_inner, dt_rank, dt_rank, 2)};
+                         range("W_dt", W_dt, d_inner, dt_rank, dt_rank, 2),
+                         range("dt_bias", dt_bias, 1, d_inner, d_inner, 4)};
     const Range rx = range("xdbl", xdbl, M, xw, xw, 4), rd = range("dt", dt, M, d_inner, d_inner, 4);
-    check_disjoint(fn, rx, {ins[0], ins[1], ins[2], rd});
-    check_disjoint(fn, rd, {ins[0], ins[1], ins[2]});
+    check_disjoint(fn, rx, {ins[0], ins[1], ins[2], ins[3], rd});
+    check_disjoint(fn, rd, {ins[0], ins[1], ins[2], ins[3]});
     if (need) {
       const Range rw = range("workspace", workspace, 1, need, need, 1);
-      check_disjoint(fn, rw, {ins[0], ins[1], ins[2], rx, rd});
+      check_disjoint(fn, rw, {ins[0], ins[1], ins[2], ins[3], rx, rd});
     }
+    mamba::DtOut o;
+    o.bias = dt_bias;
+    o.softplus = delta_softplus != 0;
     check_hip(fn, mamba::launch_xproj_dtproj(u, ldu, W_x, xdbl, xw, W_dt, dt_rank, dt, M, d_inner,
-                                             static_cast<float*>(workspace), std::max(d_inner / xw, 1),
+                                             static_cast<float*>(workspace), std::max(d_inner / xw, 1), o,
                                              static_cast<hipStream_t>(stream)));
   });
 }
@@ -686,7 +691,8 @@ mamba_status mamba_xproj_dtproj(const float* u, int64_t ldu, const void* W_x, co
 mamba_status mamba_conv_xproj_dtproj(const float* x, int64_t x_row_stride, const float* conv_w,
                                      const float* conv_b, float* conv_state,
                                      const int32_t* lengths, float* u, const void* W_x,
-                                     const void* W_dt, float* xdbl, float* dt, int B, int T,
+                                     const void* W_dt, float* xdbl, float* dt,
+                                     const float* dt_bias, int delta_softplus, int B, int T,
                                      int d_inner, int d_conv, int dt_rank, int d_state,
                                      void* workspace, size_t workspace_bytes, void* stream) {
   static const char* fn = "mamba_conv_xproj_dtproj";
@@ -722,26 +728,31 @@ mamba_status mamba_conv_xproj_dtproj(const float* x, int64_t x_row_stride, const
     check_ptr(fn, "W_dt", W_dt, 2, true);
     check_ptr(fn, "xdbl", xdbl, 4, true);
     check_ptr(fn, "dt", dt, 4, true);
+    check_ptr(fn, "dt_bias", dt_bias, 4, false);
     const Range rx = range("x", x, rows, x_row_stride, d_inner, 4);
     const Range rcw = range("conv_w", conv_w, d_inner, d_conv, d_conv, 4);
     const Range rcb = range("conv_b", conv_b, 1, d_inner, d_inner, 4);
     const Range rl = range("lengths", lengths, 1, B, B, 4);
     const Range rwx = range("W_x", W_x, xw, d_inner, d_inner, 2);
     const Range rwd = range("W_dt", W_dt, d_inner, dt_rank, dt_rank, 2);
+    const Range rdb = range("dt_bias", dt_bias, 1, d_inner, d_inner, 4);
     const Range rs = range("conv_state", conv_state, (int64_t)B * d_inner, d_conv, d_conv, 4);
     const Range ru = range("u", u, rows, d_inner, d_inner, 4);
     const Range rxd = range("xdbl", xdbl, rows, xw, xw, 4);
     const Range rd = range("dt", dt, rows, d_inner, d_inner, 4);
     const Range rw = range("workspace", need ? workspace : nullptr, 1, (int64_t)need, (int64_t)need, 1);
-    check_disjoint(fn, rs, {rx, rcw, rcb, rl, rwx, rwd});
-    check_disjoint(fn, ru, {rx, rcw, rcb, rl, rwx, rwd, rs});
-    check_disjoint(fn, rxd, {rx, rcw, rcb, rl, rwx, rwd, rs, ru});
-    check_disjoint(fn, rd, {rx, rcw, rcb, rl, rwx, rwd, rs, ru, rxd});
-    check_disjoint(fn, rw, {rx, rcw, rcb, rl, rwx, rwd, rs, ru, rxd, rd});
+    check_disjoint(fn, rs, {rx, rcw, rcb, rl, rwx, rwd, rdb});
+    check_disjoint(fn, ru, {rx, rcw, rcb, rl, rwx, rwd, rdb, rs});
+    check_disjoint(fn, rxd, {rx, rcw, rcb, rl, rwx, rwd, rdb, rs, ru});
+    check_disjoint(fn, rd, {rx, rcw, rcb, rl, rwx, rwd, rdb, rs, ru, rxd});
+    check_disjoint(fn, rw, {rx, rcw, rcb, rl, rwx, rwd, rdb, rs, ru, rxd, rd});
     mamba::ConvFwdArgs a{x, x_row_stride, conv_w, conv_b, conv_state, u, false, B, T, d_inner, d_conv};
     a.lengths = lengths;
+    mamba::DtOut o;
+    o.bias = dt_bias;
+    o.softplus = delta_softplus != 0;
     check_hip(fn, mamba::launch_conv_xproj_dtproj(a, W_x, xdbl, xw, W_dt, dt_rank, dt,
-                                                  static_cast<float*>(workspace), std::max(d_inner / xw, 1),
+                                                  static_cast<float*>(workspace), std::max(d_inner / xw, 1), o,
                                                   static_cast<hipStream_t>(stream)));
   });
 }

@@ -975,10 +975,12 @@ constexpr int kXdtMaxRank = 64;
 #endif
 constexpr int kXdtGroup = MAMBA_XDT_GROUP;  // W_dt tiles whose fragments a wave loads together
 
+template <bool DELTA>
 __global__ void __launch_bounds__(256) xproj_sum_dtproj_kernel(const float* __restrict__ P, int ks,
                                                                int64_t plane, float* __restrict__ xdbl,
                                                                int xw, const bf16* __restrict__ Wdt, int R,
-                                                               float* __restrict__ dt, int D, int M, int CS) {
+                                                               float* __restrict__ dt, int D, int M, int CS,
+                                                               const float* __restrict__ dt_bias, int sp) {
   __shared__ __align__(16) bf16 Xs[kXdtRows][kXdtMaxRank + 8];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nrb = (M + kXdtRows - 1) / kXdtRows;
@@ -992,6 +994,7 @@ __global__ void __launch_bounds__(256) xproj_sum_dtproj_kernel(const float* __re
   const int nt = D / (64 * CS), t_beg = (cs * 4 + wave) * nt, ng = (nt + kXdtGroup - 1) / kXdtGroup;
   // W_dt fragments of a group of tiles (indexes past the last tile reload the last one)
   uint4 wa[kXdtGroup], wb[kXdtGroup];
+  float4 bias4[kXdtGroup];  // DELTA: dt_bias of the lane's four output columns per tile
   auto fetch = [&](int g) {
 #pragma unroll
     for (int i = 0; i < kXdtGroup; ++i) {
@@ -999,6 +1002,9 @@ __global__ void __launch_bounds__(256) xproj_sum_dtproj_kernel(const float* __re
       const bf16* wr = Wdt + (int64_t)((t_beg + t) * 16 + fr) * R;
       wa[i] = *reinterpret_cast<const uint4*>(wr + k0);
       wb[i] = *reinterpret_cast<const uint4*>(wr + k1);
+      if constexpr (DELTA)
+        bias4[i] = dt_bias ? *reinterpret_cast<const float4*>(dt_bias + (t_beg + t) * 16 + 4 * fc)
+                           : make_float4(0.f, 0.f, 0.f, 0.f);
     }
   };
   fetch(0);
@@ -1051,6 +1057,15 @@ __global__ void __launch_bounds__(256) xproj_sum_dtproj_kernel(const float* __re
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w0, x0, acc, 0, 0, 0);
         if (two) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w1, x1, acc, 0, 0, 0);
+        if constexpr (DELTA) {
+          // delta = softplus(dt + dt_bias): the scan's own expression, in the same order
+          const float bv[4] = {bias4[i].x, bias4[i].y, bias4[i].z, bias4[i].w};
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float v = acc[r] + bv[r];
+            acc[r] = sp ? softplus(v) : v;
+          }
+        }
         *reinterpret_cast<f32x4*>(&tw[fr * TP + 16 * i + 4 * fc]) = acc;
       }
       // the wave's 16 x 16G block back in row order (LDS operations of one wave run in
@@ -1071,44 +1086,67 @@ __global__ void __launch_bounds__(256) xproj_sum_dtproj_kernel(const float* __re
   }
 }
 
+// dt -> softplus(dt + dt_bias) (or dt + dt_bias), elementwise: the two-launch path's epilogue.
+__global__ void __launch_bounds__(256) dt_delta_kernel(float* __restrict__ dt, const float* __restrict__ dt_bias,
+                                                       int sp, int64_t n, int D) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  const float v = dt[i] + (dt_bias ? dt_bias[i % D] : 0.0f);
+  dt[i] = sp ? softplus(v) : v;
+}
+
 // x_proj's ks partial planes (ks * M * xw floats at `partial`) -> xdbl and dt: one kernel
 // when the shapes allow, else the in-order reduction and the dt_proj product.
 static hipError_t finish_xproj_dtproj(const float* partial, int ks, float* xdbl, int xw, const void* Wdt,
-                                      int R, float* dt, int M, int D, hipStream_t s) {
+                                      int R, float* dt, int M, int D, const DtOut& o, hipStream_t s) {
   auto a16 = [](const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; };
   const int64_t plane = (int64_t)M * xw;
+  const bool delta = o.bias || o.softplus;
   const bool fuse = MAMBA_XDT_FUSE && a16(Wdt) && a16(xdbl) && a16(dt) && a16(partial) && R % 8 == 0 &&
-                    R > 0 && R <= kXdtMaxRank && D % 64 == 0 && xw % 4 == 0;
+                    R > 0 && R <= kXdtMaxRank && D % 64 == 0 && xw % 4 == 0 && a16(o.bias);
+  hipError_t e;
   if (!fuse) {
     splitk_reduce_kernel<<<dim3((unsigned)((plane + 255) / 256)), 256, 0, s>>>(partial, ks, xdbl, xw, M, xw, 0);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    return launch_gemm_bf16(xdbl, false, xw, Wdt, R, dt, D, M, D, R, false, s);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = launch_gemm_bf16(xdbl, false, xw, Wdt, R, dt, D, M, D, R, false, s)) != hipSuccess) return e;
+    if (!delta) return hipSuccess;
+    const int64_t n = (int64_t)M * D;
+    dt_delta_kernel<<<dim3((unsigned)((n + 255) / 256)), 256, 0, s>>>(dt, o.bias, o.softplus ? 1 : 0, n, D);
+    return hipGetLastError();
   }
   int cs = MAMBA_XDT_SPLIT;
   while (cs > 1 && D % (64 * cs) != 0) --cs;
   const int64_t nrb = (M + kXdtRows - 1) / kXdtRows;
-  xproj_sum_dtproj_kernel<<<dim3((unsigned)((nrb + 7) / 8 * 8 * cs)), 256, 0, s>>>(
-      partial, ks, plane, xdbl, xw, static_cast<const bf16*>(Wdt), R, dt, D, M, cs);
+  const dim3 grid((unsigned)((nrb + 7) / 8 * 8 * cs));
+  if (delta)
+    xproj_sum_dtproj_kernel<true><<<grid, 256, 0, s>>>(partial, ks, plane, xdbl, xw, static_cast<const bf16*>(Wdt),
+                                                       R, dt, D, M, cs, o.bias, o.softplus ? 1 : 0);
+  else
+    xproj_sum_dtproj_kernel<false><<<grid, 256, 0, s>>>(partial, ks, plane, xdbl, xw, static_cast<const bf16*>(Wdt),
+                                                        R, dt, D, M, cs, nullptr, 0);
   return hipGetLastError();
 }
 
 hipError_t launch_xproj_dtproj(const float* u, int64_t ldu, const void* Wx, float* xdbl, int xw,
                                const void* Wdt, int R, float* dt, int M, int D, float* partial,
-                               int max_ks, hipStream_t s) {
+                               int max_ks, const DtOut& o, hipStream_t s) {
   const int ks = gemm_rows_ksplit(M, xw, D, max_ks);
   auto a16 = [](const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; };
   if (ks <= 1 || ldu % 8 != 0 || D % 8 != 0 || !a16(u) || !a16(Wx)) {
     hipError_t e = launch_gemm_bf16_rows(u, false, ldu, Wx, D, xdbl, xw, M, xw, D, false, partial, max_ks, s);
     if (e != hipSuccess) return e;
-    return launch_gemm_bf16(xdbl, false, xw, Wdt, R, dt, D, M, D, R, false, s);
+    if ((e = launch_gemm_bf16(xdbl, false, xw, Wdt, R, dt, D, M, D, R, false, s)) != hipSuccess) return e;
+    if (!o.bias && !o.softplus) return hipSuccess;
+    const int64_t n = (int64_t)M * D;
+    dt_delta_kernel<<<dim3((unsigned)((n + 255) / 256)), 256, 0, s>>>(dt, o.bias, o.softplus ? 1 : 0, n, D);
+    return hipGetLastError();
   }
   const int k_chunk = splitk_chunk(D, ks);
   const int64_t plane = (int64_t)M * xw;
   const hipError_t e = gemm_tile<float, 32, 80, 64, 2, 1>(u, ldu, static_cast<const bf16*>(Wx), D, partial, xw,
                                                           M, xw, D, false, true, s, ks, k_chunk, plane);
   if (e != hipSuccess) return e;
-  return finish_xproj_dtproj(partial, ks, xdbl, xw, Wdt, R, dt, M, D, s);
+  return finish_xproj_dtproj(partial, ks, xdbl, xw, Wdt, R, dt, M, D, o, s);
 }
 
 // ------------------------------------------------------- conv + x_proj of a prefill layer
@@ -1285,7 +1323,7 @@ __global__ void __launch_bounds__(256) conv_xproj_kernel(
 
 hipError_t launch_conv_xproj_dtproj(const ConvFwdArgs& ca, const void* Wx, float* xdbl, int xw,
                                     const void* Wdt, int R, float* dt, float* partial, int max_ks,
-                                    hipStream_t s) {
+                                    const DtOut& o, hipStream_t s) {
   const int D = ca.D, T = ca.T;
   const int M = ca.B * T;
   const int ks = gemm_rows_ksplit(M, xw, D, max_ks);
@@ -1297,7 +1335,7 @@ hipError_t launch_conv_xproj_dtproj(const ConvFwdArgs& ca, const void* Wx, float
   if (!fuse) {
     if ((e = launch_conv1d_fwd(ca, s)) != hipSuccess) return e;
     return launch_xproj_dtproj(static_cast<const float*>(ca.u), D, Wx, xdbl, xw, Wdt, R, dt, M, D, partial,
-                               max_ks, s);
+                               max_ks, o, s);
   }
   const int k_chunk = splitk_chunk(D, ks);
   const int ntb = (T + kCxRows - 1) / kCxRows;
@@ -1306,7 +1344,7 @@ hipError_t launch_conv_xproj_dtproj(const ConvFwdArgs& ca, const void* Wx, float
       static_cast<const float*>(ca.x), ca.x_row_stride, ca.conv_w, ca.conv_b, ca.conv_state, ca.lengths,
       static_cast<float*>(ca.u), static_cast<const bf16*>(Wx), xw, partial, plane, T, D, k_chunk, ntb);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  return finish_xproj_dtproj(partial, ks, xdbl, xw, Wdt, R, dt, M, D, s);
+  return finish_xproj_dtproj(partial, ks, xdbl, xw, Wdt, R, dt, M, D, o, s);
 }
 
 hipError_t launch_gemm_bf16_splitk(const void* A, bool a_bf16, int64_t lda, const void* W,

@@ -19,6 +19,7 @@ namespace mamba {
 
 static size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+
 struct BackboneLayout {
   size_t h, xn, proj, u, xdbl, dt, y, last, scan, total;
 };
@@ -95,13 +96,14 @@ hipError_t run_backbone_prefill_io(const mamba_backbone_dims& d, const mamba_bac
     // F4a: conv + SiLU over the x lane, carrying this layer's conv state, computed inside
     // F4b: xdbl = u @ x_proj^T   [bt, R + 2N]: dt lane | B | C, split over K, its partial
     // planes in y, which is free until the scan writes it
-    // F4c: dt = xdbl[:, :R] @ dt_proj^T   [bt, D]  (bias applied in the scan), in the
-    // kernel that sums x_proj's planes
+    // F4c: dt = xdbl[:, :R] @ dt_proj^T   [bt, D], in the kernel that sums x_proj's planes.
+    // (The bias and softplus stay in the scan: formed in that kernel's epilogue instead, the
+    // 24-layer step measured 6.18 against 6.16 ms.)
     ConvFwdArgs ca{proj, 2 * D, w.conv_w + (int64_t)l * D * K, w.conv_b + (int64_t)l * D,
                    conv_state + (int64_t)l * B * D * K, u, false, B, T, D, K};
     ca.lengths = io.lengths;
     if ((e = launch_conv_xproj_dtproj(ca, x_proj + (int64_t)l * xw * D, xdbl, xw, dt_proj + (int64_t)l * D * R,
-                                      R, dt, y, D / xw, s)) != hipSuccess) return e;
+                                      R, dt, y, D / xw, DtOut{}, s)) != hipSuccess) return e;
     // F4d: the scan, B/C read in place from xdbl, the gate from the z lane of proj
     ScanFwdArgs sa{u, dt, w.dt_bias + (int64_t)l * D, true, w.A_log + (int64_t)l * D * N,
                    xdbl + R, xdbl + R + N, xw, w.D_skip + (int64_t)l * D, proj + D, 2 * D,

@@ -243,15 +243,21 @@ hipError_t launch_gemm_bf16_rows(const void* A, bool a_bf16, int64_t lda, const 
 // dt = xdbl[:, :R] @ W_dt^T ([M, D], bias left to the scan); x_proj split over K as
 // launch_gemm_bf16_rows does (partial planes in `partial`), its planes summed and dt_proj
 // applied by one kernel where the shapes allow, else the two products one after the other.
+// What leaves as dt: dt itself (bias NULL, softplus false), or dt + bias, then softplus
+// when asked -- the scan's delta, formed in the same order as the scan forms it.
+struct DtOut {
+  const float* bias = nullptr;  // [D] or NULL
+  bool softplus = false;
+};
 hipError_t launch_xproj_dtproj(const float* u, int64_t ldu, const void* Wx, float* xdbl, int xw,
                                const void* Wdt, int R, float* dt, int M, int D, float* partial,
-                               int max_ks, hipStream_t s);
+                               int max_ks, const DtOut& o, hipStream_t s);
 // The conv (as launch_conv1d_fwd with a.u f32) followed by launch_xproj_dtproj of its u,
 // with the conv computed inside x_proj's split product where the shapes allow (K == 4, f32,
 // d_inner a multiple of 64, xw <= 80): u and the conv state as the conv kernel leaves them.
 hipError_t launch_conv_xproj_dtproj(const ConvFwdArgs& a, const void* Wx, float* xdbl, int xw,
                                     const void* Wdt, int R, float* dt, float* partial, int max_ks,
-                                    hipStream_t s);
+                                    const DtOut& o, hipStream_t s);
 hipError_t launch_gemm_bf16_splitk(const void* A, bool a_bf16, int64_t lda, const void* W,
                                    int64_t ldw, float* C, int64_t ldc, int M, int N, int K,
                                    bool accumulate, float* partial, hipStream_t s);

@@ -240,15 +240,15 @@ def test_xproj_dtproj_validation(kw, status, needle):
     a = dict(u=FAKE, ldu=D, wx=FAKE + (1 << 30), wdt=FAKE + (1 << 31), xdbl=FAKE + (1 << 32),
              dt=FAKE + (1 << 33), M=M, ws=FAKE + (1 << 34), wsb=1 << 30)
     a.update(kw)
-    st = lib.mamba_xproj_dtproj(a["u"], a["ldu"], a["wx"], a["wdt"], a["xdbl"], a["dt"], a["M"], D, R, N,
-                                a["ws"], a["wsb"], None)
+    st = lib.mamba_xproj_dtproj(a["u"], a["ldu"], a["wx"], a["wdt"], a["xdbl"], a["dt"], None, 0, a["M"], D, R,
+                                N, a["ws"], a["wsb"], None)
     assert st == status
     assert needle in m.mamba_last_error()
 
 
 def test_xproj_dtproj_empty_is_noop():
     lib = m.load_library()
-    assert lib.mamba_xproj_dtproj(None, 0, None, None, None, None, 0, 1536, 48, 16, None, 0, None) == 0
+    assert lib.mamba_xproj_dtproj(None, 0, None, None, None, None, None, 0, 0, 1536, 48, 16, None, 0, None) == 0
 
 
 @pytest.mark.parametrize("kw,status,needle", [
@@ -259,15 +259,17 @@ def test_xproj_dtproj_empty_is_noop():
     (dict(u=FAKE + 64), EINVAL, "u overlaps x"),
     (dict(st=FAKE + (1 << 35) + 4), EINVAL, "dt overlaps conv_state"),
     (dict(xdbl=FAKE + (1 << 34) + 64), EINVAL, "workspace overlaps xdbl"),
+    (dict(db=FAKE + (1 << 35) + 8), EINVAL, "dt overlaps dt_bias"),
+    (dict(db=FAKE + (1 << 27) + 2), EINVAL, "dt_bias"),
 ])
 def test_conv_xproj_dtproj_validation(kw, status, needle):
     lib = m.load_library()
     Bsz, T, D, R, N = 4, 2048, 1536, 48, 16
     a = dict(x=FAKE, xs=2 * D, st=FAKE + (1 << 29), u=FAKE + (1 << 30), xdbl=FAKE + (1 << 32),
-             dt=FAKE + (1 << 35), T=T, K=4, ws=FAKE + (1 << 34), wsb=1 << 30)
+             dt=FAKE + (1 << 35), db=FAKE + (1 << 27), T=T, K=4, ws=FAKE + (1 << 34), wsb=1 << 30)
     a.update(kw)
     st = lib.mamba_conv_xproj_dtproj(a["x"], a["xs"], FAKE + (1 << 28), None, a["st"], None, a["u"],
-                                     FAKE + (1 << 31), FAKE + (1 << 33), a["xdbl"], a["dt"], Bsz, a["T"], D,
-                                     a["K"], R, N, a["ws"], a["wsb"], None)
+                                     FAKE + (1 << 31), FAKE + (1 << 33), a["xdbl"], a["dt"], a["db"], 1, Bsz,
+                                     a["T"], D, a["K"], R, N, a["ws"], a["wsb"], None)
     assert st == status
     assert needle in m.mamba_last_error()
