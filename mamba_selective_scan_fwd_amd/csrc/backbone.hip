@@ -69,8 +69,9 @@ __global__ void __launch_bounds__(256) rmsnorm_rows_kernel(const float* __restri
   const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (r >= rows) return;  // whole waves
   const float* xr = x + r * x_row_stride;
-  float v[4][KMAX];
+  float v[4][KMAX], wv[4][KMAX];
   float ss[4];
+  // the row and the weights are all loaded before the first use, so the wave waits once
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     ss[q] = 0.0f;
@@ -78,6 +79,7 @@ __global__ void __launch_bounds__(256) rmsnorm_rows_kernel(const float* __restri
     for (int k = 0; k < KMAX; ++k) {
       const int c = q * 64 + lane + 256 * k;
       v[q][k] = c < Dm ? xr[c] : 0.0f;
+      wv[q][k] = w && c < Dm ? w[c] : 1.0f;
     }
   }
 #pragma unroll
@@ -96,7 +98,7 @@ __global__ void __launch_bounds__(256) rmsnorm_rows_kernel(const float* __restri
 #pragma unroll
     for (int k = 0; k < KMAX; ++k) {
       const int c = q * 64 + lane + 256 * k;
-      if (c < Dm) o[c] = from_f32<OT>(v[q][k] * inv * (w ? w[c] : 1.0f));
+      if (c < Dm) o[c] = from_f32<OT>(v[q][k] * inv * wv[q][k]);
     }
 }
 
@@ -1367,9 +1369,64 @@ hipError_t launch_gemm_bf16_splitk(const void* A, bool a_bf16, int64_t lda, cons
 
 // h[r] += the out_proj partials (if any), then RMSNorm of the new h[r] (bf16 out). The
 // arithmetic is that of rmsnorm_kernel applied after a split-K reduction with accumulate.
+// A thread's KMAX elements of the row, their partial-plane values and weights are all loaded
+// before the first use, so the block waits on memory once.
+template <int KMAX>
 __global__ void __launch_bounds__(256) residual_rmsnorm_kernel(float* __restrict__ h, PartsView add,
                                                                const float* __restrict__ w, float eps,
                                                                bf16* __restrict__ out, int Dm) {
+  __shared__ float part[8];
+  const int64_t r = blockIdx.x;
+  float* hr = h + r * Dm;
+  const int ks = add.ks;
+  // Every load is issued unconditionally (addresses clamped into the row, the first plane or
+  // the row itself standing in for a missing one) and the values are selected at their use:
+  // loads under conditions make the wave wait for each one in turn.
+  const float* pp = ks > 0 ? add.p + r * add.ld : hr;
+  const int64_t pz = ks > 0 ? add.plane : 0;
+  const float* wp = w ? w : hr;
+  float v[KMAX], wv[KMAX], pv[kSplitKMaxSlices][KMAX];
+#pragma unroll
+  for (int k = 0; k < KMAX; ++k) {
+    const int c = min((int)threadIdx.x + 256 * k, Dm - 1);
+    v[k] = hr[c];
+    wv[k] = wp[c];
+#pragma unroll
+    for (int z = 0; z < kSplitKMaxSlices; ++z) pv[z][k] = pp[min(z, max(ks - 1, 0)) * pz + c];
+  }
+  float ss = 0.0f;
+#pragma unroll
+  for (int k = 0; k < KMAX; ++k) {
+    const int c = threadIdx.x + 256 * k;
+    if (c >= Dm) break;
+    if (!w) wv[k] = 1.0f;
+    if (ks > 0) {
+      float sum = 0.0f;  // the planes in slice order, as PartsView::at adds them
+#pragma unroll
+      for (int z = 0; z < kSplitKMaxSlices; ++z)
+        if (z < ks) sum += pv[z][k];
+      v[k] = v[k] + sum;
+      hr[c] = v[k];
+    }
+    ss = fmaf(v[k], v[k], ss);
+  }
+  for (int m = 32; m >= 1; m /= 2) ss += __shfl_xor(ss, m);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  const float tot = part[0] + part[1] + part[2] + part[3];
+  const float inv = 1.0f / sqrtf(tot / (float)Dm + eps);
+  bf16* o = out + r * Dm;
+#pragma unroll
+  for (int k = 0; k < KMAX; ++k) {
+    const int c = threadIdx.x + 256 * k;
+    if (c < Dm) o[c] = (bf16)(v[k] * inv * wv[k]);
+  }
+}
+
+// The same for rows wider than 8 * 256: the planes added element by element.
+__global__ void __launch_bounds__(256) residual_rmsnorm_wide_kernel(float* __restrict__ h, PartsView add,
+                                                                    const float* __restrict__ w, float eps,
+                                                                    bf16* __restrict__ out, int Dm) {
   __shared__ float part[8];
   const int64_t r = blockIdx.x;
   float* hr = h + r * Dm;
@@ -1614,7 +1671,13 @@ __global__ void __launch_bounds__(256) decode_ssm_kernel(
 
 hipError_t launch_residual_rmsnorm(float* h, const PartsView& add, const float* w, float eps, void* out,
                                    int rows, int Dm, hipStream_t s) {
-  residual_rmsnorm_kernel<<<dim3((unsigned)rows), 256, 0, s>>>(h, add, w, eps, static_cast<bf16*>(out), Dm);
+  const dim3 grid((unsigned)rows);
+  if (add.ks > kSplitKMaxSlices || Dm > 8 * 256)
+    residual_rmsnorm_wide_kernel<<<grid, 256, 0, s>>>(h, add, w, eps, static_cast<bf16*>(out), Dm);
+  else if (Dm <= 3 * 256)
+    residual_rmsnorm_kernel<3><<<grid, 256, 0, s>>>(h, add, w, eps, static_cast<bf16*>(out), Dm);
+  else
+    residual_rmsnorm_kernel<8><<<grid, 256, 0, s>>>(h, add, w, eps, static_cast<bf16*>(out), Dm);
   return hipGetLastError();
 }
 
