@@ -1493,10 +1493,20 @@ __global__ void __launch_bounds__(256) decode_conv_xproj_kernel(
     PartsView xin, const float* __restrict__ conv_w, const float* __restrict__ conv_b,
     float* __restrict__ conv_state, float* __restrict__ u, const bf16* __restrict__ Wx, int xw,
     float* __restrict__ part, int B, int D, int K) {
-  __shared__ float s_u[kConvXRows][kConvXC];
+  __shared__ __align__(16) float s_u[kConvXRows][kConvXC];
   const int sl = blockIdx.x, d0 = sl * kConvXC;
   const int b0 = blockIdx.y * kConvXRows;
   const int rows = min(kConvXRows, B - b0);
+  // x_proj: thread n takes output column n for all the group's sequences, so each W_x row
+  // slice is loaded once per workgroup; the slice of its first column is loaded here, before
+  // the conv step, so that its latency overlaps the conv step's loads
+  constexpr int kCh8 = kConvXC / 8;
+  uint4 wpre[kCh8];
+  {
+    const bf16* wr = Wx + (int64_t)min((int)threadIdx.x, xw - 1) * D + d0;
+#pragma unroll
+    for (int c = 0; c < kCh8; ++c) wpre[c] = *reinterpret_cast<const uint4*>(wr + 8 * c);
+  }
   for (int i = threadIdx.x; i < rows * kConvXC; i += 256) {
     const int bl = i / kConvXC, c = i % kConvXC, b = b0 + bl, d = d0 + c;
     float* st = conv_state + ((int64_t)b * D + d) * K;
@@ -1523,35 +1533,46 @@ __global__ void __launch_bounds__(256) decode_conv_xproj_kernel(
     s_u[bl][c] = to_f32(from_f32<bf16>(uv));
   }
   __syncthreads();
-  // the thread's outputs o = tid, tid + 256, ... advance together (independent chains); each
-  // output still sums its channels in order
+  // each output sums its channels in order
   const int64_t plane = (int64_t)B * xw;
-  const int nout = rows * xw;
-  for (int o0 = threadIdx.x; o0 < nout; o0 += kConvXOut * 256) {
-    float acc[kConvXOut];
-    const bf16* wr[kConvXOut];
-    int bl[kConvXOut];
+  for (int n = threadIdx.x; n < xw; n += 256) {
+    uint4 w8[kCh8];
+    if (n == (int)threadIdx.x) {
 #pragma unroll
-    for (int j = 0; j < kConvXOut; ++j) {
-      const int o = min(o0 + j * 256, nout - 1);  // (clamped; results past nout are not stored)
-      bl[j] = o / xw;
-      wr[j] = Wx + (int64_t)(o % xw) * D + d0;
-      acc[j] = 0.0f;
+      for (int c = 0; c < kCh8; ++c) w8[c] = wpre[c];
+    } else {
+      const bf16* wr = Wx + (int64_t)n * D + d0;
+#pragma unroll
+      for (int c = 0; c < kCh8; ++c) w8[c] = *reinterpret_cast<const uint4*>(wr + 8 * c);
     }
-    for (int c = 0; c < kConvXC; c += 8) {
-      bf16x8 w8[kConvXOut];
+    float acc[kConvXRows];
 #pragma unroll
-      for (int j = 0; j < kConvXOut; ++j) w8[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(wr[j] + c));
+    for (int bl = 0; bl < kConvXRows; ++bl) acc[bl] = 0.0f;
+    // (a rolled loop over the 8-channel chunks, the W chunks shifted down the register array,
+    // keeps the register count low)
+#pragma unroll 1
+    for (int c = 0; c < kCh8; ++c) {
+      const bf16x8 wv = __builtin_bit_cast(bf16x8, w8[0]);
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
+      for (int k = 0; k + 1 < kCh8; ++k) w8[k] = w8[k + 1];
+      float uq[kConvXRows][8];
 #pragma unroll
-        for (int j = 0; j < kConvXOut; ++j) acc[j] = fmaf(s_u[bl[j]][c + i], to_f32(w8[j][i]), acc[j]);
+      for (int bl = 0; bl < kConvXRows; ++bl) {
+        const float4 lo = *reinterpret_cast<const float4*>(&s_u[bl][8 * c]);
+        const float4 hi = *reinterpret_cast<const float4*>(&s_u[bl][8 * c + 4]);
+        uq[bl][0] = lo.x; uq[bl][1] = lo.y; uq[bl][2] = lo.z; uq[bl][3] = lo.w;
+        uq[bl][4] = hi.x; uq[bl][5] = hi.y; uq[bl][6] = hi.z; uq[bl][7] = hi.w;
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float wf = to_f32(wv[i]);
+#pragma unroll
+        for (int bl = 0; bl < kConvXRows; ++bl) acc[bl] = fmaf(uq[bl][i], wf, acc[bl]);
+      }
     }
 #pragma unroll
-    for (int j = 0; j < kConvXOut; ++j) {
-      const int o = o0 + j * 256;
-      if (o < nout) part[(int64_t)sl * plane + (int64_t)(b0 + o / xw) * xw + o % xw] = acc[j];
-    }
+    for (int bl = 0; bl < kConvXRows; ++bl)
+      if (bl < rows) part[(int64_t)sl * plane + (int64_t)(b0 + bl) * xw + n] = acc[bl];
   }
 }
 
