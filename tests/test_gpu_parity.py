@@ -135,6 +135,9 @@ FUSED_EQ = [
     (3, 2, 64, 16, 4, "f32", False),
     (2, 1500, 192, 16, 4, "bf16", True),
     (1, 1024, 64, 64, 8, "bf16", False),
+    # several chunks with a partial last block, and a partial channel group as well
+    (2, 1003, 96, 16, 4, "f32", False),
+    (1, 700, 80, 16, 4, "f32", True),
 ]
 
 
