@@ -247,6 +247,25 @@ __device__ __forceinline__ bf16x8 load_chunk_scalar(const AT* row, int k0, int K
 #define MAMBA_GEMM_LDS_EPI 1  // write C through LDS as rows of float4 (1) or from the fragments (0)
 #endif
 
+// XCD-aware tile order: the (column tile, row tile) this workgroup takes. See gemm_mfma_kernel.
+__device__ __forceinline__ void xcd_tile_order(int& bx, int& by) {
+  const int gx = gridDim.x, gy = gridDim.y, G = gx * gy;
+  const int L = blockIdx.x + gx * blockIdx.y;
+  const int xcd = L % 8, idx = L / 8, base = G / 8, rem = G % 8;
+  const int t = xcd * base + min(xcd, rem) + idx;  // a bijection of [0, G)
+  constexpr int kGroupN = 8;
+  const int full = (gx / kGroupN) * kGroupN * gy;  // tiles in whole groups
+  if (t < full) {
+    const int g = t / (kGroupN * gy), r = t % (kGroupN * gy);
+    by = r / kGroupN;
+    bx = g * kGroupN + r % kGroupN;
+  } else {
+    const int w = gx % kGroupN, r = t - full;  // the last, narrower group
+    by = r / w;
+    bx = gx - w + r % w;
+  }
+}
+
 template <typename AT, int BM, int BN, int BK, int WGM, int WGN, bool VEC, bool DL>
 __global__ void __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(MAMBA_GEMM_WPE)))
 gemm_mfma_kernel(
@@ -263,23 +282,7 @@ gemm_mfma_kernel(
   // fetched again for each row block.
   // (Split-K launches keep the plain order: their slices share no operand rows.)
   int bx = blockIdx.x, by = blockIdx.y, bz = blockIdx.z;
-  if (gridDim.z == 1) {
-    const int gx = gridDim.x, gy = gridDim.y, G = gx * gy;
-    const int L = blockIdx.x + gx * blockIdx.y;
-    const int xcd = L % 8, idx = L / 8, base = G / 8, rem = G % 8;
-    const int t = xcd * base + min(xcd, rem) + idx;  // a bijection of [0, G)
-    constexpr int kGroupN = 8;
-    const int full = (gx / kGroupN) * kGroupN * gy;  // tiles in whole groups
-    if (t < full) {
-      const int g = t / (kGroupN * gy), r = t % (kGroupN * gy);
-      by = r / kGroupN;
-      bx = g * kGroupN + r % kGroupN;
-    } else {
-      const int w = gx % kGroupN, r = t - full;  // the last, narrower group
-      by = r / w;
-      bx = gx - w + r % w;
-    }
-  }
+  if (gridDim.z == 1) xcd_tile_order(bx, by);
   // split K (gridDim.z > 1): slice z covers k in [z * k_chunk, z * k_chunk + k_chunk) and
   // writes its partial product to its own C plane (C + z * c_split_stride)
   {

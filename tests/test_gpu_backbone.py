@@ -49,6 +49,12 @@ GEMM_CASES = [
     (64, 50280, 768, "bf16", False),   # the head at B = 64
     (4100, 768, 1536, "bf16", True),   # out_proj + residual at a prefill's row count, ragged M
     (4096, 1000, 256, "f32", False),   # many rows, a narrow ragged N
+    # plain bf16 products over many rows: ragged M and N, and K of one, two and three 32-k
+    # steps (direct LDS staging only for whole 64-k slabs)
+    (4100, 3000, 768, "bf16", False),
+    (4096, 256, 32, "bf16", False),
+    (4096, 384, 64, "bf16", False),
+    (4224, 640, 96, "bf16", False),
 ]
 
 
