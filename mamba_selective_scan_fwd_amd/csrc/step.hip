@@ -105,7 +105,9 @@ static hipError_t launch_step_nq(const SsmStepArgs& a, hipStream_t s) {
   const dim3 grid((unsigned)(((int64_t)a.D * NQ + 255) / 256), (unsigned)(a.L * a.B));
   const size_t es = sizeof(IO);
   // 16-byte state / A_log rows and 4-element aligned B/C rows
-  const bool vec = a.N % 4 == 0 && a.bc_row_stride % 4 == 0 &&
+  // (16-byte paths only when the NQ lanes' four states each cover exactly N: with N = 12 or
+  // 24, say, NQ rounds up and the last lanes would reach into the next channel's row)
+  const bool vec = a.N == 4 * NQ && a.bc_row_stride % 4 == 0 &&
                    ((reinterpret_cast<uintptr_t>(a.state) | reinterpret_cast<uintptr_t>(a.A_log)) & 15) == 0 &&
                    ((reinterpret_cast<uintptr_t>(a.Bm) | reinterpret_cast<uintptr_t>(a.Cm)) % (4 * es)) == 0;
   if (vec) {
@@ -249,14 +251,118 @@ __global__ void __launch_bounds__(256) decode_step_kernel(const DecodeStepArgs a
   }
 }
 
+// The fused step for 4-tap convs with 16-byte state rows (the common case). Every load of the
+// thread -- the layer's parameters, then the conv state, x, dt, z, SSM state, B and C of all
+// R rows -- is issued before any arithmetic or store, so all of a thread's traffic is in
+// flight at once. (In decode_step_kernel the compiler keeps each row's loads behind the
+// previous row's state stores, which it cannot prove do not alias them, and waits for each
+// group of loads in turn.) Optional inputs are read from a valid stand-in address when absent
+// and their values dropped at the use, so no load sits under a branch. The arithmetic is
+// decode_step_kernel's, in the same order: the results are the same bits.
+template <typename IO, int NQ, int R>
+__global__ void __launch_bounds__(256) decode_step_k4_kernel(const DecodeStepArgs a) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  const int d = t / NQ;
+  const int q = t % NQ;
+  const int D = a.D, N = a.N;
+  if (d >= D) return;  // whole NQ-lane groups drop out together
+  const int lb0 = blockIdx.y * R;  // R consecutive (layer, batch) rows of one layer
+  const int l = lb0 / a.B;
+  const int64_t ld = (int64_t)l * D + d;
+  const int n0 = 4 * q;
+  const IO* __restrict__ x = static_cast<const IO*>(a.x);
+  const IO* __restrict__ dt = static_cast<const IO*>(a.dt);
+  const IO* __restrict__ zb = a.z ? static_cast<const IO*>(a.z) : x;
+  const int64_t zs = a.z ? a.z_row_stride : a.x_row_stride;
+  const float* __restrict__ wrow = a.conv_w + ld * 4;
+
+  // the layer's parameters
+  const float4 wv = *reinterpret_cast<const float4*>(wrow);
+  const float cb_l = *(a.conv_b ? a.conv_b + ld : wrow);
+  const float bias_l = *(a.dt_bias ? a.dt_bias + ld : wrow);
+  const float dskip_l = *(a.D_skip ? a.D_skip + ld : wrow);
+  const float4 av = *reinterpret_cast<const float4*>(a.A_log + ld * N + n0);
+  // the rows' inputs and states
+  float4 cs[R], hv[R];
+  IO xr[R], dtr[R], zr[R];
+  float bv[R][4], cv[R][4];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int lb = lb0 + r;
+    const int64_t ch = (int64_t)lb * D + d;
+    cs[r] = load_stream4(a.conv_state + ch * 4);
+    xr[r] = x[(int64_t)lb * a.x_row_stride + d];
+    dtr[r] = dt[ch];
+    zr[r] = zb[(int64_t)lb * zs + d];
+    hv[r] = load_stream4(a.ssm_state + ch * N + n0);
+    load4<IO, true>(static_cast<const IO*>(a.Bm) + (int64_t)lb * a.bc_row_stride, n0, N, bv[r]);
+    load4<IO, true>(static_cast<const IO*>(a.Cm) + (int64_t)lb * a.bc_row_stride, n0, N, cv[r]);
+  }
+
+  const float wk[4] = {wv.x, wv.y, wv.z, wv.w};
+  const float cb = a.conv_b ? cb_l : 0.0f;
+  const float bias = a.dt_bias ? bias_l : 0.0f;
+  const float dskip = a.D_skip ? dskip_l : 0.0f;
+  float a2[4];
+  {
+    const float alog[4] = {av.x, av.y, av.z, av.w};
+    // A * log2(e), A = -exp(A_log)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) a2[j] = -__builtin_amdgcn_exp2f(alog[j] * kLog2e) * kLog2e;
+  }
+
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int lb = lb0 + r;
+    const int64_t ch = (int64_t)lb * D + d;
+
+    // conv: shift register of the last 4 raw inputs, oldest first
+    const float sreg[4] = {cs[r].y, cs[r].z, cs[r].w, to_f32(xr[r])};
+    float c = cb;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) c = fmaf(wk[k], sreg[k], c);
+    if (q == 0) store_stream4(a.conv_state + ch * 4, make_float4(sreg[0], sreg[1], sreg[2], sreg[3]));
+    const float uv = silu(c);
+    if (q == 0 && a.u) static_cast<IO*>(a.u)[ch] = from_f32<IO>(uv);
+    // an IO-typed u feeds the SSM, as with the two separate calls
+    const float us = to_f32(from_f32<IO>(uv));
+
+    const float v = to_f32(dtr[r]) + bias;
+    const float delta = a.delta_softplus ? softplus(v) : v;
+    const float du = delta * us;
+
+    float h[4] = {hv[r].x, hv[r].y, hv[r].z, hv[r].w};
+    float part = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float ad = __builtin_amdgcn_exp2f(delta * a2[j]);
+      h[j] = fmaf(ad, h[j], du * bv[r][j]);
+      part = fmaf(cv[r][j], h[j], part);
+    }
+    store_stream4(a.ssm_state + ch * N + n0, make_float4(h[0], h[1], h[2], h[3]));
+#pragma unroll
+    for (int m = NQ / 2; m >= 1; m /= 2) part += __shfl_xor(part, m, NQ);
+    if (q == 0) {
+      float yv = fmaf(dskip, us, part);
+      if (a.z) yv *= silu(to_f32(zr[r]));
+      static_cast<IO*>(a.y)[ch] = from_f32<IO>(yv);
+    }
+  }
+}
+
 #ifndef MAMBA_DECODE_ROWS
 #define MAMBA_DECODE_ROWS 2  // (layer, batch) rows per thread when B allows
+#endif
+#ifndef MAMBA_DECODE_K4
+#define MAMBA_DECODE_K4 1  // the 4-tap kernel with every load issued first (1) or the general one (0)
 #endif
 
 template <typename IO, int NQ, int R>
 static hipError_t launch_decode_nqr(const DecodeStepArgs& a, bool vec, hipStream_t s) {
   const dim3 grid((unsigned)(((int64_t)a.D * NQ + 255) / 256), (unsigned)(a.L * a.B / R));
-  if (vec)
+  if (vec && a.K == 4 && MAMBA_DECODE_K4 != 0)
+    decode_step_k4_kernel<IO, NQ, R><<<grid, 256, 0, s>>>(a);
+  else if (vec)
     decode_step_kernel<IO, NQ, true, R><<<grid, 256, 0, s>>>(a);
   else
     decode_step_kernel<IO, NQ, false, R><<<grid, 256, 0, s>>>(a);
@@ -266,7 +372,9 @@ static hipError_t launch_decode_nqr(const DecodeStepArgs& a, bool vec, hipStream
 template <typename IO, int NQ>
 static hipError_t launch_decode_nq(const DecodeStepArgs& a, hipStream_t s) {
   const size_t es = sizeof(IO);
-  const bool vec = a.N % 4 == 0 && a.bc_row_stride % 4 == 0 &&
+  // (16-byte paths only when the NQ lanes' four states each cover exactly N: with N = 12 or
+  // 24, say, NQ rounds up and the last lanes would reach into the next channel's row)
+  const bool vec = a.N == 4 * NQ && a.bc_row_stride % 4 == 0 &&
                    ((reinterpret_cast<uintptr_t>(a.ssm_state) | reinterpret_cast<uintptr_t>(a.A_log) |
                      reinterpret_cast<uintptr_t>(a.conv_state) | reinterpret_cast<uintptr_t>(a.conv_w)) & 15) == 0 &&
                    ((reinterpret_cast<uintptr_t>(a.Bm) | reinterpret_cast<uintptr_t>(a.Cm)) % (4 * es)) == 0;

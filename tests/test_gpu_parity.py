@@ -316,13 +316,16 @@ def _decode_run(shape: W.DecodeShape, steps: int, seed=0, fused=False):
 
 
 @pytest.mark.parametrize("fused", [False, True])
-def test_decode_steps_small_full_check(fused):
-    _say(f"case decode L2 B3 D100 N16 30 steps fused={fused}")
-    shape = W.DecodeShape("d", L=2, B=3, D=100, N=16, K=4, steps=30)
+@pytest.mark.parametrize("N,Bsz", [(16, 3), (12, 4), (24, 3)])
+def test_decode_steps_small_full_check(fused, N, Bsz):
+    """Every step checked against the oracle; d_state 12 and 24 are multiples of 4 whose lane
+    count per channel (3, 6) rounds up, so some lanes hold no state."""
+    _say(f"case decode L2 B{Bsz} D100 N{N} 30 steps fused={fused}")
+    shape = W.DecodeShape("d", L=2, B=Bsz, D=100, N=N, K=4, steps=30)
     P, ins, ys, us, cs, hs = _decode_run(shape, 30, fused=fused)
     for l in range(2):
-        c_ref = np.zeros((3, 100, 4))
-        h_ref = np.zeros((3, 100, 16))
+        c_ref = np.zeros((Bsz, 100, 4))
+        h_ref = np.zeros((Bsz, 100, N))
         for t in range(30):
             i = ins[t]
             u_ref, c_ref = oracle.conv1d_step(i["x"][l], P["conv_w"][l], P["conv_b"][l], c_ref)
@@ -335,7 +338,8 @@ def test_decode_steps_small_full_check(fused):
 
 
 @pytest.mark.parametrize("io,N,K,strided", [("f32", 16, 4, False), ("bf16", 16, 4, True),
-                                             ("f32", 5, 3, True), ("bf16", 64, 8, False)])
+                                             ("f32", 5, 3, True), ("bf16", 64, 8, False),
+                                             ("f32", 24, 4, False), ("bf16", 12, 4, True)])
 def test_fused_decode_equals_two_calls(io, N, K, strided):
     """mamba_decode_step computes exactly what mamba_conv1d_step then mamba_ssm_step compute
     (same operations in the same order; bf16 u rounded as the two calls store it), including
