@@ -107,23 +107,25 @@ __global__ void __launch_bounds__(256) conv1d_fwd_kernel(
   }
 
   IO* ub = u + (int64_t)b * T * D + d0;
-  float cur[kConvTB][V], nxt[kConvTB][V];
+  // Two register sets, used in turn: the rows of block tb+kConvTB are loaded before block tb
+  // is computed. No load carries a condition (rows past the tile re-read its last row), no
+  // loaded register is copied, and the loop has no early exit (tokens past the tile are
+  // computed and not stored; the window has served its last token by then): a load under a
+  // branch, a copy of a register still being loaded, or paths merging after an exit make the
+  // wave wait for the prefetch as well.
+  float ra[kConvTB][V], rb[kConvTB][V];
+  auto load_block = [&](int tb, float (&r)[kConvTB][V]) {
 #pragma unroll
-  for (int j = 0; j < kConvTB; ++j) Vec<IO, V>::load(cur[j], xb + (int64_t)min(t0 + j, t1 - 1) * x_row_stride);
-  for (int tb = t0; tb < t1; tb += kConvTB) {
-    if (tb + kConvTB < t1) {
-#pragma unroll
-      for (int j = 0; j < kConvTB; ++j)
-        Vec<IO, V>::load(nxt[j], xb + (int64_t)min(tb + kConvTB + j, t1 - 1) * x_row_stride);
-    }
+    for (int j = 0; j < kConvTB; ++j) Vec<IO, V>::load(r[j], xb + (int64_t)min(tb + j, t1 - 1) * x_row_stride);
+  };
+  auto conv_block = [&](int tb, const float (&r)[kConvTB][V]) {
 #pragma unroll
     for (int j = 0; j < kConvTB; ++j) {
       const int t = tb + j;
-      if (t >= t1) break;
       float out[V];
 #pragma unroll
       for (int v = 0; v < V; ++v) {
-        win[v][K - 1] = cur[j][v];
+        win[v][K - 1] = r[j][v];
         float c = bias[v];
 #pragma unroll
         for (int k = 0; k < K; ++k) c = fmaf(w[v][k], win[v][k], c);
@@ -131,12 +133,15 @@ __global__ void __launch_bounds__(256) conv1d_fwd_kernel(
 #pragma unroll
         for (int i = 0; i + 1 < K; ++i) win[v][i] = win[v][i + 1];
       }
-      Vec<IO, V>::store(ub + (int64_t)t * D, out);
+      if (t < t1) Vec<IO, V>::store(ub + (int64_t)t * D, out);
     }
-#pragma unroll
-    for (int j = 0; j < kConvTB; ++j)
-#pragma unroll
-      for (int v = 0; v < V; ++v) cur[j][v] = nxt[j][v];
+  };
+  load_block(t0, ra);
+  for (int tb = t0; tb < t1; tb += 2 * kConvTB) {
+    load_block(tb + kConvTB, rb);
+    conv_block(tb, ra);
+    load_block(tb + 2 * kConvTB, ra);
+    conv_block(tb + kConvTB, rb);
   }
 
   if (t0 == 0 && st) {
