@@ -181,11 +181,14 @@ __global__ void __launch_bounds__(256) conv1d_step_kernel(
   float s[K];
   if constexpr (VEC) {
     static_assert(K == 4, "vector path is for K == 4");
+    // (every load first, none under a condition: an absent bias is read from the taps)
     const float4 v = *reinterpret_cast<const float4*>(st);
     const float4 wv = *reinterpret_cast<const float4*>(w);
+    const IO xr = x[(int64_t)lb * x_row_stride + d];
+    const float cb = *(conv_b ? conv_b + (int64_t)l * D + d : w);
     s[0] = v.y; s[1] = v.z; s[2] = v.w;
-    s[3] = to_f32(x[(int64_t)lb * x_row_stride + d]);
-    float c = conv_b ? conv_b[(int64_t)l * D + d] : 0.0f;
+    s[3] = to_f32(xr);
+    float c = conv_b ? cb : 0.0f;
     c = fmaf(wv.x, s[0], c);
     c = fmaf(wv.y, s[1], c);
     c = fmaf(wv.z, s[2], c);

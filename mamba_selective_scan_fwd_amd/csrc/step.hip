@@ -51,15 +51,17 @@ __global__ void __launch_bounds__(256) ssm_step_kernel(
   const int64_t ch = (int64_t)lb * D + d;
   const int64_t ld = (int64_t)l * D + d;
 
-  const float uv = to_f32(u[ch]);
-  const float v = to_f32(dt[ch]) + (dt_bias ? dt_bias[ld] : 0.0f);
-  const float delta = delta_softplus ? softplus(v) : v;
-  const float du = delta * uv;
-
+  // Every load is issued before any value is used, and none under a condition (absent
+  // vectors are read from a stand-in address and dropped at the use), so a thread's traffic
+  // is in flight at once.
   float* hs = state + ch * N;
   const float* al = A_log + ld * N;
   const int n0 = 4 * q;
-
+  const IO u_raw = u[ch];
+  const IO dt_raw = dt[ch];
+  const float bias_v = *(dt_bias ? dt_bias + ld : al);
+  const float dskip_v = *(D_skip ? D_skip + ld : al);
+  const IO z_raw = *(z ? z + (int64_t)lb * z_row_stride + d : u + ch);
   float h[4], alog[4], bv[4], cv[4];
   if constexpr (VEC) {
     const float4 hv = load_stream4(hs + n0);
@@ -75,6 +77,11 @@ __global__ void __launch_bounds__(256) ssm_step_kernel(
   }
   load4<IO, VEC>(Bm + (int64_t)lb * bc_row_stride, n0, N, bv);
   load4<IO, VEC>(Cm + (int64_t)lb * bc_row_stride, n0, N, cv);
+
+  const float uv = to_f32(u_raw);
+  const float v = to_f32(dt_raw) + (dt_bias ? bias_v : 0.0f);
+  const float delta = delta_softplus ? softplus(v) : v;
+  const float du = delta * uv;
   float part = 0.0f;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -94,8 +101,8 @@ __global__ void __launch_bounds__(256) ssm_step_kernel(
 #pragma unroll
   for (int m = NQ / 2; m >= 1; m /= 2) part += __shfl_xor(part, m, NQ);
   if (q == 0) {
-    float yv = fmaf(D_skip ? D_skip[ld] : 0.0f, uv, part);
-    if (z) yv *= silu(to_f32(z[(int64_t)lb * z_row_stride + d]));
+    float yv = fmaf(D_skip ? dskip_v : 0.0f, uv, part);
+    if (z) yv *= silu(to_f32(z_raw));
     y[ch] = from_f32<IO>(yv);
   }
 }
