@@ -58,46 +58,64 @@ __global__ void __launch_bounds__(kThreads) m3_siso_step_kernel(const M3StepArgs
   const int sub = wave * RPW + lane / LPR;
   const bool active = n0 < ds;
 
-  // the first passes' state rows, before anything else
+  // Every load of the head's prologue, then the first passes' state rows, before any value is
+  // used. No load carries a condition: indices are clamped into the tensors (a thread past
+  // d_state or headdim, a row past hd, the angle of a head with no angles read an in-bounds
+  // slot, or a stand-in address for an absent vector, and the value is dropped at the use).
+  // A load under a condition, or a use right after it, makes the wave wait right there; and
+  // since loads complete in order, the head's inputs go first, so that waiting for them does
+  // not wait for the state rows too.
+  const int o_dt = 2 * di + 2 * gs;
+  const int g = h / (nh / a.ng);
+  const int tds = min(tid, ds - 1), thd = min(tid, hd - 1);
+  const int ia = min(tds >> 1, max(na - 1, 0));  // this thread's angle pair (clamped)
+  const int64_t pb = ((int64_t)l * nh + h) * ds + tds;
+  const float r_dt = row[o_dt + h], r_a = row[o_dt + nh + h], r_lam = row[o_dt + 2 * nh + h];
+  const float r_dtb = a.dt_bias[(int64_t)l * nh + h];
+  const float r_b = row[2 * di + g * ds + tds], r_c = row[2 * di + gs + g * ds + tds];
+  const float r_kp = a.k_state[head * ds + tds];
+  const float r_x = row[di + h * hd + thd], r_vp = a.v_state[head * hd + thd], r_z = row[h * hd + thd];
+  const float r_bw = a.b_norm_w[(int64_t)l * ds + tds], r_cw = a.c_norm_w[(int64_t)l * ds + tds];
+  const float r_bb = a.b_bias[pb], r_cb = a.c_bias[pb];
+  float* const ang = a.angle + head * a.angle_stride + ia;
+  const float r_ang = *ang;
+  const float r_th = *(na > 0 ? row + o_dt + 3 * nh + ia : row + o_dt);
+  const float Dh = a.D[(int64_t)l * nh + h];
+  const float r_gw = *(a.gate_w ? a.gate_w + (int64_t)l * di + h * hd + thd : row);
+  const int n0c = active ? n0 : 0;
+  auto row_load = [&](int p) { return load_stream4(hs + (int64_t)min(p, hd - 1) * ds + n0c); };
   float4 hv[U];
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int p = sub + u * RPB;
-    hv[u] = active && p < hd ? load_stream4(hs + (int64_t)p * ds + n0)
-                             : make_float4(0.f, 0.f, 0.f, 0.f);
-  }
+  for (int u = 0; u < U; ++u) hv[u] = row_load(sub + u * RPB);
 
   __shared__ float s_braw[256], s_craw[256], s_k[256], s_q[256], s_kp[256];
   __shared__ float s_x[256], s_vp[256], s_y[256], s_red[8];
 
-  // F3: this head's scalars (every thread; the loads are uniform)
-  const int o_dt = 2 * di + 2 * gs;
-  const float dt = softplus(row[o_dt + h] + a.dt_bias[(int64_t)l * nh + h]);
-  const float A = -fmaxf(softplus(row[o_dt + nh + h]), a.a_floor);
-  const float lam = sigmoid(row[o_dt + 2 * nh + h]);
+  // F3: this head's scalars
+  const float dt = softplus(r_dt + r_dtb);
+  const float A = -fmaxf(softplus(r_a), a.a_floor);
+  const float lam = sigmoid(r_lam);
   const float alpha = fast_exp(dt * A);
   const float beta = (1.0f - lam) * dt * alpha, gamma = lam * dt;
 
   // F4: BC-norm of this head's group, then the head's bias
-  const int g = h / (nh / a.ng);
   float bv = 0.f, cv = 0.f;
   if (tid < ds) {
-    bv = row[2 * di + g * ds + tid];
-    cv = row[2 * di + gs + g * ds + tid];
-    s_kp[tid] = a.k_state[head * ds + tid];
+    bv = r_b;
+    cv = r_c;
+    s_kp[tid] = r_kp;
   }
   float zr = 0.f;
   if (tid < hd) {
-    s_x[tid] = row[di + h * hd + tid];
-    s_vp[tid] = a.v_state[head * hd + tid];
-    zr = row[h * hd + tid];
+    s_x[tid] = r_x;
+    s_vp[tid] = r_vp;
+    zr = r_z;
   }
   const float2 ss = block_sum2(bv * bv, cv * cv, s_red);
   if (tid < ds) {
     const float rb = rsqrtf(ss.x / ds + kNormEps), rc = rsqrtf(ss.y / ds + kNormEps);
-    const int64_t pb = ((int64_t)l * nh + h) * ds + tid;
-    s_braw[tid] = bv * rb * a.b_norm_w[(int64_t)l * ds + tid] + a.b_bias[pb];
-    s_craw[tid] = cv * rc * a.c_norm_w[(int64_t)l * ds + tid] + a.c_bias[pb];
+    s_braw[tid] = bv * rb * r_bw + r_bb;
+    s_craw[tid] = cv * rc * r_cw + r_cb;
   }
   __syncthreads();
   // F4: angle step and rotation of adjacent pairs; the K state takes the rotated B
@@ -105,8 +123,7 @@ __global__ void __launch_bounds__(kThreads) m3_siso_step_kernel(const M3StepArgs
     const int i = tid >> 1;
     float kb = s_braw[tid], qc = s_craw[tid];
     if (i < na) {
-      float* ang = a.angle + head * a.angle_stride + i;
-      const float theta = *ang + dt * row[o_dt + 3 * nh + i];
+      const float theta = r_ang + dt * r_th;
       float sn, cs;
       sincosf(theta, &sn, &cs);
       const float kb0 = s_braw[tid & ~1], kb1 = s_braw[tid | 1];
@@ -137,22 +154,18 @@ __global__ void __launch_bounds__(kThreads) m3_siso_step_kernel(const M3StepArgs
     xc[j] = in ? gamma * s_k[n] : 0.f;
     qv[j] = in ? s_q[n] : 0.f;
   }
-  const float Dh = a.D[(int64_t)l * nh + h];
 
   for (int p0 = 0; p0 < hd; p0 += U * RPB) {
     if (p0 > 0) {
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int p = p0 + sub + u * RPB;
-        hv[u] = active && p < hd ? load_stream4(hs + (int64_t)p * ds + n0)
-                                 : make_float4(0.f, 0.f, 0.f, 0.f);
-      }
+      for (int u = 0; u < U; ++u) hv[u] = row_load(p0 + sub + u * RPB);
     }
     float yp[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int p = p0 + sub + u * RPB;
       const bool on = active && p < hd;
+      if (!on) hv[u] = make_float4(0.f, 0.f, 0.f, 0.f);
       const float vp = on ? s_vp[p] : 0.f, xx = on ? s_x[p] : 0.f;
       float4 hn;
       hn.x = fmaf(alpha, hv[u].x, fmaf(kc[0], vp, xc[0] * xx));
@@ -178,7 +191,7 @@ __global__ void __launch_bounds__(kThreads) m3_siso_step_kernel(const M3StepArgs
   if (a.gate_w) {
     const float2 sg = block_sum2(gz * gz, 0.f, s_red);
     gz *= rsqrtf(sg.x / hd + kNormEps);
-    if (tid < hd) gz *= a.gate_w[(int64_t)l * di + h * hd + tid];
+    if (tid < hd) gz *= r_gw;
   }
   if (tid < hd) a.out[lb * di + h * hd + tid] = gz;
 }
