@@ -71,15 +71,27 @@ __global__ void __launch_bounds__(256) rmsnorm_rows_kernel(const float* __restri
   const float* xr = x + r * x_row_stride;
   float v[4][KMAX], wv[4][KMAX];
   float ss[4];
-  // the row and the weights are all loaded before the first use, so the wave waits once
+  // The row and the weights are all loaded before the first use, so the wave waits once; no
+  // load carries a condition (columns past Dm re-read the last column, an absent weight
+  // vector reads the row, and those values are replaced at the use), since a load under a
+  // condition makes the wave wait for it right there.
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) {
+      const int c = min(q * 64 + lane + 256 * k, Dm - 1);
+      v[q][k] = xr[c];
+      wv[q][k] = *(w ? w + c : xr + c);
+    }
+  }
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     ss[q] = 0.0f;
 #pragma unroll
     for (int k = 0; k < KMAX; ++k) {
-      const int c = q * 64 + lane + 256 * k;
-      v[q][k] = c < Dm ? xr[c] : 0.0f;
-      wv[q][k] = w && c < Dm ? w[c] : 1.0f;
+      const bool in = q * 64 + lane + 256 * k < Dm;
+      v[q][k] = in ? v[q][k] : 0.0f;
+      wv[q][k] = w && in ? wv[q][k] : 1.0f;
     }
   }
 #pragma unroll
@@ -1607,21 +1619,26 @@ __global__ void __launch_bounds__(256) decode_ssm_kernel(
   if (pre_w) {
 #pragma unroll
     for (int i = 0; i < kPreW; ++i)
-      wpre[i] = r0 + 4 * i < r1 ? *reinterpret_cast<const uint2*>(wr + r0 + 4 * i) : make_uint2(0, 0);
+      wpre[i] = *reinterpret_cast<const uint2*>(wr + min(r0 + 4 * i, R - 4));  // used only if inside the run
   }
   const int64_t ch = (int64_t)b * D + dc;
   float* hs = state + ch * N;
   const float* al = A_log + (int64_t)dc * N;
   const int n0 = 4 * q;
   const bool vec_state = VEC4 && N % 4 == 0;
+  // (no load under a condition: a lane past N reads the row's last four states and does not
+  // use them, absent vectors read a stand-in address; the values are selected at the use)
   float4 hv = make_float4(0.f, 0.f, 0.f, 0.f), av = hv;
-  if (vec_state && n0 < N) {
-    hv = *reinterpret_cast<const float4*>(hs + n0);
-    av = *reinterpret_cast<const float4*>(al + n0);
+  if (vec_state) {
+    const int nc = min(n0, N - 4);
+    hv = *reinterpret_cast<const float4*>(hs + nc);
+    av = *reinterpret_cast<const float4*>(al + nc);
   }
   const float uv = u[ch];
-  const float bias = dt_bias ? dt_bias[dc] : 0.0f;
-  const float dskip = D_skip ? D_skip[dc] : 0.0f;
+  const float bias_v = *(dt_bias ? dt_bias + dc : u + ch);
+  const float dskip_v = *(D_skip ? D_skip + dc : u + ch);
+  const float bias = dt_bias ? bias_v : 0.0f;
+  const float dskip = D_skip ? dskip_v : 0.0f;
 
   for (int i = threadIdx.x; i < R + 2 * N; i += 256) s_x[i] = xd.at(b, i);
   __syncthreads();
