@@ -96,6 +96,9 @@ def parse_args(argv=None):
     p.add_argument("--no-c3", action="store_true",
                    help="with --config c1, skip the second leg that also times the 2.8b-shaped "
                         "layer (c3) and reports it under the key c3")
+    p.add_argument("--no-c2", action="store_true",
+                   help="with --config c1, skip the leg that also times the batched decode step "
+                        "(c2) and reports it under the key c2")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="approximate CPU time budget for the oracle baseline")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
@@ -391,6 +394,24 @@ def second_leg_c3(args, W):
                                    unit=rl["unit"], frac=rl["frac"], call=rl["call"],
                                    avg_ms=rl["avg_ms"], hbm_achieved_gbs=rl["hbm_achieved_gbs"],
                                    hbm_frac=rl["hbm_frac"], traffic=rl["traffic"]))
+
+
+def second_leg_c2(args, W):
+    """The batched decode step (24 layers x B=64, d_inner=1536) timed after the default
+    workload, in the same process, with its own warm-up; reported beside `value`, never in
+    it."""
+    import torch
+
+    torch.cuda.empty_cache()
+    a = argparse.Namespace(**vars(args))
+    a.warmup = DEFAULT_WARMUP["c2"]
+    a.steps = min(args.steps, 200)
+    r, _ = bench_decode(a, W.C2)
+    torch.cuda.empty_cache()
+    return dict(workload=r["config"]["workload"], steps=a.steps, warmup=a.warmup,
+                warmup_run=r["warmup_run"], ms_per_step=r["ms_per_step"], value=r["value"],
+                unit=r["unit"], calls=r["calls"], layer_gbs=r["layer_gbs"],
+                layer_hbm_frac=r["layer_hbm_frac"], roofline=r["roofline"], cold=r["cold"])
 
 
 def cold_call_times(torch, fn, stream, reps=20, flush_bytes=512 << 20):
@@ -1072,9 +1093,11 @@ def main(argv=None):
         result, inp = bench_m3(args, shape)
     else:
         result, inp = bench_prefill(args, shape)
-    c3 = None
+    c3 = c2 = None
     if args.config == "c1" and not args.no_c3:
         c3 = second_leg_c3(args, W)
+    if args.config == "c1" and not args.no_c2:
+        c2 = second_leg_c2(args, W)
     cpu = None
     if not args.no_cpu_baseline and (inp is not None or args.config == "c2"):
         print("[bench] timing the CPU oracle baseline", file=sys.stderr, flush=True)
@@ -1099,6 +1122,8 @@ def main(argv=None):
             line[extra] = result[extra]
     if c3 is not None:
         line["c3"] = c3
+    if c2 is not None:
+        line["c2"] = c2
     print(json.dumps(line), flush=True)
 
 
