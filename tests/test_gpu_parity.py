@@ -398,6 +398,45 @@ def test_decode_step_equals_one_token_prefill():
     assert torch.equal(cs[0], pre["conv_state"])
 
 
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("softplus", [True, False])
+def test_decode_absent_optional_inputs(io, softplus):
+    """The decode step with the conv bias, dt bias, skip weight and gate all absent (NULL):
+    the fused call (the 4-tap kernel) equals the two calls bit for bit, and both match the
+    oracle run with the same inputs absent, at every step."""
+    _say(f"case decode with NULL conv_b/dt_bias/D_skip/z io={io} softplus={softplus}")
+    L, Bsz, D, N, K, steps = 2, 4, 96, 16, 4, 6
+    shape = W.DecodeShape("n", L=L, B=Bsz, D=D, N=N, K=K, steps=steps, io=io)
+    P = W.decode_params(shape, seed=3)
+    p = {k: dev(v) for k, v in P.items()}
+    iod = torch.bfloat16 if io == "bf16" else torch.float32
+    cs1, hs1 = torch.zeros(L, Bsz, D, K, device="cuda"), torch.zeros(L, Bsz, D, N, device="cuda")
+    cs2, hs2 = cs1.clone(), hs1.clone()
+    c_ref = [np.zeros((Bsz, D, K)) for _ in range(L)]
+    h_ref = [np.zeros((Bsz, D, N)) for _ in range(L)]
+    for t in range(steps):
+        i = W.decode_step_inputs(shape, t, seed=3)
+        x, dt, Bm, Cm = (dev(i[k], io) for k in ("x", "dt", "Bm", "Cm"))
+        y1 = torch.empty(L, Bsz, D, dtype=iod, device="cuda")
+        u1, y2, u2 = torch.empty_like(y1), torch.empty_like(y1), torch.empty_like(y1)
+        m.mamba_decode_step(x, p["conv_w"], None, cs1, dt, None, p["A_log"], Bm, Cm, None, None, hs1, y1,
+                            u=u1, delta_softplus=softplus)
+        m.mamba_conv1d_step(x, p["conv_w"], None, cs2, u2)
+        m.mamba_ssm_step(u2, dt, None, p["A_log"], Bm, Cm, None, None, hs2, y2, delta_softplus=softplus)
+        torch.cuda.synchronize()
+        assert torch.equal(y1, y2) and torch.equal(u1, u2), t
+        assert torch.equal(cs1, cs2) and torch.equal(hs1, hs2), t
+        for l in range(L):
+            u_ref, c_ref[l] = oracle.conv1d_step(i["x"][l], P["conv_w"][l], None, c_ref[l])
+            y_ref, h_ref[l] = oracle.ssm_step(u_ref, i["dt"][l], P["A_log"][l], i["Bm"][l], i["Cm"][l],
+                                              None, None, None, h_ref[l], delta_softplus=softplus)
+            assert rel_err(host(u1[l]), u_ref) <= tol(io), (t, l)
+            assert rel_err(host(y1[l]), y_ref) <= tol(io), (t, l)
+    for l in range(L):
+        assert rel_err(host(cs1[l]), c_ref[l]) <= tol(io)
+        assert rel_err(host(hs1[l]), h_ref[l]) <= tol(io)
+
+
 def test_decode_bf16_io():
     _say("case decode bf16 L2 B4 D64")
     shape = W.DecodeShape("db", L=2, B=4, D=64, N=16, K=4, steps=20, io="bf16")
