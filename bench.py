@@ -381,7 +381,7 @@ def second_leg_c3(args, W):
     torch.cuda.empty_cache()
     a = argparse.Namespace(**vars(args))
     a.warmup = DEFAULT_WARMUP["c3"]
-    a.steps = min(args.steps, 50)
+    a.steps = 50  # whatever --steps says: the leg's figure does not depend on the main line's K
     a.path = "auto"
     r, _ = bench_prefill(a, W.C3)
     torch.cuda.empty_cache()
@@ -399,13 +399,14 @@ def second_leg_c3(args, W):
 def second_leg_c2(args, W):
     """The batched decode step (24 layers x B=64, d_inner=1536) timed after the default
     workload, in the same process, with its own warm-up; reported beside `value`, never in
-    it."""
+    it. It always times 200 steps: a step is about 70 us of GPU work, so a handful of steps
+    would measure the host's enqueue of the first ones rather than the step."""
     import torch
 
     torch.cuda.empty_cache()
     a = argparse.Namespace(**vars(args))
     a.warmup = DEFAULT_WARMUP["c2"]
-    a.steps = min(args.steps, 200)
+    a.steps = 200
     r, _ = bench_decode(a, W.C2)
     torch.cuda.empty_cache()
     return dict(workload=r["config"]["workload"], steps=a.steps, warmup=a.warmup,
