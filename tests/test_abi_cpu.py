@@ -94,6 +94,14 @@ def test_workspace_size_formula():
     assert m.mamba_selective_scan_workspace_size(1, 32, 64, 16) >= 0
     assert m.mamba_selective_scan_workspace_size(8, 4096, 5120, 16) % 256 == 0
     assert m.mamba_selective_scan_workspace_size(0, 32, 64, 16) == 0
+    # a long sequence over few channels: the chunk count stops at its cap of 64 (longer chunks
+    # instead), so the workspace is 64 chunk sums and end states per channel, the carried SSM
+    # state and the carried conv state (8 slots), each rounded up to 256 bytes
+    def capped(B, D, N, chunks=64):
+        a = lambda n: (n + 255) // 256 * 256
+        return a(4 * B * chunks * D) + a(4 * B * chunks * D * N) + a(4 * B * N * D) + a(4 * B * D * 8)
+    assert m.mamba_selective_scan_workspace_size(1, 8192, 32, 16) == capped(1, 32, 16)
+    assert m.mamba_selective_scan_workspace_size(1, 32768, 64, 16) == capped(1, 64, 16)
 
 
 def test_conv_validation():

@@ -96,6 +96,8 @@ RAGGED = [
     (1, 4096, 64, 16, 4, "f32"),
     (1, 4096, 64, 16, 4, "bf16"),
     (1, 2048, 64, 64, 4, "f32"),
+    # the chunk-count cap: 64 chunks of 128 tokens (63 predecessor maps for the last chunk)
+    (1, 8192, 32, 16, 4, "f32"),
 ]
 
 
