@@ -318,10 +318,12 @@ def _decode_run(shape: W.DecodeShape, steps: int, seed=0, fused=False):
 
 
 @pytest.mark.parametrize("fused", [False, True])
-@pytest.mark.parametrize("N,Bsz", [(16, 3), (12, 4), (24, 3)])
+@pytest.mark.parametrize("N,Bsz", [(16, 3), (12, 4), (24, 3), (4, 2), (5, 3), (64, 2)])
 def test_decode_steps_small_full_check(fused, N, Bsz):
     """Every step checked against the oracle; d_state 12 and 24 are multiples of 4 whose lane
-    count per channel (3, 6) rounds up, so some lanes hold no state."""
+    count per channel (3, 6) rounds up, so some lanes hold no state; 4 is one lane per
+    channel, 5 is not a multiple of 4 (element-wise state rows, the last lane part-filled),
+    and 64 is the widest case (16 lanes per channel)."""
     _say(f"case decode L2 B{Bsz} D100 N{N} 30 steps fused={fused}")
     shape = W.DecodeShape("d", L=2, B=Bsz, D=100, N=N, K=4, steps=30)
     P, ins, ys, us, cs, hs = _decode_run(shape, 30, fused=fused)
